@@ -1,0 +1,257 @@
+"""Seeded synthetic inputs for the MoE layer (shared by the tests, the oracle
+checks and the benchmark).
+
+This module holds none of the layer's arithmetic: it only draws inputs.  It is
+the one piece of code both the oracle and the HIP path are fed from.
+
+Workloads (shapes and distributions follow the stated configurations; the
+pages give no layer shapes, so d_model=7168 / d_ff=2048 are assumed):
+
+* ``tiny``            T=8,     d=256,  E=16,  top-2,  d_ff=128,  1 shared
+* ``decode1``         T=1,     d=7168, E=896, top-16, d_ff=2048, 2 shared
+* ``decode256``       T=256,   same layer
+* ``prefill8k``       T=8192,  same layer
+* ``prefill32k_skew`` T=32768, same layer + Zipf(s=1.1) router bias
+
+Recipes
+-------
+x      : N(0, 1) drawn in float32 (numpy PCG64, seed sequence [seed, 1]),
+         rounded to bf16 with round-to-nearest-even.
+W_r    : N(0, 0.02) float32 (seed sequence [seed, 2]).
+bias   : zero, or for the skewed workload b_e = fp32(1.5 * ln p_e) with
+         p_e = (e+1)^-1.1 / sum_r r^-1.1 (expert 0 hottest).
+experts: MXFP4 bytes drawn directly by a counter-based generator (Philox4x64-10,
+         Salmon et al., SC'11), so that any expert can be regenerated alone and
+         the GPU can generate the 21 GB layer itself bit-identically.  Each E2M1
+         element takes one random byte: bit 7 is the sign, bits 0-6 pick the
+         magnitude code from 128 equiprobable slots (10, 20, 19, 16, 20, 18, 16,
+         9 slots for codes 0..7 -- the code frequencies of N(0, 1/sqrt(d))
+         blocks quantised to MXFP4).  Each block scale is 127 + e with
+         e = floor(log2(1/sqrt(d))) - 1 + delta, delta = 1 with probability 1/4
+         (one random byte per block, its low 3 bits >= 6), else 0.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Optional, Tuple
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Workload configurations
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    tokens: int
+    d_model: int
+    num_experts: int
+    top_k: int
+    d_ff: int
+    num_shared: int
+    zipf_bias: bool = False
+    seed: int = 0
+
+    def with_tokens(self, t: int) -> "LayerConfig":
+        return replace(self, tokens=t)
+
+
+CONFIGS = {
+    "tiny": LayerConfig("tiny", 8, 256, 16, 2, 128, 1),
+    "decode1": LayerConfig("decode1", 1, 7168, 896, 16, 2048, 2),
+    "decode256": LayerConfig("decode256", 256, 7168, 896, 16, 2048, 2),
+    "prefill8k": LayerConfig("prefill8k", 8192, 7168, 896, 16, 2048, 2),
+    "prefill32k_skew": LayerConfig("prefill32k_skew", 32768, 7168, 896, 16, 2048, 2, zipf_bias=True),
+}
+
+# ---------------------------------------------------------------------------
+# Dense inputs
+# ---------------------------------------------------------------------------
+
+
+def f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round-to-nearest-even (finite inputs)."""
+    u = np.ascontiguousarray(v, dtype=np.float32).view(np.uint32)
+    r = (u + (np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1)))) >> 16
+    return r.astype(np.uint16)
+
+
+def gen_x(cfg: LayerConfig, tokens: Optional[int] = None, layer: int = 0) -> np.ndarray:
+    """Activations [T, d] as bf16 bit patterns (uint16)."""
+    t = cfg.tokens if tokens is None else tokens
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 1, layer])))
+    return f32_to_bf16_bits(rng.standard_normal((t, cfg.d_model), dtype=np.float32))
+
+
+def gen_router_w(cfg: LayerConfig, layer: int = 0) -> np.ndarray:
+    """Router weight [E, d] float32, N(0, 0.02)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 2, layer])))
+    return rng.standard_normal((cfg.num_experts, cfg.d_model), dtype=np.float32) * np.float32(0.02)
+
+
+def gen_router_b(cfg: LayerConfig) -> Optional[np.ndarray]:
+    """Router bias [E] float32, or None (zero bias)."""
+    if not cfg.zipf_bias:
+        return None
+    ranks = np.arange(1, cfg.num_experts + 1, dtype=np.float64)
+    pmf = ranks ** -1.1
+    pmf /= pmf.sum()
+    return (1.5 * np.log(pmf)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Philox4x64-10 (Salmon, Moraes, Dror, Shaw: "Parallel random numbers: as easy
+# as 1, 2, 3", SC'11).  Counter-based: output = f(key, counter).
+# ---------------------------------------------------------------------------
+
+PHILOX_M0 = 0xD2E7470EE14C6C93
+PHILOX_M1 = 0xCA5A826395121157
+PHILOX_W0 = 0x9E3779B97F4A7C15
+PHILOX_W1 = 0xBB67AE8584CAA73B
+_MASK32 = np.uint64(0xFFFFFFFF)
+_S32 = np.uint64(32)
+
+
+def _mulhilo64(a_const: int, b: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(hi, lo) 64-bit halves of the 128-bit product a_const * b (uint64 arrays)."""
+    a_lo = np.uint64(a_const & 0xFFFFFFFF)
+    a_hi = np.uint64(a_const >> 32)
+    b_lo = b & _MASK32
+    b_hi = b >> _S32
+    p0 = a_lo * b_lo
+    p1 = a_lo * b_hi
+    p2 = a_hi * b_lo
+    p3 = a_hi * b_hi
+    mid = (p0 >> _S32) + (p1 & _MASK32) + (p2 & _MASK32)
+    hi = p3 + (p1 >> _S32) + (p2 >> _S32) + (mid >> _S32)
+    lo = b * np.uint64(a_const)  # wraps modulo 2**64
+    return hi, lo
+
+
+def philox4x64_10(key: Tuple[int, int], c0: np.ndarray, c1=0, c2=0, c3=0) -> np.ndarray:
+    """Philox4x64 with 10 rounds.  c0: uint64 array of counters (word 0); the
+    other counter words are scalars.  Returns [n, 4] uint64."""
+    with np.errstate(over="ignore"):
+        c0 = np.asarray(c0, dtype=np.uint64)
+        x0 = c0.copy()
+        x1 = np.full_like(c0, np.uint64(c1))
+        x2 = np.full_like(c0, np.uint64(c2))
+        x3 = np.full_like(c0, np.uint64(c3))
+        k0, k1 = int(key[0]) & 0xFFFFFFFFFFFFFFFF, int(key[1]) & 0xFFFFFFFFFFFFFFFF
+        for r in range(10):
+            if r:
+                k0 = (k0 + PHILOX_W0) & 0xFFFFFFFFFFFFFFFF
+                k1 = (k1 + PHILOX_W1) & 0xFFFFFFFFFFFFFFFF
+            hi0, lo0 = _mulhilo64(PHILOX_M0, x0)
+            hi1, lo1 = _mulhilo64(PHILOX_M1, x2)
+            x0, x1, x2, x3 = hi1 ^ x1 ^ np.uint64(k0), lo1, hi0 ^ x3 ^ np.uint64(k1), lo0
+    return np.stack([x0, x1, x2, x3], axis=-1)
+
+
+def philox_bytes(key: Tuple[int, int], first: int, count: int, c1: int = 0) -> np.ndarray:
+    """32 bytes per counter value, for counters first..first+count-1:
+    [count, 32] uint8, byte j of a call = byte j%8 (little-endian) of word j/8."""
+    ctr = np.arange(first, first + count, dtype=np.uint64)
+    words = philox4x64_10(key, ctr, c1)
+    return words.astype("<u8").view(np.uint8).reshape(count, 32)
+
+
+# ---------------------------------------------------------------------------
+# Direct MXFP4 weight generation
+# ---------------------------------------------------------------------------
+
+# slots (out of 128) per E2M1 magnitude code 0..7
+MAG_SLOTS = (10, 20, 19, 16, 20, 18, 16, 9)
+MAG_TABLE = np.repeat(np.arange(8, dtype=np.uint8), MAG_SLOTS)
+assert MAG_TABLE.size == 128
+# block-scale exponent offset from the low 3 bits of a random byte
+DELTA_TABLE = np.array([0, 0, 0, 0, 0, 0, 1, 1], dtype=np.int64)
+
+KIND_GU_CODES, KIND_GU_SCALES, KIND_DN_CODES, KIND_DN_SCALES = 1, 2, 3, 4
+SHARED_BASE = 0x10000
+
+
+def scale_exponent_base(d_model: int) -> int:
+    """floor(log2(1/sqrt(d))) - 1, in integers: -(smallest n with 4**n >= d) - 1."""
+    n = 0
+    while 4 ** n < d_model:
+        n += 1
+    return -n - 1
+
+
+def stream_id(kind: int, expert_slot: int, layer: int = 0) -> int:
+    return (layer << 48) | (kind << 32) | expert_slot
+
+
+def expert_slot(kind: str, index: int) -> int:
+    return index if kind == "routed" else SHARED_BASE + index
+
+
+def gen_mx_matrix(seed: int, code_stream: int, scale_stream: int, rows: int, k: int,
+                  e_base: int, row0: int = 0, nrows: Optional[int] = None):
+    """Rows [row0, row0+nrows) of one MXFP4 matrix [rows, k]:
+    (packed codes [n, k/2] uint8, scales [n, k/32] uint8)."""
+    n = rows - row0 if nrows is None else nrows
+    nb = k // 32
+    b0 = row0 * nb
+    nblk = n * nb
+    # element codes: one Philox call per block of 32 elements
+    rb = philox_bytes((seed, code_stream), b0, nblk)  # [nblk, 32]
+    codes = MAG_TABLE[rb & 0x7F] | ((rb >> 7) << 3)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8).reshape(n, k // 2)
+    # scales: one Philox call per 32 blocks
+    c_first = b0 // 32
+    c_last = (b0 + nblk - 1) // 32
+    sb = philox_bytes((seed, scale_stream), c_first, c_last - c_first + 1).reshape(-1)
+    sb = sb[b0 - c_first * 32: b0 - c_first * 32 + nblk]
+    scales = (127 + e_base + DELTA_TABLE[sb & 7]).astype(np.uint8).reshape(n, nb)
+    return packed, scales
+
+
+def gen_expert(cfg: LayerConfig, kind: str, index: int, layer: int = 0):
+    """(gu_codes [2 d_ff, d/2], gu_scales [2 d_ff, d/32],
+        dn_codes [d, d_ff/2],   dn_scales [d, d_ff/32]) of one expert."""
+    slot = expert_slot(kind, index)
+    eb = scale_exponent_base(cfg.d_model)
+    guc, gus = gen_mx_matrix(cfg.seed, stream_id(KIND_GU_CODES, slot, layer),
+                             stream_id(KIND_GU_SCALES, slot, layer), 2 * cfg.d_ff, cfg.d_model, eb)
+    dnc, dns = gen_mx_matrix(cfg.seed, stream_id(KIND_DN_CODES, slot, layer),
+                             stream_id(KIND_DN_SCALES, slot, layer), cfg.d_model, cfg.d_ff, eb)
+    return guc, gus, dnc, dns
+
+
+class ExpertWeights:
+    """Lazily generated, cached per-expert weights: callable as weights(kind, i)."""
+
+    def __init__(self, cfg: LayerConfig, layer: int = 0, cache: bool = True):
+        self.cfg, self.layer, self.cache = cfg, layer, cache
+        self._c = {}
+
+    def __call__(self, kind: str, index: int):
+        key = (kind, index)
+        if key in self._c:
+            return self._c[key]
+        w = gen_expert(self.cfg, kind, index, self.layer)
+        if self.cache:
+            self._c[key] = w
+        return w
+
+    def stacked(self):
+        """All routed and shared experts stacked (small configs only)."""
+        e, s = self.cfg.num_experts, self.cfg.num_shared
+        r = [self("routed", i) for i in range(e)]
+        sh = [self("shared", i) for i in range(s)]
+        stack = lambda lst, j: np.stack([w[j] for w in lst]) if lst else None
+        return ([stack(r, j) for j in range(4)], [stack(sh, j) for j in range(4)])
+
+
+def matrix_bytes(rows: int, k: int) -> int:
+    return rows * k // 2 + rows * k // 32
+
+
+def expert_bytes(cfg: LayerConfig) -> int:
+    return matrix_bytes(2 * cfg.d_ff, cfg.d_model) + matrix_bytes(cfg.d_model, cfg.d_ff)
+

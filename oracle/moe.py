@@ -1,0 +1,276 @@
+"""The sparse MoE layer, step by step, in float64 (oracle).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.
+
+Structure from the pages ("Kimi K3 Tech Intro", section 4.3 "MXFP4 MoE +
+SiTU"): input token -> router (top-16) -> routed experts + shared expert(s);
+16 of 896 routed experts per token ("Kimi K3 Tech Intro", section 1 table;
+"K3部署推理引擎指南", Stable LatentMoE paragraph) and 2 shared experts
+("Kimi K3本地部署指南", section 1 spec table); MXFP4 expert weights with MXFP8
+activations ("Kimi K3 ... MoE推理系统工程分析").  The pages leave the router's
+score function, the activation (SiTU is named, not defined) and the combine
+rule open; the readings taken are:
+
+* logits l = x W_r^T + b (x bf16, W_r and b fp32), selection on l, ties to the
+  lower expert index, ids reported in ascending order;
+* weights w = sigmoid(l) / sum of sigmoid(l) over the selected experts;
+* expert MLP: [g | u] = A W_gu^T, h = silu(g) * u (SwiGLU standing in for SiTU),
+  h re-quantised to MXFP8 along d_ff, o = h W_dn^T; A is x quantised to MXFP8;
+* y = sum_j w[t, j] o_j + sum_s o_s (shared experts unweighted).
+
+Everything runs in float64 on exactly decoded MX values.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Callable, Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import mx
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 (exact: bf16 is the top half of fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(v) -> np.ndarray:
+    """float64 -> bf16 bit patterns, round-to-nearest-even on the bf16 grid.
+
+    Done in exact arithmetic: split |v| into binary exponent and a 53-bit
+    significand, keep 8 significant bits with ties to even.  Finite inputs only.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    assert np.all(np.isfinite(v))
+    out = np.zeros(v.shape, dtype=np.uint16)
+    a = np.abs(v)
+    nz = a > 0
+    m, ex = np.frexp(a)  # a = m * 2**ex, m in [0.5, 1)
+    # bf16 normal: 8 significant bits; below 2**-126 the grid step is 2**-133
+    step_exp = np.maximum(ex - 8, -133)
+    q = a / np.exp2(step_exp)  # exact (power-of-two scaling)
+    r = np.floor(q)
+    frac = q - r
+    r = r + ((frac > 0.5) | ((frac == 0.5) & (np.fmod(r, 2) == 1)))
+    val = r * np.exp2(step_exp)  # the rounded magnitude, exact
+    f32 = val.astype(np.float32)  # exactly representable -> exact cast
+    bits = (f32.view(np.uint32) >> 16).astype(np.uint16)
+    out[nz] = bits[nz]
+    out = out | np.where(np.signbit(v), 0x8000, 0).astype(np.uint16)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Router
+# --------------------------------------------------------------------------
+
+
+def router_logits(x_bf16, w_r, b=None) -> np.ndarray:
+    """l[t, e] = sum_i x[t, i] * W_r[e, i] + b[e], float64.
+
+    Products of a bf16 and an fp32 value are exact in float64, so the only
+    rounding is the float64 summation.
+    """
+    x = bf16_to_f64(x_bf16)
+    w = np.asarray(w_r, dtype=np.float32).astype(np.float64)
+    l = x @ w.T
+    if b is not None:
+        l = l + np.asarray(b, dtype=np.float32).astype(np.float64)[None, :]
+    return l
+
+
+def topk_select(logits, k: int):
+    """Per row: the k experts with the largest logits (ties -> lower index).
+
+    Returns (ids ascending [T, k] int32, gap [T]) where gap is the difference
+    between the k-th and (k+1)-th largest logits (inf when k == E): tokens whose
+    gap is tiny are the ones where a different but equally valid set may come
+    out of a lower-precision computation.
+    """
+    l = np.asarray(logits, dtype=np.float64)
+    t_count, e_count = l.shape
+    ids = np.zeros((t_count, k), dtype=np.int32)
+    gap = np.full(t_count, np.inf)
+    idx = np.arange(e_count)
+    for t in range(t_count):
+        order = np.lexsort((idx, -l[t]))  # primary: logit desc, then index asc
+        ids[t] = np.sort(order[:k])
+        if k < e_count:
+            gap[t] = l[t, order[k - 1]] - l[t, order[k]]
+    return ids, gap
+
+
+def sigmoid(v):
+    v = np.asarray(v, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-v))
+
+
+def routing_weights(logits, ids) -> np.ndarray:
+    """w[t, j] = sigmoid(l[t, ids[t, j]]) / sum_j' sigmoid(l[t, ids[t, j']])."""
+    sel = np.take_along_axis(np.asarray(logits, np.float64), np.asarray(ids, np.int64), axis=1)
+    s = sigmoid(sel)
+    return s / s.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Permutation
+# --------------------------------------------------------------------------
+
+
+def permute(ids, num_experts: int):
+    """Expert-contiguous order of the (token, slot) pairs.
+
+    Pairs are sorted by (expert ascending, token ascending); pair p = t*k + j.
+    Returns counts [E], offsets [E+1], row_src [T*k] (pair index of each
+    permuted row) and token_row [T, k] (permuted row of each pair).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    t_count, k = ids.shape
+    pair_expert = ids.reshape(-1)
+    pair_token = np.repeat(np.arange(t_count), k)
+    key = pair_expert * t_count + pair_token
+    row_src = np.argsort(key, kind="stable").astype(np.int32)
+    counts = np.bincount(pair_expert, minlength=num_experts).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    token_row = np.empty(t_count * k, dtype=np.int32)
+    token_row[row_src] = np.arange(t_count * k, dtype=np.int32)
+    return counts, offsets, row_src, token_row.reshape(t_count, k)
+
+
+# --------------------------------------------------------------------------
+# Experts
+# --------------------------------------------------------------------------
+
+
+def silu(g):
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def expert_mlp(a_codes, a_scales, gu_codes, gu_scales, dn_codes, dn_scales, d_ff: int):
+    """One expert on a set of MXFP8 rows.
+
+    A = decoded MXFP8 rows [n, d]; [g | u] = A W_gu^T with W_gu [2 d_ff, d]
+    (rows [0, d_ff) gate, [d_ff, 2 d_ff) up); h = silu(g) * u; h quantised to
+    MXFP8 along d_ff; o = dec(h_q) W_dn^T with W_dn [d, d_ff].
+    Returns (h_codes [n, d_ff], h_scales [n, d_ff/32], o [n, d] float64).
+    """
+    a = mx.mx_decode(a_codes, a_scales, "e4m3")
+    wgu = mx.mx_decode(gu_codes, gu_scales, "e2m1")
+    gu = a @ wgu.T
+    del wgu
+    g, u = gu[:, :d_ff], gu[:, d_ff:]
+    h = silu(g) * u
+    h_codes, h_scales = mx.mx_quantize(h, "e4m3")
+    hq = mx.mx_decode(h_codes, h_scales, "e4m3")
+    wdn = mx.mx_decode(dn_codes, dn_scales, "e2m1")
+    o = hq @ wdn.T
+    return h_codes, h_scales, o
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+
+# weights(kind, index) -> (gu_codes, gu_scales, dn_codes, dn_scales) of routed
+# expert `index` (kind "routed") or shared expert `index` (kind "shared")
+WeightSource = Callable[[str, int], Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]]
+
+
+@dataclass
+class LayerResult:
+    logits: np.ndarray
+    gap: np.ndarray
+    topk_ids: np.ndarray
+    topk_w: np.ndarray
+    counts: np.ndarray
+    offsets: np.ndarray
+    row_src: np.ndarray
+    token_row: np.ndarray
+    x_codes: np.ndarray
+    x_scales: np.ndarray
+    tokens: np.ndarray  # tokens whose outputs below were computed
+    y_routed: np.ndarray  # [len(tokens), d] float64
+    y_shared: np.ndarray
+    y: np.ndarray
+    # h in permuted-row order for the computed tokens: {row: (codes, scales)}
+    h_rows: Dict[int, Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict)
+    # shared-expert h for the computed tokens: {(s, t): (codes, scales)}
+    h_shared: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict)
+
+
+def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: int,
+            num_shared: int, d_ff: int, tokens: Optional[Sequence[int]] = None) -> LayerResult:
+    """Full layer.  Routing, permutation and the MXFP8 quantisation of x are
+    computed for every token; expert outputs only for ``tokens`` (all when
+    None).  Each token's output depends only on its own row, so a subset gives
+    exactly the rows the full computation would.  Experts are visited one at a
+    time so the decoded float64 weights of only one expert are live.
+    """
+    x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
+    t_count, d = x_bf16.shape
+    logits = router_logits(x_bf16, w_r, b)
+    ids, gap = topk_select(logits, top_k)
+    w = routing_weights(logits, ids)
+    counts, offsets, row_src, token_row = permute(ids, num_experts)
+    x_codes, x_scales = mx.mx_quantize(bf16_to_f64(x_bf16), "e4m3")
+
+    toks = np.arange(t_count) if tokens is None else np.asarray(sorted(set(int(t) for t in tokens)))
+    pos = {int(t): i for i, t in enumerate(toks)}
+    y_routed = np.zeros((len(toks), d))
+    y_shared = np.zeros((len(toks), d))
+    res_h: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
+    res_hs: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]] = {}
+
+    want = np.zeros(t_count, dtype=bool)
+    want[toks] = True
+    for e in range(num_experts):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        rows = rows[want[row_src[rows] // top_k]]
+        if rows.size == 0:
+            continue
+        pairs = row_src[rows]
+        tk = pairs // top_k
+        jj = pairs % top_k
+        h_c, h_s, o = expert_mlp(x_codes[tk], x_scales[tk], *weights("routed", e), d_ff=d_ff)
+        for i in range(rows.size):
+            res_h[int(rows[i])] = (h_c[i], h_s[i])
+            y_routed[pos[int(tk[i])]] += w[tk[i], jj[i]] * o[i]
+    for s in range(num_shared):
+        h_c, h_s, o = expert_mlp(x_codes[toks], x_scales[toks], *weights("shared", s), d_ff=d_ff)
+        for i, t in enumerate(toks):
+            res_hs[(s, int(t))] = (h_c[i], h_s[i])
+        y_shared += o
+    return LayerResult(logits=logits, gap=gap, topk_ids=ids, topk_w=w, counts=counts,
+                       offsets=offsets, row_src=row_src, token_row=token_row,
+                       x_codes=x_codes, x_scales=x_scales, tokens=toks,
+                       y_routed=y_routed, y_shared=y_shared, y=y_routed + y_shared,
+                       h_rows=res_h, h_shared=res_hs)
+
+
+def forward_dense(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: int,
+                  num_shared: int, d_ff: int) -> np.ndarray:
+    """The same layer computed densely: every expert on every token, scaled by a
+    full [T, E] weight matrix that is zero for unselected experts.  Used only to
+    pin :func:`forward` (sparse gather/scatter) against a computation that has
+    no permutation at all.
+    """
+    x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
+    t_count, d = x_bf16.shape
+    logits = router_logits(x_bf16, w_r, b)
+    ids, _ = topk_select(logits, top_k)
+    w = routing_weights(logits, ids)
+    dense_w = np.zeros((t_count, num_experts))
+    np.put_along_axis(dense_w, ids.astype(np.int64), w, axis=1)
+    x_codes, x_scales = mx.mx_quantize(bf16_to_f64(x_bf16), "e4m3")
+    y = np.zeros((t_count, d))
+    for e in range(num_experts):
+        _, _, o = expert_mlp(x_codes, x_scales, *weights("routed", e), d_ff=d_ff)
+        y += dense_w[:, e:e + 1] * o
+    for s in range(num_shared):
+        _, _, o = expert_mlp(x_codes, x_scales, *weights("shared", s), d_ff=d_ff)
+        y += o
+    return y

@@ -1,0 +1,160 @@
+"""Pins for the oracle's router, permutation, expert MLP and combine (CPU only).
+
+* top-k against a brute-force search over every k-subset;
+* routing weights against torch's softmax of log-sigmoid (a different route
+  to sigmoid(l)/sum sigmoid(l));
+* the permutation against a plain loop over experts and tokens, plus its
+  invariants;
+* the sparse layer against a dense all-experts masked computation;
+* E=1, k=1, no shared expert against a textbook SwiGLU MLP in torch float64
+  with torch's float8 cast doing the MXFP8 element rounding of h.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from mxfp4_expert_grouped_amd import inputs as I
+from oracle import moe, mx
+
+
+def test_topk_matches_subset_brute_force_tiny():
+    cfg = I.CONFIGS["tiny"]
+    x = I.gen_x(cfg)
+    logits = moe.router_logits(x, I.gen_router_w(cfg), I.gen_router_b(cfg))
+    ids, gap = moe.topk_select(logits, cfg.top_k)
+    for t in range(cfg.tokens):
+        best = max(itertools.combinations(range(cfg.num_experts), cfg.top_k),
+                   key=lambda s: (sum(logits[t, list(s)]), [-i for i in s]))
+        assert tuple(ids[t]) == best
+        srt = np.sort(logits[t])[::-1]
+        assert gap[t] == srt[cfg.top_k - 1] - srt[cfg.top_k]
+
+
+def test_topk_ties_go_to_lower_index():
+    l = np.array([[2.0, 1.0, 1.0, 0.0, 1.0], [0.5, 0.5, 0.5, 0.5, 0.5]])
+    ids, gap = moe.topk_select(l, 2)
+    assert ids.tolist() == [[0, 1], [0, 1]]
+    assert gap.tolist() == [0.0, 0.0]
+    # brute force: among max-sum subsets, the lexicographically smallest
+    for t in range(2):
+        subs = list(itertools.combinations(range(5), 2))
+        m = max(sum(l[t, list(s)]) for s in subs)
+        assert tuple(ids[t]) == min(s for s in subs if sum(l[t, list(s)]) == m)
+
+
+def test_topk_random_against_full_sort():
+    rng = np.random.default_rng(7)
+    l = rng.standard_normal((50, 896))
+    ids, _ = moe.topk_select(l, 16)
+    for t in range(50):
+        assert set(ids[t]) == set(np.argsort(-l[t], kind="stable")[:16])
+        assert np.all(np.diff(ids[t]) > 0)
+
+
+def test_routing_weights_library_and_invariants():
+    rng = np.random.default_rng(8)
+    l = rng.standard_normal((20, 64)) * 2
+    ids, _ = moe.topk_select(l, 16)
+    w = moe.routing_weights(l, ids)
+    sel = torch.from_numpy(np.take_along_axis(l, ids.astype(np.int64), 1))
+    ref = torch.softmax(torch.nn.functional.logsigmoid(sel), dim=1).numpy()
+    assert np.allclose(w, ref, rtol=1e-13, atol=0)
+    assert np.all(np.abs(w.sum(1) - 1) <= 1e-12) and np.all(w > 0)
+    # equal logits -> equal weights 1/k
+    assert np.allclose(moe.routing_weights(np.zeros((1, 8)), np.arange(4)[None]), 0.25)
+
+
+def test_router_logits_exact_products():
+    # small integers: the float64 sum is exact, so it must equal an integer matmul
+    rng = np.random.default_rng(9)
+    xi = rng.integers(-4, 5, size=(3, 64))
+    wi = rng.integers(-4, 5, size=(5, 64))
+    x_bits = I.f32_to_bf16_bits(xi.astype(np.float32))
+    l = moe.router_logits(x_bits, wi.astype(np.float32), np.arange(5, dtype=np.float32))
+    assert np.array_equal(l, (xi @ wi.T + np.arange(5)).astype(np.float64))
+
+
+def test_permute_against_loop_and_invariants():
+    rng = np.random.default_rng(10)
+    t_count, e_count, k = 37, 11, 3
+    ids = np.stack([np.sort(rng.choice(e_count, k, replace=False)) for _ in range(t_count)])
+    counts, offsets, row_src, token_row = moe.permute(ids, e_count)
+    order = []
+    for e in range(e_count):
+        for t in range(t_count):
+            for j in range(k):
+                if ids[t, j] == e:
+                    order.append(t * k + j)
+    assert row_src.tolist() == order
+    assert counts.sum() == t_count * k and offsets[0] == 0 and offsets[-1] == t_count * k
+    assert np.all(np.diff(offsets) == counts)
+    assert sorted(row_src.tolist()) == list(range(t_count * k))
+    for t in range(t_count):
+        for j in range(k):
+            r = token_row[t, j]
+            assert row_src[r] == t * k + j
+            assert offsets[ids[t, j]] <= r < offsets[ids[t, j] + 1]
+
+
+def test_sparse_equals_dense_tiny():
+    cfg = I.CONFIGS["tiny"]
+    x, wr, b = I.gen_x(cfg), I.gen_router_w(cfg), I.gen_router_b(cfg)
+    W = I.ExpertWeights(cfg)
+    kw = dict(num_experts=cfg.num_experts, top_k=cfg.top_k, num_shared=cfg.num_shared, d_ff=cfg.d_ff)
+    res = moe.forward(x, wr, b, W, **kw)
+    dense = moe.forward_dense(x, wr, b, W, **kw)
+    rel = np.linalg.norm(res.y - dense) / np.linalg.norm(dense)
+    assert rel <= 1e-12
+    assert np.linalg.norm(res.y_routed) > 0 and np.linalg.norm(res.y_shared) > 0
+
+
+def test_sparse_equals_dense_with_bias_and_subset():
+    cfg = I.LayerConfig("t2", 12, 128, 24, 4, 64, 2, zipf_bias=True, seed=3)
+    x, wr, b = I.gen_x(cfg), I.gen_router_w(cfg), I.gen_router_b(cfg)
+    W = I.ExpertWeights(cfg)
+    kw = dict(num_experts=cfg.num_experts, top_k=cfg.top_k, num_shared=cfg.num_shared, d_ff=cfg.d_ff)
+    dense = moe.forward_dense(x, wr, b, W, **kw)
+    sub = moe.forward(x, wr, b, W, tokens=[5, 2, 11], **kw)
+    assert sub.tokens.tolist() == [2, 5, 11]
+    assert np.allclose(sub.y, dense[[2, 5, 11]], rtol=1e-12, atol=1e-14 * np.abs(dense).max())
+
+
+def _torch_mx8_roundtrip(h: torch.Tensor) -> torch.Tensor:
+    """Independent MXFP8 fake-quant of h along its last axis with torch ops."""
+    blocks = h.reshape(h.shape[0], -1, 32)
+    amax = blocks.abs().amax(dim=2, keepdim=True)
+    _, ex = torch.frexp(amax)
+    e = torch.clamp(ex.to(torch.int64) - 1 - 8, -127, 127).to(torch.float64)
+    scale = torch.pow(2.0, e)
+    q = (blocks / scale).clamp(-448, 448).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64)
+    return (q * scale).reshape(h.shape)
+
+
+def test_single_expert_is_textbook_swiglu_mlp():
+    cfg = I.LayerConfig("one", 4, 128, 1, 1, 64, 0, seed=5)
+    x, wr = I.gen_x(cfg), I.gen_router_w(cfg)
+    W = I.ExpertWeights(cfg)
+    res = moe.forward(x, wr, None, W, num_experts=1, top_k=1, num_shared=0, d_ff=cfg.d_ff)
+    assert np.all(res.topk_w == 1.0)
+    guc, gus, dnc, dns = W("routed", 0)
+    xt = torch.from_numpy(moe.bf16_to_f64(x))
+    a = _torch_mx8_roundtrip(xt)
+    wgu = torch.from_numpy(mx.mx_decode(guc, gus, "e2m1"))
+    wdn = torch.from_numpy(mx.mx_decode(dnc, dns, "e2m1"))
+    g = a @ wgu[:64].T
+    u = a @ wgu[64:].T
+    h = torch.nn.functional.silu(g) * u
+    y = _torch_mx8_roundtrip(h) @ wdn.T
+    assert np.allclose(res.y, y.numpy(), rtol=1e-12, atol=1e-13 * float(y.abs().max()))
+
+
+def test_layer_outputs_nontrivial_tiny():
+    cfg = I.CONFIGS["tiny"]
+    res = moe.forward(I.gen_x(cfg), I.gen_router_w(cfg), None, I.ExpertWeights(cfg),
+                      num_experts=16, top_k=2, num_shared=1, d_ff=128)
+    assert len(set(res.topk_ids.reshape(-1).tolist())) >= 6  # several experts touched
+    assert np.all(np.isfinite(res.y)) and res.y.std() > 0
+    assert len(res.h_rows) == 16 and len(res.h_shared) == 8
