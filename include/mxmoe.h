@@ -1,0 +1,134 @@
+/*
+ * mxmoe.h -- C ABI of the MI355X (gfx950) sparse MoE layer with MXFP4 expert
+ * weights and MXFP8 activations.
+ *
+ * The operation (one MoE layer, one GPU):
+ *   router   : logits l = x W_r^T + b; per token the top_k experts by logit
+ *              (ties -> lower index), weights w = sigmoid(l)/sum sigmoid(l)
+ *              over the selected experts.  The pages give the router as
+ *              "top-16" over 896 experts ("Kimi K3 Tech Intro", section 4.3
+ *              "MXFP4 MoE + SiTU"; section 1 architecture table); the sigmoid
+ *              score and the renormalisation are the readings taken.
+ *   permute  : (token, slot) pairs regrouped expert by expert, tokens in
+ *              ascending order inside an expert.
+ *   quantise : x -> MXFP8 (E4M3 elements, one E8M0 scale per 32 elements
+ *              along d): "MXFP4 weights and MXFP8 activations" ("Kimi K3 ...
+ *              MoE推理系统工程分析"); bit formats per OCP MX v1.0.
+ *   experts  : per routed and shared expert, [g | u] = A W_gu^T (MXFP8 x MXFP4,
+ *              fp32 accumulate), h = silu(g) * u (SwiGLU, standing in for the
+ *              SiTU activation the pages name but do not define), h -> MXFP8
+ *              along d_ff, o = h W_dn^T.  Routed experts plus shared experts
+ *              ("Kimi K3 Tech Intro", section 4.3; 2 shared per
+ *              "Kimi K3本地部署指南", section 1 spec table).
+ *   combine  : y[t] = sum_j w[t,j] o_(t,j) + sum_s o_s[t] (fp32, fixed order),
+ *              rounded to bf16.
+ *
+ * Layouts (all row-major, all device memory, all owned by the caller):
+ *   x          bf16  [T][d_model]
+ *   y          bf16  [T][d_model]
+ *   router_w   fp32  [E][d_model];  router_b fp32 [E] or NULL (zero bias)
+ *   gu_codes   u8    [E][2*d_ff][d_model/2]   E2M1 pairs, element 2i in the
+ *                                             low nibble of byte i; rows
+ *                                             [0,d_ff) gate, [d_ff,2 d_ff) up
+ *   gu_scales  u8    [E][2*d_ff][d_model/32]  E8M0
+ *   dn_codes   u8    [E][d_model][d_ff/2]
+ *   dn_scales  u8    [E][d_model][d_ff/32]
+ *   sgu_* / sdn_*    the same per shared expert, [num_shared][...]
+ *
+ * Errors: every argument is checked on the host before anything is enqueued;
+ * on an error nothing is written and the call returns a non-zero status
+ * (details from moe_last_error(), thread-local).  Device work is enqueued on
+ * `stream` (a hipStream_t, NULL = default stream) without host
+ * synchronisation; asynchronous faults surface at the caller's next sync.
+ * No call allocates or frees device memory.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum        */
+  MOE_ERR_UNSUPPORTED = 2, /* shape outside what the kernels handle        */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small   */
+  MOE_ERR_DEVICE = 4       /* no usable gfx950 device or a launch failed   */
+} moe_status;
+
+typedef enum { MOE_SRC_BF16 = 0, MOE_SRC_FP32 = 1 } moe_src_dtype;
+
+/* Layer shape.  d_model and d_ff: multiples of 128.  1 <= num_experts <= 1024.
+ * 1 <= top_k <= min(32, num_experts).  0 <= num_shared <= 8.
+ * 1 <= max_tokens <= 2^20.  flags: reserved, must be 0. */
+typedef struct {
+  int32_t d_model, d_ff, num_experts, top_k, num_shared;
+  int64_t max_tokens;
+  uint32_t flags;
+} moe_config;
+
+/* Opaque plan: host memory owned by the library, immutable after moe_plan. */
+typedef struct moe_plan_s moe_plan_t;
+
+typedef struct {
+  const uint8_t *gu_codes, *gu_scales, *dn_codes, *dn_scales;
+  const uint8_t *sgu_codes, *sgu_scales, *sdn_codes, *sdn_scales; /* NULL if num_shared==0 */
+  const float *router_w;
+  const float *router_b; /* may be NULL */
+} moe_weights;
+
+/* Optional device outputs for inspection; each NULL pointer is skipped.
+ * Permuted rows: R = T*top_k routed rows (expert-major, tokens ascending)
+ * followed by num_shared blocks of T rows (shared expert s, token t at
+ * T*top_k + s*T + t). */
+typedef struct {
+  float *logits;          /* [T][E]   router logits incl. bias (fp32)        */
+  int32_t *topk_ids;      /* [T][top_k] selected experts, ascending          */
+  float *topk_w;          /* [T][top_k] routing weights                      */
+  int32_t *expert_offsets;/* [E+1]    first permuted row of each expert      */
+  int32_t *row_src;       /* [T*top_k] pair index t*top_k+j of each row      */
+  int32_t *token_row;     /* [T][top_k] permuted row of each pair            */
+  uint8_t *x_codes;       /* [T][d_model]  MXFP8 E4M3 codes of x             */
+  uint8_t *x_scales;      /* [T][d_model/32] E8M0                            */
+  uint8_t *h_codes;       /* [R][d_ff]     MXFP8 codes of h, permuted rows   */
+  uint8_t *h_scales;      /* [R][d_ff/32]                                    */
+  float *gu_acc;          /* [R][2*d_ff]   fp32 gate|up accumulators         */
+  float *y_routed;        /* [T][d_model]  sum_j w o (fp32)                  */
+  float *y_shared;        /* [T][d_model]  sum_s o_s (fp32)                  */
+} moe_taps;
+
+/* Validate `cfg` and build a plan (host only; no device call). */
+moe_status moe_plan(const moe_config *cfg, moe_plan_t **out_plan);
+void moe_plan_destroy(moe_plan_t *plan);
+
+/* Bytes of device workspace moe_forward needs for num_tokens tokens. */
+moe_status moe_workspace_bytes(const moe_plan_t *plan, int64_t num_tokens, size_t *out_bytes);
+
+/* MXFP8-quantise rows of a bf16 or fp32 matrix along its columns: per row and
+ * per 32 consecutive columns, e = clamp(floor(log2 amax) - 8, -127, 127)
+ * (amax == 0 -> -127), codes = E4M3 round-to-nearest-even of v / 2^e with
+ * saturation to +-448 (sign kept on zero), scale byte = e + 127.
+ * src [rows][ld_src] (elements), codes [rows][cols], scales [rows][cols/32].
+ * cols % 32 == 0, ld_src >= cols.  Inputs must be finite. */
+moe_status moe_quantize_act(const void *src, moe_src_dtype dt, int64_t rows, int64_t cols,
+                            int64_t ld_src, uint8_t *codes, uint8_t *scales, void *stream);
+
+/* The whole layer for T = num_tokens tokens (0 <= T <= max_tokens; T == 0
+ * enqueues nothing).  workspace: device memory of at least
+ * moe_workspace_bytes(plan, T) bytes, 256-byte aligned; its contents on entry
+ * do not matter.  Concurrent calls need distinct workspaces. */
+moe_status moe_forward(const moe_plan_t *plan, const moe_weights *w, const void *x_bf16,
+                       int64_t num_tokens, void *y_bf16, void *workspace, size_t workspace_bytes,
+                       const moe_taps *taps, void *stream);
+
+const char *moe_status_string(moe_status s);
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXMOE_H */

@@ -1,0 +1,284 @@
+// C ABI of the MoE layer: argument checks, plan, workspace layout and the
+// launch sequence router -> top-k/quantise -> permute -> gate_up -> down ->
+// combine on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/mxmoe.h"
+#include "internal.h"
+
+using namespace mxmoe;
+
+struct moe_plan_s {
+  moe_config cfg;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checked once per device: a visible gfx950 device is current.
+moe_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_DEVICE, "no HIP device available");
+  }
+  static int checked[64] = {0};  // 0 unknown, 1 ok, 2 bad
+  if (dev < 64 && checked[dev] == 1) return MOE_OK;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+  }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    if (dev < 64) checked[dev] = 2;
+    return fail(MOE_ERR_DEVICE, "device %d is %s, the kernels are built for gfx950", dev,
+                prop.gcnArchName);
+  }
+  if (dev < 64) checked[dev] = 1;
+  return MOE_OK;
+}
+
+// rows per grouped-GEMM tile: 16 when experts see few rows (decode), else 64
+int choose_bm(const moe_config& c, int64_t T) {
+  int64_t avg = (T * c.top_k) / c.num_experts;
+  return avg >= 24 ? 64 : 16;
+}
+
+struct Layout {
+  size_t logits, topk_ids, topk_w, x_codes, x_scales, counts, offsets, row_src, row_token,
+      token_row, chunk_mask, chunk_base, tiles, tile_count, h_codes, h_scales, o, total;
+  int bm, max_tiles, nchunks;
+};
+
+Layout make_layout(const moe_config& c, int64_t T) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  const int64_t E = c.num_experts, k = c.top_k, S = c.num_shared, d = c.d_model, f = c.d_ff;
+  const int64_t Rr = T * k, R = Rr + S * T;
+  L.bm = choose_bm(c, T);
+  L.nchunks = static_cast<int>((T + 63) / 64);
+  L.max_tiles = static_cast<int>((Rr + L.bm - 1) / L.bm + std::min<int64_t>(E, Rr) +
+                                 S * ((T + L.bm - 1) / L.bm));
+  L.logits = take(T * E * 4);
+  L.topk_ids = take(T * k * 4);
+  L.topk_w = take(T * k * 4);
+  L.x_codes = take(T * d);
+  L.x_scales = take(T * d / 32);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.row_src = take(Rr * 4);
+  L.row_token = take(Rr * 4);
+  L.token_row = take(T * k * 4);
+  L.chunk_mask = take(size_t(L.nchunks) * E * 8);
+  L.chunk_base = take(size_t(L.nchunks) * E * 4);
+  L.tiles = take(size_t(std::max(L.max_tiles, 1)) * sizeof(Tile));
+  L.tile_count = take(4);
+  L.h_codes = take(R * f);
+  L.h_scales = take(R * f / 32);
+  L.o = take(R * d * 4);
+  L.total = off;
+  return L;
+}
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->d_model <= 0 || c->d_ff <= 0 || c->num_experts <= 0 || c->top_k <= 0 ||
+      c->num_shared < 0 || c->max_tokens <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "non-positive size in config");
+  if (c->flags != 0) return fail(MOE_ERR_INVALID_ARG, "flags must be 0");
+  if (c->d_model % 128 || c->d_ff % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model (%d) and d_ff (%d) must be multiples of 128",
+                c->d_model, c->d_ff);
+  if (c->d_model > 65536 || c->d_ff > 65536)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be <= 65536");
+  if (c->num_experts > 1024) return fail(MOE_ERR_UNSUPPORTED, "num_experts must be <= 1024");
+  if (c->top_k > 32 || c->top_k > c->num_experts)
+    return fail(MOE_ERR_UNSUPPORTED, "top_k must be <= min(32, num_experts)");
+  if (c->num_shared > 8) return fail(MOE_ERR_UNSUPPORTED, "num_shared must be <= 8");
+  if (c->max_tokens > (1 << 20)) return fail(MOE_ERR_UNSUPPORTED, "max_tokens must be <= 2^20");
+  // permuted-row indices and element offsets must fit the kernels' int32 row math
+  if ((c->max_tokens * (c->top_k + c->num_shared)) > (int64_t(1) << 30))
+    return fail(MOE_ERR_UNSUPPORTED, "max_tokens * (top_k + num_shared) too large");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_plan(const moe_config* cfg, moe_plan_t** out_plan) {
+  if (!out_plan) return fail(MOE_ERR_INVALID_ARG, "out_plan is NULL");
+  *out_plan = nullptr;
+  moe_status s = check_config(cfg);
+  if (s != MOE_OK) return s;
+  moe_plan_t* p = new (std::nothrow) moe_plan_t;
+  if (!p) return fail(MOE_ERR_INVALID_ARG, "out of host memory");
+  p->cfg = *cfg;
+  *out_plan = p;
+  return MOE_OK;
+}
+
+void moe_plan_destroy(moe_plan_t* plan) { delete plan; }
+
+moe_status moe_workspace_bytes(const moe_plan_t* plan, int64_t num_tokens, size_t* out_bytes) {
+  if (!plan || !out_bytes) return fail(MOE_ERR_INVALID_ARG, "plan or out_bytes is NULL");
+  if (num_tokens < 0 || num_tokens > plan->cfg.max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld outside [0, max_tokens]",
+                static_cast<long long>(num_tokens));
+  *out_bytes = num_tokens == 0 ? 0 : make_layout(plan->cfg, num_tokens).total;
+  return MOE_OK;
+}
+
+moe_status moe_quantize_act(const void* src, moe_src_dtype dt, int64_t rows, int64_t cols,
+                            int64_t ld_src, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (dt != MOE_SRC_BF16 && dt != MOE_SRC_FP32) return fail(MOE_ERR_INVALID_ARG, "bad dtype");
+  if (rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "negative size");
+  if (cols % 32) return fail(MOE_ERR_UNSUPPORTED, "cols (%lld) must be a multiple of 32",
+                             static_cast<long long>(cols));
+  if (ld_src < cols) return fail(MOE_ERR_INVALID_ARG, "ld_src < cols");
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!src || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "NULL buffer");
+  const int esz = dt == MOE_SRC_FP32 ? 4 : 2;
+  if (!aligned(src, 16) || (ld_src * esz) % 16 || !aligned(codes, 16))
+    return fail(MOE_ERR_UNSUPPORTED, "src/codes must be 16-byte aligned and rows 16-byte strided");
+  moe_status s = check_device();
+  if (s != MOE_OK) return s;
+  hipError_t e = launch_quantize(src, dt == MOE_SRC_FP32, rows, cols, ld_src, codes, scales,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void* x_bf16,
+                       int64_t num_tokens, void* y_bf16, void* workspace, size_t workspace_bytes,
+                       const moe_taps* taps, void* stream) {
+  if (!plan) return fail(MOE_ERR_INVALID_ARG, "plan is NULL");
+  const moe_config& c = plan->cfg;
+  if (num_tokens < 0 || num_tokens > c.max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld outside [0, %lld]",
+                static_cast<long long>(num_tokens), static_cast<long long>(c.max_tokens));
+  if (num_tokens == 0) return MOE_OK;
+  if (!w || !x_bf16 || !y_bf16) return fail(MOE_ERR_INVALID_ARG, "weights, x or y is NULL");
+  if (!w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales || !w->router_w)
+    return fail(MOE_ERR_INVALID_ARG, "routed-expert or router weight pointer is NULL");
+  if (c.num_shared > 0 && (!w->sgu_codes || !w->sgu_scales || !w->sdn_codes || !w->sdn_scales))
+    return fail(MOE_ERR_INVALID_ARG, "shared-expert weight pointer is NULL");
+  if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16) || !aligned(w->router_w, 16) ||
+      !aligned(w->gu_codes, 16) || !aligned(w->dn_codes, 16) || !aligned(w->gu_scales, 4) ||
+      !aligned(w->dn_scales, 4) || (w->router_b && !aligned(w->router_b, 4)) ||
+      (c.num_shared > 0 && (!aligned(w->sgu_codes, 16) || !aligned(w->sdn_codes, 16) ||
+                            !aligned(w->sgu_scales, 4) || !aligned(w->sdn_scales, 4))))
+    return fail(MOE_ERR_INVALID_ARG,
+                "misaligned buffer (x, y, codes, router_w: 16 bytes; scales, bias: 4 bytes)");
+  const Layout L = make_layout(c, num_tokens);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", L.total,
+                workspace_bytes, workspace ? "" : " (NULL)");
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (taps) {
+    if ((taps->x_codes && !aligned(taps->x_codes, 16)) ||
+        (taps->y_routed && !aligned(taps->y_routed, 16)) ||
+        (taps->y_shared && !aligned(taps->y_shared, 16)) ||
+        (taps->logits && !aligned(taps->logits, 4)) || (taps->topk_w && !aligned(taps->topk_w, 4)) ||
+        (taps->topk_ids && !aligned(taps->topk_ids, 4)) ||
+        (taps->expert_offsets && !aligned(taps->expert_offsets, 4)) ||
+        (taps->row_src && !aligned(taps->row_src, 4)) ||
+        (taps->token_row && !aligned(taps->token_row, 4)) || (taps->gu_acc && !aligned(taps->gu_acc, 4)))
+      return fail(MOE_ERR_INVALID_ARG, "misaligned tap buffer");
+  }
+  moe_status s = check_device();
+  if (s != MOE_OK) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  FwdArgs a{};
+  a.T = static_cast<int>(num_tokens);
+  a.d = c.d_model; a.dff = c.d_ff; a.E = c.num_experts; a.k = c.top_k; a.S = c.num_shared;
+  a.Rr = a.T * a.k;
+  a.R = a.Rr + a.S * a.T;
+  a.x = static_cast<const uint16_t*>(x_bf16);
+  a.wr = w->router_w; a.br = w->router_b;
+  a.gu_c = w->gu_codes; a.gu_s = w->gu_scales; a.dn_c = w->dn_codes; a.dn_s = w->dn_scales;
+  a.sgu_c = w->sgu_codes; a.sgu_s = w->sgu_scales; a.sdn_c = w->sdn_codes; a.sdn_s = w->sdn_scales;
+  a.y = static_cast<uint16_t*>(y_bf16);
+  auto pick = [&](auto* tap, size_t off, auto* type_tag) {
+    using P = decltype(type_tag);
+    return tap ? reinterpret_cast<P>(tap) : reinterpret_cast<P>(ws + off);
+  };
+  const moe_taps none{};
+  const moe_taps& tp = taps ? *taps : none;
+  a.logits = pick(tp.logits, L.logits, static_cast<float*>(nullptr));
+  a.topk_ids = pick(tp.topk_ids, L.topk_ids, static_cast<int32_t*>(nullptr));
+  a.topk_w = pick(tp.topk_w, L.topk_w, static_cast<float*>(nullptr));
+  a.x_codes = pick(tp.x_codes, L.x_codes, static_cast<uint8_t*>(nullptr));
+  a.x_scales = pick(tp.x_scales, L.x_scales, static_cast<uint8_t*>(nullptr));
+  a.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  a.offsets = pick(tp.expert_offsets, L.offsets, static_cast<int32_t*>(nullptr));
+  a.row_src = pick(tp.row_src, L.row_src, static_cast<int32_t*>(nullptr));
+  a.row_token = reinterpret_cast<int32_t*>(ws + L.row_token);
+  a.token_row = pick(tp.token_row, L.token_row, static_cast<int32_t*>(nullptr));
+  a.chunk_mask = reinterpret_cast<uint64_t*>(ws + L.chunk_mask);
+  a.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
+  a.tiles = reinterpret_cast<Tile*>(ws + L.tiles);
+  a.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
+  a.h_codes = pick(tp.h_codes, L.h_codes, static_cast<uint8_t*>(nullptr));
+  a.h_scales = pick(tp.h_scales, L.h_scales, static_cast<uint8_t*>(nullptr));
+  a.o = reinterpret_cast<float*>(ws + L.o);
+  a.gu_acc = tp.gu_acc;
+  a.y_routed = tp.y_routed;
+  a.y_shared = tp.y_shared;
+  a.bm = L.bm;
+  a.max_tiles = L.max_tiles;
+  a.nchunks = L.nchunks;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = launch_router(a, st)) != hipSuccess ||
+      (e = launch_topk_quant(a, st)) != hipSuccess ||
+      (e = launch_permute(a, st)) != hipSuccess ||
+      (e = launch_gemm_gate_up(a, st)) != hipSuccess ||
+      (e = launch_gemm_down(a, st)) != hipSuccess ||
+      (e = launch_combine(a, st)) != hipSuccess)
+    return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+// One unit of grouped-GEMM work: rows [row_begin, row_end) of expert `ex`
+// (ex < E: routed expert; ex >= E: shared expert ex - E).
+struct Tile {
+  int32_t ex, row_begin, row_end, pad;
+};
+
+// Everything the kernels of one forward need; all pointers are device memory.
+struct FwdArgs {
+  // shape
+  int T, d, dff, E, k, S;
+  int R;         // permuted rows: T*k routed + S*T shared
+  int Rr;        // routed rows T*k
+  // inputs
+  const uint16_t* x;    // bf16 [T][d]
+  const float* wr;      // [E][d]
+  const float* br;      // [E] or null
+  const uint8_t *gu_c, *gu_s, *dn_c, *dn_s;      // routed weights
+  const uint8_t *sgu_c, *sgu_s, *sdn_c, *sdn_s;  // shared weights
+  // outputs
+  uint16_t* y;  // bf16 [T][d]
+  // workspace buffers (or caller taps substituted for them)
+  float* logits;        // [T][E]
+  int32_t* topk_ids;    // [T][k]
+  float* topk_w;        // [T][k]
+  uint8_t* x_codes;     // [T][d]
+  uint8_t* x_scales;    // [T][d/32]
+  int32_t* counts;      // [E]
+  int32_t* offsets;     // [E+1]
+  int32_t* row_src;     // [Rr]   pair index
+  int32_t* row_token;   // [Rr]   token of each routed row
+  int32_t* token_row;   // [T][k]
+  uint64_t* chunk_mask; // [nchunks][E]
+  int32_t* chunk_base;  // [E][nchunks]
+  Tile* tiles;          // [max_tiles]
+  int32_t* tile_count;  // [1]
+  uint8_t* h_codes;     // [R][dff]
+  uint8_t* h_scales;    // [R][dff/32]
+  float* o;             // [R][d]
+  // optional taps (null = skip)
+  float* gu_acc;        // [R][2*dff]
+  float* y_routed;      // [T][d]
+  float* y_shared;      // [T][d]
+  // launch-time choices
+  int bm;               // rows per tile
+  int max_tiles;
+  int nchunks;          // 64-token chunks
+};
+
+// Launchers (kernels_*.hip).  Each returns hipSuccess or the launch error.
+hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t cols, int64_t ld,
+                           uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_router(const FwdArgs& a, hipStream_t st);
+hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st);
+hipError_t launch_permute(const FwdArgs& a, hipStream_t st);
+hipError_t launch_gemm_gate_up(const FwdArgs& a, hipStream_t st);
+hipError_t launch_gemm_down(const FwdArgs& a, hipStream_t st);
+hipError_t launch_combine(const FwdArgs& a, hipStream_t st);
+
+// token counts at or below which the single-workgroup permutation is used
+constexpr int kPermSmallMaxTokens = 1024;
+
+}  // namespace mxmoe

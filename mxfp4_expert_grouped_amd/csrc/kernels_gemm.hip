@@ -1,0 +1,219 @@
+// Grouped expert GEMMs on the gfx950 scaled MFMA (MXFP8 activations x MXFP4
+// weights, fp32 accumulate): gate_up with a fused SwiGLU + MXFP8 re-quantise
+// epilogue, and down.  "Kimi K3 Tech Intro", section 4.3 names the routed +
+// shared experts and the A8W4 fused operators on MI355X; SwiGLU stands in for
+// the SiTU activation the pages name without defining.
+//
+// Operand layout of V_MFMA_SCALE_F32_16X16X128_F8F6F4 (established by probes
+// in the exact-arithmetic regime):
+//   * an FP4 operand lane (row r = lane%16, group g = lane/16) holds 32
+//     consecutive logical k = 32g .. 32g+31 (16 bytes, element 2i in the low
+//     nibble of byte i);
+//   * an FP8 operand lane holds bytes j = 0..31 at logical k = 64(j/16) + 16g
+//     + j%16, i.e. two 16-byte halves from logical blocks g/2 and 2 + g/2;
+//   * the scale byte of lane (r, g) applies to logical block g (k = 32g..32g+31)
+//     of row r; the result of lane l, register i is D[4(l/16)+i][l%16].
+// Since a dot product does not care how k is ordered, each MFMA step maps its
+// four logical blocks onto four MX blocks of the data; both operands and both
+// scales follow the same map, so each FP4 lane reads one whole MX block.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "mx_device.h"
+
+namespace mxmoe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, v4f c, uint32_t sa, uint32_t sb) {
+  // A: FP8 E4M3 (format 0), B: FP4 E2M1 (format 4); scale in byte 0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, static_cast<int>(sa), 0,
+                                                          static_cast<int>(sb));
+}
+
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ v8i make_a(uint4 lo, uint4 hi) {
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+__device__ __forceinline__ v8i make_b(uint4 v) {
+  v8i r;
+  r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
+// MI: 16-row M subtiles per wave; NI: 16-column N subtiles per wave (h columns
+// for gate_up, each needing a gate and an up subtile); NW: waves per workgroup
+// along N; G4: K handled in groups of 512 (4 MFMA steps sharing a scale dword),
+// else one 128-wide step at a time.
+template <int MI, int NI, int NW, bool G4, bool GU>
+__global__ void __launch_bounds__(64 * NW) k_gemm(FwdArgs a) {
+  constexpr int NB = GU ? 2 * NI : NI;
+  const int tile_idx = blockIdx.x;
+  if (tile_idx >= *a.tile_count) return;
+  const Tile tile = a.tiles[tile_idx];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int K = GU ? a.d : a.dff;
+  const int N = GU ? a.dff : a.d;
+  const int col0 = blockIdx.y * (16 * NI * NW) + wave * (16 * NI);
+
+  // weights of this expert
+  const bool shared = tile.ex >= a.E;
+  const int sidx = tile.ex - a.E;
+  const int64_t wrows = GU ? 2 * a.dff : a.d;
+  const int64_t wc_stride = wrows * (K / 2), ws_stride = wrows * (K / 32);
+  const uint8_t* wc = GU ? (shared ? a.sgu_c + sidx * wc_stride : a.gu_c + tile.ex * wc_stride)
+                         : (shared ? a.sdn_c + sidx * wc_stride : a.dn_c + tile.ex * wc_stride);
+  const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + tile.ex * ws_stride)
+                         : (shared ? a.sdn_s + sidx * ws_stride : a.dn_s + tile.ex * ws_stride);
+
+  // activation rows (clamped to a valid row for padding lanes)
+  const uint8_t* ap[MI];
+  const uint8_t* asp[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    int row = tile.row_begin + 16 * mi + r16;
+    if (row >= tile.row_end) row = tile.row_begin;
+    int64_t src;
+    if (GU)
+      src = row < a.Rr ? a.row_token[row] : row - a.Rr - sidx * a.T;
+    else
+      src = row;
+    const uint8_t* base_c = GU ? a.x_codes : a.h_codes;
+    const uint8_t* base_s = GU ? a.x_scales : a.h_scales;
+    ap[mi] = base_c + src * K;
+    asp[mi] = base_s + src * (K / 32);
+  }
+  const uint8_t* bp[NB];
+  const uint8_t* bsp[NB];
+#pragma unroll
+  for (int nj = 0; nj < NB; ++nj) {
+    int n = col0 + 16 * (nj % NI) + r16;
+    int64_t wrow = (GU && nj >= NI) ? a.dff + n : n;
+    bp[nj] = wc + wrow * (K / 2);
+    bsp[nj] = ws + wrow * (K / 32);
+  }
+
+  v4f acc[MI][NB];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < NB; ++nj) acc[mi][nj] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (G4) {
+    const int nq = K / 512;
+    for (int q = 0; q < nq; ++q) {
+      uint32_t sa[MI], sb[NB];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) sa[mi] = *reinterpret_cast<const uint32_t*>(asp[mi] + 16 * q + 4 * g);
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj) sb[nj] = *reinterpret_cast<const uint32_t*>(bsp[nj] + 16 * q + 4 * g);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        v8i av[MI], bv[NB];
+        const int aoff = 512 * q + 128 * (g >> 1) + 32 * s + 16 * (g & 1);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) av[mi] = make_a(ld16(ap[mi] + aoff), ld16(ap[mi] + aoff + 256));
+        const int boff = 256 * q + 64 * g + 16 * s;
+#pragma unroll
+        for (int nj = 0; nj < NB; ++nj) bv[nj] = make_b(ld16(bp[nj] + boff));
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int nj = 0; nj < NB; ++nj)
+            acc[mi][nj] = mfma_mx(av[mi], bv[nj], acc[mi][nj], sa[mi] >> (8 * s), sb[nj] >> (8 * s));
+      }
+    }
+  } else {
+    const int ns = K / 128;
+    for (int s = 0; s < ns; ++s) {
+      v8i av[MI], bv[NB];
+      uint32_t sa[MI], sb[NB];
+      const int aoff = 128 * s + 16 * g;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        av[mi] = make_a(ld16(ap[mi] + aoff), ld16(ap[mi] + aoff + 64));
+        sa[mi] = asp[mi][4 * s + g];
+      }
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj) {
+        bv[nj] = make_b(ld16(bp[nj] + 64 * s + 16 * g));
+        sb[nj] = bsp[nj][4 * s + g];
+      }
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < NB; ++nj) acc[mi][nj] = mfma_mx(av[mi], bv[nj], acc[mi][nj], sa[mi], sb[nj]);
+    }
+  }
+
+  // epilogue
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile.row_begin + 16 * mi + 4 * g + i;
+      const bool valid = row < tile.row_end;
+      if (GU) {
+#pragma unroll
+        for (int p = 0; p < NI / 2; ++p) {
+          float h[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int j = 2 * p + hh;
+            const float gt = acc[mi][j][i], up = acc[mi][NI + j][i];
+            h[hh] = gt / (1.0f + expf(-gt)) * up;
+            if (valid && a.gu_acc) {
+              const int col = col0 + 16 * j + r16;
+              a.gu_acc[int64_t(row) * 2 * a.dff + col] = gt;
+              a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + col] = up;
+            }
+          }
+          const float amax = group_max<16>(fmaxf(fabsf(h[0]), fabsf(h[1])));
+          const int e = mx8_block_exp(amax);
+          if (valid) {
+            const int col = col0 + 32 * p + r16;
+            uint8_t* hc = a.h_codes + int64_t(row) * a.dff;
+            hc[col] = static_cast<uint8_t>(mx8_encode(h[0], e));
+            hc[col + 16] = static_cast<uint8_t>(mx8_encode(h[1], e));
+            if (r16 == 0) a.h_scales[int64_t(row) * (a.dff / 32) + (col0 + 32 * p) / 32] = static_cast<uint8_t>(e + 127);
+          }
+        }
+      } else if (valid) {
+#pragma unroll
+        for (int nj = 0; nj < NB; ++nj) a.o[int64_t(row) * N + col0 + 16 * nj + r16] = acc[mi][nj][i];
+      }
+    }
+  }
+}
+
+template <int MI, int NI, int NW, bool GU>
+static hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
+  const int K = GU ? a.d : a.dff;
+  const int N = GU ? a.dff : a.d;
+  dim3 grid(a.max_tiles, N / (16 * NI * NW));
+  if (K % 512 == 0)
+    hipLaunchKernelGGL((k_gemm<MI, NI, NW, true, GU>), grid, dim3(64 * NW), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm<MI, NI, NW, false, GU>), grid, dim3(64 * NW), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_gate_up(const FwdArgs& a, hipStream_t st) {
+  if (a.bm == 16) return launch_cfg<1, 2, 1, true>(a, st);
+  return launch_cfg<4, 2, 4, true>(a, st);
+}
+
+hipError_t launch_gemm_down(const FwdArgs& a, hipStream_t st) {
+  if (a.bm == 16) return launch_cfg<1, 2, 4, false>(a, st);
+  return launch_cfg<4, 2, 4, false>(a, st);
+}
+
+}  // namespace mxmoe

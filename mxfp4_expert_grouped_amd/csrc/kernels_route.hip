@@ -1,0 +1,524 @@
+// Router, top-k, activation quantiser, token permutation and combine kernels.
+//
+// Router and top-k follow "Kimi K3 Tech Intro", section 4.3 ("Router (Top-16,
+// ...)") and the 16-of-896 routing of the section 1 architecture table; the
+// sigmoid score with renormalisation over the selected experts is the reading
+// taken for the unspecified score function.  The MXFP8 activation format is
+// the "MXFP8 activations" of "Kimi K3 ... MoE推理系统工程分析".
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "mx_device.h"
+
+namespace mxmoe {
+
+// ---------------------------------------------------------------------------
+// MXFP8 quantisation of 32-element blocks
+// ---------------------------------------------------------------------------
+
+// Quantise 32 floats -> 32 codes (two 16-byte stores) + returns the scale byte.
+__device__ __forceinline__ uint32_t quant_block32(const float* v, uint8_t* codes) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int e = mx8_block_exp(amax);
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w[i] = mx8_encode(v[4 * i], e) | (mx8_encode(v[4 * i + 1], e) << 8) |
+           (mx8_encode(v[4 * i + 2], e) << 16) | (mx8_encode(v[4 * i + 3], e) << 24);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  return static_cast<uint32_t>(e + 127);
+}
+
+__device__ __forceinline__ void load_block32_bf16(const uint16_t* src, float* v) {
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint4 u = s[q];
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * q + 2 * i] = __uint_as_float(w[i] << 16);
+      v[8 * q + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ void load_block32_f32(const float* src, float* v) {
+  const float4* s = reinterpret_cast<const float4*>(src);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    float4 f = s[q];
+    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+  }
+}
+
+template <bool F32>
+__global__ void __launch_bounds__(256) k_quantize(const void* __restrict__ src, int64_t rows,
+                                                  int64_t cols, int64_t ld,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales) {
+  const int64_t nb = cols / 32;
+  const int64_t total = rows * nb;
+  for (int64_t b = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; b < total;
+       b += int64_t(gridDim.x) * blockDim.x) {
+    int64_t r = b / nb, c = b - r * nb;
+    float v[32];
+    if (F32)
+      load_block32_f32(static_cast<const float*>(src) + r * ld + c * 32, v);
+    else
+      load_block32_bf16(static_cast<const uint16_t*>(src) + r * ld + c * 32, v);
+    scales[r * nb + c] = static_cast<uint8_t>(quant_block32(v, codes + r * cols + c * 32));
+  }
+}
+
+hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t cols, int64_t ld,
+                           uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  int64_t total = rows * (cols / 32);
+  int64_t grid = (total + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  if (grid < 1) grid = 1;
+  if (src_fp32)
+    hipLaunchKernelGGL(k_quantize<true>, dim3(grid), dim3(256), 0, st, src, rows, cols, ld, codes, scales);
+  else
+    hipLaunchKernelGGL(k_quantize<false>, dim3(grid), dim3(256), 0, st, src, rows, cols, ld, codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router logits  l[t][e] = sum_i x[t][i] W_r[e][i] + b[e]   (fp32 accumulate)
+// ---------------------------------------------------------------------------
+
+// Few tokens: one wave per expert streams its W_r row once per 8 tokens.
+constexpr int kRouterSmallMaxT = 32;
+
+__global__ void __launch_bounds__(256) k_router_small(const uint16_t* __restrict__ x,
+                                                      const float* __restrict__ wr,
+                                                      const float* __restrict__ br,
+                                                      float* __restrict__ logits, int T, int d,
+                                                      int E) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const float4* w4 = reinterpret_cast<const float4*>(wr + int64_t(e) * d);
+  const int n4 = d / 4;
+  const float bias = br ? br[e] : 0.f;
+  for (int t0 = 0; t0 < T; t0 += 8) {
+    const int nt = T - t0 < 8 ? T - t0 : 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int c = lane; c < n4; c += 64) {
+      float4 w = w4[c];
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        if (tt < nt) {
+          uint2 xb = *reinterpret_cast<const uint2*>(x + int64_t(t0 + tt) * d + 4 * c);
+          acc[tt] = fmaf(__uint_as_float(xb.x << 16), w.x, acc[tt]);
+          acc[tt] = fmaf(__uint_as_float(xb.x & 0xFFFF0000u), w.y, acc[tt]);
+          acc[tt] = fmaf(__uint_as_float(xb.y << 16), w.z, acc[tt]);
+          acc[tt] = fmaf(__uint_as_float(xb.y & 0xFFFF0000u), w.w, acc[tt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      float s = group_sum<64>(acc[tt]);
+      if (lane == 0 && tt < nt) logits[int64_t(t0 + tt) * E + e] = s + bias;
+    }
+  }
+}
+
+// Many tokens: 64x64 output tile per 256-thread workgroup, K staged in LDS.
+__global__ void __launch_bounds__(256) k_router_gemm(const uint16_t* __restrict__ x,
+                                                     const float* __restrict__ wr,
+                                                     const float* __restrict__ br,
+                                                     float* __restrict__ logits, int T, int d,
+                                                     int E) {
+  __shared__ float xs[32][68];
+  __shared__ float ws[32][68];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int tx = tid & 15, ty = tid >> 4;
+  float acc[4][4] = {};
+  const int lr = tid >> 2, lk = (tid & 3) * 8;
+  const int xt = min(t0 + lr, T - 1), we = min(e0 + lr, E - 1);
+  for (int k0 = 0; k0 < d; k0 += 32) {
+    uint4 xv = *reinterpret_cast<const uint4*>(x + int64_t(xt) * d + k0 + lk);
+    const float4* wp = reinterpret_cast<const float4*>(wr + int64_t(we) * d + k0 + lk);
+    float4 w0 = wp[0], w1 = wp[1];
+    __syncthreads();
+    uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xs[lk + 2 * i][lr] = __uint_as_float(xw[i] << 16);
+      xs[lk + 2 * i + 1][lr] = __uint_as_float(xw[i] & 0xFFFF0000u);
+    }
+    ws[lk + 0][lr] = w0.x; ws[lk + 1][lr] = w0.y; ws[lk + 2][lr] = w0.z; ws[lk + 3][lr] = w0.w;
+    ws[lk + 4][lr] = w1.x; ws[lk + 5][lr] = w1.y; ws[lk + 6][lr] = w1.z; ws[lk + 7][lr] = w1.w;
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int t = t0 + ty + 16 * i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int e = e0 + tx + 16 * j;
+      if (e < E) logits[int64_t(t) * E + e] = acc[i][j] + (br ? br[e] : 0.f);
+    }
+  }
+}
+
+hipError_t launch_router(const FwdArgs& a, hipStream_t st) {
+  if (a.T <= kRouterSmallMaxT) {
+    hipLaunchKernelGGL(k_router_small, dim3((a.E + 3) / 4), dim3(256), 0, st, a.x, a.wr, a.br,
+                       a.logits, a.T, a.d, a.E);
+  } else {
+    dim3 grid((a.T + 63) / 64, (a.E + 63) / 64);
+    hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, st, a.x, a.wr, a.br, a.logits, a.T, a.d,
+                       a.E);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-k + sigmoid renormalisation + MXFP8 quantisation of x: one wave per token
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxSlots = 16;  // E <= 1024 = 64 lanes x 16 slots
+
+__global__ void __launch_bounds__(256) k_topk_quant(FwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const float* lg = a.logits + int64_t(t) * a.E;
+  uint64_t key[kMaxSlots];
+  float val[kMaxSlots];
+#pragma unroll
+  for (int i = 0; i < kMaxSlots; ++i) {
+    int e = lane + 64 * i;
+    if (e < a.E) {
+      val[i] = lg[e];
+      key[i] = (uint64_t(float_order_key(val[i])) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(e));
+    } else {
+      val[i] = 0.f;
+      key[i] = 0;
+    }
+  }
+  uint32_t sel = 0;
+  for (int r = 0; r < a.k; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxSlots; ++i) best = key[i] > best ? key[i] : best;
+    uint64_t wbest = wave_max_u64(best);
+#pragma unroll
+    for (int i = 0; i < kMaxSlots; ++i) {
+      if (key[i] == wbest) {  // unique: keys embed the expert index
+        key[i] = 0;
+        sel |= 1u << i;
+      }
+    }
+  }
+  // ascending expert order: slot i of lane l is expert l + 64 i
+  int pos[kMaxSlots];
+  float sig[kMaxSlots];
+  float local = 0.f;
+  int base = 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int i = 0; i < kMaxSlots; ++i) {
+    bool s = (sel >> i) & 1u;
+    uint64_t m = __ballot(s);
+    pos[i] = base + __popcll(m & lt_mask);
+    base += __popcll(m);
+    sig[i] = 1.0f / (1.0f + expf(-val[i]));
+    if (s) local += sig[i];
+  }
+  const float denom = group_sum<64>(local);
+  const float inv = 1.0f / denom;
+  int32_t* ids = a.topk_ids + int64_t(t) * a.k;
+  float* wts = a.topk_w + int64_t(t) * a.k;
+#pragma unroll
+  for (int i = 0; i < kMaxSlots; ++i) {
+    if ((sel >> i) & 1u) {
+      ids[pos[i]] = lane + 64 * i;
+      wts[pos[i]] = sig[i] * inv;
+    }
+  }
+  // MXFP8 codes of this token's activation row
+  const int nb = a.d / 32;
+  const uint16_t* xr = a.x + int64_t(t) * a.d;
+  for (int b = lane; b < nb; b += 64) {
+    float v[32];
+    load_block32_bf16(xr + b * 32, v);
+    a.x_scales[int64_t(t) * nb + b] =
+        static_cast<uint8_t>(quant_block32(v, a.x_codes + int64_t(t) * a.d + b * 32));
+  }
+}
+
+hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_topk_quant, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Permutation: pairs (t, j) -> rows grouped by expert, tokens ascending.
+// Ranks come from per-chunk bitmasks of the 64 tokens in a chunk, so the
+// result is deterministic and needs no ordered atomics.
+// ---------------------------------------------------------------------------
+
+// Exclusive scan of n <= 2048 ints held in LDS `v` (in place); returns the total.
+// Must be called by all threads of a 1024-thread workgroup.
+__device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < n; base += 1024) {
+    int i = base + tid;
+    int x = i < n ? v[i] : 0;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wave_tot[wv] = incl;
+    __syncthreads();
+    if (wv == 0) {
+      int w = lane < 16 ? wave_tot[lane] : 0;
+      int wi = w;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        int y = __shfl_up(wi, o, 64);
+        if (lane >= o) wi += y;
+      }
+      if (lane < 16) wave_tot[16 + lane] = wi - w;  // exclusive wave offsets
+      if (lane == 15) wave_tot[32] = wi;            // chunk total
+    }
+    __syncthreads();
+    if (i < n) v[i] = carry + wave_tot[16 + wv] + incl - x;
+    carry += wave_tot[32];
+    __syncthreads();
+  }
+  return carry;
+}
+
+// Offsets, counts and the tile list from per-expert counts held in LDS `cnt`
+// (routed experts [0, E)); shared experts contribute T rows each.
+__device__ void write_offsets_and_tiles(const FwdArgs& a, int* cnt, int* scan, int* wave_tot) {
+  const int tid = threadIdx.x;
+  const int nex = a.E + a.S;
+  for (int e = tid; e < a.E; e += 1024) scan[e] = cnt[e];
+  __syncthreads();
+  block_exclusive_scan(scan, a.E, wave_tot);
+  for (int e = tid; e < a.E; e += 1024) {
+    a.offsets[e] = scan[e];
+    a.counts[e] = cnt[e];
+  }
+  if (tid == 0) a.offsets[a.E] = a.Rr;
+  __syncthreads();
+  // tiles per expert -> LDS cnt reused as tile counts; scan[] keeps row starts
+  for (int ex = tid; ex < nex; ex += 1024) {
+    int rows = ex < a.E ? cnt[ex] : a.T;
+    cnt[ex] = (rows + a.bm - 1) / a.bm;
+    if (ex >= a.E) scan[ex] = a.Rr + (ex - a.E) * a.T;
+  }
+  __syncthreads();
+  // scan tile counts into tile_start (stored in cnt)
+  int ntiles = block_exclusive_scan(cnt, nex, wave_tot);
+  for (int ex = tid; ex < nex; ex += 1024) {
+    int rb = scan[ex];
+    int rows = ex < a.E ? (ex + 1 < a.E ? scan[ex + 1] : a.Rr) - rb : a.T;
+    int re = rb + rows;
+    int first = cnt[ex];
+    int nt = (rows + a.bm - 1) / a.bm;
+    for (int i = 0; i < nt; ++i) {
+      Tile tl;
+      tl.ex = ex;
+      tl.row_begin = rb + i * a.bm;
+      tl.row_end = min(rb + (i + 1) * a.bm, re);
+      tl.pad = 0;
+      a.tiles[first + i] = tl;
+    }
+  }
+  if (tid == 0) *a.tile_count = ntiles;
+}
+
+// Whole permutation in one workgroup (moderate token counts).
+__global__ void __launch_bounds__(1024) k_permute_small(FwdArgs a) {
+  __shared__ int cnt[1032];
+  __shared__ int scan[1032];
+  __shared__ int run[1024];
+  __shared__ unsigned long long mask[1024];
+  __shared__ int wave_tot[40];
+  const int tid = threadIdx.x;
+  const int npairs = a.T * a.k;
+  for (int e = tid; e < a.E; e += 1024) { cnt[e] = 0; run[e] = 0; }
+  __syncthreads();
+  for (int p = tid; p < npairs; p += 1024) atomicAdd(&cnt[a.topk_ids[p]], 1);
+  __syncthreads();
+  write_offsets_and_tiles(a, cnt, scan, wave_tot);
+  __syncthreads();
+  // scan[e] now holds the first row of routed expert e
+  for (int t0 = 0; t0 < a.T; t0 += 64) {
+    for (int e = tid; e < a.E; e += 1024) mask[e] = 0ull;
+    __syncthreads();
+    const int tend = min(t0 + 64, a.T);
+    const int p0 = t0 * a.k, p1 = tend * a.k;
+    for (int p = p0 + tid; p < p1; p += 1024) {
+      int t = p / a.k;
+      atomicOr(&mask[a.topk_ids[p]], 1ull << (t - t0));
+    }
+    __syncthreads();
+    for (int p = p0 + tid; p < p1; p += 1024) {
+      int t = p / a.k;
+      int e = a.topk_ids[p];
+      unsigned long long below = (t - t0) == 0 ? 0ull : (~0ull >> (64 - (t - t0)));
+      int row = scan[e] + run[e] + __popcll(mask[e] & below);
+      a.row_src[row] = p;
+      a.row_token[row] = t;
+      a.token_row[p] = row;
+    }
+    __syncthreads();
+    for (int e = tid; e < a.E; e += 1024) run[e] += __popcll(mask[e]);
+    __syncthreads();
+  }
+}
+
+// Large token counts: per-chunk masks and counts ...
+__global__ void __launch_bounds__(256) k_perm_count(FwdArgs a) {
+  __shared__ unsigned long long mask[1024];
+  const int c = blockIdx.x, tid = threadIdx.x;
+  for (int e = tid; e < a.E; e += 256) mask[e] = 0ull;
+  __syncthreads();
+  const int t0 = c * 64, tend = min(t0 + 64, a.T);
+  for (int p = t0 * a.k + tid; p < tend * a.k; p += 256) {
+    int t = p / a.k;
+    atomicOr(&mask[a.topk_ids[p]], 1ull << (t - t0));
+  }
+  __syncthreads();
+  for (int e = tid; e < a.E; e += 256) {
+    unsigned long long m = mask[e];
+    a.chunk_mask[int64_t(c) * a.E + e] = m;
+    a.chunk_base[int64_t(e) * a.nchunks + c] = __popcll(m);
+  }
+}
+
+// ... per-expert exclusive scan over chunks (one wave per expert) ...
+__global__ void __launch_bounds__(256) k_perm_scan_chunks(FwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= a.E) return;
+  int32_t* cb = a.chunk_base + int64_t(e) * a.nchunks;
+  int carry = 0;
+  for (int c0 = 0; c0 < a.nchunks; c0 += 64) {
+    int c = c0 + lane;
+    int x = c < a.nchunks ? cb[c] : 0;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (c < a.nchunks) cb[c] = carry + incl - x;
+    carry += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) a.counts[e] = carry;
+}
+
+// ... expert offsets and tile list ...
+__global__ void __launch_bounds__(1024) k_perm_offsets(FwdArgs a) {
+  __shared__ int cnt[1032];
+  __shared__ int scan[1032];
+  __shared__ int wave_tot[40];
+  for (int e = threadIdx.x; e < a.E; e += 1024) cnt[e] = a.counts[e];
+  __syncthreads();
+  write_offsets_and_tiles(a, cnt, scan, wave_tot);
+}
+
+// ... and the scatter.
+__global__ void __launch_bounds__(256) k_perm_scatter(FwdArgs a) {
+  const int c = blockIdx.x, tid = threadIdx.x;
+  const int t0 = c * 64, tend = min(t0 + 64, a.T);
+  for (int p = t0 * a.k + tid; p < tend * a.k; p += 256) {
+    int t = p / a.k;
+    int e = a.topk_ids[p];
+    unsigned long long m = a.chunk_mask[int64_t(c) * a.E + e];
+    unsigned long long below = (t - t0) == 0 ? 0ull : (~0ull >> (64 - (t - t0)));
+    int row = a.offsets[e] + a.chunk_base[int64_t(e) * a.nchunks + c] + __popcll(m & below);
+    a.row_src[row] = p;
+    a.row_token[row] = t;
+    a.token_row[p] = row;
+  }
+}
+
+hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
+  if (a.T <= kPermSmallMaxTokens) {
+    hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(1024), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_perm_count, dim3(a.nchunks), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_perm_scan_chunks, dim3((a.E + 3) / 4), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_perm_offsets, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(k_perm_scatter, dim3(a.nchunks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Combine: y[t] = sum_j w[t][j] o[row(t,j)] + sum_s o[shared row(s,t)]
+// (fixed order: slots ascending = expert id ascending, then shared experts)
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) k_combine(FwdArgs a) {
+  __shared__ int rows[32];
+  __shared__ float wts[32];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < a.k) {
+    rows[tid] = a.token_row[int64_t(t) * a.k + tid];
+    wts[tid] = a.topk_w[int64_t(t) * a.k + tid];
+  }
+  __syncthreads();
+  const int n4 = a.d / 4;
+  for (int c = tid; c < n4; c += 256) {
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < a.k; ++j) {
+      float4 v = reinterpret_cast<const float4*>(a.o + int64_t(rows[j]) * a.d)[c];
+      float w = wts[j];
+      r.x = fmaf(w, v.x, r.x); r.y = fmaf(w, v.y, r.y);
+      r.z = fmaf(w, v.z, r.z); r.w = fmaf(w, v.w, r.w);
+    }
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sh = 0; sh < a.S; ++sh) {
+      float4 v = reinterpret_cast<const float4*>(a.o + int64_t(a.Rr + sh * a.T + t) * a.d)[c];
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    uint2 yb;
+    yb.x = uint32_t(f32_to_bf16_rne(r.x + s.x)) | (uint32_t(f32_to_bf16_rne(r.y + s.y)) << 16);
+    yb.y = uint32_t(f32_to_bf16_rne(r.z + s.z)) | (uint32_t(f32_to_bf16_rne(r.w + s.w)) << 16);
+    reinterpret_cast<uint2*>(a.y + int64_t(t) * a.d)[c] = yb;
+    if (a.y_routed) reinterpret_cast<float4*>(a.y_routed + int64_t(t) * a.d)[c] = r;
+    if (a.y_shared) reinterpret_cast<float4*>(a.y_shared + int64_t(t) * a.d)[c] = s;
+  }
+}
+
+hipError_t launch_combine(const FwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_combine, dim3(a.T), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace mxmoe

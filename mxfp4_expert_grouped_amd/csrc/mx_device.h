@@ -1,0 +1,99 @@
+// Device-side helpers for the MX formats and wavefront reductions (gfx950).
+//
+// Formats (OCP Microscaling v1.0, the encodings behind the "MXFP4 weights,
+// MXFP8 activations" of the Kimi K3 pages):
+//   E4M3 ("fn"): 1 sign, 4 exponent (bias 7), 3 mantissa; max finite 448.
+//   E8M0 scale : 2^(k-127).
+// Quantisation of a block of 32 values: e = clamp(floor(log2 amax) - 8,
+// -127, 127) (amax == 0 -> -127); element code = round-to-nearest-even of
+// v * 2^-e on the E4M3 grid, saturated to +-448, sign kept on zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxmoe {
+
+constexpr int kWave = 64;
+
+// floor(log2 |a|) of a finite float, subnormals included; |a| == 0 -> -150.
+__device__ __forceinline__ int floor_log2_f32(float a) {
+  uint32_t u = __float_as_uint(a) & 0x7fffffffu;
+  int ef = static_cast<int>(u >> 23);
+  if (ef > 0) return ef - 127;
+  return (u == 0) ? -150 : (31 - __clz(u)) - 149;
+}
+
+// Shared exponent of an MXFP8 block from its largest magnitude.
+__device__ __forceinline__ int mx8_block_exp(float amax) {
+  int e = floor_log2_f32(amax) - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 2^n as a float for n in [-126, 127] (normal range).
+__device__ __forceinline__ float exp2_int(int n) {
+  return __uint_as_float(static_cast<uint32_t>(n + 127) << 23);
+}
+
+// E4M3 code of q: round-to-nearest-even, saturating to +-448, sign kept.
+// Done on the float's bits so it does not depend on any conversion instruction.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float q) {
+  uint32_t u = __float_as_uint(q);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |q| >= 448
+  if (a < 0x3C800000u) {                      // |q| < 2^-6: subnormal grid, step 2^-9
+    float r = rintf(__uint_as_float(a) * 512.0f);  // exact scaling, RNE
+    return sign | static_cast<uint32_t>(r);        // r == 8 is the code of 2^-6
+  }
+  uint32_t code = ((((a >> 23) - 127u + 7u)) << 3) | ((a >> 20) & 7u);
+  uint32_t rem = a & 0xFFFFFu;  // the 20 dropped mantissa bits
+  if (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) code += 1u;  // carry may bump exponent
+  return sign | code;
+}
+
+// Quantise one value given the block exponent e (e <= 126 always holds for
+// finite fp32 blocks, so 2^-e is a normal float).
+__device__ __forceinline__ uint32_t mx8_encode(float v, int e) {
+  return e4m3_rne_sat(v * exp2_int(-e));
+}
+
+// bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Reductions across the lanes of a wave (or of aligned lane groups).
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
+  return v;
+}
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Order-preserving map of a float to an unsigned key (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace mxmoe

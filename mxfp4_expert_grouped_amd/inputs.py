@@ -33,6 +33,8 @@ experts: MXFP4 bytes drawn directly by a counter-based generator (Philox4x64-10,
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace
 from typing import Optional, Tuple
 
@@ -198,10 +200,24 @@ def gen_mx_matrix(seed: int, code_stream: int, scale_stream: int, rows: int, k: 
     nb = k // 32
     b0 = row0 * nb
     nblk = n * nb
-    # element codes: one Philox call per block of 32 elements
-    rb = philox_bytes((seed, code_stream), b0, nblk)  # [nblk, 32]
-    codes = MAG_TABLE[rb & 0x7F] | ((rb >> 7) << 3)
-    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8).reshape(n, k // 2)
+    # element codes: one Philox call per block of 32 elements (chunked over
+    # threads; numpy releases the GIL inside its array operations)
+    packed = np.empty((nblk, 16), dtype=np.uint8)
+
+    def fill(lo: int, hi: int) -> None:
+        rb = philox_bytes((seed, code_stream), b0 + lo, hi - lo)  # [hi-lo, 32]
+        codes = MAG_TABLE[rb & 0x7F] | ((rb >> 7) << 3)
+        packed[lo:hi] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+
+    step = 1 << 15
+    spans = [(lo, min(lo + step, nblk)) for lo in range(0, nblk, step)]
+    if len(spans) > 1:
+        with ThreadPoolExecutor(max_workers=min(len(spans), os.cpu_count() or 1, 16)) as ex:
+            list(ex.map(lambda sp: fill(*sp), spans))
+    else:
+        for sp in spans:
+            fill(*sp)
+    packed = packed.reshape(n, k // 2)
     # scales: one Philox call per 32 blocks
     c_first = b0 // 32
     c_last = (b0 + nblk - 1) // 32

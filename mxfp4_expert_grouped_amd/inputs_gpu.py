@@ -1,0 +1,87 @@
+"""Seeded synthetic inputs placed on the GPU.
+
+Dense inputs (x, W_r, bias) come from :mod:`.inputs` on the host and are
+copied over.  The MXFP4 expert weights (21 GB for the full layer) are drawn on
+the device by ``libmxmoe_inputs.so``, the GPU twin of the Philox recipe in
+:mod:`.inputs`, which produces the same bytes as the numpy generator.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_int, c_int64, c_uint64, c_void_p
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import inputs as I
+from .layer import DeviceWeights
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+GEN_LIB_PATH = os.path.join(_PKG, "libmxmoe_inputs.so")
+_gen = None
+
+
+def _genlib():
+    global _gen
+    if _gen is None:
+        if not os.path.exists(GEN_LIB_PATH):
+            raise ImportError(f"{GEN_LIB_PATH} is not built")
+        lib = ctypes.CDLL(GEN_LIB_PATH)
+        lib.mxmoe_gen_mx_matrix.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_uint64,
+                                            c_uint64, c_uint64, c_int, c_void_p]
+        lib.mxmoe_gen_mx_matrix.restype = c_int
+        _gen = lib
+    return _gen
+
+
+def gen_mx_matrix_device(codes: torch.Tensor, scales: torch.Tensor, rows: int, k: int, seed: int,
+                         code_stream: int, scale_stream: int, e_base: int) -> None:
+    rc = _genlib().mxmoe_gen_mx_matrix(codes.data_ptr(), scales.data_ptr(), rows, k, seed,
+                                       code_stream, scale_stream, e_base,
+                                       torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"mxmoe_gen_mx_matrix failed ({rc})")
+
+
+def gen_experts_device(cfg: I.LayerConfig, kind: str, count: int, layer: int = 0,
+                       device="cuda") -> Tuple[torch.Tensor, ...]:
+    """Stacked (gu_codes, gu_scales, dn_codes, dn_scales) of `count` experts."""
+    d, f = cfg.d_model, cfg.d_ff
+    guc = torch.empty((count, 2 * f, d // 2), dtype=torch.uint8, device=device)
+    gus = torch.empty((count, 2 * f, d // 32), dtype=torch.uint8, device=device)
+    dnc = torch.empty((count, d, f // 2), dtype=torch.uint8, device=device)
+    dns = torch.empty((count, d, f // 32), dtype=torch.uint8, device=device)
+    eb = I.scale_exponent_base(d)
+    for i in range(count):
+        slot = I.expert_slot(kind, i)
+        gen_mx_matrix_device(guc[i], gus[i], 2 * f, d, cfg.seed,
+                             I.stream_id(I.KIND_GU_CODES, slot, layer),
+                             I.stream_id(I.KIND_GU_SCALES, slot, layer), eb)
+        gen_mx_matrix_device(dnc[i], dns[i], d, f, cfg.seed,
+                             I.stream_id(I.KIND_DN_CODES, slot, layer),
+                             I.stream_id(I.KIND_DN_SCALES, slot, layer), eb)
+    return guc, gus, dnc, dns
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def device_weights(cfg: I.LayerConfig, layer: int = 0, device="cuda") -> DeviceWeights:
+    guc, gus, dnc, dns = gen_experts_device(cfg, "routed", cfg.num_experts, layer, device)
+    if cfg.num_shared:
+        sguc, sgus, sdnc, sdns = gen_experts_device(cfg, "shared", cfg.num_shared, layer, device)
+    else:
+        sguc = sgus = sdnc = sdns = None
+    wr = torch.from_numpy(I.gen_router_w(cfg, layer)).to(device)
+    b = I.gen_router_b(cfg)
+    br = torch.from_numpy(b).to(device) if b is not None else None
+    return DeviceWeights(guc, gus, dnc, dns, sguc, sgus, sdnc, sdns, wr, br)
+
+
+def device_x(cfg: I.LayerConfig, tokens: Optional[int] = None, layer: int = 0,
+             device="cuda") -> torch.Tensor:
+    return bf16_tensor(I.gen_x(cfg, tokens, layer), device)

@@ -92,14 +92,14 @@ def topk_select(logits, k: int):
     """
     l = np.asarray(logits, dtype=np.float64)
     t_count, e_count = l.shape
-    ids = np.zeros((t_count, k), dtype=np.int32)
+    idx = np.broadcast_to(np.arange(e_count), l.shape)
+    # per row: primary key logit descending, then expert index ascending
+    order = np.lexsort((idx, -l), axis=-1)
+    ids = np.sort(order[:, :k], axis=1).astype(np.int32)
     gap = np.full(t_count, np.inf)
-    idx = np.arange(e_count)
-    for t in range(t_count):
-        order = np.lexsort((idx, -l[t]))  # primary: logit desc, then index asc
-        ids[t] = np.sort(order[:k])
-        if k < e_count:
-            gap[t] = l[t, order[k - 1]] - l[t, order[k]]
+    if k < e_count:
+        rows = np.arange(t_count)
+        gap = l[rows, order[:, k - 1]] - l[rows, order[:, k]]
     return ids, gap
 
 
@@ -190,9 +190,9 @@ class LayerResult:
     offsets: np.ndarray
     row_src: np.ndarray
     token_row: np.ndarray
-    x_codes: np.ndarray
+    tokens: np.ndarray  # tokens whose activations and outputs below were computed
+    x_codes: np.ndarray  # [len(tokens), d]
     x_scales: np.ndarray
-    tokens: np.ndarray  # tokens whose outputs below were computed
     y_routed: np.ndarray  # [len(tokens), d] float64
     y_shared: np.ndarray
     y: np.ndarray
@@ -216,10 +216,11 @@ def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: i
     ids, gap = topk_select(logits, top_k)
     w = routing_weights(logits, ids)
     counts, offsets, row_src, token_row = permute(ids, num_experts)
-    x_codes, x_scales = mx.mx_quantize(bf16_to_f64(x_bf16), "e4m3")
 
     toks = np.arange(t_count) if tokens is None else np.asarray(sorted(set(int(t) for t in tokens)))
     pos = {int(t): i for i, t in enumerate(toks)}
+    # MXFP8 activations of the computed tokens (row i <-> token toks[i])
+    x_codes, x_scales = mx.mx_quantize(bf16_to_f64(x_bf16[toks]), "e4m3")
     y_routed = np.zeros((len(toks), d))
     y_shared = np.zeros((len(toks), d))
     res_h: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
@@ -235,12 +236,13 @@ def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: i
         pairs = row_src[rows]
         tk = pairs // top_k
         jj = pairs % top_k
-        h_c, h_s, o = expert_mlp(x_codes[tk], x_scales[tk], *weights("routed", e), d_ff=d_ff)
+        xi = np.array([pos[int(t)] for t in tk])
+        h_c, h_s, o = expert_mlp(x_codes[xi], x_scales[xi], *weights("routed", e), d_ff=d_ff)
         for i in range(rows.size):
             res_h[int(rows[i])] = (h_c[i], h_s[i])
             y_routed[pos[int(tk[i])]] += w[tk[i], jj[i]] * o[i]
     for s in range(num_shared):
-        h_c, h_s, o = expert_mlp(x_codes[toks], x_scales[toks], *weights("shared", s), d_ff=d_ff)
+        h_c, h_s, o = expert_mlp(x_codes, x_scales, *weights("shared", s), d_ff=d_ff)
         for i, t in enumerate(toks):
             res_hs[(s, int(t))] = (h_c[i], h_s[i])
         y_shared += o

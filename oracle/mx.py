@@ -79,10 +79,12 @@ def mx_decode(codes, scales, fmt: str) -> np.ndarray:
     for "e2m1".  scales: [rows, K/32] E8M0 bytes.  Each block of 32 elements
     along K is multiplied by its own scale (exact: a power of two).
     """
+    # decode through the format's value table (same values as the bit-field
+    # decoders, looked up per code for speed on large matrices)
     if fmt == "e2m1":
-        vals = decode_e2m1(unpack_fp4(codes))
+        vals = decode_e2m1(np.arange(16))[unpack_fp4(codes)]
     elif fmt == "e4m3":
-        vals = decode_e4m3(codes)
+        vals = decode_e4m3(np.arange(256))[np.asarray(codes, dtype=np.uint8)]
     else:
         raise ValueError(fmt)
     rows, k = vals.shape

@@ -1,0 +1,158 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function the header declares, and rejects bad arguments with the documented
+status before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxmoe.h")
+
+
+@pytest.fixture(scope="module")
+def M():
+    from mxfp4_expert_grouped_amd import mxmoe
+    if not os.path.exists(mxmoe.LIB_PATH):
+        from mxfp4_expert_grouped_amd import build
+        build.build()
+    mxmoe.load_library()
+    return mxmoe
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_header_function(M):
+    fns = header_functions()
+    assert set(fns) == set(M.EXPORTED), fns
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for name in fns:
+        assert hasattr(lib, name), name
+
+
+def test_input_generator_library_exports():
+    from mxfp4_expert_grouped_amd import inputs_gpu
+    if not os.path.exists(inputs_gpu.GEN_LIB_PATH):
+        from mxfp4_expert_grouped_amd import build
+        build.build()
+    lib = ctypes.CDLL(inputs_gpu.GEN_LIB_PATH)
+    assert hasattr(lib, "mxmoe_gen_mx_matrix")
+
+
+def test_status_strings(M):
+    lib = M.load_library()
+    for s in range(5):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_model=7168, d_ff=2048, num_experts=896, top_k=16, num_shared=2, max_tokens=32768), 0),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 0),
+    (dict(d_model=200, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 2),
+    (dict(d_model=256, d_ff=96, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 2),
+    (dict(d_model=256, d_ff=128, num_experts=1025, top_k=2, num_shared=1, max_tokens=8), 2),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=17, num_shared=1, max_tokens=8), 2),
+    (dict(d_model=256, d_ff=128, num_experts=64, top_k=33, num_shared=1, max_tokens=8), 2),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=0, num_shared=1, max_tokens=8), 1),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=-1, max_tokens=8), 1),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=9, max_tokens=8), 2),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=0), 1),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8, flags=1), 1),
+])
+def test_plan_validation(M, kw, status):
+    if status == 0:
+        p = M.moe_plan(**kw)
+        assert p.value
+        M.moe_plan_destroy(p)
+    else:
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_plan(**kw)
+        assert ei.value.status == status
+        assert ei.value.detail
+
+
+def test_workspace_bytes(M):
+    p = M.moe_plan(7168, 2048, 896, 16, 2, 32768)
+    try:
+        assert M.moe_workspace_bytes(p, 0) == 0
+        w1 = M.moe_workspace_bytes(p, 1)
+        w256 = M.moe_workspace_bytes(p, 256)
+        w32k = M.moe_workspace_bytes(p, 32768)
+        assert 0 < w1 < w256 < w32k
+        # at least the fp32 expert outputs: (T*k + S*T) rows of d floats
+        assert w32k >= 32768 * 18 * 7168 * 4
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_workspace_bytes(p, 32769)
+        assert ei.value.status == M.MOE_ERR_INVALID_ARG
+    finally:
+        M.moe_plan_destroy(p)
+
+
+def test_forward_argument_errors_before_any_device_call(M):
+    p = M.moe_plan(256, 128, 16, 2, 1, 8)
+    fake = 1 << 20  # never dereferenced: every call below fails validation first
+    W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None)
+    ws = M.moe_workspace_bytes(p, 8)
+    try:
+        # T == 0 is a no-op even with null buffers
+        M.moe_forward(p, W, None, 0, None, None, 0)
+        cases = [
+            (dict(num_tokens=9), M.MOE_ERR_INVALID_ARG),
+            (dict(num_tokens=-1), M.MOE_ERR_INVALID_ARG),
+            (dict(x=0), M.MOE_ERR_INVALID_ARG),
+            (dict(workspace=0), M.MOE_ERR_WORKSPACE),
+            (dict(workspace_bytes=ws - 1), M.MOE_ERR_WORKSPACE),
+            (dict(workspace=fake + 16), M.MOE_ERR_WORKSPACE),
+            (dict(x=fake + 2), M.MOE_ERR_INVALID_ARG),
+        ]
+        for over, status in cases:
+            args = dict(x=fake, num_tokens=8, y=fake, workspace=fake, workspace_bytes=ws)
+            args.update(over)
+            with pytest.raises(M.MoeError) as ei:
+                M.moe_forward(p, W, args["x"] or None, args["num_tokens"], args["y"],
+                              args["workspace"] or None, args["workspace_bytes"])
+            assert ei.value.status == status, (over, ei.value)
+        # missing shared weights
+        W2 = M.MoeWeights(fake, fake, fake, fake, None, None, None, None, fake, None)
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_forward(p, W2, fake, 8, fake, fake, ws)
+        assert ei.value.status == M.MOE_ERR_INVALID_ARG
+    finally:
+        M.moe_plan_destroy(p)
+
+
+def test_quantize_argument_errors(M):
+    fake = 1 << 20
+    M.moe_quantize_act(None, M.MOE_SRC_BF16, 0, 64, 64, None, None)  # empty: no-op
+    for args, status in [
+        ((fake, 7, 4, 64, 64, fake, fake), M.MOE_ERR_INVALID_ARG),
+        ((fake, M.MOE_SRC_BF16, 4, 48, 48, fake, fake), M.MOE_ERR_UNSUPPORTED),
+        ((fake, M.MOE_SRC_BF16, 4, 64, 32, fake, fake), M.MOE_ERR_INVALID_ARG),
+        ((None, M.MOE_SRC_BF16, 4, 64, 64, fake, fake), M.MOE_ERR_INVALID_ARG),
+        ((fake + 4, M.MOE_SRC_FP32, 4, 64, 64, fake, fake), M.MOE_ERR_UNSUPPORTED),
+    ]:
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_quantize_act(*args)
+        assert ei.value.status == status
+
+
+def test_no_device_reports_device_error(M):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    p = M.moe_plan(256, 128, 16, 2, 1, 8)
+    fake = 1 << 20
+    W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None)
+    try:
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_forward(p, W, fake, 8, fake, fake, M.moe_workspace_bytes(p, 8))
+        assert ei.value.status == M.MOE_ERR_DEVICE
+    finally:
+        M.moe_plan_destroy(p)

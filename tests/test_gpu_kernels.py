@@ -1,0 +1,239 @@
+"""GPU parity at small and medium sizes, through the C ABI, against the oracle.
+
+Covers: the GPU twin of the input generator, the MXFP8 quantiser (bit-exact,
+bf16 and fp32 sources, adversarial blocks), the scaled-MFMA operand layout in
+the exact-arithmetic regime (bit-exact gate/up accumulators), the tiny layer
+with every tap, ragged token counts on both permutation paths and both tile
+heights, a single expert receiving every token, k=1 without shared experts,
+determinism and indifference to workspace contents.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mxfp4_expert_grouped_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mxfp4_expert_grouped_amd import mxmoe
+    mxmoe.load_library()  # raises if the HIP library is missing: no fallback
+    torch.cuda.set_device(0)
+    yield
+
+
+import parity as P  # noqa: E402  (after the marker; imports torch-side helpers)
+
+
+# ---------------------------------------------------------------------------
+# input generator twin
+# ---------------------------------------------------------------------------
+
+def test_gpu_generator_matches_numpy_tiny_all_experts():
+    cfg = I.CONFIGS["tiny"]
+    W = P.IG.device_weights(cfg)
+    ref = I.ExpertWeights(cfg)
+    for e in range(cfg.num_experts):
+        for got, want in zip((W.gu_codes[e], W.gu_scales[e], W.dn_codes[e], W.dn_scales[e]),
+                             ref("routed", e)):
+            assert np.array_equal(got.cpu().numpy(), want)
+    for got, want in zip((W.sgu_codes[0], W.sgu_scales[0], W.sdn_codes[0], W.sdn_scales[0]),
+                         ref("shared", 0)):
+        assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_gpu_generator_matches_numpy_full_shape_sample():
+    cfg = I.CONFIGS["decode1"]
+    guc, gus, dnc, dns = P.IG.gen_experts_device(cfg, "routed", 1)
+    eb = I.scale_exponent_base(cfg.d_model)
+    c, s = I.gen_mx_matrix(cfg.seed, I.stream_id(I.KIND_GU_CODES, 0), I.stream_id(I.KIND_GU_SCALES, 0),
+                           2 * cfg.d_ff, cfg.d_model, eb, row0=1000, nrows=64)
+    assert np.array_equal(guc[0, 1000:1064].cpu().numpy(), c)
+    assert np.array_equal(gus[0, 1000:1064].cpu().numpy(), s)
+    c, s = I.gen_mx_matrix(cfg.seed, I.stream_id(I.KIND_DN_CODES, 0), I.stream_id(I.KIND_DN_SCALES, 0),
+                           cfg.d_model, cfg.d_ff, eb, row0=7100, nrows=68)
+    assert np.array_equal(dnc[0, 7100:].cpu().numpy(), c)
+    assert np.array_equal(dns[0, 7100:].cpu().numpy(), s)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 quantiser
+# ---------------------------------------------------------------------------
+
+def _adversarial_rows(rng, cols):
+    rows = []
+    rows.append(rng.standard_normal(cols))
+    rows.append(rng.standard_normal(cols) * 1e-30)
+    rows.append(rng.standard_normal(cols) * 3e4)
+    rows.append(np.zeros(cols))
+    r = rng.standard_normal(cols)
+    r[::32] = 1.9 * 8  # saturating block maxima
+    rows.append(r)
+    # exact E4M3 midpoints at scale 1 (amax forced to 256 -> e = 0)
+    mids = (OXgrid[:-1] + OXgrid[1:]) / 2
+    r = np.resize(np.concatenate([mids, -mids]), cols)
+    r[::32] = 256.0
+    rows.append(r)
+    r = np.full(cols, -0.0)
+    rows.append(r)
+    r = rng.standard_normal(cols) * 2.0 ** -130  # fp32 subnormals
+    rows.append(r)
+    r = rng.standard_normal(cols)
+    r[5::32] = 2.0 ** -140  # tiny element in a normal block
+    rows.append(r)
+    return np.array(rows)
+
+
+from oracle import mx as OX  # noqa: E402
+
+OXgrid = OX.decode_e4m3(np.arange(0, 0x7F))
+
+
+@pytest.mark.parametrize("src", ["fp32", "bf16"])
+def test_quantize_act_bit_exact(src):
+    from mxfp4_expert_grouped_amd.layer import quantize_act
+    rng = np.random.default_rng(11)
+    cols = 7168
+    v = np.concatenate([_adversarial_rows(rng, cols), rng.standard_normal((55, cols)) * 5])
+    v32 = v.astype(np.float32)
+    if src == "bf16":
+        bits = I.f32_to_bf16_bits(v32)
+        t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        ref_in = P.OM.bf16_to_f64(bits)
+    else:
+        t = torch.from_numpy(v32).cuda()
+        ref_in = v32.astype(np.float64)
+    codes, scales = quantize_act(t)
+    torch.cuda.synchronize()
+    rc, rs = OX.mx_quantize(ref_in, "e4m3")
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_act_strided_and_ragged_rows():
+    from mxfp4_expert_grouped_amd import mxmoe as M
+    rng = np.random.default_rng(12)
+    full = rng.standard_normal((37, 160)).astype(np.float32)
+    t = torch.from_numpy(full).cuda()
+    view = t[:, :96]  # ld = 160 elements, cols = 96
+    codes = torch.empty((37, 96), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((37, 3), dtype=torch.uint8, device="cuda")
+    M.moe_quantize_act(view.data_ptr(), M.MOE_SRC_FP32, 37, 96, 160, codes.data_ptr(),
+                       scales.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rc, rs = OX.mx_quantize(full[:, :96].astype(np.float64), "e4m3")
+    assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rs)
+
+
+# ---------------------------------------------------------------------------
+# exact-arithmetic regime: gate/up accumulators bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,f", [(256, 128), (1024, 512)])
+def test_gate_up_accumulators_exact(d, f):
+    """x integer-valued in [-16, 16]: every MXFP8 element is exact and every
+    partial sum is an integer multiple of 2^-7 below 2^14, so fp32 accumulation
+    is exact and the GPU's gate/up values must equal the float64 ones bit for bit
+    (any lane/K/scale layout error shows up as a mismatch)."""
+    cfg = I.LayerConfig("exact", 40, d, 8, 2, f, 1, seed=21)
+    rng = np.random.default_rng(5)
+    xi = rng.integers(-16, 17, size=(cfg.tokens, d)).astype(np.float32)
+    bits = I.f32_to_bf16_bits(xi)
+    x = P.IG.bf16_tensor(bits)
+    W = P.IG.device_weights(cfg)
+    g = P.run_gpu(cfg, W, x)
+    ref = I.ExpertWeights(cfg)
+    res = P.OM.forward(bits, I.gen_router_w(cfg), None, ref, num_experts=8, top_k=2, num_shared=1, d_ff=f)
+    assert np.array_equal(g["topk_ids"], res.topk_ids)
+    R = cfg.tokens * 2
+    nmis = 0
+    for r in range(R):
+        p = int(res.row_src[r])
+        t, e = p // 2, int(res.topk_ids[p // 2, p % 2])
+        a = OX.mx_decode(res.x_codes[t:t + 1], res.x_scales[t:t + 1], "e4m3")
+        guc, gus, _, _ = ref("routed", e)
+        want = a @ OX.mx_decode(guc, gus, "e2m1").T
+        assert np.all(np.abs(want) < 2 ** 14)
+        nmis += int(np.sum(g["gu_acc"][r].astype(np.float64) != want[0]))
+    for t in range(cfg.tokens):
+        a = OX.mx_decode(res.x_codes[t:t + 1], res.x_scales[t:t + 1], "e4m3")
+        guc, gus, _, _ = ref("shared", 0)
+        want = a @ OX.mx_decode(guc, gus, "e2m1").T
+        nmis += int(np.sum(g["gu_acc"][R + t].astype(np.float64) != want[0]))
+    assert nmis == 0
+
+
+# ---------------------------------------------------------------------------
+# whole layer at small sizes
+# ---------------------------------------------------------------------------
+
+def _layer_case(cfg, bias=None, tokens=None):
+    x_bits = I.gen_x(cfg)
+    x = P.IG.bf16_tensor(x_bits)
+    W = P.IG.device_weights(cfg)
+    b = I.gen_router_b(cfg) if bias is None else np.asarray(bias, np.float32)
+    if b is not None:
+        W.router_b = torch.from_numpy(b).cuda()
+    P.log(f"case {cfg}")
+    g = P.run_gpu(cfg, W, x)
+    return P.compare_layer(cfg, x_bits, I.gen_router_w(cfg), b, I.ExpertWeights(cfg), g, tokens)
+
+
+def test_tiny_layer_all_taps():
+    cfg = I.CONFIGS["tiny"]
+    res, differ = _layer_case(cfg)
+    assert not differ
+
+
+@pytest.mark.parametrize("T", [1, 3, 13, 64, 65, 200, 256, 1100, 1500])
+def test_ragged_token_counts(T):
+    # 256 and above use 64-row tiles (>= 24 rows per expert on average);
+    # above 1024 tokens the multi-kernel permutation path runs
+    cfg = I.LayerConfig("ragged", T, 256, 16, 2, 128, 1, seed=T)
+    tokens = None if T <= 256 else list(range(0, T, max(1, T // 40)))
+    _layer_case(cfg, tokens=tokens)
+
+
+def test_medium_layer_k4_two_shared():
+    cfg = I.LayerConfig("mid", 96, 1024, 32, 4, 512, 2, seed=7)
+    _layer_case(cfg)
+
+
+def test_all_tokens_to_one_expert_k1_no_shared():
+    cfg = I.LayerConfig("hot", 300, 256, 16, 1, 128, 0, seed=8)
+    bias = np.zeros(16, np.float32)
+    bias[5] = 50.0
+    res, _ = _layer_case(cfg, bias=bias)
+    assert np.all(res.topk_ids == 5)
+
+
+def test_zipf_bias_small():
+    cfg = I.LayerConfig("skew", 400, 512, 64, 4, 256, 2, zipf_bias=True, seed=9)
+    _layer_case(cfg)
+
+
+def test_zero_tokens_is_noop():
+    from mxfp4_expert_grouped_amd.layer import MoeLayer
+    cfg = I.CONFIGS["tiny"]
+    W = P.IG.device_weights(cfg)
+    layer = MoeLayer(256, 128, 16, 2, 1, 8, W)
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
+    y = layer.forward(x)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 256)
+
+
+def test_deterministic_and_workspace_independent():
+    cfg = I.LayerConfig("det", 200, 1024, 32, 4, 512, 2, seed=10)
+    x = P.IG.device_x(cfg)
+    W = P.IG.device_weights(cfg)
+    a = P.run_gpu(cfg, W, x, taps=False, workspace_fill=0)["y"]
+    b = P.run_gpu(cfg, W, x, taps=False, workspace_fill=0xFF)["y"]
+    c = P.run_gpu(cfg, W, x, taps=True, workspace_fill=0x5A)["y"]
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
