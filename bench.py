@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4/MXFP8 sparse MoE layer on one MI355X.
+
+One step = one whole forward of the layer (router, top-k, MXFP8 quantisation,
+permutation, gate_up + SwiGLU + re-quantisation, down, combine) over one batch
+of synthetic tokens, inputs already resident in HBM.
+
+Default workload: decode with 1 token (d=7168, 896 experts, top-16, d_ff=2048,
+2 shared).  Consecutive steps use different token batches and rotate over
+several independently generated copies of the layer's weights, so no step finds
+its experts in the 256 MB last-level cache (as in a real decode step, where the
+other layers' weights pass through in between).
+
+Prints ONE JSON line.  Also reports the dominant kernel's achieved bandwidth
+(or MFMA rate) against the MI355X peak, timed with HIP events inside the timed
+region, and the CPU oracle's throughput on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "MoE-layer tokens/s + HBM GB/s (decode) / MXFP4 TFLOPS (prefill) vs peak"
+HBM_PEAK_GBS = 8000.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # dense FP8 (the rate of FP8 x FP4 operand pairs)
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # dense MXFP4 x MXFP4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="decode1",
+                    choices=["tiny", "decode1", "decode256", "prefill8k", "prefill32k_skew"])
+    ap.add_argument("--layers", type=int, default=None,
+                    help="independent weight copies rotated per step")
+    ap.add_argument("--batches", type=int, default=None, help="distinct token batches per layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the forward as a HIP graph")
+    ap.add_argument("--breakdown", action="store_true", help="also time every stage (untimed pass)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the layer fits one "
+                                   "MI355X and nothing here shards it; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from mxfp4_expert_grouped_amd import inputs as I
+    from mxfp4_expert_grouped_amd import inputs_gpu as IG
+    from mxfp4_expert_grouped_amd import mxmoe as M
+    from mxfp4_expert_grouped_amd.layer import MoeLayer
+
+    M.load_library()
+    torch.cuda.set_device(0)
+    cfg = I.CONFIGS[args.config]
+    decode = cfg.tokens <= 256
+    steps = args.steps or (200 if decode else 10)
+    warmup = args.warmup if args.warmup is not None else (20 if decode else 2)
+    nlayers = args.layers or (4 if decode else 1)
+    nbatch = args.batches or (8 if cfg.tokens <= 256 else 1)
+    T = cfg.tokens
+
+    # ---- inputs resident in HBM ------------------------------------------------
+    t0 = time.time()
+    layers, xs = [], []
+    for li in range(nlayers):
+        W = IG.device_weights(cfg, layer=li)
+        layers.append(MoeLayer(cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k, cfg.num_shared, T, W))
+        xs.append([IG.device_x(cfg, layer=1000 * li + bi) for bi in range(nbatch)])
+    ws = torch.empty(layers[0].workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    ys = torch.empty((T, cfg.d_model), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    # realised routing of every (layer, batch): touched experts -> algorithmic bytes
+    gu_bytes = I.matrix_bytes(2 * cfg.d_ff, cfg.d_model)
+    dn_bytes = I.matrix_bytes(cfg.d_model, cfg.d_ff)
+    touched = {}
+    offs = torch.empty(cfg.num_experts + 1, dtype=torch.int32, device="cuda")
+    for li, L in enumerate(layers):
+        for bi, x in enumerate(xs[li]):
+            L.forward(x, y=ys, taps={"expert_offsets": offs}, workspace=ws)
+            counts = np.diff(offs.cpu().numpy())
+            touched[(li, bi)] = (int((counts > 0).sum()), counts)
+    R = T * cfg.top_k + cfg.num_shared * T
+    act_in = T * (cfg.d_model + cfg.d_model // 32)            # MXFP8 x rows
+    h_bytes = R * (cfg.d_ff + cfg.d_ff // 32)                  # MXFP8 h rows
+    router_bytes = cfg.num_experts * cfg.d_model * 4
+    xy_bytes = 2 * T * cfg.d_model * 2
+
+    def step_bytes(key):
+        n = touched[key][0] + cfg.num_shared
+        return n * (gu_bytes + dn_bytes) + router_bytes + xy_bytes
+
+    def gate_up_bytes(key):
+        n = touched[key][0] + cfg.num_shared
+        return n * gu_bytes + act_in + h_bytes
+
+    sched = [(s % nlayers, (s // nlayers) % nbatch) for s in range(steps)]
+
+    def run(s):
+        li, bi = sched[s % len(sched)] if s >= 0 else (0, 0)
+        layers[li].forward(xs[li][bi], y=ys, workspace=ws)
+
+    graphs = None
+    if args.graph:
+        graphs = {}
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            for key in set(sched):
+                layers[key[0]].forward(xs[key[0]][key[1]], y=ys, workspace=ws)
+        torch.cuda.current_stream().wait_stream(st)
+        for key in set(sched):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layers[key[0]].forward(xs[key[0]][key[1]], y=ys, workspace=ws)
+            graphs[key] = g
+
+        def run(s):  # noqa: F811
+            graphs[sched[s % len(sched)]].replay()
+
+    # ---- warmup, then the timed region ----------------------------------------------
+    for s in range(warmup):
+        run(s)
+    torch.cuda.synchronize()
+    if not args.graph:
+        for L in layers:
+            M.moe_profile_begin(L.plan, ["gate_up"], steps)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for s in range(steps):
+        run(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall_ms / steps
+    gu_ms = None
+    if not args.graph:
+        tot, calls = 0.0, 0
+        for L in layers:
+            stage_ms, n = M.moe_profile_end(L.plan)
+            tot += stage_ms["gate_up"]
+            calls += n
+        gu_ms = tot / max(calls, 1)
+
+    stage_avg = None
+    if args.breakdown:
+        for L in layers:
+            M.moe_profile_begin(L.plan, list(M.STAGES), max(1, steps // nlayers + 1))
+        for s in range(min(steps, 8 * nlayers)):
+            run(s)
+        torch.cuda.synchronize()
+        acc = {k: 0.0 for k in M.STAGES}
+        calls = 0
+        for L in layers:
+            sm, n = M.moe_profile_end(L.plan)
+            calls += n
+            for k in acc:
+                acc[k] += sm[k]
+        stage_avg = {k: round(v / max(calls, 1), 5) for k, v in acc.items()}
+
+    # ---- derived figures ------------------------------------------------------------------
+    mean_step_bytes = float(np.mean([step_bytes(k) for k in sched]))
+    mean_gu_bytes = float(np.mean([gate_up_bytes(k) for k in sched]))
+    flops = 2.0 * R * 3 * cfg.d_model * cfg.d_ff
+    tokens_per_s = T / (ms_per_step / 1e3)
+    layer_gbs = mean_step_bytes / (ms_per_step / 1e3) / 1e9
+    layer_tflops = flops / (ms_per_step / 1e3) / 1e12
+    if decode:
+        kern_ms = gu_ms if gu_ms else ms_per_step
+        achieved = mean_gu_bytes / (kern_ms / 1e3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "gate_up grouped GEMM (k_gemm, 16-row tiles)",
+                    "kernel_ms": round(kern_ms, 5),
+                    "algorithmic_bytes_per_launch": int(mean_gu_bytes)}
+    else:
+        kern_ms = gu_ms if gu_ms else ms_per_step
+        gu_flops = 2.0 * R * cfg.d_model * 2 * cfg.d_ff
+        achieved = gu_flops / (kern_ms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4),
+                    "frac_of_mxfp4_peak": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4),
+                    "traffic": None, "kernel": "gate_up grouped GEMM (k_gemm, 64-row tiles)",
+                    "kernel_ms": round(kern_ms, 5), "algorithmic_flops_per_launch": gu_flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8 x mxfp4, fp32 accumulate",
+        "data": "synthetic (seeded; random-init MXFP4 weights)",
+        "config": {"workload": f"{cfg.name}: T={T}, d_model={cfg.d_model}, experts={cfg.num_experts}, "
+                               f"top_k={cfg.top_k}, d_ff={cfg.d_ff}, shared={cfg.num_shared}"
+                               + (", Zipf(1.1) router bias" if cfg.zipf_bias else ""),
+                   "tokens_per_step": T, "weight_copies_rotated": nlayers,
+                   "token_batches": nbatch, "hip_graph": bool(args.graph)},
+        "layer_hbm_gbps": round(layer_gbs, 1),
+        "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+        "layer_tflops": round(layer_tflops, 2),
+        "algorithmic_bytes_per_step": int(mean_step_bytes),
+        "gpu_event_ms_per_step": round(gpu_ms / steps, 5),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    if stage_avg:
+        out["stage_ms"] = stage_avg
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg):
+    """The oracle, untuned, on the host cores for a bounded sample of the workload."""
+    from mxfp4_expert_grouped_amd import inputs as I
+    from oracle import moe as OM
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    ntok = 1 if cfg.tokens <= 16 else 2
+    # the decode sample is the whole step (the first batch of the first layer);
+    # larger workloads: the first tokens of the batch (rows are independent)
+    x_all = I.gen_x(cfg, layer=0)
+    x = x_all[:ntok]
+    wr, b = I.gen_router_w(cfg, 0), I.gen_router_b(cfg)
+    W = I.ExpertWeights(cfg)
+    ids = OM.topk_select(OM.router_logits(x, wr, b), cfg.top_k)[0]
+    for e in sorted(set(ids.reshape(-1).tolist())):  # input generation stays outside the timing
+        W("routed", e)
+    for s in range(cfg.num_shared):
+        W("shared", s)
+    t0 = time.perf_counter()
+    OM.forward(x, wr, b, W, num_experts=cfg.num_experts, top_k=cfg.top_k,
+               num_shared=cfg.num_shared, d_ff=cfg.d_ff)
+    sec = time.perf_counter() - t0
+    return {"value": round(ntok / sec, 4), "unit": "tokens/s",
+            "cores": int(max(blas_threads, 1)), "kind": "oracle",
+            "sample": f"{ntok} token(s) of the {cfg.name} workload (layer copy 0, batch 0): "
+                      f"routing, MXFP8 quantisation, {len(set(ids.reshape(-1).tolist()))} routed + "
+                      f"{cfg.num_shared} shared experts in float64; {sec:.1f} s",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -71,7 +71,8 @@ typedef struct {
   uint32_t flags;
 } moe_config;
 
-/* Opaque plan: host memory owned by the library, immutable after moe_plan. */
+/* Opaque plan: host memory owned by the library; its shape is immutable after
+ * moe_plan (only the optional profiling state below changes). */
 typedef struct moe_plan_s moe_plan_t;
 
 typedef struct {
@@ -124,6 +125,28 @@ moe_status moe_quantize_act(const void *src, moe_src_dtype dt, int64_t rows, int
 moe_status moe_forward(const moe_plan_t *plan, const moe_weights *w, const void *x_bf16,
                        int64_t num_tokens, void *y_bf16, void *workspace, size_t workspace_bytes,
                        const moe_taps *taps, void *stream);
+
+/* Stages of moe_forward, for per-stage timing. */
+typedef enum {
+  MOE_STAGE_ROUTER = 0,  /* router logits                                   */
+  MOE_STAGE_TOPK = 1,    /* top-k, routing weights, MXFP8 quantisation of x */
+  MOE_STAGE_PERMUTE = 2, /* permutation and grouped-GEMM tile list          */
+  MOE_STAGE_GATE_UP = 3, /* gate_up grouped GEMM + SwiGLU + MXFP8 of h      */
+  MOE_STAGE_DOWN = 4,    /* down grouped GEMM                               */
+  MOE_STAGE_COMBINE = 5, /* weighted combine -> y                           */
+  MOE_NUM_STAGES = 6
+} moe_stage;
+
+/* Per-stage timing with HIP events recorded on the forward's stream: after
+ * moe_profile_begin, each of the next max_calls (1..65536) moe_forward calls
+ * on this plan records an event pair around every stage whose bit
+ * (1u << stage) is set in stage_mask.  moe_profile_end waits for those events,
+ * writes the summed milliseconds per stage to stage_ms[MOE_NUM_STAGES] (zero
+ * for unrecorded stages) and the number of recorded calls to *calls, and stops
+ * recording.  Host-side state of the plan; no device memory is allocated.
+ * Profiling a plan that is used by several threads at once is not supported. */
+moe_status moe_profile_begin(moe_plan_t *plan, uint32_t stage_mask, int32_t max_calls);
+moe_status moe_profile_end(moe_plan_t *plan, double *stage_ms, int32_t *calls);
 
 const char *moe_status_string(moe_status s);
 const char *moe_last_error(void);

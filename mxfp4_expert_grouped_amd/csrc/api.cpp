@@ -9,6 +9,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/mxmoe.h"
 #include "internal.h"
@@ -17,6 +18,10 @@ using namespace mxmoe;
 
 struct moe_plan_s {
   moe_config cfg;
+  // optional per-stage timing (moe_profile_begin / moe_profile_end)
+  uint32_t prof_mask = 0;
+  int prof_cap = 0, prof_n = 0;
+  std::vector<hipEvent_t> prof_ev;  // [prof_cap][MOE_NUM_STAGES][2]
 };
 
 namespace {
@@ -125,6 +130,10 @@ moe_status check_config(const moe_config* c) {
   // permuted-row indices and element offsets must fit the kernels' int32 row math
   if ((c->max_tokens * (c->top_k + c->num_shared)) > (int64_t(1) << 30))
     return fail(MOE_ERR_UNSUPPORTED, "max_tokens * (top_k + num_shared) too large");
+  // MXFP8 activation buffers are addressed with 31-bit byte offsets
+  if (c->max_tokens * c->d_model >= (int64_t(1) << 31) ||
+      c->max_tokens * (c->top_k + c->num_shared) * c->d_ff >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "activation buffers exceed 2^31 bytes");
   return MOE_OK;
 }
 
@@ -157,7 +166,12 @@ moe_status moe_plan(const moe_config* cfg, moe_plan_t** out_plan) {
   return MOE_OK;
 }
 
-void moe_plan_destroy(moe_plan_t* plan) { delete plan; }
+void moe_plan_destroy(moe_plan_t* plan) {
+  if (!plan) return;
+  for (hipEvent_t x : plan->prof_ev)
+    if (x) (void)hipEventDestroy(x);
+  delete plan;
+}
 
 moe_status moe_workspace_bytes(const moe_plan_t* plan, int64_t num_tokens, size_t* out_bytes) {
   if (!plan || !out_bytes) return fail(MOE_ERR_INVALID_ARG, "plan or out_bytes is NULL");
@@ -270,15 +284,77 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
   a.nchunks = L.nchunks;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if ((e = launch_router(a, st)) != hipSuccess ||
-      (e = launch_topk_quant(a, st)) != hipSuccess ||
-      (e = launch_permute(a, st)) != hipSuccess ||
-      (e = launch_gemm_gate_up(a, st)) != hipSuccess ||
-      (e = launch_gemm_down(a, st)) != hipSuccess ||
-      (e = launch_combine(a, st)) != hipSuccess)
-    return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  moe_plan_t* pl = const_cast<moe_plan_t*>(plan);
+  const bool prof = pl->prof_mask && pl->prof_n < pl->prof_cap;
+  hipEvent_t* ev = prof ? &pl->prof_ev[size_t(pl->prof_n) * MOE_NUM_STAGES * 2] : nullptr;
+  typedef hipError_t (*Launch)(const FwdArgs&, hipStream_t);
+  static const Launch stages[MOE_NUM_STAGES] = {launch_router,       launch_topk_quant,
+                                                launch_permute,      launch_gemm_gate_up,
+                                                launch_gemm_down,    launch_combine};
+  for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+    const bool rec = prof && ((pl->prof_mask >> i) & 1u);
+    if (rec) (void)hipEventRecord(ev[2 * i], st);
+    hipError_t e = stages[i](a, st);
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+    if (rec) (void)hipEventRecord(ev[2 * i + 1], st);
+  }
+  if (prof) pl->prof_n++;
   return MOE_OK;
+}
+
+moe_status moe_profile_begin(moe_plan_t* plan, uint32_t stage_mask, int32_t max_calls) {
+  if (!plan) return fail(MOE_ERR_INVALID_ARG, "plan is NULL");
+  if (max_calls < 1 || max_calls > 65536) return fail(MOE_ERR_INVALID_ARG, "max_calls outside [1, 65536]");
+  if (stage_mask == 0 || stage_mask >= (1u << MOE_NUM_STAGES))
+    return fail(MOE_ERR_INVALID_ARG, "bad stage mask 0x%x", stage_mask);
+  if (plan->prof_mask) return fail(MOE_ERR_INVALID_ARG, "profiling already active on this plan");
+  moe_status s = check_device();
+  if (s != MOE_OK) return s;
+  plan->prof_ev.assign(size_t(max_calls) * MOE_NUM_STAGES * 2, nullptr);
+  for (int n = 0; n < max_calls; ++n)
+    for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+      if (!((stage_mask >> i) & 1u)) continue;
+      for (int j = 0; j < 2; ++j) {
+        hipEvent_t& e = plan->prof_ev[(size_t(n) * MOE_NUM_STAGES + i) * 2 + j];
+        if (hipEventCreate(&e) != hipSuccess) {
+          (void)hipGetLastError();
+          for (hipEvent_t x : plan->prof_ev)
+            if (x) (void)hipEventDestroy(x);
+          plan->prof_ev.clear();
+          return fail(MOE_ERR_DEVICE, "hipEventCreate failed");
+        }
+      }
+    }
+  plan->prof_cap = max_calls;
+  plan->prof_n = 0;
+  plan->prof_mask = stage_mask;
+  return MOE_OK;
+}
+
+moe_status moe_profile_end(moe_plan_t* plan, double* stage_ms, int32_t* calls) {
+  if (!plan || !stage_ms || !calls) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+  if (!plan->prof_mask) return fail(MOE_ERR_INVALID_ARG, "profiling is not active on this plan");
+  moe_status st = MOE_OK;
+  for (int i = 0; i < MOE_NUM_STAGES; ++i) stage_ms[i] = 0.0;
+  for (int n = 0; n < plan->prof_n; ++n)
+    for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+      if (!((plan->prof_mask >> i) & 1u)) continue;
+      hipEvent_t a = plan->prof_ev[(size_t(n) * MOE_NUM_STAGES + i) * 2];
+      hipEvent_t b = plan->prof_ev[(size_t(n) * MOE_NUM_STAGES + i) * 2 + 1];
+      float ms = 0.f;
+      if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess) {
+        (void)hipGetLastError();
+        st = fail(MOE_ERR_DEVICE, "reading profiling events failed");
+      }
+      stage_ms[i] += ms;
+    }
+  *calls = plan->prof_n;
+  for (hipEvent_t x : plan->prof_ev)
+    if (x) (void)hipEventDestroy(x);
+  plan->prof_ev.clear();
+  plan->prof_mask = 0;
+  plan->prof_cap = plan->prof_n = 0;
+  return st;
 }
 
 }  // extern "C"

@@ -35,6 +35,23 @@ __device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, v4f c, uint32
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Raw buffer access (offsets in bytes): an offset past num_records reads as
+// zero without touching memory, which gives padding rows for free.
+constexpr uint32_t kBufOOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+__device__ __forceinline__ uint32_t buf4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+__device__ __forceinline__ uint32_t buf1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(r, static_cast<int>(off), 0, 0));
+}
+
 __device__ __forceinline__ v8i make_a(uint4 lo, uint4 hi) {
   v8i r;
   r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
@@ -194,6 +211,197 @@ __global__ void __launch_bounds__(64 * NW) k_gemm(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode variant: 16-row tiles (a few tokens per expert), weight-streaming.
+// Each wave owns 16*NI output columns (gate and up subtiles for gate_up) over
+// a contiguous share of K; the KS waves of a workgroup split K and reduce
+// through LDS in a fixed order.  Loads of the next K group (512 wide, or 128
+// when K is not a multiple of 512) are issued before the MFMAs of the current
+// one, so a whole group of weight bytes per wave is always in flight.
+// ---------------------------------------------------------------------------
+
+template <int NB, int GS>
+struct DecFrag {
+  uint4 b[NB][GS];
+  uint4 a[GS][2];
+  uint32_t sa;
+  uint32_t sb[NB];
+};
+
+template <int NI, int KS, bool G4, bool GU>
+__global__ void __launch_bounds__(64 * KS) k_gemm_dec(FwdArgs a) {
+  constexpr int NB = GU ? 2 * NI : NI;
+  constexpr int GS = G4 ? 4 : 1;  // MFMA steps per K group
+  const int tile_idx = blockIdx.x;
+  if (tile_idx >= *a.tile_count) return;
+  const Tile tile = a.tiles[tile_idx];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int K = GU ? a.d : a.dff;
+  const int N = GU ? a.dff : a.d;
+  const int col0 = blockIdx.y * (16 * NI);
+
+  const bool shared = tile.ex >= a.E;
+  const int sidx = tile.ex - a.E;
+  const int64_t wrows = GU ? 2 * a.dff : a.d;
+  const int64_t wc_stride = wrows * (K / 2), ws_stride = wrows * (K / 32);
+  const uint8_t* wc = GU ? (shared ? a.sgu_c + sidx * wc_stride : a.gu_c + tile.ex * wc_stride)
+                         : (shared ? a.sdn_c + sidx * wc_stride : a.dn_c + tile.ex * wc_stride);
+  const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + tile.ex * ws_stride)
+                         : (shared ? a.sdn_s + sidx * ws_stride : a.dn_s + tile.ex * ws_stride);
+
+  const int arow = tile.row_begin + r16;
+  const bool avalid = arow < tile.row_end;
+  uint32_t src = 0;
+  if (avalid) src = GU ? (arow < a.Rr ? a.row_token[arow] : arow - a.Rr - sidx * a.T) : arow;
+  const uint32_t a_rows = GU ? a.T : a.R;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(GU ? a.x_codes : a.h_codes, a_rows * uint32_t(K));
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(GU ? a.x_scales : a.h_scales, a_rows * uint32_t(K / 32));
+  const uint32_t a_base = avalid ? src * uint32_t(K) : kBufOOB;
+  const uint32_t as_base = avalid ? src * uint32_t(K / 32) : kBufOOB;
+  const uint8_t* bp[NB];
+  const uint8_t* bsp[NB];
+#pragma unroll
+  for (int nj = 0; nj < NB; ++nj) {
+    int n = col0 + 16 * (nj % NI) + r16;
+    int64_t wrow = (GU && nj >= NI) ? a.dff + n : n;
+    bp[nj] = wc + wrow * (K / 2);
+    bsp[nj] = ws + wrow * (K / 32);
+  }
+
+  // K groups of this wave: a contiguous range
+  const int nq = K / (128 * GS);
+  const int q0 = (nq * wave) / KS, q1 = (nq * (wave + 1)) / KS;
+  const int n = q1 - q0;
+
+  auto load = [&](DecFrag<NB, GS>& f, int q) {
+    if (G4) {
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj) {
+        f.sb[nj] = *reinterpret_cast<const uint32_t*>(bsp[nj] + 16 * q + 4 * g);
+#pragma unroll
+        for (int s = 0; s < GS; ++s) f.b[nj][s] = ld16(bp[nj] + 256 * q + 64 * g + 16 * s);
+      }
+      f.sa = buf4(ras, as_base + 16 * q + 4 * g);
+#pragma unroll
+      for (int s = 0; s < GS; ++s) {
+        const uint32_t aoff = a_base + 512 * q + 128 * (g >> 1) + 32 * s + 16 * (g & 1);
+        f.a[s][0] = buf16(ra, aoff);
+        f.a[s][1] = buf16(ra, aoff + 256);
+      }
+    } else {
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj) {
+        f.sb[nj] = bsp[nj][4 * q + g];
+        f.b[nj][0] = ld16(bp[nj] + 64 * q + 16 * g);
+      }
+      f.sa = buf1(ras, as_base + 4 * q + g);
+      f.a[0][0] = buf16(ra, a_base + 128 * q + 16 * g);
+      f.a[0][1] = buf16(ra, a_base + 128 * q + 16 * g + 64);
+    }
+  };
+  v4f acc[NB];
+#pragma unroll
+  for (int nj = 0; nj < NB; ++nj) acc[nj] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const DecFrag<NB, GS>& f) {
+#pragma unroll
+    for (int s = 0; s < GS; ++s) {
+      const v8i av = make_a(f.a[s][0], f.a[s][1]);
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj)
+        acc[nj] = mfma_mx(av, make_b(f.b[nj][s]), acc[nj], f.sa >> (8 * s), f.sb[nj] >> (8 * s));
+    }
+  };
+
+  DecFrag<NB, GS> f0, f1;
+  if (n > 0) {
+    load(f0, q0);
+    int i = 0;
+    for (; i + 2 < n; i += 2) {  // f0 holds group q0 + i
+      load(f1, q0 + i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(f0, q0 + i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (n - i == 2) {
+      load(f1, q0 + i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(f1);
+    } else {
+      compute(f0);
+    }
+  }
+
+  // split-K reduction in wave order (deterministic)
+  if (KS > 1) {
+    __shared__ v4f red[KS > 1 ? (KS - 1) * NB * 64 : 1];
+    if (wave > 0) {
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj) red[((wave - 1) * NB + nj) * 64 + lane] = acc[nj];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 1; w < KS; ++w)
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj) acc[nj] += red[((w - 1) * NB + nj) * 64 + lane];
+  }
+
+  // epilogue (wave 0)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = tile.row_begin + 4 * g + i;
+    const bool valid = row < tile.row_end;
+    if (GU) {
+#pragma unroll
+      for (int p = 0; p < NI / 2; ++p) {
+        float h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int j = 2 * p + hh;
+          const float gt = acc[j][i], up = acc[NI + j][i];
+          h[hh] = gt / (1.0f + expf(-gt)) * up;
+          if (valid && a.gu_acc) {
+            const int col = col0 + 16 * j + r16;
+            a.gu_acc[int64_t(row) * 2 * a.dff + col] = gt;
+            a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + col] = up;
+          }
+        }
+        const float amax = group_max<16>(fmaxf(fabsf(h[0]), fabsf(h[1])));
+        const int e = mx8_block_exp(amax);
+        if (valid) {
+          const int col = col0 + 32 * p + r16;
+          uint8_t* hc = a.h_codes + int64_t(row) * a.dff;
+          hc[col] = static_cast<uint8_t>(mx8_encode(h[0], e));
+          hc[col + 16] = static_cast<uint8_t>(mx8_encode(h[1], e));
+          if (r16 == 0) a.h_scales[int64_t(row) * (a.dff / 32) + (col0 + 32 * p) / 32] = static_cast<uint8_t>(e + 127);
+        }
+      }
+    } else if (valid) {
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj) a.o[int64_t(row) * N + col0 + 16 * nj + r16] = acc[nj][i];
+    }
+  }
+}
+
+template <int NI, int KS, bool GU>
+static hipError_t launch_dec(const FwdArgs& a, hipStream_t st) {
+  const int K = GU ? a.d : a.dff;
+  const int N = GU ? a.dff : a.d;
+  dim3 grid(a.max_tiles, N / (16 * NI));
+  if (K % 512 == 0)
+    hipLaunchKernelGGL((k_gemm_dec<NI, KS, true, GU>), grid, dim3(64 * KS), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm_dec<NI, KS, false, GU>), grid, dim3(64 * KS), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int MI, int NI, int NW, bool GU>
 static hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
   const int K = GU ? a.d : a.dff;
@@ -207,12 +415,12 @@ static hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm_gate_up(const FwdArgs& a, hipStream_t st) {
-  if (a.bm == 16) return launch_cfg<1, 2, 1, true>(a, st);
+  if (a.bm == 16) return launch_dec<2, 2, true>(a, st);
   return launch_cfg<4, 2, 4, true>(a, st);
 }
 
 hipError_t launch_gemm_down(const FwdArgs& a, hipStream_t st) {
-  if (a.bm == 16) return launch_cfg<1, 2, 4, false>(a, st);
+  if (a.bm == 16) return launch_dec<2, 1, false>(a, st);
   return launch_cfg<4, 2, 4, false>(a, st);
 }
 

@@ -94,41 +94,65 @@ hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t 
 // Router logits  l[t][e] = sum_i x[t][i] W_r[e][i] + b[e]   (fp32 accumulate)
 // ---------------------------------------------------------------------------
 
-// Few tokens: one wave per expert streams its W_r row once per 8 tokens.
+// Few tokens: one 256-thread workgroup per expert streams its W_r row (8 float4
+// loads in flight per thread) once per 8 tokens.  The same launch quantises x
+// to MXFP8: workgroup e handles activation blocks e, e + E, e + 2E, ...
 constexpr int kRouterSmallMaxT = 32;
 
-__global__ void __launch_bounds__(256) k_router_small(const uint16_t* __restrict__ x,
-                                                      const float* __restrict__ wr,
-                                                      const float* __restrict__ br,
-                                                      float* __restrict__ logits, int T, int d,
-                                                      int E) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
-  const float4* w4 = reinterpret_cast<const float4*>(wr + int64_t(e) * d);
+__global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
+  __shared__ float part[4][8];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int e = blockIdx.x;
+  const int d = a.d, T = a.T;
+  // fused MXFP8 quantisation of x (one 32-element block per thread)
+  const int nb = d / 32;
+  for (int b = e + a.E * tid; b < T * nb; b += a.E * 256) {
+    const int t = b / nb, c = b - t * nb;
+    float v[32];
+    load_block32_bf16(a.x + int64_t(t) * d + c * 32, v);
+    a.x_scales[int64_t(t) * nb + c] =
+        static_cast<uint8_t>(quant_block32(v, a.x_codes + int64_t(t) * d + c * 32));
+  }
+  const float4* w4 = reinterpret_cast<const float4*>(a.wr + int64_t(e) * d);
   const int n4 = d / 4;
-  const float bias = br ? br[e] : 0.f;
+  const float bias = a.br ? a.br[e] : 0.f;
   for (int t0 = 0; t0 < T; t0 += 8) {
     const int nt = T - t0 < 8 ? T - t0 : 8;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int c = lane; c < n4; c += 64) {
-      float4 w = w4[c];
+    for (int base = 0; base < n4; base += 256 * 8) {
+      float4 w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = base + tid + 256 * i;
+        w[i] = c < n4 ? w4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         if (tt < nt) {
-          uint2 xb = *reinterpret_cast<const uint2*>(x + int64_t(t0 + tt) * d + 4 * c);
-          acc[tt] = fmaf(__uint_as_float(xb.x << 16), w.x, acc[tt]);
-          acc[tt] = fmaf(__uint_as_float(xb.x & 0xFFFF0000u), w.y, acc[tt]);
-          acc[tt] = fmaf(__uint_as_float(xb.y << 16), w.z, acc[tt]);
-          acc[tt] = fmaf(__uint_as_float(xb.y & 0xFFFF0000u), w.w, acc[tt]);
+          const uint2* xr = reinterpret_cast<const uint2*>(a.x + int64_t(t0 + tt) * d);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int c = base + tid + 256 * i;
+            if (c < n4) {
+              uint2 xb = xr[c];
+              acc[tt] = fmaf(__uint_as_float(xb.x << 16), w[i].x, acc[tt]);
+              acc[tt] = fmaf(__uint_as_float(xb.x & 0xFFFF0000u), w[i].y, acc[tt]);
+              acc[tt] = fmaf(__uint_as_float(xb.y << 16), w[i].z, acc[tt]);
+              acc[tt] = fmaf(__uint_as_float(xb.y & 0xFFFF0000u), w[i].w, acc[tt]);
+            }
+          }
         }
       }
     }
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       float s = group_sum<64>(acc[tt]);
-      if (lane == 0 && tt < nt) logits[int64_t(t0 + tt) * E + e] = s + bias;
+      if (lane == 0) part[wv][tt] = s;
     }
+    __syncthreads();
+    if (tid < nt) a.logits[int64_t(t0 + tid) * a.E + e] =
+        ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) + bias;
+    __syncthreads();
   }
 }
 
@@ -187,8 +211,7 @@ __global__ void __launch_bounds__(256) k_router_gemm(const uint16_t* __restrict_
 
 hipError_t launch_router(const FwdArgs& a, hipStream_t st) {
   if (a.T <= kRouterSmallMaxT) {
-    hipLaunchKernelGGL(k_router_small, dim3((a.E + 3) / 4), dim3(256), 0, st, a.x, a.wr, a.br,
-                       a.logits, a.T, a.d, a.E);
+    hipLaunchKernelGGL(k_router_small, dim3(a.E), dim3(256), 0, st, a);
   } else {
     dim3 grid((a.T + 63) / 64, (a.E + 63) / 64);
     hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, st, a.x, a.wr, a.br, a.logits, a.T, a.d,
@@ -201,12 +224,10 @@ hipError_t launch_router(const FwdArgs& a, hipStream_t st) {
 // Top-k + sigmoid renormalisation + MXFP8 quantisation of x: one wave per token
 // ---------------------------------------------------------------------------
 
-constexpr int kMaxSlots = 16;  // E <= 1024 = 64 lanes x 16 slots
+constexpr int kMaxSlots = 16;
 
-__global__ void __launch_bounds__(256) k_topk_quant(FwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
+// Top-k of token t by one wave: ids ascending, w = sigmoid / sum sigmoid.
+__device__ void topk_token(const FwdArgs& a, int t, int lane) {
   const float* lg = a.logits + int64_t(t) * a.E;
   uint64_t key[kMaxSlots];
   float val[kMaxSlots];
@@ -247,11 +268,10 @@ __global__ void __launch_bounds__(256) k_topk_quant(FwdArgs a) {
     uint64_t m = __ballot(s);
     pos[i] = base + __popcll(m & lt_mask);
     base += __popcll(m);
-    sig[i] = 1.0f / (1.0f + expf(-val[i]));
-    if (s) local += sig[i];
+    sig[i] = s ? 1.0f / (1.0f + expf(-val[i])) : 0.f;
+    local += sig[i];
   }
-  const float denom = group_sum<64>(local);
-  const float inv = 1.0f / denom;
+  const float inv = 1.0f / group_sum<64>(local);
   int32_t* ids = a.topk_ids + int64_t(t) * a.k;
   float* wts = a.topk_w + int64_t(t) * a.k;
 #pragma unroll
@@ -261,7 +281,14 @@ __global__ void __launch_bounds__(256) k_topk_quant(FwdArgs a) {
       wts[pos[i]] = sig[i] * inv;
     }
   }
-  // MXFP8 codes of this token's activation row
+}
+
+// Many tokens: one wave per token, top-k then the token's MXFP8 row.
+__global__ void __launch_bounds__(256) k_topk_quant(FwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  topk_token(a, t, lane);
   const int nb = a.d / 32;
   const uint16_t* xr = a.x + int64_t(t) * a.d;
   for (int b = lane; b < nb; b += 64) {
@@ -272,10 +299,7 @@ __global__ void __launch_bounds__(256) k_topk_quant(FwdArgs a) {
   }
 }
 
-hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_topk_quant, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
+
 
 // ---------------------------------------------------------------------------
 // Permutation: pairs (t, j) -> rows grouped by expert, tokens ascending.
@@ -359,45 +383,63 @@ __device__ void write_offsets_and_tiles(const FwdArgs& a, int* cnt, int* scan, i
   if (tid == 0) *a.tile_count = ntiles;
 }
 
-// Whole permutation in one workgroup (moderate token counts).
-__global__ void __launch_bounds__(1024) k_permute_small(FwdArgs a) {
-  __shared__ int cnt[1032];
-  __shared__ int scan[1032];
-  __shared__ int run[1024];
-  __shared__ unsigned long long mask[1024];
-  __shared__ int wave_tot[40];
+// Whole permutation in one 1024-thread workgroup (moderate token counts).
+struct PermLds {
+  int cnt[1032];
+  int scan[1032];
+  int run[1024];
+  unsigned long long mask[1024];
+  int wave_tot[40];
+};
+
+__device__ void permute_block(const FwdArgs& a, PermLds& L) {
   const int tid = threadIdx.x;
   const int npairs = a.T * a.k;
-  for (int e = tid; e < a.E; e += 1024) { cnt[e] = 0; run[e] = 0; }
+  for (int e = tid; e < a.E; e += 1024) { L.cnt[e] = 0; L.run[e] = 0; }
   __syncthreads();
-  for (int p = tid; p < npairs; p += 1024) atomicAdd(&cnt[a.topk_ids[p]], 1);
+  for (int p = tid; p < npairs; p += 1024) atomicAdd(&L.cnt[a.topk_ids[p]], 1);
   __syncthreads();
-  write_offsets_and_tiles(a, cnt, scan, wave_tot);
+  write_offsets_and_tiles(a, L.cnt, L.scan, L.wave_tot);
   __syncthreads();
   // scan[e] now holds the first row of routed expert e
   for (int t0 = 0; t0 < a.T; t0 += 64) {
-    for (int e = tid; e < a.E; e += 1024) mask[e] = 0ull;
+    for (int e = tid; e < a.E; e += 1024) L.mask[e] = 0ull;
     __syncthreads();
     const int tend = min(t0 + 64, a.T);
     const int p0 = t0 * a.k, p1 = tend * a.k;
     for (int p = p0 + tid; p < p1; p += 1024) {
       int t = p / a.k;
-      atomicOr(&mask[a.topk_ids[p]], 1ull << (t - t0));
+      atomicOr(&L.mask[a.topk_ids[p]], 1ull << (t - t0));
     }
     __syncthreads();
     for (int p = p0 + tid; p < p1; p += 1024) {
       int t = p / a.k;
       int e = a.topk_ids[p];
       unsigned long long below = (t - t0) == 0 ? 0ull : (~0ull >> (64 - (t - t0)));
-      int row = scan[e] + run[e] + __popcll(mask[e] & below);
+      int row = L.scan[e] + L.run[e] + __popcll(L.mask[e] & below);
       a.row_src[row] = p;
       a.row_token[row] = t;
       a.token_row[p] = row;
     }
     __syncthreads();
-    for (int e = tid; e < a.E; e += 1024) run[e] += __popcll(mask[e]);
+    for (int e = tid; e < a.E; e += 1024) L.run[e] += __popcll(L.mask[e]);
     __syncthreads();
   }
+}
+
+__global__ void __launch_bounds__(1024) k_permute_small(FwdArgs a) {
+  __shared__ PermLds L;
+  permute_block(a, L);
+}
+
+// Few tokens: top-k of every token (one wave each) and the permutation in a
+// single workgroup; x was already quantised by the router launch.
+__global__ void __launch_bounds__(1024) k_topk_permute_small(FwdArgs a) {
+  __shared__ PermLds L;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int t = wv; t < a.T; t += 16) topk_token(a, t, lane);
+  __syncthreads();  // top-k results (global memory) visible to the workgroup
+  permute_block(a, L);
 }
 
 // Large token counts: per-chunk masks and counts ...
@@ -467,7 +509,16 @@ __global__ void __launch_bounds__(256) k_perm_scatter(FwdArgs a) {
   }
 }
 
+hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st) {
+  if (a.T <= kRouterSmallMaxT)
+    hipLaunchKernelGGL(k_topk_permute_small, dim3(1), dim3(1024), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_topk_quant, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
+  if (a.T <= kRouterSmallMaxT) return hipSuccess;  // done with the top-k launch
   if (a.T <= kPermSmallMaxTokens) {
     hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(1024), 0, st, a);
     return hipGetLastError();
@@ -493,31 +544,44 @@ __global__ void __launch_bounds__(256) k_combine(FwdArgs a) {
     wts[tid] = a.topk_w[int64_t(t) * a.k + tid];
   }
   __syncthreads();
-  const int n4 = a.d / 4;
-  for (int c = tid; c < n4; c += 256) {
-    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < a.k; ++j) {
-      float4 v = reinterpret_cast<const float4*>(a.o + int64_t(rows[j]) * a.d)[c];
-      float w = wts[j];
-      r.x = fmaf(w, v.x, r.x); r.y = fmaf(w, v.y, r.y);
-      r.z = fmaf(w, v.z, r.z); r.w = fmaf(w, v.w, r.w);
+  const int c = blockIdx.y * 256 + tid;  // float4 column
+  if (c >= a.d / 4) return;
+  const float4* o4 = reinterpret_cast<const float4*>(a.o);
+  const int64_t rs = a.d / 4;
+  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+  int j = 0;
+  for (; j + 4 <= a.k; j += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = o4[int64_t(rows[j + u]) * rs + c];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = wts[j + u];
+      r.x = fmaf(w, v[u].x, r.x); r.y = fmaf(w, v[u].y, r.y);
+      r.z = fmaf(w, v[u].z, r.z); r.w = fmaf(w, v[u].w, r.w);
     }
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sh = 0; sh < a.S; ++sh) {
-      float4 v = reinterpret_cast<const float4*>(a.o + int64_t(a.Rr + sh * a.T + t) * a.d)[c];
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-    }
-    uint2 yb;
-    yb.x = uint32_t(f32_to_bf16_rne(r.x + s.x)) | (uint32_t(f32_to_bf16_rne(r.y + s.y)) << 16);
-    yb.y = uint32_t(f32_to_bf16_rne(r.z + s.z)) | (uint32_t(f32_to_bf16_rne(r.w + s.w)) << 16);
-    reinterpret_cast<uint2*>(a.y + int64_t(t) * a.d)[c] = yb;
-    if (a.y_routed) reinterpret_cast<float4*>(a.y_routed + int64_t(t) * a.d)[c] = r;
-    if (a.y_shared) reinterpret_cast<float4*>(a.y_shared + int64_t(t) * a.d)[c] = s;
   }
+  for (; j < a.k; ++j) {
+    const float4 v = o4[int64_t(rows[j]) * rs + c];
+    const float w = wts[j];
+    r.x = fmaf(w, v.x, r.x); r.y = fmaf(w, v.y, r.y);
+    r.z = fmaf(w, v.z, r.z); r.w = fmaf(w, v.w, r.w);
+  }
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sh = 0; sh < a.S; ++sh) {
+    const float4 v = o4[int64_t(a.Rr + sh * a.T + t) * rs + c];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  uint2 yb;
+  yb.x = uint32_t(f32_to_bf16_rne(r.x + s.x)) | (uint32_t(f32_to_bf16_rne(r.y + s.y)) << 16);
+  yb.y = uint32_t(f32_to_bf16_rne(r.z + s.z)) | (uint32_t(f32_to_bf16_rne(r.w + s.w)) << 16);
+  reinterpret_cast<uint2*>(a.y + int64_t(t) * a.d)[c] = yb;
+  if (a.y_routed) reinterpret_cast<float4*>(a.y_routed + int64_t(t) * a.d)[c] = r;
+  if (a.y_shared) reinterpret_cast<float4*>(a.y_shared + int64_t(t) * a.d)[c] = s;
 }
 
 hipError_t launch_combine(const FwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(a.T), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.T, (a.d / 4 + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

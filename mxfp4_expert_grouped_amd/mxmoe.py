@@ -18,7 +18,9 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEV
 MOE_SRC_BF16, MOE_SRC_FP32 = 0, 1
 
 EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_workspace_bytes", "moe_quantize_act",
-            "moe_forward", "moe_status_string", "moe_last_error")
+            "moe_forward", "moe_profile_begin", "moe_profile_end", "moe_status_string",
+            "moe_last_error")
+STAGES = ("router", "topk", "permute", "gate_up", "down", "combine")
 
 
 class MoeError(RuntimeError):
@@ -71,6 +73,10 @@ def load_library(path: str = LIB_PATH):
     lib.moe_forward.argtypes = [c_void_p, POINTER(MoeWeights), c_void_p, c_int64, c_void_p,
                                 c_void_p, c_size_t, POINTER(MoeTaps), c_void_p]
     lib.moe_forward.restype = c_int
+    lib.moe_profile_begin.argtypes = [c_void_p, c_uint32, c_int32]
+    lib.moe_profile_begin.restype = c_int
+    lib.moe_profile_end.argtypes = [c_void_p, POINTER(ctypes.c_double), POINTER(c_int32)]
+    lib.moe_profile_end.restype = c_int
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_status_string.restype = c_char_p
     lib.moe_last_error.argtypes = []
@@ -114,3 +120,19 @@ def moe_forward(plan: c_void_p, weights: MoeWeights, x: int, num_tokens: int, y:
     _check(load_library().moe_forward(plan, ctypes.byref(weights), x, num_tokens, y, workspace,
                                       workspace_bytes, ctypes.byref(taps) if taps else None,
                                       stream))
+
+
+def moe_profile_begin(plan: c_void_p, stages, max_calls: int) -> None:
+    """Record HIP events around the named stages of the next max_calls forwards."""
+    mask = 0
+    for st in stages:
+        mask |= 1 << STAGES.index(st)
+    _check(load_library().moe_profile_begin(plan, mask, max_calls))
+
+
+def moe_profile_end(plan: c_void_p):
+    """-> ({stage: summed ms}, recorded calls)"""
+    ms = (ctypes.c_double * len(STAGES))()
+    n = c_int32()
+    _check(load_library().moe_profile_end(plan, ms, ctypes.byref(n)))
+    return dict(zip(STAGES, list(ms))), n.value

@@ -153,9 +153,15 @@ def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g,
     differ = check_routing(cfg, res, g)
     check_permutation(cfg, res, g, differ)
     same = np.array([t for t in range(T) if t not in differ])
-    werr = np.abs(g["topk_w"][same] - res.topk_w[same]).max()
-    log(f"topk_w max abs err {werr:.3e}")
-    assert werr < 2e-6
+    # w = sigmoid(l)/sum sigmoid(l): d(log w_j)/d l_i = (1 - s_j) delta_ij - w_i (1 - s_i),
+    # so a logit error dl moves w_j by at most w_j * 2 * max|dl| (first order),
+    # plus fp32 rounding of the sigmoid and the normalisation
+    dl = np.abs(g["logits"].astype(np.float64) - res.logits).max(axis=1)[same, None]
+    wref = res.topk_w[same]
+    werr = np.abs(g["topk_w"][same] - wref)
+    bound = wref * (2.0 * dl + 1e-6) + 1e-8
+    log(f"topk_w max abs err {werr.max():.3e} (max err/bound {np.max(werr / bound):.2f})")
+    assert np.all(werr <= bound)
     # MXFP8 bytes of x: bit-exact
     toks = res.tokens
     assert np.array_equal(g["x_codes"][toks], res.x_codes)
