@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the forward as a HIP graph")
     ap.add_argument("--breakdown", action="store_true", help="also time every stage (untimed pass)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, copy this many MiB device-to-device once (a plain copy "
+                         "kernel of known size, to calibrate hardware byte counters)")
     return ap.parse_args()
 
 
@@ -157,6 +160,15 @@ def main():
             tot += stage_ms["gate_up"]
             calls += n
         gu_ms = tot / max(calls, 1)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     stage_avg = None
     if args.breakdown:

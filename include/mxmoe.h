@@ -23,17 +23,18 @@
  *   combine  : y[t] = sum_j w[t,j] o_(t,j) + sum_s o_s[t] (fp32, fixed order),
  *              rounded to bf16.
  *
- * Layouts (all row-major, all device memory, all owned by the caller):
- *   x          bf16  [T][d_model]
- *   y          bf16  [T][d_model]
+ * Layouts (all device memory, all owned by the caller):
+ *   x          bf16  [T][d_model] row-major
+ *   y          bf16  [T][d_model] row-major
  *   router_w   fp32  [E][d_model];  router_b fp32 [E] or NULL (zero bias)
- *   gu_codes   u8    [E][2*d_ff][d_model/2]   E2M1 pairs, element 2i in the
- *                                             low nibble of byte i; rows
- *                                             [0,d_ff) gate, [d_ff,2 d_ff) up
- *   gu_scales  u8    [E][2*d_ff][d_model/32]  E8M0
- *   dn_codes   u8    [E][d_model][d_ff/2]
- *   dn_scales  u8    [E][d_model][d_ff/32]
- *   sgu_* / sdn_*    the same per shared expert, [num_shared][...]
+ *   Expert weights in canonical MXFP4 form are, per expert,
+ *     W_gu  [2*d_ff][d_model]  (rows [0,d_ff) gate, [d_ff,2 d_ff) up)
+ *     W_dn  [d_model][d_ff]
+ *   each as codes u8 [rows][K/2] (E2M1 pairs, element 2i in the low nibble of
+ *   byte i) and scales u8 [rows][K/32] (E8M0), K the reduction width.
+ *   moe_forward takes them in the packed tile order made by moe_pack_mx4
+ *   (below): gu_codes/gu_scales hold E packed W_gu matrices back to back,
+ *   dn_codes/dn_scales E packed W_dn matrices, sgu_* / sdn_* the shared ones.
  *
  * Errors: every argument is checked on the host before anything is enqueued;
  * on an error nothing is written and the call returns a non-zero status
@@ -101,6 +102,25 @@ typedef struct {
   float *y_routed;        /* [T][d_model]  sum_j w o (fp32)                  */
   float *y_shared;        /* [T][d_model]  sum_s o_s (fp32)                  */
 } moe_taps;
+
+/* Packed MXFP4 matrix (one-time conversion at weight-load time).  For a
+ * canonical matrix with `rows` rows (a multiple of 16) and reduction width k
+ * (a multiple of 128), 16-row blocks b and 128-wide K steps s, lane
+ * l = 16*g + r (g = l/16, r = l%16):
+ *   codes_p [rows/16][k/128][64][16]: entry (b, s, l) = canonical code bytes
+ *           64*s + 16*g .. +16 of row 16*b + r (MX block 4*s + g);
+ *   scales_p[rows/16][ceil(k/512)][64][4]: byte j of entry (b, q, l) = the
+ *           canonical scale of row 16*b + r, block 16*q + 4*j + g, or 0 past
+ *           the end of the row.
+ * One 16-row x 128-wide MFMA step of a wave is then one contiguous 1 KB in
+ * lane order, and its scales one dword per lane per four steps.
+ * codes_p is rows*k/2 bytes; scales_p is moe_packed_scale_bytes(rows, k). */
+size_t moe_packed_scale_bytes(int64_t rows, int64_t k);
+/* Pack `mats` matrices stored back to back (canonical codes [mats][rows][k/2],
+ * scales [mats][rows][k/32]) into codes_p/scales_p (packed, back to back).
+ * Device buffers; codes and codes_p 16-byte aligned, scales_p 4-byte aligned. */
+moe_status moe_pack_mx4(const uint8_t *codes, const uint8_t *scales, int64_t mats, int64_t rows,
+                        int64_t k, uint8_t *codes_p, uint8_t *scales_p, void *stream);
 
 /* Validate `cfg` and build a plan (host only; no device call). */
 moe_status moe_plan(const moe_config *cfg, moe_plan_t **out_plan);

@@ -29,7 +29,7 @@ FLAGS = [
 ]
 
 LIBS = {
-    "libmxmoe.so": ["api.cpp", "kernels_route.hip", "kernels_gemm.hip"],
+    "libmxmoe.so": ["api.cpp", "kernels_route.hip", "kernels_gemm.hip", "kernels_pack.hip"],
     "libmxmoe_inputs.so": ["gen_inputs.hip"],
 }
 

@@ -202,6 +202,28 @@ moe_status moe_quantize_act(const void* src, moe_src_dtype dt, int64_t rows, int
   return MOE_OK;
 }
 
+size_t moe_packed_scale_bytes(int64_t rows, int64_t k) {
+  if (rows <= 0 || k <= 0) return 0;
+  return static_cast<size_t>(packed_scale_bytes(rows, k));
+}
+
+moe_status moe_pack_mx4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int64_t rows,
+                        int64_t k, uint8_t* codes_p, uint8_t* scales_p, void* stream) {
+  if (mats < 0 || rows < 0 || k < 0) return fail(MOE_ERR_INVALID_ARG, "negative size");
+  if (rows % 16 || k % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "rows must be a multiple of 16 and k of 128");
+  if (mats == 0 || rows == 0 || k == 0) return MOE_OK;
+  if (!codes || !scales || !codes_p || !scales_p) return fail(MOE_ERR_INVALID_ARG, "NULL buffer");
+  if (!aligned(codes, 16) || !aligned(codes_p, 16) || !aligned(scales_p, 4))
+    return fail(MOE_ERR_INVALID_ARG, "codes/codes_p need 16-byte, scales_p 4-byte alignment");
+  moe_status s = check_device();
+  if (s != MOE_OK) return s;
+  hipError_t e = launch_pack_mx4(codes, scales, mats, rows, k, codes_p, scales_p,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
 moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void* x_bf16,
                        int64_t num_tokens, void* y_bf16, void* workspace, size_t workspace_bytes,
                        const moe_taps* taps, void* stream) {

@@ -63,6 +63,11 @@ hipError_t launch_permute(const FwdArgs& a, hipStream_t st);
 hipError_t launch_gemm_gate_up(const FwdArgs& a, hipStream_t st);
 hipError_t launch_gemm_down(const FwdArgs& a, hipStream_t st);
 hipError_t launch_combine(const FwdArgs& a, hipStream_t st);
+hipError_t launch_pack_mx4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int64_t rows,
+                           int64_t k, uint8_t* codes_p, uint8_t* scales_p, hipStream_t st);
+
+// bytes of one packed scale matrix [rows/16][ceil(k/512)][64][4]
+__host__ __device__ inline int64_t packed_scale_bytes(int64_t rows, int64_t k) { return (rows / 16) * ((k + 511) / 512) * 256; }
 
 // token counts at or below which the single-workgroup permutation is used
 constexpr int kPermSmallMaxTokens = 1024;

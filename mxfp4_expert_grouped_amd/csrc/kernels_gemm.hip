@@ -13,9 +13,10 @@
 //     + j%16, i.e. two 16-byte halves from logical blocks g/2 and 2 + g/2;
 //   * the scale byte of lane (r, g) applies to logical block g (k = 32g..32g+31)
 //     of row r; the result of lane l, register i is D[4(l/16)+i][l%16].
-// Since a dot product does not care how k is ordered, each MFMA step maps its
-// four logical blocks onto four MX blocks of the data; both operands and both
-// scales follow the same map, so each FP4 lane reads one whole MX block.
+// MFMA step s covers K = 128s .. 128s+127 in natural order.  Weights arrive
+// packed (moe_pack_mx4): the FP4 operand of one 16-row block and step is 1 KB
+// contiguous in lane order, and the block scales of four steps one dword per
+// lane (byte j for step 4q + j).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,10 +49,6 @@ __device__ __forceinline__ uint4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t buf4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
 }
-__device__ __forceinline__ uint32_t buf1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(r, static_cast<int>(off), 0, 0));
-}
-
 __device__ __forceinline__ v8i make_a(uint4 lo, uint4 hi) {
   v8i r;
   r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
@@ -69,7 +66,7 @@ __device__ __forceinline__ v8i make_b(uint4 v) {
 // for gate_up, each needing a gate and an up subtile); NW: waves per workgroup
 // along N; G4: K handled in groups of 512 (4 MFMA steps sharing a scale dword),
 // else one 128-wide step at a time.
-template <int MI, int NI, int NW, bool G4, bool GU>
+template <int MI, int NI, int NW, bool GU>
 __global__ void __launch_bounds__(64 * NW) k_gemm(FwdArgs a) {
   constexpr int NB = GU ? 2 * NI : NI;
   const int tile_idx = blockIdx.x;
@@ -79,13 +76,14 @@ __global__ void __launch_bounds__(64 * NW) k_gemm(FwdArgs a) {
   const int g = lane >> 4, r16 = lane & 15;
   const int K = GU ? a.d : a.dff;
   const int N = GU ? a.dff : a.d;
+  const int nsteps = K / 128, nq4 = (K + 511) / 512;
   const int col0 = blockIdx.y * (16 * NI * NW) + wave * (16 * NI);
 
-  // weights of this expert
+  // packed weights of this expert
   const bool shared = tile.ex >= a.E;
   const int sidx = tile.ex - a.E;
   const int64_t wrows = GU ? 2 * a.dff : a.d;
-  const int64_t wc_stride = wrows * (K / 2), ws_stride = wrows * (K / 32);
+  const int64_t wc_stride = wrows * (K / 2), ws_stride = packed_scale_bytes(wrows, K);
   const uint8_t* wc = GU ? (shared ? a.sgu_c + sidx * wc_stride : a.gu_c + tile.ex * wc_stride)
                          : (shared ? a.sdn_c + sidx * wc_stride : a.dn_c + tile.ex * wc_stride);
   const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + tile.ex * ws_stride)
@@ -103,19 +101,17 @@ __global__ void __launch_bounds__(64 * NW) k_gemm(FwdArgs a) {
       src = row < a.Rr ? a.row_token[row] : row - a.Rr - sidx * a.T;
     else
       src = row;
-    const uint8_t* base_c = GU ? a.x_codes : a.h_codes;
-    const uint8_t* base_s = GU ? a.x_scales : a.h_scales;
-    ap[mi] = base_c + src * K;
-    asp[mi] = base_s + src * (K / 32);
+    ap[mi] = (GU ? a.x_codes : a.h_codes) + src * K + 16 * g;
+    asp[mi] = (GU ? a.x_scales : a.h_scales) + src * (K / 32) + g;
   }
   const uint8_t* bp[NB];
   const uint8_t* bsp[NB];
 #pragma unroll
   for (int nj = 0; nj < NB; ++nj) {
-    int n = col0 + 16 * (nj % NI) + r16;
-    int64_t wrow = (GU && nj >= NI) ? a.dff + n : n;
-    bp[nj] = wc + wrow * (K / 2);
-    bsp[nj] = ws + wrow * (K / 32);
+    const int n = col0 + 16 * (nj % NI);
+    const int64_t blk = ((GU && nj >= NI) ? a.dff + n : n) / 16;
+    bp[nj] = wc + blk * nsteps * 1024 + 16 * lane;
+    bsp[nj] = ws + blk * nq4 * 256 + 4 * lane;
   }
 
   v4f acc[MI][NB];
@@ -124,51 +120,26 @@ __global__ void __launch_bounds__(64 * NW) k_gemm(FwdArgs a) {
 #pragma unroll
     for (int nj = 0; nj < NB; ++nj) acc[mi][nj] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  if (G4) {
-    const int nq = K / 512;
-    for (int q = 0; q < nq; ++q) {
-      uint32_t sa[MI], sb[NB];
+  uint32_t sb[NB];
+  for (int st = 0; st < nsteps; ++st) {
+    if ((st & 3) == 0) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) sa[mi] = *reinterpret_cast<const uint32_t*>(asp[mi] + 16 * q + 4 * g);
-#pragma unroll
-      for (int nj = 0; nj < NB; ++nj) sb[nj] = *reinterpret_cast<const uint32_t*>(bsp[nj] + 16 * q + 4 * g);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        v8i av[MI], bv[NB];
-        const int aoff = 512 * q + 128 * (g >> 1) + 32 * s + 16 * (g & 1);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) av[mi] = make_a(ld16(ap[mi] + aoff), ld16(ap[mi] + aoff + 256));
-        const int boff = 256 * q + 64 * g + 16 * s;
-#pragma unroll
-        for (int nj = 0; nj < NB; ++nj) bv[nj] = make_b(ld16(bp[nj] + boff));
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int nj = 0; nj < NB; ++nj)
-            acc[mi][nj] = mfma_mx(av[mi], bv[nj], acc[mi][nj], sa[mi] >> (8 * s), sb[nj] >> (8 * s));
-      }
+      for (int nj = 0; nj < NB; ++nj) sb[nj] = *reinterpret_cast<const uint32_t*>(bsp[nj] + (st >> 2) * 256);
     }
-  } else {
-    const int ns = K / 128;
-    for (int s = 0; s < ns; ++s) {
-      v8i av[MI], bv[NB];
-      uint32_t sa[MI], sb[NB];
-      const int aoff = 128 * s + 16 * g;
+    v8i av[MI], bv[NB];
+    uint32_t sa[MI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        av[mi] = make_a(ld16(ap[mi] + aoff), ld16(ap[mi] + aoff + 64));
-        sa[mi] = asp[mi][4 * s + g];
-      }
-#pragma unroll
-      for (int nj = 0; nj < NB; ++nj) {
-        bv[nj] = make_b(ld16(bp[nj] + 64 * s + 16 * g));
-        sb[nj] = bsp[nj][4 * s + g];
-      }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < NB; ++nj) acc[mi][nj] = mfma_mx(av[mi], bv[nj], acc[mi][nj], sa[mi], sb[nj]);
+    for (int mi = 0; mi < MI; ++mi) {
+      av[mi] = make_a(ld16(ap[mi] + 128 * st), ld16(ap[mi] + 128 * st + 64));
+      sa[mi] = asp[mi][4 * st];
     }
+#pragma unroll
+    for (int nj = 0; nj < NB; ++nj) bv[nj] = make_b(ld16(bp[nj] + st * 1024));
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < NB; ++nj)
+        acc[mi][nj] = mfma_mx(av[mi], bv[nj], acc[mi][nj], sa[mi], sb[nj] >> (8 * (st & 3)));
   }
 
   // epilogue
@@ -215,23 +186,24 @@ __global__ void __launch_bounds__(64 * NW) k_gemm(FwdArgs a) {
 // Decode variant: 16-row tiles (a few tokens per expert), weight-streaming.
 // Each wave owns 16*NI output columns (gate and up subtiles for gate_up) over
 // a contiguous share of K; the KS waves of a workgroup split K and reduce
-// through LDS in a fixed order.  Loads of the next K group (512 wide, or 128
-// when K is not a multiple of 512) are issued before the MFMAs of the current
-// one, so a whole group of weight bytes per wave is always in flight.
+// through LDS in a fixed order.  K is walked in groups of GS MFMA steps; the
+// loads of the next group are issued before the MFMAs of the current one, so
+// a whole group of weight bytes per wave stays in flight.  Padding rows of the
+// tile read as zero through out-of-range buffer loads (no memory traffic).
 // ---------------------------------------------------------------------------
 
 template <int NB, int GS>
 struct DecFrag {
   uint4 b[NB][GS];
   uint4 a[GS][2];
-  uint32_t sa;
+  uint32_t sa[GS];
   uint32_t sb[NB];
+  uint32_t bsh;  // byte offset of this group's first step inside the scale dword
 };
 
-template <int NI, int KS, bool G4, bool GU>
+template <int NI, int KS, int GS, bool GU>
 __global__ void __launch_bounds__(64 * KS) k_gemm_dec(FwdArgs a) {
   constexpr int NB = GU ? 2 * NI : NI;
-  constexpr int GS = G4 ? 4 : 1;  // MFMA steps per K group
   const int tile_idx = blockIdx.x;
   if (tile_idx >= *a.tile_count) return;
   const Tile tile = a.tiles[tile_idx];
@@ -239,12 +211,13 @@ __global__ void __launch_bounds__(64 * KS) k_gemm_dec(FwdArgs a) {
   const int g = lane >> 4, r16 = lane & 15;
   const int K = GU ? a.d : a.dff;
   const int N = GU ? a.dff : a.d;
+  const int nsteps = K / 128, nq4 = (K + 511) / 512;
   const int col0 = blockIdx.y * (16 * NI);
 
   const bool shared = tile.ex >= a.E;
   const int sidx = tile.ex - a.E;
   const int64_t wrows = GU ? 2 * a.dff : a.d;
-  const int64_t wc_stride = wrows * (K / 2), ws_stride = wrows * (K / 32);
+  const int64_t wc_stride = wrows * (K / 2), ws_stride = packed_scale_bytes(wrows, K);
   const uint8_t* wc = GU ? (shared ? a.sgu_c + sidx * wc_stride : a.gu_c + tile.ex * wc_stride)
                          : (shared ? a.sdn_c + sidx * wc_stride : a.dn_c + tile.ex * wc_stride);
   const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + tile.ex * ws_stride)
@@ -257,47 +230,38 @@ __global__ void __launch_bounds__(64 * KS) k_gemm_dec(FwdArgs a) {
   const uint32_t a_rows = GU ? a.T : a.R;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(GU ? a.x_codes : a.h_codes, a_rows * uint32_t(K));
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(GU ? a.x_scales : a.h_scales, a_rows * uint32_t(K / 32));
-  const uint32_t a_base = avalid ? src * uint32_t(K) : kBufOOB;
+  const uint32_t a_base = avalid ? src * uint32_t(K) + 16 * g : kBufOOB;
   const uint32_t as_base = avalid ? src * uint32_t(K / 32) : kBufOOB;
   const uint8_t* bp[NB];
   const uint8_t* bsp[NB];
 #pragma unroll
   for (int nj = 0; nj < NB; ++nj) {
-    int n = col0 + 16 * (nj % NI) + r16;
-    int64_t wrow = (GU && nj >= NI) ? a.dff + n : n;
-    bp[nj] = wc + wrow * (K / 2);
-    bsp[nj] = ws + wrow * (K / 32);
+    const int n = col0 + 16 * (nj % NI);
+    const int64_t blk = ((GU && nj >= NI) ? a.dff + n : n) / 16;
+    bp[nj] = wc + blk * nsteps * 1024 + 16 * lane;
+    bsp[nj] = ws + blk * nq4 * 256 + 4 * lane;
   }
 
   // K groups of this wave: a contiguous range
-  const int nq = K / (128 * GS);
+  const int nq = nsteps / GS;
   const int q0 = (nq * wave) / KS, q1 = (nq * (wave + 1)) / KS;
   const int n = q1 - q0;
 
   auto load = [&](DecFrag<NB, GS>& f, int q) {
-    if (G4) {
+    const int st0 = q * GS;
+    f.bsh = 8 * (st0 & 3);
 #pragma unroll
-      for (int nj = 0; nj < NB; ++nj) {
-        f.sb[nj] = *reinterpret_cast<const uint32_t*>(bsp[nj] + 16 * q + 4 * g);
+    for (int nj = 0; nj < NB; ++nj) {
+      f.sb[nj] = *reinterpret_cast<const uint32_t*>(bsp[nj] + (st0 >> 2) * 256);
 #pragma unroll
-        for (int s = 0; s < GS; ++s) f.b[nj][s] = ld16(bp[nj] + 256 * q + 64 * g + 16 * s);
-      }
-      f.sa = buf4(ras, as_base + 16 * q + 4 * g);
+      for (int s = 0; s < GS; ++s) f.b[nj][s] = ld16(bp[nj] + (st0 + s) * 1024);
+    }
 #pragma unroll
-      for (int s = 0; s < GS; ++s) {
-        const uint32_t aoff = a_base + 512 * q + 128 * (g >> 1) + 32 * s + 16 * (g & 1);
-        f.a[s][0] = buf16(ra, aoff);
-        f.a[s][1] = buf16(ra, aoff + 256);
-      }
-    } else {
-#pragma unroll
-      for (int nj = 0; nj < NB; ++nj) {
-        f.sb[nj] = bsp[nj][4 * q + g];
-        f.b[nj][0] = ld16(bp[nj] + 64 * q + 16 * g);
-      }
-      f.sa = buf1(ras, as_base + 4 * q + g);
-      f.a[0][0] = buf16(ra, a_base + 128 * q + 16 * g);
-      f.a[0][1] = buf16(ra, a_base + 128 * q + 16 * g + 64);
+    for (int s = 0; s < GS; ++s) {
+      // scale bytes 4*step .. 4*step+3 of the row; lane group g uses byte g
+      f.sa[s] = buf4(ras, as_base + 4 * (st0 + s));
+      f.a[s][0] = buf16(ra, a_base + 128 * (st0 + s));
+      f.a[s][1] = buf16(ra, a_base + 128 * (st0 + s) + 64);
     }
   };
   v4f acc[NB];
@@ -307,9 +271,10 @@ __global__ void __launch_bounds__(64 * KS) k_gemm_dec(FwdArgs a) {
 #pragma unroll
     for (int s = 0; s < GS; ++s) {
       const v8i av = make_a(f.a[s][0], f.a[s][1]);
+      const uint32_t sa = f.sa[s] >> (8 * g);
 #pragma unroll
       for (int nj = 0; nj < NB; ++nj)
-        acc[nj] = mfma_mx(av, make_b(f.b[nj][s]), acc[nj], f.sa >> (8 * s), f.sb[nj] >> (8 * s));
+        acc[nj] = mfma_mx(av, make_b(f.b[nj][s]), acc[nj], sa, f.sb[nj] >> (f.bsh + 8 * s));
     }
   };
 
@@ -395,22 +360,18 @@ static hipError_t launch_dec(const FwdArgs& a, hipStream_t st) {
   const int K = GU ? a.d : a.dff;
   const int N = GU ? a.dff : a.d;
   dim3 grid(a.max_tiles, N / (16 * NI));
-  if (K % 512 == 0)
-    hipLaunchKernelGGL((k_gemm_dec<NI, KS, true, GU>), grid, dim3(64 * KS), 0, st, a);
+  if (K % 256 == 0)
+    hipLaunchKernelGGL((k_gemm_dec<NI, KS, 2, GU>), grid, dim3(64 * KS), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_dec<NI, KS, false, GU>), grid, dim3(64 * KS), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_dec<NI, KS, 1, GU>), grid, dim3(64 * KS), 0, st, a);
   return hipGetLastError();
 }
 
 template <int MI, int NI, int NW, bool GU>
 static hipError_t launch_cfg(const FwdArgs& a, hipStream_t st) {
-  const int K = GU ? a.d : a.dff;
   const int N = GU ? a.dff : a.d;
   dim3 grid(a.max_tiles, N / (16 * NI * NW));
-  if (K % 512 == 0)
-    hipLaunchKernelGGL((k_gemm<MI, NI, NW, true, GU>), grid, dim3(64 * NW), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_gemm<MI, NI, NW, false, GU>), grid, dim3(64 * NW), 0, st, a);
+  hipLaunchKernelGGL((k_gemm<MI, NI, NW, GU>), grid, dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 

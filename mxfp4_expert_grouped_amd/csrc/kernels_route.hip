@@ -104,14 +104,23 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int e = blockIdx.x;
   const int d = a.d, T = a.T;
-  // fused MXFP8 quantisation of x (one 32-element block per thread)
+  // fused MXFP8 quantisation of x: 8 threads per 32-element block, 32 blocks
+  // per workgroup (workgroup e takes blocks 32e .. 32e+31 of all T*d/32)
   const int nb = d / 32;
-  for (int b = e + a.E * tid; b < T * nb; b += a.E * 256) {
-    const int t = b / nb, c = b - t * nb;
-    float v[32];
-    load_block32_bf16(a.x + int64_t(t) * d + c * 32, v);
-    a.x_scales[int64_t(t) * nb + c] =
-        static_cast<uint8_t>(quant_block32(v, a.x_codes + int64_t(t) * d + c * 32));
+  {
+    const int b = 32 * e + (tid >> 3), j = tid & 7;
+    if (b < T * nb) {
+      const int t = b / nb, c = b - t * nb;
+      const uint2 raw = *reinterpret_cast<const uint2*>(a.x + int64_t(t) * d + c * 32 + 4 * j);
+      float v[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
+                    __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u)};
+      const float amax = group_max<8>(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+      const int ex = mx8_block_exp(amax);
+      const uint32_t w = mx8_encode(v[0], ex) | (mx8_encode(v[1], ex) << 8) |
+                         (mx8_encode(v[2], ex) << 16) | (mx8_encode(v[3], ex) << 24);
+      *reinterpret_cast<uint32_t*>(a.x_codes + int64_t(t) * d + c * 32 + 4 * j) = w;
+      if (j == 0) a.x_scales[int64_t(t) * nb + c] = static_cast<uint8_t>(ex + 127);
+    }
   }
   const float4* w4 = reinterpret_cast<const float4*>(a.wr + int64_t(e) * d);
   const int n4 = d / 4;
@@ -146,8 +155,10 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
     }
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      float s = group_sum<64>(acc[tt]);
-      if (lane == 0) part[wv][tt] = s;
+      if (tt < nt) {
+        float s = group_sum<64>(acc[tt]);
+        if (lane == 0) part[wv][tt] = s;
+      }
     }
     __syncthreads();
     if (tid < nt) a.logits[int64_t(t0 + tid) * a.E + e] =
@@ -210,7 +221,8 @@ __global__ void __launch_bounds__(256) k_router_gemm(const uint16_t* __restrict_
 }
 
 hipError_t launch_router(const FwdArgs& a, hipStream_t st) {
-  if (a.T <= kRouterSmallMaxT) {
+  // the small-batch router also quantises x: 32 blocks per expert workgroup
+  if (a.T <= kRouterSmallMaxT && a.T * (a.d / 32) <= 32 * a.E) {
     hipLaunchKernelGGL(k_router_small, dim3(a.E), dim3(256), 0, st, a);
   } else {
     dim3 grid((a.T + 63) / 64, (a.E + 63) / 64);
@@ -226,69 +238,119 @@ hipError_t launch_router(const FwdArgs& a, hipStream_t st) {
 
 constexpr int kMaxSlots = 16;
 
+// k-th largest of one key per lane (keys of 0 never count): the threshold is
+// built bit by bit from the top, counting candidates with a ballot.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t key, int k) {
+  uint32_t th = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    th = __popcll(__ballot(key >= cand)) >= k ? cand : th;
+  }
+  return th;
+}
+
+__device__ __forceinline__ float order_key_to_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+}
+
 // Top-k of token t by one wave: ids ascending, w = sigmoid / sum sigmoid.
-__device__ void topk_token(const FwdArgs& a, int t, int lane) {
-  const float* lg = a.logits + int64_t(t) * a.E;
-  uint64_t key[kMaxSlots];
-  float val[kMaxSlots];
+// Keys are order-preserving 32-bit images of the logits; slot i of lane l
+// holds expert l + 64 i (slots past E hold key 0, which never counts).
+// 1. The k-th largest of the 64 per-lane maxima is a lower bound L of the
+//    k-th largest key (at least k lanes hold a key >= L).
+// 2. Keys >= L are compacted in (slot, lane) = ascending expert order into
+//    `cand` (LDS, 64 entries per wave); if more than 64 qualify, the full
+//    16-slot search runs instead.
+// 3. With one candidate per lane, the k-th largest key th is found by a
+//    one-slot radix select; keys > th are taken and keys == th fill the
+//    remaining places in ascending expert order (ties -> lower index).
+__device__ void topk_token(const FwdArgs& a, int t, int lane, uint2* cand) {
+  const __amdgpu_buffer_rsrc_t rl =
+      __builtin_amdgcn_make_buffer_rsrc(a.logits + int64_t(t) * a.E, static_cast<short>(0), a.E * 4, 0x00020000);
+  uint32_t key[kMaxSlots];
 #pragma unroll
   for (int i = 0; i < kMaxSlots; ++i) {
-    int e = lane + 64 * i;
-    if (e < a.E) {
-      val[i] = lg[e];
-      key[i] = (uint64_t(float_order_key(val[i])) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(e));
-    } else {
-      val[i] = 0.f;
-      key[i] = 0;
-    }
+    const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * (lane + 64 * i), 0, 0));
+    key[i] = (lane + 64 * i < a.E) ? float_order_key(v) : 0u;
   }
-  uint32_t sel = 0;
-  for (int r = 0; r < a.k; ++r) {
-    uint64_t best = 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t lmax = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxSlots; ++i) best = key[i] > best ? key[i] : best;
-    uint64_t wbest = wave_max_u64(best);
+  for (int i = 0; i < kMaxSlots; ++i) lmax = max(lmax, key[i]);
+  const uint32_t lo = wave_kth_largest(lmax, a.k);
+  int ncand = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSlots; ++i) ncand += __popcll(__ballot(key[i] >= lo));
+
+  uint32_t ck;   // this lane's candidate key (0: none)
+  int cidx;      // its expert index
+  if (ncand <= 64) {
+    int base = 0;
 #pragma unroll
     for (int i = 0; i < kMaxSlots; ++i) {
-      if (key[i] == wbest) {  // unique: keys embed the expert index
-        key[i] = 0;
-        sel |= 1u << i;
-      }
+      const bool c = key[i] >= lo;
+      const uint64_t m = __ballot(c);
+      if (c) cand[base + __popcll(m & lt_mask)] = make_uint2(key[i], uint32_t(lane + 64 * i));
+      base += __popcll(m);
     }
-  }
-  // ascending expert order: slot i of lane l is expert l + 64 i
-  int pos[kMaxSlots];
-  float sig[kMaxSlots];
-  float local = 0.f;
-  int base = 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint2 cv = lane < ncand ? cand[lane] : make_uint2(0u, 0u);
+    ck = cv.x;
+    cidx = static_cast<int>(cv.y);
+  } else {
+    // many equal or clustered keys: radix select over all slots, then keep the
+    // selected keys as candidates (at most k <= 32 of them)
+    uint32_t th = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = th | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) {
-    bool s = (sel >> i) & 1u;
-    uint64_t m = __ballot(s);
-    pos[i] = base + __popcll(m & lt_mask);
-    base += __popcll(m);
-    sig[i] = s ? 1.0f / (1.0f + expf(-val[i])) : 0.f;
-    local += sig[i];
-  }
-  const float inv = 1.0f / group_sum<64>(local);
-  int32_t* ids = a.topk_ids + int64_t(t) * a.k;
-  float* wts = a.topk_w + int64_t(t) * a.k;
-#pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) {
-    if ((sel >> i) & 1u) {
-      ids[pos[i]] = lane + 64 * i;
-      wts[pos[i]] = sig[i] * inv;
+      for (int i = 0; i < kMaxSlots; ++i) cnt += __popcll(__ballot(key[i] >= c));
+      th = cnt >= a.k ? c : th;
     }
+    int need = a.k;
+#pragma unroll
+    for (int i = 0; i < kMaxSlots; ++i) need -= __popcll(__ballot(key[i] > th));
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxSlots; ++i) {
+      const uint64_t eq = __ballot(key[i] == th);
+      const bool take = key[i] > th || (key[i] == th && __popcll(eq & lt_mask) < need);
+      need -= min(need, __popcll(eq));
+      const uint64_t m = __ballot(take);
+      if (take) cand[base + __popcll(m & lt_mask)] = make_uint2(key[i], uint32_t(lane + 64 * i));
+      base += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint2 cv = lane < a.k ? cand[lane] : make_uint2(0u, 0u);
+    ck = cv.x;
+    cidx = static_cast<int>(cv.y);
+  }
+  const uint32_t th = wave_kth_largest(ck, a.k);
+  const int need = a.k - __popcll(__ballot(ck > th));
+  const uint64_t eq = __ballot(ck == th && ck != 0u);
+  const bool take = ck > th || (ck == th && ck != 0u && __popcll(eq & lt_mask) < need);
+  const uint64_t m = __ballot(take);
+  const float sig = 1.0f / (1.0f + expf(-order_key_to_float(ck)));
+  const float inv = 1.0f / group_sum<64>(take ? sig : 0.f);
+  if (take) {
+    const int pos = __popcll(m & lt_mask);  // candidates are in ascending expert order
+    a.topk_ids[int64_t(t) * a.k + pos] = cidx;
+    a.topk_w[int64_t(t) * a.k + pos] = sig * inv;
   }
 }
 
 // Many tokens: one wave per token, top-k then the token's MXFP8 row.
 __global__ void __launch_bounds__(256) k_topk_quant(FwdArgs a) {
+  __shared__ uint2 cand[4][64];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  topk_token(a, t, lane);
+  topk_token(a, t, lane, cand[threadIdx.x >> 6]);
   const int nb = a.d / 32;
   const uint16_t* xr = a.x + int64_t(t) * a.d;
   for (int b = lane; b < nb; b += 64) {
@@ -436,8 +498,9 @@ __global__ void __launch_bounds__(1024) k_permute_small(FwdArgs a) {
 // single workgroup; x was already quantised by the router launch.
 __global__ void __launch_bounds__(1024) k_topk_permute_small(FwdArgs a) {
   __shared__ PermLds L;
+  __shared__ uint2 cand[16][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int t = wv; t < a.T; t += 16) topk_token(a, t, lane);
+  for (int t = wv; t < a.T; t += 16) topk_token(a, t, lane, cand[wv]);
   __syncthreads();  // top-k results (global memory) visible to the workgroup
   permute_block(a, L);
 }
@@ -510,7 +573,7 @@ __global__ void __launch_bounds__(256) k_perm_scatter(FwdArgs a) {
 }
 
 hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st) {
-  if (a.T <= kRouterSmallMaxT)
+  if (a.T <= kRouterSmallMaxT && a.T * (a.d / 32) <= 32 * a.E)
     hipLaunchKernelGGL(k_topk_permute_small, dim3(1), dim3(1024), 0, st, a);
   else
     hipLaunchKernelGGL(k_topk_quant, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
@@ -518,7 +581,8 @@ hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
-  if (a.T <= kRouterSmallMaxT) return hipSuccess;  // done with the top-k launch
+  if (a.T <= kRouterSmallMaxT && a.T * (a.d / 32) <= 32 * a.E)
+    return hipSuccess;  // done with the top-k launch
   if (a.T <= kPermSmallMaxTokens) {
     hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(1024), 0, st, a);
     return hipGetLastError();

@@ -3,7 +3,8 @@
 Dense inputs (x, W_r, bias) come from :mod:`.inputs` on the host and are
 copied over.  The MXFP4 expert weights (21 GB for the full layer) are drawn on
 the device by ``libmxmoe_inputs.so``, the GPU twin of the Philox recipe in
-:mod:`.inputs`, which produces the same bytes as the numpy generator.
+:mod:`.inputs`, which produces the same canonical bytes as the numpy
+generator; the layer library then packs them into its tile order.
 """
 
 from __future__ import annotations
@@ -17,6 +18,7 @@ import numpy as np
 import torch
 
 from . import inputs as I
+from . import mxmoe as M
 from .layer import DeviceWeights
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -70,10 +72,41 @@ def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
 
 
+def packed_experts_device(cfg: I.LayerConfig, kind: str, count: int, layer: int = 0,
+                          device="cuda") -> Tuple[torch.Tensor, ...]:
+    """(gu_codes, gu_scales, dn_codes, dn_scales) of `count` experts in the
+    packed tile order moe_forward reads, one flat row per expert.  Each expert
+    is drawn in canonical form into a scratch buffer and packed on the device."""
+    d, f = cfg.d_model, cfg.d_ff
+    gsb, dsb = M.moe_packed_scale_bytes(2 * f, d), M.moe_packed_scale_bytes(d, f)
+    out = (torch.empty((count, f * d), dtype=torch.uint8, device=device),
+           torch.empty((count, gsb), dtype=torch.uint8, device=device),
+           torch.empty((count, d * f // 2), dtype=torch.uint8, device=device),
+           torch.empty((count, dsb), dtype=torch.uint8, device=device))
+    tgc = torch.empty((2 * f, d // 2), dtype=torch.uint8, device=device)
+    tgs = torch.empty((2 * f, d // 32), dtype=torch.uint8, device=device)
+    tdc = torch.empty((d, f // 2), dtype=torch.uint8, device=device)
+    tds = torch.empty((d, f // 32), dtype=torch.uint8, device=device)
+    eb = I.scale_exponent_base(d)
+    st = torch.cuda.current_stream().cuda_stream
+    for i in range(count):
+        slot = I.expert_slot(kind, i)
+        gen_mx_matrix_device(tgc, tgs, 2 * f, d, cfg.seed, I.stream_id(I.KIND_GU_CODES, slot, layer),
+                             I.stream_id(I.KIND_GU_SCALES, slot, layer), eb)
+        gen_mx_matrix_device(tdc, tds, d, f, cfg.seed, I.stream_id(I.KIND_DN_CODES, slot, layer),
+                             I.stream_id(I.KIND_DN_SCALES, slot, layer), eb)
+        M.moe_pack_mx4(tgc.data_ptr(), tgs.data_ptr(), 1, 2 * f, d, out[0][i].data_ptr(),
+                       out[1][i].data_ptr(), st)
+        M.moe_pack_mx4(tdc.data_ptr(), tds.data_ptr(), 1, d, f, out[2][i].data_ptr(),
+                       out[3][i].data_ptr(), st)
+    return out
+
+
 def device_weights(cfg: I.LayerConfig, layer: int = 0, device="cuda") -> DeviceWeights:
-    guc, gus, dnc, dns = gen_experts_device(cfg, "routed", cfg.num_experts, layer, device)
+    """The layer's weights on the GPU, expert matrices packed for moe_forward."""
+    guc, gus, dnc, dns = packed_experts_device(cfg, "routed", cfg.num_experts, layer, device)
     if cfg.num_shared:
-        sguc, sgus, sdnc, sdns = gen_experts_device(cfg, "shared", cfg.num_shared, layer, device)
+        sguc, sgus, sdnc, sdns = packed_experts_device(cfg, "shared", cfg.num_shared, layer, device)
     else:
         sguc = sgus = sdnc = sdns = None
     wr = torch.from_numpy(I.gen_router_w(cfg, layer)).to(device)

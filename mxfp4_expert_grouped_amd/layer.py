@@ -13,11 +13,12 @@ from . import mxmoe as M
 
 @dataclass
 class DeviceWeights:
-    """MXFP4 expert weights and router parameters resident on one GPU."""
-    gu_codes: torch.Tensor    # uint8 [E, 2 d_ff, d/2]
-    gu_scales: torch.Tensor   # uint8 [E, 2 d_ff, d/32]
-    dn_codes: torch.Tensor    # uint8 [E, d, d_ff/2]
-    dn_scales: torch.Tensor   # uint8 [E, d, d_ff/32]
+    """MXFP4 expert weights (packed tile order, one flat row per expert) and
+    router parameters resident on one GPU."""
+    gu_codes: torch.Tensor    # uint8 [E, d_ff*d]
+    gu_scales: torch.Tensor   # uint8 [E, moe_packed_scale_bytes(2 d_ff, d)]
+    dn_codes: torch.Tensor    # uint8 [E, d*d_ff/2]
+    dn_scales: torch.Tensor   # uint8 [E, moe_packed_scale_bytes(d, d_ff)]
     sgu_codes: Optional[torch.Tensor]
     sgu_scales: Optional[torch.Tensor]
     sdn_codes: Optional[torch.Tensor]

@@ -18,8 +18,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEV
 MOE_SRC_BF16, MOE_SRC_FP32 = 0, 1
 
 EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_workspace_bytes", "moe_quantize_act",
-            "moe_forward", "moe_profile_begin", "moe_profile_end", "moe_status_string",
-            "moe_last_error")
+            "moe_forward", "moe_profile_begin", "moe_profile_end", "moe_packed_scale_bytes",
+            "moe_pack_mx4", "moe_status_string", "moe_last_error")
 STAGES = ("router", "topk", "permute", "gate_up", "down", "combine")
 
 
@@ -77,6 +77,11 @@ def load_library(path: str = LIB_PATH):
     lib.moe_profile_begin.restype = c_int
     lib.moe_profile_end.argtypes = [c_void_p, POINTER(ctypes.c_double), POINTER(c_int32)]
     lib.moe_profile_end.restype = c_int
+    lib.moe_packed_scale_bytes.argtypes = [c_int64, c_int64]
+    lib.moe_packed_scale_bytes.restype = c_size_t
+    lib.moe_pack_mx4.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p,
+                                 c_void_p, c_void_p]
+    lib.moe_pack_mx4.restype = c_int
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_status_string.restype = c_char_p
     lib.moe_last_error.argtypes = []
@@ -136,3 +141,12 @@ def moe_profile_end(plan: c_void_p):
     n = c_int32()
     _check(load_library().moe_profile_end(plan, ms, ctypes.byref(n)))
     return dict(zip(STAGES, list(ms))), n.value
+
+
+def moe_packed_scale_bytes(rows: int, k: int) -> int:
+    return load_library().moe_packed_scale_bytes(rows, k)
+
+
+def moe_pack_mx4(codes: int, scales: int, mats: int, rows: int, k: int, codes_p: int,
+                 scales_p: int, stream: Optional[int] = None) -> None:
+    _check(load_library().moe_pack_mx4(codes, scales, mats, rows, k, codes_p, scales_p, stream))

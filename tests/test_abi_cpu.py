@@ -25,7 +25,7 @@ def M():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_header_function(M):
@@ -156,3 +156,22 @@ def test_no_device_reports_device_error(M):
         assert ei.value.status == M.MOE_ERR_DEVICE
     finally:
         M.moe_plan_destroy(p)
+
+
+def test_pack_sizes_and_argument_errors(M):
+    assert M.moe_packed_scale_bytes(4096, 7168) == 4096 * 224
+    assert M.moe_packed_scale_bytes(7168, 2048) == 7168 * 64
+    assert M.moe_packed_scale_bytes(256, 256) == 16 * 256  # K padded to 512
+    assert M.moe_packed_scale_bytes(0, 128) == 0
+    fake = 1 << 20
+    M.moe_pack_mx4(None, None, 0, 32, 256, None, None)  # nothing to pack
+    for args, status in [
+        ((fake, fake, 1, 24, 256, fake, fake), M.MOE_ERR_UNSUPPORTED),
+        ((fake, fake, 1, 32, 192, fake, fake), M.MOE_ERR_UNSUPPORTED),
+        ((fake, fake, -1, 32, 256, fake, fake), M.MOE_ERR_INVALID_ARG),
+        ((None, fake, 1, 32, 256, fake, fake), M.MOE_ERR_INVALID_ARG),
+        ((fake + 8, fake, 1, 32, 256, fake, fake), M.MOE_ERR_INVALID_ARG),
+    ]:
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_pack_mx4(*args)
+        assert ei.value.status == status

@@ -36,15 +36,55 @@ import parity as P  # noqa: E402  (after the marker; imports torch-side helpers)
 
 def test_gpu_generator_matches_numpy_tiny_all_experts():
     cfg = I.CONFIGS["tiny"]
-    W = P.IG.device_weights(cfg)
     ref = I.ExpertWeights(cfg)
+    Wr = P.IG.gen_experts_device(cfg, "routed", cfg.num_experts)
+    Ws = P.IG.gen_experts_device(cfg, "shared", cfg.num_shared)
     for e in range(cfg.num_experts):
-        for got, want in zip((W.gu_codes[e], W.gu_scales[e], W.dn_codes[e], W.dn_scales[e]),
-                             ref("routed", e)):
+        for got, want in zip((t[e] for t in Wr), ref("routed", e)):
             assert np.array_equal(got.cpu().numpy(), want)
-    for got, want in zip((W.sgu_codes[0], W.sgu_scales[0], W.sdn_codes[0], W.sdn_scales[0]),
-                         ref("shared", 0)):
+    for got, want in zip((t[0] for t in Ws), ref("shared", 0)):
         assert np.array_equal(got.cpu().numpy(), want)
+
+
+def _pack_reference(codes, scales, rows, k):
+    """The packed tile order, written out with plain loops over its definition."""
+    nsteps, nq = k // 128, (k + 511) // 512
+    cp = np.zeros((rows // 16, nsteps, 64, 16), np.uint8)
+    sp = np.zeros((rows // 16, nq, 64, 4), np.uint8)
+    for b in range(rows // 16):
+        for lane in range(64):
+            g, r = lane // 16, lane % 16
+            for s in range(nsteps):
+                cp[b, s, lane] = codes[16 * b + r, 64 * s + 16 * g: 64 * s + 16 * g + 16]
+            for q in range(nq):
+                for j in range(4):
+                    blk = 16 * q + 4 * j + g
+                    if blk < k // 32:
+                        sp[b, q, lane, j] = scales[16 * b + r, blk]
+    return cp.reshape(-1), sp.reshape(-1)
+
+
+@pytest.mark.parametrize("rows,k", [(32, 128), (16, 256), (48, 640), (64, 2048), (32, 7168)])
+def test_pack_mx4_layout(rows, k):
+    from mxfp4_expert_grouped_amd import mxmoe as M
+    rng = np.random.default_rng(rows + k)
+    mats = 3
+    codes = rng.integers(0, 256, size=(mats, rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(0, 255, size=(mats, rows, k // 32), dtype=np.uint8)
+    sb = M.moe_packed_scale_bytes(rows, k)
+    assert sb == (rows // 16) * ((k + 511) // 512) * 256
+    cp = torch.empty(mats * rows * k // 2, dtype=torch.uint8, device="cuda")
+    spk = torch.empty(mats * sb, dtype=torch.uint8, device="cuda")
+    M.moe_pack_mx4(None, None, 0, rows, k, None, None)  # zero matrices: no-op
+    tc, ts = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    M.moe_pack_mx4(tc.data_ptr(), ts.data_ptr(), mats, rows, k, cp.data_ptr(), spk.data_ptr(),
+                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    cpn, spn = cp.cpu().numpy(), spk.cpu().numpy()
+    for m in range(mats):
+        rc, rs = _pack_reference(codes[m], scales[m], rows, k)
+        assert np.array_equal(cpn[m * rows * k // 2:(m + 1) * rows * k // 2], rc)
+        assert np.array_equal(spn[m * sb:(m + 1) * sb], rs)
 
 
 def test_gpu_generator_matches_numpy_full_shape_sample():
