@@ -197,7 +197,8 @@ def main():
         kern_ms = gu_ms if gu_ms else ms_per_step
         achieved = mean_gu_bytes / (kern_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": profiled_traffic(cfg.name),
                     "kernel": "gate_up grouped GEMM (k_gemm, 16-row tiles)",
                     "kernel_ms": round(kern_ms, 5),
                     "algorithmic_bytes_per_launch": int(mean_gu_bytes)}
@@ -245,6 +246,28 @@ def main():
     if stage_avg:
         out["stage_ms"] = stage_avg
     print(json.dumps(out), flush=True)
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed hardware-
+    counter summary, if one exists for this workload and the kernel sources are
+    unchanged since it was taken (else None)."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"gate_up_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("kernels_gemm.hip", "mx_device.h", "internal.h"):
+        h.update(open(os.path.join(root, "mxfp4_expert_grouped_amd", "csrc", f), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg):
