@@ -63,7 +63,7 @@ typedef enum {
 
 typedef enum { MOE_SRC_BF16 = 0, MOE_SRC_FP32 = 1 } moe_src_dtype;
 
-/* Layer shape.  d_model and d_ff: multiples of 128.  1 <= num_experts <= 1024.
+/* Layer shape.  d_model: a multiple of 256; d_ff: a multiple of 128.  1 <= num_experts <= 1024.
  * 1 <= top_k <= min(32, num_experts).  0 <= num_shared <= 8.
  * 1 <= max_tokens <= 2^20.  flags: reserved, must be 0. */
 typedef struct {
@@ -87,6 +87,7 @@ typedef struct {
  * Permuted rows: R = T*top_k routed rows (expert-major, tokens ascending)
  * followed by num_shared blocks of T rows (shared expert s, token t at
  * T*top_k + s*T + t). */
+/* Alignment: x_codes and h_codes 16 bytes, every other tap 4 bytes. */
 typedef struct {
   float *logits;          /* [T][E]   router logits incl. bias (fp32)        */
   int32_t *topk_ids;      /* [T][top_k] selected experts, ascending          */

@@ -64,15 +64,16 @@ moe_status check_device() {
   return MOE_OK;
 }
 
-// rows per grouped-GEMM tile: 16 when experts see few rows (decode), else 64
+// rows per grouped-GEMM tile: 16 when experts see few rows (weight-streaming
+// decode kernels), else 128 (LDS-staged prefill kernels)
 int choose_bm(const moe_config& c, int64_t T) {
   int64_t avg = (T * c.top_k) / c.num_experts;
-  return avg >= 24 ? 64 : 16;
+  return avg >= 24 ? 128 : 16;
 }
 
 struct Layout {
   size_t logits, topk_ids, topk_w, x_codes, x_scales, counts, offsets, row_src, row_token,
-      token_row, chunk_mask, chunk_base, tiles, tile_count, h_codes, h_scales, o, total;
+      token_row, chunk_mask, chunk_base, tiles, tile_count, ex_tiles, h_codes, h_scales, o, total;
   int bm, max_tiles, nchunks;
 };
 
@@ -104,9 +105,10 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.chunk_base = take(size_t(L.nchunks) * E * 4);
   L.tiles = take(size_t(std::max(L.max_tiles, 1)) * sizeof(Tile));
   L.tile_count = take(4);
+  L.ex_tiles = take((E + S + 1) * 4);
   L.h_codes = take(R * f);
   L.h_scales = take(R * f / 32);
-  L.o = take(R * d * 4);
+  L.o = take(R * d * (L.bm == 16 ? 4 : 2));
   L.total = off;
   return L;
 }
@@ -117,8 +119,8 @@ moe_status check_config(const moe_config* c) {
       c->num_shared < 0 || c->max_tokens <= 0)
     return fail(MOE_ERR_INVALID_ARG, "non-positive size in config");
   if (c->flags != 0) return fail(MOE_ERR_INVALID_ARG, "flags must be 0");
-  if (c->d_model % 128 || c->d_ff % 128)
-    return fail(MOE_ERR_UNSUPPORTED, "d_model (%d) and d_ff (%d) must be multiples of 128",
+  if (c->d_model % 256 || c->d_ff % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model (%d) must be a multiple of 256 and d_ff (%d) of 128",
                 c->d_model, c->d_ff);
   if (c->d_model > 65536 || c->d_ff > 65536)
     return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be <= 65536");
@@ -252,6 +254,9 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
   if (!aligned(workspace, 256)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (taps) {
     if ((taps->x_codes && !aligned(taps->x_codes, 16)) ||
+        (taps->h_codes && !aligned(taps->h_codes, 16)) ||
+        (taps->x_scales && !aligned(taps->x_scales, 4)) ||
+        (taps->h_scales && !aligned(taps->h_scales, 4)) ||
         (taps->y_routed && !aligned(taps->y_routed, 16)) ||
         (taps->y_shared && !aligned(taps->y_shared, 16)) ||
         (taps->logits && !aligned(taps->logits, 4)) || (taps->topk_w && !aligned(taps->topk_w, 4)) ||
@@ -295,9 +300,11 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
   a.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
   a.tiles = reinterpret_cast<Tile*>(ws + L.tiles);
   a.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
+  a.ex_tiles = reinterpret_cast<int32_t*>(ws + L.ex_tiles);
   a.h_codes = pick(tp.h_codes, L.h_codes, static_cast<uint8_t*>(nullptr));
   a.h_scales = pick(tp.h_scales, L.h_scales, static_cast<uint8_t*>(nullptr));
   a.o = reinterpret_cast<float*>(ws + L.o);
+  a.o16 = reinterpret_cast<uint16_t*>(ws + L.o);
   a.gu_acc = tp.gu_acc;
   a.y_routed = tp.y_routed;
   a.y_shared = tp.y_shared;

@@ -39,17 +39,19 @@ struct FwdArgs {
   int32_t* token_row;   // [T][k]
   uint64_t* chunk_mask; // [nchunks][E]
   int32_t* chunk_base;  // [E][nchunks]
-  Tile* tiles;          // [max_tiles]
+  Tile* tiles;          // [max_tiles], grouped by expert (routed ascending, then shared)
   int32_t* tile_count;  // [1]
+  int32_t* ex_tiles;    // [E+S+1] first tile of each expert (prefix over tile counts)
   uint8_t* h_codes;     // [R][dff]
   uint8_t* h_scales;    // [R][dff/32]
-  float* o;             // [R][d]
+  float* o;             // [R][d] fp32 (16-row tiles)
+  uint16_t* o16;        // [R][d] bf16 (128-row tiles); same workspace region as o
   // optional taps (null = skip)
   float* gu_acc;        // [R][2*dff]
   float* y_routed;      // [T][d]
   float* y_shared;      // [T][d]
   // launch-time choices
-  int bm;               // rows per tile
+  int bm;               // rows per tile: 16 (decode kernels) or 128 (prefill kernels)
   int max_tiles;
   int nchunks;          // 64-token chunks
 };

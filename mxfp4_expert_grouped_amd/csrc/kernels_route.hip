@@ -427,6 +427,8 @@ __device__ void write_offsets_and_tiles(const FwdArgs& a, int* cnt, int* scan, i
   __syncthreads();
   // scan tile counts into tile_start (stored in cnt)
   int ntiles = block_exclusive_scan(cnt, nex, wave_tot);
+  for (int ex = tid; ex < nex; ex += 1024) a.ex_tiles[ex] = cnt[ex];
+  if (tid == 0) a.ex_tiles[nex] = ntiles;
   for (int ex = tid; ex < nex; ex += 1024) {
     int rb = scan[ex];
     int rows = ex < a.E ? (ex + 1 < a.E ? scan[ex + 1] : a.Rr) - rb : a.T;
@@ -608,16 +610,24 @@ __global__ void __launch_bounds__(256) k_combine(FwdArgs a) {
     wts[tid] = a.topk_w[int64_t(t) * a.k + tid];
   }
   __syncthreads();
-  const int c = blockIdx.y * 256 + tid;  // float4 column
+  const int c = blockIdx.y * 256 + tid;  // 4-column group
   if (c >= a.d / 4) return;
-  const float4* o4 = reinterpret_cast<const float4*>(a.o);
-  const int64_t rs = a.d / 4;
+  // o rows are fp32 after the 16-row-tile kernels, bf16 after the 128-row ones
+  const bool o16 = a.bm != 16;
+  auto load4 = [&](int64_t row) -> float4 {
+    if (o16) {
+      const uint2 u = reinterpret_cast<const uint2*>(a.o16 + row * a.d)[c];
+      return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                         __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    }
+    return reinterpret_cast<const float4*>(a.o + row * a.d)[c];
+  };
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
   int j = 0;
   for (; j + 4 <= a.k; j += 4) {
     float4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = o4[int64_t(rows[j + u]) * rs + c];
+    for (int u = 0; u < 4; ++u) v[u] = load4(rows[j + u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float w = wts[j + u];
@@ -626,14 +636,14 @@ __global__ void __launch_bounds__(256) k_combine(FwdArgs a) {
     }
   }
   for (; j < a.k; ++j) {
-    const float4 v = o4[int64_t(rows[j]) * rs + c];
+    const float4 v = load4(rows[j]);
     const float w = wts[j];
     r.x = fmaf(w, v.x, r.x); r.y = fmaf(w, v.y, r.y);
     r.z = fmaf(w, v.z, r.z); r.w = fmaf(w, v.w, r.w);
   }
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int sh = 0; sh < a.S; ++sh) {
-    const float4 v = o4[int64_t(a.Rr + sh * a.T + t) * rs + c];
+    const float4 v = load4(int64_t(a.Rr + sh * a.T + t));
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
   uint2 yb;

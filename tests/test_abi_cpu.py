@@ -56,6 +56,7 @@ def test_status_strings(M):
     (dict(d_model=7168, d_ff=2048, num_experts=896, top_k=16, num_shared=2, max_tokens=32768), 0),
     (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 0),
     (dict(d_model=200, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 2),
+    (dict(d_model=384, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 2),
     (dict(d_model=256, d_ff=96, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 2),
     (dict(d_model=256, d_ff=128, num_experts=1025, top_k=2, num_shared=1, max_tokens=8), 2),
     (dict(d_model=256, d_ff=128, num_experts=16, top_k=17, num_shared=1, max_tokens=8), 2),
@@ -86,8 +87,8 @@ def test_workspace_bytes(M):
         w256 = M.moe_workspace_bytes(p, 256)
         w32k = M.moe_workspace_bytes(p, 32768)
         assert 0 < w1 < w256 < w32k
-        # at least the fp32 expert outputs: (T*k + S*T) rows of d floats
-        assert w32k >= 32768 * 18 * 7168 * 4
+        # at least the bf16 expert outputs at prefill: (T*k + S*T) rows of d values
+        assert w32k >= 32768 * 18 * 7168 * 2
         with pytest.raises(M.MoeError) as ei:
             M.moe_workspace_bytes(p, 32769)
         assert ei.value.status == M.MOE_ERR_INVALID_ARG
