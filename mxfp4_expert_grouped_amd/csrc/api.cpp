@@ -65,10 +65,10 @@ moe_status check_device() {
 }
 
 // rows per grouped-GEMM tile: 16 when experts see few rows (weight-streaming
-// decode kernels), else 128 (LDS-staged prefill kernels)
+// decode kernels), else 256 (LDS-staged prefill kernels)
 int choose_bm(const moe_config& c, int64_t T) {
   int64_t avg = (T * c.top_k) / c.num_experts;
-  return avg >= 24 ? 128 : 16;
+  return avg >= 24 ? 256 : 16;
 }
 
 struct Layout {

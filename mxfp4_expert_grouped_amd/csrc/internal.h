@@ -51,7 +51,7 @@ struct FwdArgs {
   float* y_routed;      // [T][d]
   float* y_shared;      // [T][d]
   // launch-time choices
-  int bm;               // rows per tile: 16 (decode kernels) or 128 (prefill kernels)
+  int bm;               // rows per tile: 16 (decode kernels) or 256 (prefill kernels)
   int max_tiles;
   int nchunks;          // 64-token chunks
 };

@@ -248,26 +248,52 @@ static hipError_t launch_dec(const FwdArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill variant: 128-row x 256-weight-row workgroup tiles, MFMA-bound.
-// Operands move global -> LDS with direct-to-LDS loads placed in MFMA lane
-// order (each 1 KB copy is one A half-operand of a 16-row subtile or one
-// packed 16-row weight step), so every LDS read is one conflict-free read per
-// lane and no registers stage the copies.  The block scales travel the same
-// way (4 bytes per A row, the packed scale dword per weight block and lane).
-// Four LDS stages of one 128-wide K step each keep three steps in flight;
-// each wave issues 13 copies per stage and waits on its own copies before the
-// barrier that publishes the stage.  Wave w computes rows 32w .. 32w+31
-// against all 256 weight rows; a wave whose rows are all past the tile's end
-// skips its MFMAs.
+// Prefill variant: 256-row x 256-weight-row workgroup tiles, eight waves (two
+// per SIMD) on the 32x32x64 scaled MFMA.
+//
+// Operands move global -> LDS with direct-to-LDS copies (no registers stage
+// them) through a ring of three K-step slots, so two steps are in flight
+// while one is computed.  A slot holds
+//   * A codes, 32 KB: for row block mb (32 rows), K half h and piece c, 1 KB
+//     in MFMA lane order: lane l holds row 32mb + l%32, bytes
+//     64h + 32c + 16(l/32) .. +15 of the step (the two 16-byte pieces of the
+//     32x32x64 FP8 operand);
+//   * B codes, 16 KB: the 16 packed 1 KB weight chunks (16 rows x 128 K);
+//     the FP4 operand of 32 rows x 64 K is a per-lane gather over two chunks
+//     that touches 16 consecutive bytes per lane group (conflict free);
+//   * A scales, 2 KB: one dword (the step's four block scales) per row, in
+//     eight 256-byte copies of 32 rows.
+// The packed weight scales (one dword per lane covering four steps) go to
+// two 4 KB slots, one per group of four steps.  Every wave issues its own
+// share of the copies (4 A, 2 B, 1 A-scale per step, 2 B-scale per group)
+// and waits on its own copies before the barrier that publishes a step.
+//
+// Wave w computes rows 64(w%4) .. +63 (two 32-row blocks) against 128 of
+// the 256 weight rows: gate and up rows of the same 64 h columns for
+// gate_up, 128 output columns for down.  Row blocks past the tile's end
+// skip their MFMAs.
 // ---------------------------------------------------------------------------
 
-// stage slot: A codes 16 KB | B codes 16 KB | A scales 4 x 256 B | B scales 16 x 256 B
-constexpr int kPfA = 0, kPfB = 16384, kPfAS = 32768, kPfBS = 33792, kPfStageBytes = 37888;
-constexpr int kPfCopies = 13;  // per wave per stage: 4 A + 4 B + 1 A-scale + 4 B-scale
-__shared__ __attribute__((aligned(1024))) uint8_t pf_s0[kPfStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t pf_s1[kPfStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t pf_s2[kPfStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t pf_s3[kPfStageBytes];
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// A: FP8 E4M3 with its scale in byte 0; B: FP4 E2M1 with its scale in byte SB
+template <int SB>
+__device__ __forceinline__ v16f mfma32_mx(const v8i& a, const v8i& b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, static_cast<int>(sa), SB,
+                                                         static_cast<int>(sb));
+}
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+constexpr int kPfSlot = 51200;                 // A 32 KB | B 16 KB | A scales 2 KB
+constexpr int kPfA = 0, kPfB = 32768, kPfAS = 49152;
+constexpr int kPfBS = 3 * kPfSlot;             // two 4 KB weight-scale slots
+constexpr int kPfLds = kPfBS + 2 * 4096;       // 161792 bytes
+constexpr int kPfCopies = 7;                   // per wave per step (plus 2 per group)
+__shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -292,11 +318,14 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 #define PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
 
 // Work order of the prefill GEMMs: items (tile, column block) expert-major,
-// column block next, tile fastest, cut into 8 contiguous ranges, one per XCD
-// (workgroups go to the XCDs round-robin by linear id).  An expert's tiles
-// and column blocks then run on one XCD close together in time, so its
-// activation rows and each weight block come from that XCD's L2 after the
-// first touch.  Returns false for a workgroup with no item.
+// cut into 8 contiguous ranges, one per XCD (workgroups go to the XCDs
+// round-robin by linear id).  Inside an expert the items run in groups of
+// kPfGroupTiles tiles, column block next and tile fastest, so the workgroups
+// an XCD runs at once cover a few tiles x several column blocks: every
+// activation window and every weight window they read in the same K step is
+// shared by several of them and comes from that XCD's L2.  Returns false for
+// a workgroup with no item.
+constexpr int kPfGroupTiles = 4;
 __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int* tile_out, int* blk_out) {
   const int total = *a.tile_count * nblocks;
   const int per_xcd = (total + 7) / 8;
@@ -312,18 +341,23 @@ __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int*
   }
   const int t0 = a.ex_tiles[lo], nt = a.ex_tiles[lo + 1] - t0;
   const int local = w - t0 * nblocks;
-  *blk_out = local / nt;
-  *tile_out = t0 + local % nt;
+  const int tg = local / (kPfGroupTiles * nblocks);           // tile group
+  const int gsize = min(kPfGroupTiles, nt - tg * kPfGroupTiles);
+  const int rem = local - tg * kPfGroupTiles * nblocks;
+  *blk_out = rem / gsize;
+  *tile_out = t0 + tg * kPfGroupTiles + rem % gsize;
   return true;
 }
 
 template <bool GU>
-__global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
+__global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
   int tile_idx, nblk;
   if (!pf_work_item(a, GU ? a.dff / 128 : a.d / 256, &tile_idx, &nblk)) return;
   const Tile tile = a.tiles[tile_idx];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
+  const int l32 = lane & 31, g32 = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy of the wave index
+  const int wm = wu & 3, wn = wu >> 2;
   const int K = GU ? a.d : a.dff;
   const int nsteps = K / 128, nq4 = (K + 511) / 512;
 
@@ -336,141 +370,223 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + tile.ex * ws_stride)
                          : (shared ? a.sdn_s + sidx * ws_stride : a.dn_s + tile.ex * ws_stride);
 
-  // 16 weight-row blocks of this tile: gate then up (gate_up) or 256 outputs (down)
+  // the tile's 16 weight-row blocks (16 rows each): gate then up (gate_up), or
+  // 256 consecutive output rows (down)
   const int c0 = GU ? nblk * 128 : nblk * 256;
   auto wblk = [&](int j) -> int64_t {
     if (GU) return j < 8 ? (c0 + 16 * j) / 16 : (a.dff + c0 + 16 * (j - 8)) / 16;
     return (c0 + 16 * j) / 16;
   };
-  // activation row of this wave's row slot q (0..31); padding rows read row_begin
-  auto src_row = [&](int q) -> int64_t {
-    int row = tile.row_begin + 32 * wave + q;
+  // activation row r of the tile; padding rows read the tile's first row
+  auto src_row = [&](int r) -> int64_t {
+    int row = tile.row_begin + r;
     if (row >= tile.row_end) row = tile.row_begin;
     return GU ? (row < a.Rr ? a.row_token[row] : row - a.Rr - sidx * a.T) : row;
   };
 
-  // copy sources of this wave: its A subtiles 2w, 2w+1, weight blocks 4w..4w+3
-  const uint8_t* a_src[2];
+  // ---- copy sources of this wave: row block wu, weight blocks 2wu, 2wu+1
+  const uint8_t* a_src = (GU ? a.x_codes : a.h_codes) + src_row(32 * wu + l32) * K + 16 * g32;
+  const uint8_t* as_src = (GU ? a.x_scales : a.h_scales) + src_row(32 * wu + l32) * (K / 32);
+  const uint8_t* b_src[2];
+  const uint8_t* bs_src[2];
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms) a_src[ms] = (GU ? a.x_codes : a.h_codes) + src_row(16 * ms + r16) * K + 16 * g;
-  const uint8_t* as_src = (GU ? a.x_scales : a.h_scales) + src_row(lane & 31) * (K / 32);
-  const uint8_t* b_src[4];
-  const uint8_t* bs_src[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    b_src[j] = wc + wblk(4 * wave + j) * nsteps * 1024 + 16 * lane;
-    bs_src[j] = ws + wblk(4 * wave + j) * nq4 * 256 + 4 * lane;
+  for (int jj = 0; jj < 2; ++jj) {
+    b_src[jj] = wc + wblk(2 * wu + jj) * nsteps * 1024 + 16 * lane;
+    bs_src[jj] = ws + wblk(2 * wu + jj) * nq4 * 256 + 4 * lane;
   }
+  const uint32_t lds0 = lds_addr(pf_lds);
 
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for M0
-  auto issue = [&](int st, uint8_t* buf) {
-    const uint32_t base = lds_addr(buf);
+  // copies of step st into slot st % 3 (and of the weight scales of group
+  // st / 4 when st starts a group)
+  auto issue = [&](int st, bool group_start) {
+    const uint32_t slot = lds0 + (st % 3) * kPfSlot;
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms)
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        lds_copy16(a_src + 128 * st + 64 * h + 32 * c, slot + kPfA + ((wu * 2 + h) * 2 + c) * 1024);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) lds_copy16(b_src[jj] + st * 1024, slot + kPfB + (2 * wu + jj) * 1024);
+    lds_copy4(as_src + 4 * st, slot + kPfAS + wu * 256);
+    if (group_start) {
+      const int q = st >> 2;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        lds_copy4(bs_src[jj] + q * 256, lds0 + kPfBS + (q & 1) * 4096 + (2 * wu + jj) * 256);
+    }
+  };
+
+  // ---- per-lane LDS read offsets
+  // weight fragment p (32 rows) starts at chunk j0(p) of the tile's 16
+  auto j0 = [&](int p) -> int { return GU ? (p < 2 ? 4 * wn + 2 * p : 8 + 4 * wn + 2 * (p - 2)) : 8 * wn + 2 * p; };
+  const int b_lane = ((l32 >> 4) << 10) + 16 * (16 * g32 + (lane & 15));  // + j0*1024 + 512h
+  const int bs_lane = ((l32 >> 4) << 8) + 4 * (16 * g32 + (lane & 15));   // + j0*256 + 128h
+  const int rows_left = tile.row_end - tile.row_begin - 64 * wm;
+  const int nact = rows_left <= 0 ? 0 : (rows_left <= 32 ? 1 : 2);   // active row blocks
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc[i][p] = v16f{};
+
+  auto main_loop = [&](auto nact_c) {
+    constexpr int NACT = decltype(nact_c)::value;
+    uint32_t bsr[4][2];  // weight scale dwords of the current group
+
+    auto compute = [&](int st, auto ic) {
+      constexpr int I = decltype(ic)::value;  // st % 4
+      if (NACT == 0) return;
+      const uint8_t* sb = pf_lds + (st % 3) * kPfSlot;
+      if (I == 0) {
+        const uint8_t* bsb = pf_lds + kPfBS + ((st >> 2) & 1) * 4096 + bs_lane;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            bsr[pp][h] = *reinterpret_cast<const uint32_t*>(bsb + j0(pp) * 256 + 128 * h);
+      }
+      uint32_t asr[2];
+      v8i av[2][2];
+      v8i bv[2][4];
+#pragma unroll
+      for (int i = 0; i < NACT; ++i)
+        asr[i] = *reinterpret_cast<const uint32_t*>(sb + kPfAS + (2 * wm + i) * 256 + 4 * l32);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < NACT; ++i) {
+          const uint8_t* pa = sb + kPfA + (((2 * wm + i) * 2 + h) * 2) * 1024 + 16 * lane;
+          av[h][i] = make_a(ld16(pa), ld16(pa + 1024));
+        }
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) bv[h][pp] = make_b(ld16(sb + kPfB + j0(pp) * 1024 + 512 * h + b_lane));
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        lds_copy16(a_src[ms] + 128 * st + 64 * h, base + kPfA + ((2 * wave_u + ms) * 2 + h) * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_copy16(b_src[j] + st * 1024, base + kPfB + (4 * wave_u + j) * 1024);
-    // scale bytes 4st .. 4st+3 of this wave's 32 rows (lanes 32..63 repeat 0..31)
-    lds_copy4(as_src + 4 * st, base + kPfAS + wave_u * 256);
+        for (int i = 0; i < NACT; ++i) {
+          const uint32_t sa = asr[i] >> (8 * (2 * h + g32));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_copy4(bs_src[j] + (st >> 2) * 256, base + kPfBS + (4 * wave_u + j) * 256);
-  };
+          for (int pp = 0; pp < 4; ++pp) acc[i][pp] = mfma32_mx<I>(av[h][i], bv[h][pp], acc[i][pp], sa, bsr[pp][h]);
+        }
+    };
 
-  const bool active = tile.row_begin + 32 * wave < tile.row_end;
-  v4f acc[2][16];
-#pragma unroll
-  for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) acc[ms][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    // step st: wait for this wave's copies of st (the next step's may stay
+    // in flight), publish with a barrier, refill the slot of step st-1 with
+    // step st+2, then compute
+    auto stage = [&](int st, auto ic) {
+      constexpr int I = decltype(ic)::value;
+      if (st + 1 < nsteps) {
+        if (((I + 1) & 3) == 0) PF_WAIT_VM(kPfCopies + 2);
+        else PF_WAIT_VM(kPfCopies);
+      } else {
+        PF_WAIT_VM(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 2 < nsteps) issue(st + 2, ((I + 2) & 3) == 0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st, ic);
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-  auto compute = [&](int st, const uint8_t* buf) {
-    if (!active) return;
-    v8i av[2];
-    uint32_t sa[2];
-#pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-      const uint8_t* p = buf + kPfA + (2 * wave + ms) * 2048 + 16 * lane;
-      av[ms] = make_a(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 1024));
-      sa[ms] = *reinterpret_cast<const uint32_t*>(buf + kPfAS + wave * 256 + (16 * ms + r16) * 4) >> (8 * g);
+    issue(0, true);
+    if (1 < nsteps) issue(1, false);
+    for (int st0 = 0; st0 < nsteps; st0 += 4) {
+      stage(st0, IntC<0>{});
+      if (st0 + 1 < nsteps) stage(st0 + 1, IntC<1>{});
+      if (st0 + 2 < nsteps) stage(st0 + 2, IntC<2>{});
+      if (st0 + 3 < nsteps) stage(st0 + 3, IntC<3>{});
     }
-    const int bsh = 8 * (st & 3);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const v8i bv = make_b(*reinterpret_cast<const uint4*>(buf + kPfB + j * 1024 + 16 * lane));
-      const uint32_t sb = *reinterpret_cast<const uint32_t*>(buf + kPfBS + j * 256 + 4 * lane) >> bsh;
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms) acc[ms][j] = mfma_mx(av[ms], bv, acc[ms][j], sa[ms], sb);
-    }
   };
+  if (nact == 2) main_loop(IntC<2>{});
+  else if (nact == 1) main_loop(IntC<1>{});
+  else main_loop(IntC<0>{});
 
-  // stage st: wait for this wave's copies of st (later stages may stay in
-  // flight), publish with a barrier, refill the slot stage st-1 used with
-  // stage st+3, then compute.
-  auto stage = [&](int st, const uint8_t* cur, uint8_t* nxt) {
-    const int later = nsteps - 1 - st;  // stages issued after st: min(later, 2)
-    if (later >= 2) PF_WAIT_VM(2 * kPfCopies);
-    else if (later == 1) PF_WAIT_VM(kPfCopies);
-    else PF_WAIT_VM(0);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    if (st + 3 < nsteps) issue(st + 3, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(st, cur);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  issue(0, pf_s0);
-  if (1 < nsteps) issue(1, pf_s1);
-  if (2 < nsteps) issue(2, pf_s2);
-  for (int st0 = 0; st0 < nsteps; st0 += 4) {
-    stage(st0, pf_s0, pf_s3);
-    if (st0 + 1 < nsteps) stage(st0 + 1, pf_s1, pf_s0);
-    if (st0 + 2 < nsteps) stage(st0 + 2, pf_s2, pf_s1);
-    if (st0 + 3 < nsteps) stage(st0 + 3, pf_s3, pf_s2);
-  }
-  if (!active) return;
-
-  // epilogue: rows 32w + 16ms + 4g + i
+  // ---- epilogue through LDS: every wave is past its last operand read
+  // after this barrier, and each wave then owns a private stage region.
+  // acc[i][p] register r holds tile row 64wm + 32i + 8(r/4) + 4 g32 + r%4
+  // and column l32 of weight fragment p.
+  __syncthreads();
+  if (nact == 0) return;
+  if (GU) {
+    // h = silu(gate) * up as fp32 [64 rows][64 h columns] (row stride 68)
+    float* hs = reinterpret_cast<float*>(pf_lds) + wu * (64 * 68);
 #pragma unroll
-  for (int ms = 0; ms < 2; ++ms) {
+    for (int i = 0; i < 2; ++i) {
+      if (i >= nact) break;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = tile.row_begin + 32 * wave + 16 * ms + 4 * g + i;
-      const bool valid = row < tile.row_end;
-      if (GU) {
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          float h[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int j = 2 * p + hh;
-            const float gt = acc[ms][j][i], up = acc[ms][8 + j][i];
-            h[hh] = gt / (1.0f + expf(-gt)) * up;
-            if (valid && a.gu_acc) {
-              const int col = c0 + 16 * j + r16;
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 32 * i + 8 * (r / 4) + 4 * g32 + (r % 4);
+          const float gt = acc[i][pp][r], up = acc[i][pp + 2][r];
+          hs[rl * 68 + 32 * pp + l32] = gt / (1.0f + __expf(-gt)) * up;
+          if (a.gu_acc) {
+            const int row = tile.row_begin + 64 * wm + rl;
+            if (row < tile.row_end) {
+              const int col = c0 + 64 * wn + 32 * pp + l32;
               a.gu_acc[int64_t(row) * 2 * a.dff + col] = gt;
               a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + col] = up;
             }
           }
-          const float amax = group_max<16>(fmaxf(fabsf(h[0]), fabsf(h[1])));
-          const int e = mx8_block_exp(amax);
-          if (valid) {
-            const int col = c0 + 32 * p + r16;
-            uint8_t* hc = a.h_codes + int64_t(row) * a.dff;
-            hc[col] = static_cast<uint8_t>(mx8_encode(h[0], e));
-            hc[col + 16] = static_cast<uint8_t>(mx8_encode(h[1], e));
-            if (r16 == 0) a.h_scales[int64_t(row) * (a.dff / 32) + (c0 + 32 * p) / 32] = static_cast<uint8_t>(e + 127);
-          }
         }
-      } else if (valid) {
-        uint16_t* orow = a.o16 + int64_t(row) * a.d + c0 + r16;
+    }
+    // lane l quantises row l: two MXFP8 blocks of 32 h values
+    const int row = tile.row_begin + 64 * wm + lane;
+    if (row < tile.row_end) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) orow[16 * j] = f32_to_bf16_rne(acc[ms][j][i]);
+      for (int blk = 0; blk < 2; ++blk) {
+        const float4* src = reinterpret_cast<const float4*>(hs + lane * 68 + 32 * blk);
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 t = src[q];
+          v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
+        const int e = mx8_block_exp(amax);
+        const float sc = exp2_int(-e);
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          w[q] = e4m3_cvt4(v[4 * q] * sc, v[4 * q + 1] * sc, v[4 * q + 2] * sc, v[4 * q + 3] * sc);
+        const int col = c0 + 64 * wn + 32 * blk;
+        uint4* dst = reinterpret_cast<uint4*>(a.h_codes + int64_t(row) * a.dff + col);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        a.h_scales[int64_t(row) * (a.dff / 32) + (col >> 5)] = static_cast<uint8_t>(e + 127);
+      }
+    }
+  } else {
+    // bf16 outputs [64 rows][128 columns] (row stride 136 halves), then
+    // 16-byte row chunks: 16 per row, 1024 per wave, 16 per lane
+    uint16_t* os = reinterpret_cast<uint16_t*>(pf_lds) + wu * (64 * 136);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i >= nact) break;
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 32 * i + 8 * (r / 4) + 4 * g32 + (r % 4);
+          os[rl * 136 + 32 * pp + l32] = f32_to_bf16_rne(acc[i][pp][r]);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int ch = q * 64 + lane;          // chunk: row ch / 16, 8 columns at 8 (ch % 16)
+      const int rl = ch >> 4, cc = 8 * (ch & 15);
+      const int row = tile.row_begin + 64 * wm + rl;
+      if (row < tile.row_end) {
+        const uint4 t = *reinterpret_cast<const uint4*>(os + rl * 136 + cc);
+        *reinterpret_cast<uint4*>(a.o16 + int64_t(row) * a.d + c0 + 128 * wn + cc) = t;
       }
     }
   }
@@ -480,7 +596,7 @@ template <bool GU>
 static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
   const int64_t N = GU ? a.dff / 128 : a.d / 256;
   const int64_t items = int64_t(a.max_tiles) * N;
-  hipLaunchKernelGGL((k_gemm_pf<GU>), dim3(8 * ((items + 7) / 8)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_gemm_pf<GU>), dim3(8 * ((items + 7) / 8)), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

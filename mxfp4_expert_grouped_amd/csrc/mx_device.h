@@ -52,6 +52,25 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float q) {
   return sign | code;
 }
 
+// The same code from the conversion instruction: with its input clamped to
+// +-448, V_CVT_PK_FP8_F32 (OCP E4M3, round-to-nearest-even, denormals kept)
+// gives e4m3_rne_sat's code for every finite float (checked over all 2^32
+// bit patterns).  Two values per instruction: bytes 0 and 1 of the result.
+__device__ __forceinline__ uint32_t e4m3_cvt2(float a, float b) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false)) & 0xFFFFu;
+}
+// four codes in one dword, byte i from value i
+__device__ __forceinline__ uint32_t e4m3_cvt4(float a, float b, float c, float d) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  const float cc = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  const float cd = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, lo, true));
+}
+
 // Quantise one value given the block exponent e (e <= 126 always holds for
 // finite fp32 blocks, so 2^-e is a normal float).
 __device__ __forceinline__ uint32_t mx8_encode(float v, int e) {
