@@ -254,15 +254,19 @@ static hipError_t launch_dec(const FwdArgs& a, hipStream_t st) {
 // Operands move global -> LDS with direct-to-LDS copies (no registers stage
 // them) through a ring of three K-step slots, so two steps are in flight
 // while one is computed.  A slot holds
-//   * A codes, 32 KB: for row block mb (32 rows), K half h and piece c, 1 KB
-//     in MFMA lane order: lane l holds row 32mb + l%32, bytes
-//     64h + 32c + 16(l/32) .. +15 of the step (the two 16-byte pieces of the
-//     32x32x64 FP8 operand);
+//   * A codes, 32 KB: row-major, 128 bytes per row, with the 16-byte chunks
+//     of row r XOR-swizzled by (r/2)%8.  One copy moves 8 whole rows (8
+//     lanes per row, each 128-byte line read once) and the MFMA fragment
+//     reads (32 rows x one chunk) hit every bank once per 16 lanes;
 //   * B codes, 16 KB: the 16 packed 1 KB weight chunks (16 rows x 128 K);
 //     the FP4 operand of 32 rows x 64 K is a per-lane gather over two chunks
 //     that touches 16 consecutive bytes per lane group (conflict free);
 //   * A scales, 2 KB: one dword (the step's four block scales) per row, in
-//     eight 256-byte copies of 32 rows.
+//     eight 256-byte copies of 32 rows -- only when K is not a multiple of
+//     512.  Otherwise the activation scales of four steps (16 bytes per row)
+//     come once per group: waves 0-3 each copy 64 rows into 1 KB of the
+//     (then unused) A-scale areas of slots 0 and 1, and every wave keeps its
+//     rows' 16 bytes in registers for the group.
 // The packed weight scales (one dword per lane covering four steps) go to
 // two 4 KB slots, one per group of four steps.  Every wave issues its own
 // share of the copies (4 A, 2 B, 1 A-scale per step, 2 B-scale per group)
@@ -292,7 +296,8 @@ constexpr int kPfSlot = 51200;                 // A 32 KB | B 16 KB | A scales 2
 constexpr int kPfA = 0, kPfB = 32768, kPfAS = 49152;
 constexpr int kPfBS = 3 * kPfSlot;             // two 4 KB weight-scale slots
 constexpr int kPfLds = kPfBS + 2 * 4096;       // 161792 bytes
-constexpr int kPfCopies = 7;                   // per wave per step (plus 2 per group)
+// copies per wave per step: 4 A + 2 B (+1 A-scale dword when scales are not
+// grouped); per group: 2 weight-scale dwords (+1 A-scale group copy, waves 0-3)
 __shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -349,8 +354,12 @@ __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int*
   return true;
 }
 
-template <bool GU>
+// LDS address of the A-scale group area written by wave w (0..3)
+__device__ __forceinline__ int pf_asg_off(int w) { return (w >> 1) * kPfSlot + kPfAS + (w & 1) * 1024; }
+
+template <bool GU, bool AG>
 __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
+  constexpr int kCopies = AG ? 6 : 7;
   int tile_idx, nblk;
   if (!pf_work_item(a, GU ? a.dff / 128 : a.d / 256, &tile_idx, &nblk)) return;
   const Tile tile = a.tiles[tile_idx];
@@ -384,9 +393,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
     return GU ? (row < a.Rr ? a.row_token[row] : row - a.Rr - sidx * a.T) : row;
   };
 
-  // ---- copy sources of this wave: row block wu, weight blocks 2wu, 2wu+1
-  const uint8_t* a_src = (GU ? a.x_codes : a.h_codes) + src_row(32 * wu + l32) * K + 16 * g32;
-  const uint8_t* as_src = (GU ? a.x_scales : a.h_scales) + src_row(32 * wu + l32) * (K / 32);
+  // ---- copy sources of this wave: rows 32wu .. 32wu+31, weight blocks 2wu, 2wu+1.
+  // A copy q covers rows 32wu + 8q .. +7: lane l reads chunk (l%8) ^ swz(row)
+  // of row 32wu + 8q + l/8 and lands at LDS row*128 + 16(l%8).
+  const uint8_t* a_src[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rl = 32 * wu + 8 * q + (lane >> 3);
+    a_src[q] = (GU ? a.x_codes : a.h_codes) + src_row(rl) * K + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
+  }
+  const uint8_t* as_src = (GU ? a.x_scales : a.h_scales) + src_row(AG ? (64 * wu + lane) & 255 : 32 * wu + l32) * (K / 32);
   const uint8_t* b_src[2];
   const uint8_t* bs_src[2];
 #pragma unroll
@@ -401,14 +417,12 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
   auto issue = [&](int st, bool group_start) {
     const uint32_t slot = lds0 + (st % 3) * kPfSlot;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        lds_copy16(a_src + 128 * st + 64 * h + 32 * c, slot + kPfA + ((wu * 2 + h) * 2 + c) * 1024);
+    for (int q = 0; q < 4; ++q) lds_copy16(a_src[q] + 128 * st, slot + kPfA + (32 * wu + 8 * q) * 128);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) lds_copy16(b_src[jj] + st * 1024, slot + kPfB + (2 * wu + jj) * 1024);
-    lds_copy4(as_src + 4 * st, slot + kPfAS + wu * 256);
+    if (!AG) lds_copy4(as_src + 4 * st, slot + kPfAS + wu * 256);
     if (group_start) {
+      if (AG && wu < 4) lds_copy16(as_src + 16 * (st >> 2), lds0 + pf_asg_off(wu));
       const int q = st >> 2;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
@@ -420,6 +434,12 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
   // weight fragment p (32 rows) starts at chunk j0(p) of the tile's 16
   auto j0 = [&](int p) -> int { return GU ? (p < 2 ? 4 * wn + 2 * p : 8 + 4 * wn + 2 * (p - 2)) : 8 * wn + 2 * p; };
   const int b_lane = ((l32 >> 4) << 10) + 16 * (16 * g32 + (lane & 15));  // + j0*1024 + 512h
+  // A fragment (row l32 of a 32-row block, K half h, piece c): chunk 4h+2c+g32
+  int a_lane[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) a_lane[h][c] = l32 * 128 + 16 * ((4 * h + 2 * c + g32) ^ ((l32 >> 1) & 7));
   const int bs_lane = ((l32 >> 4) << 8) + 4 * (16 * g32 + (lane & 15));   // + j0*256 + 128h
   const int rows_left = tile.row_end - tile.row_begin - 64 * wm;
   const int nact = rows_left <= 0 ? 0 : (rows_left <= 32 ? 1 : 2);   // active row blocks
@@ -433,6 +453,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
   auto main_loop = [&](auto nact_c) {
     constexpr int NACT = decltype(nact_c)::value;
     uint32_t bsr[4][2];  // weight scale dwords of the current group
+    uint4 asg[2];        // grouped activation scales of this lane's rows
 
     auto compute = [&](int st, auto ic) {
       constexpr int I = decltype(ic)::value;  // st % 4
@@ -445,19 +466,26 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             bsr[pp][h] = *reinterpret_cast<const uint32_t*>(bsb + j0(pp) * 256 + 128 * h);
+        if (AG) {
+#pragma unroll
+          for (int i = 0; i < NACT; ++i)
+            asg[i] = *reinterpret_cast<const uint4*>(pf_lds + pf_asg_off(wm) + (32 * i + l32) * 16);
+        }
       }
       uint32_t asr[2];
       v8i av[2][2];
       v8i bv[2][4];
 #pragma unroll
-      for (int i = 0; i < NACT; ++i)
-        asr[i] = *reinterpret_cast<const uint32_t*>(sb + kPfAS + (2 * wm + i) * 256 + 4 * l32);
+      for (int i = 0; i < NACT; ++i) {
+        if (AG) asr[i] = I == 0 ? asg[i].x : I == 1 ? asg[i].y : I == 2 ? asg[i].z : asg[i].w;
+        else asr[i] = *reinterpret_cast<const uint32_t*>(sb + kPfAS + (2 * wm + i) * 256 + 4 * l32);
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int i = 0; i < NACT; ++i) {
-          const uint8_t* pa = sb + kPfA + (((2 * wm + i) * 2 + h) * 2) * 1024 + 16 * lane;
-          av[h][i] = make_a(ld16(pa), ld16(pa + 1024));
+          const uint8_t* pa = sb + kPfA + (2 * wm + i) * 4096;
+          av[h][i] = make_a(ld16(pa + a_lane[h][0]), ld16(pa + a_lane[h][1]));
         }
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) bv[h][pp] = make_b(ld16(sb + kPfB + j0(pp) * 1024 + 512 * h + b_lane));
@@ -478,8 +506,12 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
     auto stage = [&](int st, auto ic) {
       constexpr int I = decltype(ic)::value;
       if (st + 1 < nsteps) {
-        if (((I + 1) & 3) == 0) PF_WAIT_VM(kPfCopies + 2);
-        else PF_WAIT_VM(kPfCopies);
+        if (((I + 1) & 3) == 0) {
+          if (AG && wu < 4) PF_WAIT_VM(kCopies + 3);
+          else PF_WAIT_VM(kCopies + 2);
+        } else {
+          PF_WAIT_VM(kCopies);
+        }
       } else {
         PF_WAIT_VM(0);
       }
@@ -596,7 +628,12 @@ template <bool GU>
 static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
   const int64_t N = GU ? a.dff / 128 : a.d / 256;
   const int64_t items = int64_t(a.max_tiles) * N;
-  hipLaunchKernelGGL((k_gemm_pf<GU>), dim3(8 * ((items + 7) / 8)), dim3(512), 0, st, a);
+  const int K = GU ? a.d : a.dff;
+  const dim3 grid(8 * ((items + 7) / 8));
+  if (K % 512 == 0)
+    hipLaunchKernelGGL((k_gemm_pf<GU, true>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm_pf<GU, false>), grid, dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
