@@ -72,9 +72,9 @@ int choose_bm(const moe_config& c, int64_t T) {
 }
 
 struct Layout {
-  size_t logits, topk_ids, topk_w, x_codes, x_scales, counts, offsets, row_src, row_token,
+  size_t logits, router_part, topk_ids, topk_w, x_codes, x_scales, counts, offsets, row_src, row_token,
       token_row, chunk_mask, chunk_base, tiles, tile_count, ex_tiles, h_codes, h_scales, o, total;
-  int bm, max_tiles, nchunks;
+  int bm, max_tiles, nchunks, router_ks;
 };
 
 Layout make_layout(const moe_config& c, int64_t T) {
@@ -92,6 +92,8 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.max_tiles = static_cast<int>((Rr + L.bm - 1) / L.bm + std::min<int64_t>(E, Rr) +
                                  S * ((T + L.bm - 1) / L.bm));
   L.logits = take(T * E * 4);
+  L.router_ks = router_small(T, d, E) ? 1 : router_splits(T, E, d);
+  L.router_part = take(L.router_ks > 1 ? size_t(L.router_ks) * T * E * 4 : 0);
   L.topk_ids = take(T * k * 4);
   L.topk_w = take(T * k * 4);
   L.x_codes = take(T * d);
@@ -309,6 +311,8 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
   a.y_routed = tp.y_routed;
   a.y_shared = tp.y_shared;
   a.bm = L.bm;
+  a.router_ks = L.router_ks;
+  a.router_part = reinterpret_cast<float*>(ws + L.router_part);
   a.max_tiles = L.max_tiles;
   a.nchunks = L.nchunks;
 

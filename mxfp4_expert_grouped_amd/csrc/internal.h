@@ -28,6 +28,7 @@ struct FwdArgs {
   uint16_t* y;  // bf16 [T][d]
   // workspace buffers (or caller taps substituted for them)
   float* logits;        // [T][E]
+  float* router_part;   // [router_ks][T][E] split-K partial logits (router_ks > 1)
   int32_t* topk_ids;    // [T][k]
   float* topk_w;        // [T][k]
   uint8_t* x_codes;     // [T][d]
@@ -51,6 +52,7 @@ struct FwdArgs {
   float* y_routed;      // [T][d]
   float* y_shared;      // [T][d]
   // launch-time choices
+  int router_ks;        // K slices of the MFMA router (1: no partials)
   int bm;               // rows per tile: 16 (decode kernels) or 256 (prefill kernels)
   int max_tiles;
   int nchunks;          // 64-token chunks
@@ -59,6 +61,22 @@ struct FwdArgs {
 // Launchers (kernels_*.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t cols, int64_t ld,
                            uint8_t* codes, uint8_t* scales, hipStream_t st);
+// Tokens up to which the per-expert GEMV router (with the x quantisation
+// fused) runs; above it, the bf16 MFMA router.
+constexpr int kRouterSmallMaxT = 32;
+inline bool router_small(int64_t T, int64_t d, int64_t E) { return T <= kRouterSmallMaxT && T * (d / 32) <= 32 * E; }
+
+// K slices of the MFMA router for T tokens: few 128x128 output tiles are
+// spread over the GPU by cutting d into up to 16 slices of at least 512.
+inline int router_splits(int64_t T, int64_t E, int64_t d) {
+  const int64_t tiles = ((T + 127) / 128) * ((E + 127) / 128);
+  if (tiles >= 256) return 1;
+  int64_t ks = (256 + tiles - 1) / tiles;
+  if (ks > d / 512) ks = d / 512;
+  if (ks > 16) ks = 16;
+  return ks < 1 ? 1 : static_cast<int>(ks);
+}
+
 hipError_t launch_router(const FwdArgs& a, hipStream_t st);
 hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st);
 hipError_t launch_permute(const FwdArgs& a, hipStream_t st);

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "internal.h"
 #include "mx_device.h"
 
@@ -97,7 +99,6 @@ hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t 
 // Few tokens: one 256-thread workgroup per expert streams its W_r row (8 float4
 // loads in flight per thread) once per 8 tokens.  The same launch quantises x
 // to MXFP8: workgroup e handles activation blocks e, e + E, e + 2E, ...
-constexpr int kRouterSmallMaxT = 32;
 
 __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
   __shared__ float part[4][8];
@@ -167,67 +168,176 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
   }
 }
 
-// Many tokens: 64x64 output tile per 256-thread workgroup, K staged in LDS.
-__global__ void __launch_bounds__(256) k_router_gemm(const uint16_t* __restrict__ x,
-                                                     const float* __restrict__ wr,
-                                                     const float* __restrict__ br,
-                                                     float* __restrict__ logits, int T, int d,
-                                                     int E) {
-  __shared__ float xs[32][68];
-  __shared__ float ws[32][68];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tx = tid & 15, ty = tid >> 4;
-  float acc[4][4] = {};
-  const int lr = tid >> 2, lk = (tid & 3) * 8;
-  const int xt = min(t0 + lr, T - 1), we = min(e0 + lr, E - 1);
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    uint4 xv = *reinterpret_cast<const uint4*>(x + int64_t(xt) * d + k0 + lk);
-    const float4* wp = reinterpret_cast<const float4*>(wr + int64_t(we) * d + k0 + lk);
-    float4 w0 = wp[0], w1 = wp[1];
-    __syncthreads();
-    uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+// Many tokens: router logits on the bf16 MFMA.  x is bf16 already; every
+// fp32 router weight w is cut exactly into three bf16 terms by truncation
+// (hi = w with the low 16 mantissa bits cleared, mid the same of w - hi, lo =
+// w - hi - mid, which has at most 8 significant bits), so x.w = x.hi + x.mid
+// + x.lo with every product exact and fp32 accumulation, i.e. fp32 GEMM
+// accuracy at bf16 MFMA rate.
+//
+// Workgroup: 128 tokens x 128 experts, four waves of 64 x 64 (2 x 2 blocks of
+// V_MFMA_F32_32X32X16_BF16), K in steps of 32.  Each step's x tile and the
+// three weight planes sit in LDS rows of 80 bytes (conflict-free fragment
+// reads); the next step's global loads are in registers while the current
+// one computes.  With router_ks > 1, blockIdx.z takes one K slice and writes
+// partial logits that k_router_reduce sums in slice order.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f_r __attribute__((ext_vector_type(16)));
+
+constexpr int kRtRow = 80;                   // bytes per LDS row (32 bf16 + pad)
+constexpr int kRtPlane = 128 * kRtRow;       // one 128-row operand plane
+constexpr int kRtStage = 4 * kRtPlane;       // x, w_hi, w_mid, w_lo
+
+__device__ __forceinline__ uint32_t pack_bf16_hi(float a, float b) {
+  // upper halves of two floats whose low 16 bits are zero: (b, a) bf16 pair
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+}
+
+__global__ void __launch_bounds__(256) k_router_mfma(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kRtStage];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int t0 = blockIdx.x * 128, e0 = blockIdx.y * 128;
+  const int kslice = ((a.d / a.router_ks + 31) / 32) * 32;
+  const int kb = blockIdx.z * kslice, ke = min(a.d, kb + kslice);
+  const int nsteps = ke > kb ? (ke - kb) / 32 : 0;
+
+  // global -> register loads: thread -> row tid/2, 16 K values at 16(tid%2)
+  const int lr = tid >> 1, lk = 16 * (tid & 1);
+  const uint16_t* xp = a.x + int64_t(min(t0 + lr, a.T - 1)) * a.d + kb + lk;
+  const float* wp = a.wr + int64_t(min(e0 + lr, a.E - 1)) * a.d + kb + lk;
+  uint4 xr[2];
+  float4 wr4[4];
+  auto load = [&](int st) {
+    const uint4* xs = reinterpret_cast<const uint4*>(xp + 32 * st);
+    xr[0] = xs[0];
+    xr[1] = xs[1];
+    const float4* ws = reinterpret_cast<const float4*>(wp + 32 * st);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xs[lk + 2 * i][lr] = __uint_as_float(xw[i] << 16);
-      xs[lk + 2 * i + 1][lr] = __uint_as_float(xw[i] & 0xFFFF0000u);
+    for (int q = 0; q < 4; ++q) wr4[q] = ws[q];
+  };
+  // split the weights into three bf16 planes and store the step to LDS buffer b
+  auto store = [&](int b) {
+    uint8_t* base = lds + b * kRtStage + lr * kRtRow + 2 * lk;
+    *reinterpret_cast<uint4*>(base) = xr[0];
+    *reinterpret_cast<uint4*>(base + 16) = xr[1];
+    float w[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[4 * q] = wr4[q].x; w[4 * q + 1] = wr4[q].y; w[4 * q + 2] = wr4[q].z; w[4 * q + 3] = wr4[q].w;
     }
-    ws[lk + 0][lr] = w0.x; ws[lk + 1][lr] = w0.y; ws[lk + 2][lr] = w0.z; ws[lk + 3][lr] = w0.w;
-    ws[lk + 4][lr] = w1.x; ws[lk + 5][lr] = w1.y; ws[lk + 6][lr] = w1.z; ws[lk + 7][lr] = w1.w;
+    uint32_t hi[8], mid[8], lo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float h2[2], m2[2], l2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float v = w[2 * j + u];
+        const float h = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+        const float r = v - h;
+        const float m = __uint_as_float(__float_as_uint(r) & 0xFFFF0000u);
+        h2[u] = h;
+        m2[u] = m;
+        l2[u] = r - m;
+      }
+      hi[j] = pack_bf16_hi(h2[0], h2[1]);
+      mid[j] = pack_bf16_hi(m2[0], m2[1]);
+      lo[j] = pack_bf16_hi(l2[0], l2[1]);
+    }
+    uint8_t* wb = lds + b * kRtStage + kRtPlane + lr * kRtRow + 2 * lk;
+    *reinterpret_cast<uint4*>(wb) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(wb + 16) = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+    *reinterpret_cast<uint4*>(wb + kRtPlane) = make_uint4(mid[0], mid[1], mid[2], mid[3]);
+    *reinterpret_cast<uint4*>(wb + kRtPlane + 16) = make_uint4(mid[4], mid[5], mid[6], mid[7]);
+    *reinterpret_cast<uint4*>(wb + 2 * kRtPlane) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(wb + 2 * kRtPlane + 16) = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+  };
+
+  v16f_r acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f_r{};
+  // fragment lane: row l%32 of a 32-row block, K elements 8(l/32) .. +7 of a 16-chunk
+  const int frag = (lane & 31) * kRtRow + 16 * (lane >> 5);
+  auto compute = [&](int b) {
+    const uint8_t* base = lds + b * kRtStage;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      v8bf av[2], bv[3][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        av[i] = *reinterpret_cast<const v8bf*>(base + (64 * wm + 32 * i) * kRtRow + frag + 32 * kc);
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bv[pl][j] = *reinterpret_cast<const v8bf*>(base + (pl + 1) * kRtPlane + (64 * wn + 32 * j) * kRtRow +
+                                                     frag + 32 * kc);
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[pl][j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  if (nsteps > 0) {
+    load(0);
+    store(0);
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    for (int st = 0; st < nsteps; ++st) {
+      const int cur = st & 1;
+      if (st + 1 < nsteps) load(st + 1);
+      compute(cur);
+      if (st + 1 < nsteps) store(cur ^ 1);
+      __syncthreads();
     }
   }
+
+  // acc[i][j] register r: token 64wm + 32i + 8(r/4) + 4(lane/32) + r%4,
+  // expert 64wn + 32j + lane%32
+  const bool partial = a.router_ks > 1;
+  float* out = partial ? a.router_part + int64_t(blockIdx.z) * a.T * a.E : a.logits;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int t = t0 + ty + 16 * i;
-    if (t >= T) continue;
+  for (int j = 0; j < 2; ++j) {
+    const int e = e0 + 64 * wn + 32 * j + (lane & 31);
+    if (e >= a.E) continue;
+    const float bias = (!partial && a.br) ? a.br[e] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int e = e0 + tx + 16 * j;
-      if (e < E) logits[int64_t(t) * E + e] = acc[i][j] + (br ? br[e] : 0.f);
-    }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + 64 * wm + 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+        if (t < a.T) out[int64_t(t) * a.E + e] = acc[i][j][r] + bias;
+      }
+  }
+}
+
+// logits = sum of the K-slice partials in slice order, plus the bias
+__global__ void __launch_bounds__(256) k_router_reduce(FwdArgs a) {
+  const int64_t n = int64_t(a.T) * a.E;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    float s = 0.0f;
+    for (int ks = 0; ks < a.router_ks; ++ks) s += a.router_part[ks * n + i];
+    a.logits[i] = s + (a.br ? a.br[i % a.E] : 0.0f);
   }
 }
 
 hipError_t launch_router(const FwdArgs& a, hipStream_t st) {
   // the small-batch router also quantises x: 32 blocks per expert workgroup
-  if (a.T <= kRouterSmallMaxT && a.T * (a.d / 32) <= 32 * a.E) {
+  if (router_small(a.T, a.d, a.E)) {
     hipLaunchKernelGGL(k_router_small, dim3(a.E), dim3(256), 0, st, a);
   } else {
-    dim3 grid((a.T + 63) / 64, (a.E + 63) / 64);
-    hipLaunchKernelGGL(k_router_gemm, grid, dim3(256), 0, st, a.x, a.wr, a.br, a.logits, a.T, a.d,
-                       a.E);
+    dim3 grid((a.T + 127) / 128, (a.E + 127) / 128, a.router_ks);
+    hipLaunchKernelGGL(k_router_mfma, grid, dim3(256), 0, st, a);
+    if (a.router_ks > 1) {
+      const int64_t n = int64_t(a.T) * a.E;
+      const int blocks = static_cast<int>(std::min<int64_t>((n + 255) / 256, 4096));
+      hipLaunchKernelGGL(k_router_reduce, dim3(blocks), dim3(256), 0, st, a);
+    }
   }
   return hipGetLastError();
 }
@@ -575,7 +685,7 @@ __global__ void __launch_bounds__(256) k_perm_scatter(FwdArgs a) {
 }
 
 hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st) {
-  if (a.T <= kRouterSmallMaxT && a.T * (a.d / 32) <= 32 * a.E)
+  if (router_small(a.T, a.d, a.E))
     hipLaunchKernelGGL(k_topk_permute_small, dim3(1), dim3(1024), 0, st, a);
   else
     hipLaunchKernelGGL(k_topk_quant, dim3((a.T + 3) / 4), dim3(256), 0, st, a);
@@ -583,7 +693,7 @@ hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
-  if (a.T <= kRouterSmallMaxT && a.T * (a.d / 32) <= 32 * a.E)
+  if (router_small(a.T, a.d, a.E))
     return hipSuccess;  // done with the top-k launch
   if (a.T <= kPermSmallMaxTokens) {
     hipLaunchKernelGGL(k_permute_small, dim3(1), dim3(1024), 0, st, a);
