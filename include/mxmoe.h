@@ -105,23 +105,31 @@ typedef struct {
 } moe_taps;
 
 /* Packed MXFP4 matrix (one-time conversion at weight-load time).  For a
- * canonical matrix with `rows` rows (a multiple of 16) and reduction width k
- * (a multiple of 128), 16-row blocks b and 128-wide K steps s, lane
- * l = 16*g + r (g = l/16, r = l%16):
- *   codes_p [rows/16][k/128][64][16]: entry (b, s, l) = canonical code bytes
- *           64*s + 16*g .. +16 of row 16*b + r (MX block 4*s + g);
- *   scales_p[rows/16][ceil(k/512)][64][4]: byte j of entry (b, q, l) = the
- *           canonical scale of row 16*b + r, block 16*q + 4*j + g, or 0 past
- *           the end of the row.
- * One 16-row x 128-wide MFMA step of a wave is then one contiguous 1 KB in
- * lane order, and its scales one dword per lane per four steps.
- * codes_p is rows*k/2 bytes; scales_p is moe_packed_scale_bytes(rows, k). */
+ * canonical matrix with `rows` rows (a multiple of 64) and reduction width k
+ * (a multiple of 128): 64-row groups G, 128-wide K steps s, 16-row blocks
+ * j = 0..3 of a group, lane l = 16*g + r (g = l/16, r = l%16), and
+ *   row(G, j, r) = 64*G + 16*j + r                                (plain), or
+ *   row(G, j, r) = (j/2)*(rows/2) + 32*G + 16*(j%2) + r      (interleave != 0:
+ *                  group G pairs rows 32G..32G+31 of the two halves -- the
+ *                  gate and up rows of the same outputs for W_gu):
+ *   codes_p [rows/64][k/128][4][64][16]: entry (G, s, j, l) = canonical code
+ *           bytes 64*s + 16*g .. +16 of row(G, j, r) (MX block 4*s + g);
+ *   scales_p[rows/64][k/128][64][4]: byte j of entry (G, s, l) = canonical
+ *           scale of row(G, j, r), block 4*s + g.
+ * The four 16-row x 128-wide MFMA operands of a group and step are then 4 KB
+ * contiguous in lane order, and their scales one dword per lane.
+ * codes_p is rows*k/2 bytes; scales_p is moe_packed_scale_bytes(rows, k)
+ * = rows*k/32 bytes (0 for sizes the layout does not cover). */
 size_t moe_packed_scale_bytes(int64_t rows, int64_t k);
 /* Pack `mats` matrices stored back to back (canonical codes [mats][rows][k/2],
  * scales [mats][rows][k/32]) into codes_p/scales_p (packed, back to back).
- * Device buffers; codes and codes_p 16-byte aligned, scales_p 4-byte aligned. */
+ * moe_forward expects W_gu (routed and shared) packed with interleave = 1 and
+ * W_dn with interleave = 0.  Device buffers; codes and codes_p 16-byte
+ * aligned, scales_p 4-byte aligned.  rows not a multiple of 64 or k not a
+ * multiple of 128: MOE_ERR_UNSUPPORTED. */
 moe_status moe_pack_mx4(const uint8_t *codes, const uint8_t *scales, int64_t mats, int64_t rows,
-                        int64_t k, uint8_t *codes_p, uint8_t *scales_p, void *stream);
+                        int64_t k, int interleave, uint8_t *codes_p, uint8_t *scales_p,
+                        void *stream);
 
 /* Validate `cfg` and build a plan (host only; no device call). */
 moe_status moe_plan(const moe_config *cfg, moe_plan_t **out_plan);

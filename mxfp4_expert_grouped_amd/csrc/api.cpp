@@ -41,15 +41,20 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Checked once per device: a visible gfx950 device is current.
-moe_status check_device() {
+// Checked once per device: a visible gfx950 device is current.  Also gives
+// its compute-unit count.
+moe_status check_device(int* num_cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
     (void)hipGetLastError();
     return fail(MOE_ERR_DEVICE, "no HIP device available");
   }
   static int checked[64] = {0};  // 0 unknown, 1 ok, 2 bad
-  if (dev < 64 && checked[dev] == 1) return MOE_OK;
+  static int cus[64] = {0};
+  if (dev < 64 && checked[dev] == 1) {
+    if (num_cus) *num_cus = cus[dev];
+    return MOE_OK;
+  }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
     (void)hipGetLastError();
@@ -60,15 +65,19 @@ moe_status check_device() {
     return fail(MOE_ERR_DEVICE, "device %d is %s, the kernels are built for gfx950", dev,
                 prop.gcnArchName);
   }
-  if (dev < 64) checked[dev] = 1;
+  if (dev < 64) {
+    checked[dev] = 1;
+    cus[dev] = prop.multiProcessorCount;
+  }
+  if (num_cus) *num_cus = prop.multiProcessorCount;
   return MOE_OK;
 }
 
-// rows per grouped-GEMM tile: 16 when experts see few rows (weight-streaming
+// rows per grouped-GEMM tile: 8 when experts see few rows (weight-streaming
 // decode kernels), else 256 (LDS-staged prefill kernels)
 int choose_bm(const moe_config& c, int64_t T) {
   int64_t avg = (T * c.top_k) / c.num_experts;
-  return avg >= 24 ? 256 : 16;
+  return avg >= 24 ? 256 : kDecodeMaxRows;
 }
 
 struct Layout {
@@ -110,7 +119,7 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.ex_tiles = take((E + S + 1) * 4);
   L.h_codes = take(R * f);
   L.h_scales = take(R * f / 32);
-  L.o = take(R * d * (L.bm == 16 ? 4 : 2));
+  L.o = take(R * d * (L.bm <= kDecodeMaxRows ? 4 : 2));
   L.total = off;
   return L;
 }
@@ -207,22 +216,24 @@ moe_status moe_quantize_act(const void* src, moe_src_dtype dt, int64_t rows, int
 }
 
 size_t moe_packed_scale_bytes(int64_t rows, int64_t k) {
-  if (rows <= 0 || k <= 0) return 0;
+  if (rows <= 0 || k <= 0 || rows % 64 || k % 128) return 0;
   return static_cast<size_t>(packed_scale_bytes(rows, k));
 }
 
 moe_status moe_pack_mx4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int64_t rows,
-                        int64_t k, uint8_t* codes_p, uint8_t* scales_p, void* stream) {
+                        int64_t k, int interleave, uint8_t* codes_p, uint8_t* scales_p,
+                        void* stream) {
   if (mats < 0 || rows < 0 || k < 0) return fail(MOE_ERR_INVALID_ARG, "negative size");
-  if (rows % 16 || k % 128)
-    return fail(MOE_ERR_UNSUPPORTED, "rows must be a multiple of 16 and k of 128");
+  if (interleave != 0 && interleave != 1) return fail(MOE_ERR_INVALID_ARG, "interleave must be 0 or 1");
+  if (rows % 64 || k % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "rows must be a multiple of 64 and k of 128");
   if (mats == 0 || rows == 0 || k == 0) return MOE_OK;
   if (!codes || !scales || !codes_p || !scales_p) return fail(MOE_ERR_INVALID_ARG, "NULL buffer");
   if (!aligned(codes, 16) || !aligned(codes_p, 16) || !aligned(scales_p, 4))
     return fail(MOE_ERR_INVALID_ARG, "codes/codes_p need 16-byte, scales_p 4-byte alignment");
   moe_status s = check_device();
   if (s != MOE_OK) return s;
-  hipError_t e = launch_pack_mx4(codes, scales, mats, rows, k, codes_p, scales_p,
+  hipError_t e = launch_pack_mx4(codes, scales, mats, rows, k, interleave, codes_p, scales_p,
                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
@@ -268,11 +279,13 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
         (taps->token_row && !aligned(taps->token_row, 4)) || (taps->gu_acc && !aligned(taps->gu_acc, 4)))
       return fail(MOE_ERR_INVALID_ARG, "misaligned tap buffer");
   }
-  moe_status s = check_device();
+  int num_cus = 0;
+  moe_status s = check_device(&num_cus);
   if (s != MOE_OK) return s;
 
   char* ws = static_cast<char*>(workspace);
   FwdArgs a{};
+  a.num_cus = num_cus > 0 ? num_cus : 256;
   a.T = static_cast<int>(num_tokens);
   a.d = c.d_model; a.dff = c.d_ff; a.E = c.num_experts; a.k = c.top_k; a.S = c.num_shared;
   a.Rr = a.T * a.k;
@@ -320,17 +333,19 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
   moe_plan_t* pl = const_cast<moe_plan_t*>(plan);
   const bool prof = pl->prof_mask && pl->prof_n < pl->prof_cap;
   hipEvent_t* ev = prof ? &pl->prof_ev[size_t(pl->prof_n) * MOE_NUM_STAGES * 2] : nullptr;
-  typedef hipError_t (*Launch)(const FwdArgs&, hipStream_t);
-  static const Launch stages[MOE_NUM_STAGES] = {launch_router,       launch_topk_quant,
-                                                launch_permute,      launch_gemm_gate_up,
-                                                launch_gemm_down,    launch_combine};
-  for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+  auto stage = [&](int i, hipError_t (*launch)(const FwdArgs&, hipStream_t), const FwdArgs& args) -> bool {
     const bool rec = prof && ((pl->prof_mask >> i) & 1u);
     if (rec) (void)hipEventRecord(ev[2 * i], st);
-    hipError_t e = stages[i](a, st);
-    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+    if (launch(args, st) != hipSuccess) return false;
     if (rec) (void)hipEventRecord(ev[2 * i + 1], st);
-  }
+    return true;
+  };
+
+  static hipError_t (*const stages[MOE_NUM_STAGES])(const FwdArgs&, hipStream_t) = {
+      launch_router, launch_topk_quant, launch_permute, launch_gemm_gate_up, launch_gemm_down, launch_combine};
+  for (int i = 0; i < MOE_NUM_STAGES; ++i)
+    if (!stage(i, stages[i], a))
+      return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(hipGetLastError()));
   if (prof) pl->prof_n++;
   return MOE_OK;
 }

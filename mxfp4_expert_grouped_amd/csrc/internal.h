@@ -53,7 +53,8 @@ struct FwdArgs {
   float* y_shared;      // [T][d]
   // launch-time choices
   int router_ks;        // K slices of the MFMA router (1: no partials)
-  int bm;               // rows per tile: 16 (decode kernels) or 256 (prefill kernels)
+  int bm;               // rows per tile: 8 (decode kernels) or 256 (prefill kernels)
+  int num_cus;          // compute units of the device (persistent decode grid)
   int max_tiles;
   int nchunks;          // 64-token chunks
 };
@@ -63,6 +64,10 @@ hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t 
                            uint8_t* codes, uint8_t* scales, hipStream_t st);
 // Tokens up to which the per-expert GEMV router (with the x quantisation
 // fused) runs; above it, the bf16 MFMA router.
+// Rows per tile of the decode (weight-streaming) kernels; larger tiles go to
+// the prefill kernels.
+constexpr int kDecodeMaxRows = 8;
+
 constexpr int kRouterSmallMaxT = 32;
 inline bool router_small(int64_t T, int64_t d, int64_t E) { return T <= kRouterSmallMaxT && T * (d / 32) <= 32 * E; }
 
@@ -84,10 +89,10 @@ hipError_t launch_gemm_gate_up(const FwdArgs& a, hipStream_t st);
 hipError_t launch_gemm_down(const FwdArgs& a, hipStream_t st);
 hipError_t launch_combine(const FwdArgs& a, hipStream_t st);
 hipError_t launch_pack_mx4(const uint8_t* codes, const uint8_t* scales, int64_t mats, int64_t rows,
-                           int64_t k, uint8_t* codes_p, uint8_t* scales_p, hipStream_t st);
+                           int64_t k, int interleave, uint8_t* codes_p, uint8_t* scales_p, hipStream_t st);
 
 // bytes of one packed scale matrix [rows/16][ceil(k/512)][64][4]
-__host__ __device__ inline int64_t packed_scale_bytes(int64_t rows, int64_t k) { return (rows / 16) * ((k + 511) / 512) * 256; }
+__host__ __device__ inline int64_t packed_scale_bytes(int64_t rows, int64_t k) { return rows * (k / 32); }
 
 // token counts at or below which the single-workgroup permutation is used
 constexpr int kPermSmallMaxTokens = 1024;

@@ -62,244 +62,6 @@ __device__ __forceinline__ v8i make_b(uint4 v) {
   return r;
 }
 
-// ---------------------------------------------------------------------------
-// Decode variant: 16-row tiles (a few tokens per expert), weight-streaming.
-// Each wave owns 16*NI output columns (gate and up subtiles for gate_up) over
-// a contiguous share of K; the KS waves of a workgroup split K and reduce
-// through LDS in a fixed order.  K is walked in groups of GS MFMA steps; the
-// loads of the next group are issued before the MFMAs of the current one, so
-// a whole group of weight bytes per wave stays in flight.  Padding rows of the
-// tile read as zero through out-of-range buffer loads (no memory traffic).
-// ---------------------------------------------------------------------------
-
-template <int NB, int GS>
-struct DecFrag {
-  uint4 b[NB][GS];
-  uint4 a[GS][2];
-  uint32_t sa[GS];
-  uint32_t sb[NB];
-  uint32_t bsh;  // byte offset of this group's first step inside the scale dword
-};
-
-template <int NI, int KS, int GS, bool GU>
-__global__ void __launch_bounds__(64 * KS) k_gemm_dec(FwdArgs a) {
-  constexpr int NB = GU ? 2 * NI : NI;
-  const int tile_idx = blockIdx.x;
-  if (tile_idx >= *a.tile_count) return;
-  const Tile tile = a.tiles[tile_idx];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int K = GU ? a.d : a.dff;
-  const int N = GU ? a.dff : a.d;
-  const int nsteps = K / 128, nq4 = (K + 511) / 512;
-  const int col0 = blockIdx.y * (16 * NI);
-
-  const bool shared = tile.ex >= a.E;
-  const int sidx = tile.ex - a.E;
-  const int64_t wrows = GU ? 2 * a.dff : a.d;
-  const int64_t wc_stride = wrows * (K / 2), ws_stride = packed_scale_bytes(wrows, K);
-  const uint8_t* wc = GU ? (shared ? a.sgu_c + sidx * wc_stride : a.gu_c + tile.ex * wc_stride)
-                         : (shared ? a.sdn_c + sidx * wc_stride : a.dn_c + tile.ex * wc_stride);
-  const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + tile.ex * ws_stride)
-                         : (shared ? a.sdn_s + sidx * ws_stride : a.dn_s + tile.ex * ws_stride);
-
-  const int arow = tile.row_begin + r16;
-  const bool avalid = arow < tile.row_end;
-  uint32_t src = 0;
-  if (avalid) src = GU ? (arow < a.Rr ? a.row_token[arow] : arow - a.Rr - sidx * a.T) : arow;
-  const uint32_t a_rows = GU ? a.T : a.R;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(GU ? a.x_codes : a.h_codes, a_rows * uint32_t(K));
-  const __amdgpu_buffer_rsrc_t ras = make_rsrc(GU ? a.x_scales : a.h_scales, a_rows * uint32_t(K / 32));
-  const uint32_t a_base = avalid ? src * uint32_t(K) + 16 * g : kBufOOB;
-  const uint32_t as_base = avalid ? src * uint32_t(K / 32) : kBufOOB;
-  const uint8_t* bp[NB];
-  const uint8_t* bsp[NB];
-#pragma unroll
-  for (int nj = 0; nj < NB; ++nj) {
-    const int n = col0 + 16 * (nj % NI);
-    const int64_t blk = ((GU && nj >= NI) ? a.dff + n : n) / 16;
-    bp[nj] = wc + blk * nsteps * 1024 + 16 * lane;
-    bsp[nj] = ws + blk * nq4 * 256 + 4 * lane;
-  }
-
-  // K groups of this wave: a contiguous range
-  const int nq = nsteps / GS;
-  const int q0 = (nq * wave) / KS, q1 = (nq * (wave + 1)) / KS;
-  const int n = q1 - q0;
-
-  auto load = [&](DecFrag<NB, GS>& f, int q) {
-    const int st0 = q * GS;
-    f.bsh = 8 * (st0 & 3);
-#pragma unroll
-    for (int nj = 0; nj < NB; ++nj) {
-      f.sb[nj] = *reinterpret_cast<const uint32_t*>(bsp[nj] + (st0 >> 2) * 256);
-#pragma unroll
-      for (int s = 0; s < GS; ++s) f.b[nj][s] = ld16(bp[nj] + (st0 + s) * 1024);
-    }
-#pragma unroll
-    for (int s = 0; s < GS; ++s) {
-      // scale bytes 4*step .. 4*step+3 of the row; lane group g uses byte g
-      f.sa[s] = buf4(ras, as_base + 4 * (st0 + s));
-      f.a[s][0] = buf16(ra, a_base + 128 * (st0 + s));
-      f.a[s][1] = buf16(ra, a_base + 128 * (st0 + s) + 64);
-    }
-  };
-  v4f acc[NB];
-#pragma unroll
-  for (int nj = 0; nj < NB; ++nj) acc[nj] = v4f{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const DecFrag<NB, GS>& f) {
-#pragma unroll
-    for (int s = 0; s < GS; ++s) {
-      const v8i av = make_a(f.a[s][0], f.a[s][1]);
-      const uint32_t sa = f.sa[s] >> (8 * g);
-#pragma unroll
-      for (int nj = 0; nj < NB; ++nj)
-        acc[nj] = mfma_mx(av, make_b(f.b[nj][s]), acc[nj], sa, f.sb[nj] >> (f.bsh + 8 * s));
-    }
-  };
-
-  DecFrag<NB, GS> f0, f1;
-  if (n > 0) {
-    load(f0, q0);
-    int i = 0;
-    for (; i + 2 < n; i += 2) {  // f0 holds group q0 + i
-      load(f1, q0 + i + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(f0);
-      __builtin_amdgcn_sched_barrier(0);
-      load(f0, q0 + i + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(f1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (n - i == 2) {
-      load(f1, q0 + i + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(f0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(f1);
-    } else {
-      compute(f0);
-    }
-  }
-
-  // split-K reduction in wave order (deterministic)
-  if (KS > 1) {
-    __shared__ v4f red[KS > 1 ? (KS - 1) * NB * 64 : 1];
-    if (wave > 0) {
-#pragma unroll
-      for (int nj = 0; nj < NB; ++nj) red[((wave - 1) * NB + nj) * 64 + lane] = acc[nj];
-    }
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int w = 1; w < KS; ++w)
-#pragma unroll
-      for (int nj = 0; nj < NB; ++nj) acc[nj] += red[((w - 1) * NB + nj) * 64 + lane];
-  }
-
-  // epilogue (wave 0)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = tile.row_begin + 4 * g + i;
-    const bool valid = row < tile.row_end;
-    if (GU) {
-#pragma unroll
-      for (int p = 0; p < NI / 2; ++p) {
-        float h[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int j = 2 * p + hh;
-          const float gt = acc[j][i], up = acc[NI + j][i];
-          h[hh] = gt / (1.0f + expf(-gt)) * up;
-          if (valid && a.gu_acc) {
-            const int col = col0 + 16 * j + r16;
-            a.gu_acc[int64_t(row) * 2 * a.dff + col] = gt;
-            a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + col] = up;
-          }
-        }
-        const float amax = group_max<16>(fmaxf(fabsf(h[0]), fabsf(h[1])));
-        const int e = mx8_block_exp(amax);
-        if (valid) {
-          const int col = col0 + 32 * p + r16;
-          uint8_t* hc = a.h_codes + int64_t(row) * a.dff;
-          hc[col] = static_cast<uint8_t>(mx8_encode(h[0], e));
-          hc[col + 16] = static_cast<uint8_t>(mx8_encode(h[1], e));
-          if (r16 == 0) a.h_scales[int64_t(row) * (a.dff / 32) + (col0 + 32 * p) / 32] = static_cast<uint8_t>(e + 127);
-        }
-      }
-    } else if (valid) {
-#pragma unroll
-      for (int nj = 0; nj < NB; ++nj) a.o[int64_t(row) * N + col0 + 16 * nj + r16] = acc[nj][i];
-    }
-  }
-}
-
-template <int NI, int KS, bool GU>
-static hipError_t launch_dec(const FwdArgs& a, hipStream_t st) {
-  const int K = GU ? a.d : a.dff;
-  const int N = GU ? a.dff : a.d;
-  dim3 grid(a.max_tiles, N / (16 * NI));
-  if (K % 256 == 0)
-    hipLaunchKernelGGL((k_gemm_dec<NI, KS, 2, GU>), grid, dim3(64 * KS), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_gemm_dec<NI, KS, 1, GU>), grid, dim3(64 * KS), 0, st, a);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Prefill variant: 256-row x 256-weight-row workgroup tiles, eight waves (two
-// per SIMD) on the 32x32x64 scaled MFMA.
-//
-// Operands move global -> LDS with direct-to-LDS copies (no registers stage
-// them) through a ring of three K-step slots, so two steps are in flight
-// while one is computed.  A slot holds
-//   * A codes, 32 KB: row-major, 128 bytes per row, with the 16-byte chunks
-//     of row r XOR-swizzled by (r/2)%8.  One copy moves 8 whole rows (8
-//     lanes per row, each 128-byte line read once) and the MFMA fragment
-//     reads (32 rows x one chunk) hit every bank once per 16 lanes;
-//   * B codes, 16 KB: the 16 packed 1 KB weight chunks (16 rows x 128 K);
-//     the FP4 operand of 32 rows x 64 K is a per-lane gather over two chunks
-//     that touches 16 consecutive bytes per lane group (conflict free);
-//   * A scales, 2 KB: one dword (the step's four block scales) per row, in
-//     eight 256-byte copies of 32 rows -- only when K is not a multiple of
-//     512.  Otherwise the activation scales of four steps (16 bytes per row)
-//     come once per group: waves 0-3 each copy 64 rows into 1 KB of the
-//     (then unused) A-scale areas of slots 0 and 1, and every wave keeps its
-//     rows' 16 bytes in registers for the group.
-// The packed weight scales (one dword per lane covering four steps) go to
-// two 4 KB slots, one per group of four steps.  Every wave issues its own
-// share of the copies (4 A, 2 B, 1 A-scale per step, 2 B-scale per group)
-// and waits on its own copies before the barrier that publishes a step.
-//
-// Wave w computes rows 64(w%4) .. +63 (two 32-row blocks) against 128 of
-// the 256 weight rows: gate and up rows of the same 64 h columns for
-// gate_up, 128 output columns for down.  Row blocks past the tile's end
-// skip their MFMAs.
-// ---------------------------------------------------------------------------
-
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-// A: FP8 E4M3 with its scale in byte 0; B: FP4 E2M1 with its scale in byte SB
-template <int SB>
-__device__ __forceinline__ v16f mfma32_mx(const v8i& a, const v8i& b, v16f c, uint32_t sa, uint32_t sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, static_cast<int>(sa), SB,
-                                                         static_cast<int>(sb));
-}
-
-template <int N>
-struct IntC {
-  static constexpr int value = N;
-};
-
-constexpr int kPfSlot = 51200;                 // A 32 KB | B 16 KB | A scales 2 KB
-constexpr int kPfA = 0, kPfB = 32768, kPfAS = 49152;
-constexpr int kPfBS = 3 * kPfSlot;             // two 4 KB weight-scale slots
-constexpr int kPfLds = kPfBS + 2 * 4096;       // 161792 bytes
-// copies per wave per step: 4 A + 2 B (+1 A-scale dword when scales are not
-// grouped); per group: 2 weight-scale dwords (+1 A-scale group copy, waves 0-3)
-__shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Direct-to-LDS copy of 16 (or 4) bytes per lane to LDS byte address
@@ -321,6 +83,307 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 
 // s_waitcnt with vmcnt = n, lgkmcnt and expcnt left unconstrained
 #define PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
+
+// ---------------------------------------------------------------------------
+// Decode variant (tiles of at most 8 rows: a few tokens per expert), weight
+// streaming.  A persistent grid of one 4-wave workgroup per CU walks the
+// items (tile, 64-row packed weight group) round-robin, so at any time the
+// grid streams neighbouring groups of a few experts (DRAM-page friendly;
+// per-workgroup contiguous item ranges measured slower).  For gate_up a group
+// is the gate and up rows of 32 h columns (interleaved packing), for down 64
+// output columns.  Wave w takes the K steps w, w+4, w+8, ... of every item
+// (so the four waves' current elements are 16 KB of contiguous weights) and
+// streams them through a private ring of kDsS LDS slots filled by direct-to-LDS copies,
+// kDsS - 1 elements (one K step of one item) ahead, across item boundaries;
+// the stream itself has no workgroup barrier.  After its last step of an
+// item a wave parks its partial sums in the slot it just consumed; between
+// two barriers every wave sums the four quarters in wave order for a quarter
+// of the output lanes and writes that part of the epilogue.  The MFMA's rows
+// 8-15 repeat rows 0-7 and are discarded.
+// Slot (5632 bytes): weights 4 KB (the group's step, as packed) | A 8 rows x
+// 128 B (16-byte chunks XOR-swizzled by (row/2)%4; only the tile's rows are
+// copied) | A scales (dword per row, lanes 0-7) | weight scales (the packed
+// dword of each lane, byte = block).
+// ---------------------------------------------------------------------------
+constexpr int kDsS = 7;                        // ring slots per wave
+constexpr int kDsNC = 7;                       // copies per element: 4 weights, A, A scales, weight scales
+constexpr int kDsW = 0, kDsA = 4096, kDsAS = 5120, kDsBS = 5376, kDsSlot = 5632;
+constexpr int kDsWave = kDsS * kDsSlot;
+constexpr int kDsFifo = 4 * kDsWave;           // per wave: 8 x {ex, row_begin, row_end, group}
+constexpr int kDsLds = kDsFifo + 4 * 8 * 16;   // 158208 bytes
+__shared__ __attribute__((aligned(1024))) uint8_t ds_lds[kDsLds];
+
+typedef int v4i_s __attribute__((ext_vector_type(4)));
+typedef int v8i_s __attribute__((ext_vector_type(8)));
+
+// Scalar loads of wave-uniform metadata, waited for inside the statement so
+// that no vector-memory count is involved (the copies own vmcnt).
+__device__ __forceinline__ v4i_s sload4(const void* p) {
+  v4i_s v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ v8i_s sload8(const void* p) {
+  v8i_s v;
+  asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ int sload1(const void* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+template <bool GU>
+__global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int g = lane >> 4, r16 = lane & 15;
+  const int K = GU ? a.d : a.dff;
+  const int ns = K / 128;
+  auto wsteps = [&](int w) { return (ns - w + 3) / 4; };  // K steps of wave w per item: w, w+4, ...
+  const int nsw = wsteps(wu);
+  const int ngrp = GU ? a.dff / 32 : a.d / 64;
+  const int nitems = sload1(a.tile_count) * ngrp;
+  const int bid = blockIdx.x, nwg = gridDim.x;
+  const int my_items = nitems > bid ? (nitems - bid + nwg - 1) / nwg : 0;
+  const int nel = my_items * nsw;
+  const int64_t wrows = GU ? 2 * a.dff : a.d;
+  const int64_t wc_stride = wrows * (K / 2), ws_stride = packed_scale_bytes(wrows, K);
+  const uint32_t wbase = lds_addr(ds_lds) + wu * kDsWave;
+  const uint8_t* wlds = ds_lds + wu * kDsWave;
+  // item metadata, issue side -> epilogue: every wave writes its own queue;
+  // the epilogue reads wave 0's, the one wave with K steps whenever K >= 128
+  int* fifo = reinterpret_cast<int*>(ds_lds + kDsFifo) + wu * 32;
+  const int* fifo0 = reinterpret_cast<const int*>(ds_lds + kDsFifo);
+
+  // ---- issue side: copy sources of the item being issued
+  const uint8_t* w_src = nullptr;
+  const uint8_t* bs_src = nullptr;
+  const uint8_t* a_src = nullptr;
+  const uint8_t* as_src = nullptr;
+  const int ar = lane >> 3;                           // A row of this lane's copy
+  const int achunk = (lane & 7) ^ ((ar >> 1) & 3);    // global chunk landing at chunk lane&7
+  int cur_tile = -1, ex = 0, rb = 0, nr = 0;
+  auto item_setup = [&](int il) {
+    const int item = bid + il * nwg;
+    const int tidx = item / ngrp, G = item - tidx * ngrp;
+    const bool new_tile = tidx != cur_tile;
+    if (new_tile) {
+      cur_tile = tidx;
+      const v4i_s tl = sload4(a.tiles + tidx);        // ex, row_begin, row_end
+      ex = tl.x;
+      rb = tl.y;
+      nr = tl.z - tl.y;
+    }
+    if (lane < 4) fifo[(il & 7) * 4 + lane] = lane == 0 ? ex : lane == 1 ? rb : lane == 2 ? rb + nr : G;
+    const bool shared = ex >= a.E;
+    const int sidx = ex - a.E;
+    const uint8_t* wc = GU ? (shared ? a.sgu_c + sidx * wc_stride : a.gu_c + ex * wc_stride)
+                           : (shared ? a.sdn_c + sidx * wc_stride : a.dn_c + ex * wc_stride);
+    const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + ex * ws_stride)
+                           : (shared ? a.sdn_s + sidx * ws_stride : a.dn_s + ex * ws_stride);
+    w_src = wc + int64_t(G) * ns * 4096 + 16 * lane;
+    bs_src = ws + int64_t(G) * ns * 256 + 4 * lane;
+    if (!new_tile) return;
+    // activation rows of the tile (rows past the end repeat the first)
+    int src_a, src_s;
+    const int r_a = ar < nr ? ar : 0, r_s = (lane & 7) < nr ? (lane & 7) : 0;
+    if (!GU) {
+      src_a = rb + r_a;
+      src_s = rb + r_s;
+    } else if (shared) {
+      src_a = rb - a.Rr - sidx * a.T + r_a;
+      src_s = rb - a.Rr - sidx * a.T + r_s;
+    } else {
+      const v8i_s rt = sload8(a.row_token + rb);     // may read past Rr: only rows < nr are used
+      src_a = rt[0];
+      src_s = rt[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) {
+        src_a = r_a == j ? rt[j] : src_a;
+        src_s = r_s == j ? rt[j] : src_s;
+      }
+    }
+    a_src = (GU ? a.x_codes : a.h_codes) + int64_t(src_a) * K + 16 * achunk;
+    as_src = (GU ? a.x_scales : a.h_scales) + int64_t(src_s) * (K / 32);
+  };
+  auto issue = [&](int el) {
+    const int il = el / nsw, si = el - il * nsw;
+    if (si == 0) item_setup(il);
+    const int st = wu + 4 * si;
+    const uint32_t slot = wbase + (el % kDsS) * kDsSlot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_copy16(w_src + st * 4096 + j * 1024, slot + kDsW + j * 1024);
+    // only the tile's rows (tiles are never empty, so the copy is always
+    // issued and every element counts kDsNC copies)
+    if (lane < 8 * nr) lds_copy16(a_src + 128 * st, slot + kDsA);
+    lds_copy4(as_src + 4 * st, slot + kDsAS);
+    lds_copy4(bs_src + st * 256, slot + kDsBS);
+  };
+
+  // ---- consume side
+  const int arow = r16 & 7;
+  const int a_off0 = arow * 128 + 16 * (g ^ ((arow >> 1) & 3));
+  const int a_off1 = arow * 128 + 16 * ((4 + g) ^ ((arow >> 1) & 3));
+  v4f acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int el) {
+    const uint8_t* sl = wlds + (el % kDsS) * kDsSlot;
+    const v8i av = make_a(ld16(sl + kDsA + a_off0), ld16(sl + kDsA + a_off1));
+    const uint32_t sa = *reinterpret_cast<const uint32_t*>(sl + kDsAS + 4 * arow) >> (8 * g);
+    const uint32_t sbw = *reinterpret_cast<const uint32_t*>(sl + kDsBS + 4 * lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v8i bv = make_b(ld16(sl + kDsW + j * 1024 + 16 * lane));
+      acc[j] = mfma_mx(av, bv, acc[j], sa, sbw >> (8 * j));
+    }
+  };
+  // end of item il: partial sums into the slot just consumed (a wave without
+  // K steps uses slot 0 of its idle ring), then wave w reduces output lanes
+  // 16w .. 16w+15 (tile rows 4w .. 4w+3) in wave order and writes them
+  auto part_slot = [&](int w, int il) -> const v4f* {
+    const int n = wsteps(w);
+    const int sl = n > 0 ? ((il + 1) * n - 1) % kDsS : 0;
+    return reinterpret_cast<const v4f*>(ds_lds + w * kDsWave + sl * kDsSlot);
+  };
+  auto item_end = [&](int il) {
+    v4f* mine = const_cast<v4f*>(part_slot(wu, il));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mine[j * 64 + lane] = acc[j];
+      acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+    const int* md = fifo0 + (il & 7) * 4;
+    const int t_rb = md[1], t_re = md[2], G = md[3];
+    const int i = lane >> 4, col = lane & 15;
+    const int row = t_rb + 4 * wu + i;
+    if (4 * wu < t_re - t_rb) {                       // else this wave's rows are all padding
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) sum += part_slot(w, il)[j * 64 + 16 * wu + col][i];
+        v[j] = sum;
+      }
+      const bool valid = row < t_re;
+      if (GU) {
+        // blocks 0-1: gate rows of h columns 32G + 16j + col; blocks 2-3: up rows
+        float h[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          h[j] = v[j] / (1.0f + __expf(-v[j])) * v[2 + j];
+          if (valid && a.gu_acc) {
+            const int c = 32 * G + 16 * j + col;
+            a.gu_acc[int64_t(row) * 2 * a.dff + c] = v[j];
+            a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + c] = v[2 + j];
+          }
+        }
+        const int e = mx8_block_exp(group_max<16>(fmaxf(fabsf(h[0]), fabsf(h[1]))));
+        const float sc = exp2_int(-e);
+        const uint32_t codes = e4m3_cvt2(h[0] * sc, h[1] * sc);
+        if (valid) {
+          uint8_t* hc = a.h_codes + int64_t(row) * a.dff + 32 * G + col;
+          hc[0] = static_cast<uint8_t>(codes & 0xFFu);
+          hc[16] = static_cast<uint8_t>(codes >> 8);
+          if (col == 0) a.h_scales[int64_t(row) * (a.dff / 32) + G] = static_cast<uint8_t>(e + 127);
+        }
+      } else if (valid) {
+        float* orow = a.o + int64_t(row) * a.d + 64 * G + col;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) orow[16 * j] = v[j];
+      }
+    }
+    __syncthreads();  // the parked partials are read: their slots may be refilled
+  };
+
+  int iss = 0;
+  for (; iss < nel && iss < kDsS - 1; ++iss) issue(iss);
+  int el = 0;
+  for (int il = 0; il < my_items; ++il) {
+    for (int k = 0; k < nsw; ++k, ++el) {
+      if (iss < nel) issue(iss++);
+      // copies issued after element el are still allowed in flight
+      switch (iss - 1 - el) {
+        case 0: PF_WAIT_VM(0); break;
+        case 1: PF_WAIT_VM(kDsNC); break;
+        case 2: PF_WAIT_VM(2 * kDsNC); break;
+        case 3: PF_WAIT_VM(3 * kDsNC); break;
+        case 4: PF_WAIT_VM(4 * kDsNC); break;
+        case 5: PF_WAIT_VM(5 * kDsNC); break;
+        default: PF_WAIT_VM(6 * kDsNC); break;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      compute(el);
+    }
+    item_end(il);
+  }
+}
+
+template <bool GU>
+static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_gemm_stream<GU>), dim3(a.num_cus), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Prefill variant: 256-row x 256-weight-row workgroup tiles, eight waves (two
+// per SIMD) on the 32x32x64 scaled MFMA.
+//
+// Operands move global -> LDS with direct-to-LDS copies (no registers stage
+// them) through a ring of three K-step slots, so two steps are in flight
+// while one is computed.  A slot holds
+//   * A codes, 32 KB: row-major, 128 bytes per row, with the 16-byte chunks
+//     of row r XOR-swizzled by (r/2)%8.  One copy moves 8 whole rows (8
+//     lanes per row, each 128-byte line read once) and the MFMA fragment
+//     reads (32 rows x one chunk) hit every bank once per 16 lanes;
+//   * B codes, 16 KB: the tile's four packed 64-row groups (4 KB each: four
+//     1 KB chunks of 16 rows x 128 K); the FP4 operand of 32 rows x 64 K is a
+//     per-lane gather over two chunks that touches 16 consecutive bytes per
+//     lane group (conflict free);
+//   * A scales, 2 KB: one dword (the step's four block scales) per row, in
+//     eight 256-byte copies of 32 rows -- only when K is not a multiple of
+//     512.  Otherwise the activation scales of four steps (16 bytes per row)
+//     come once per group: waves 0-3 each copy 64 rows into 1 KB of the
+//     (then unused) A-scale areas of slots 0 and 1, and every wave keeps its
+//     rows' 16 bytes in registers for the group.
+//   * B scales, 1 KB: the step's packed scale dwords of the four groups (one
+//     byte per 16-row block).
+// Every wave issues its own share of the copies (4 A, 2 B, 1 B-scale and, per
+// step or per group, the A scales) and waits on its own copies before the
+// barrier that publishes a step.
+//
+// Wave w computes rows 64(w%4) .. +63 (two 32-row blocks) against 128 of
+// the 256 weight rows: gate and up rows of the same 64 h columns for
+// gate_up, 128 output columns for down.  Row blocks past the tile's end
+// skip their MFMAs.
+// ---------------------------------------------------------------------------
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// A: FP8 E4M3 with its scale in byte 0; B: FP4 E2M1 with its scale in byte SB
+template <int SB>
+__device__ __forceinline__ v16f mfma32_mx(const v8i& a, const v8i& b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, static_cast<int>(sa), SB,
+                                                         static_cast<int>(sb));
+}
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+constexpr int kPfSlot = 52224;                 // A 32 KB | B 16 KB | A scales 2 KB | B scales 1 KB
+constexpr int kPfA = 0, kPfB = 32768, kPfAS = 49152, kPfBS = 51200;
+constexpr int kPfLds = 3 * kPfSlot;            // 156672 bytes
+// copies per wave per step: 4 A + 2 B + 1 B-scale (+1 A-scale dword when
+// activation scales are not grouped); per group: 1 A-scale copy (waves 0-3)
+__shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
+
 
 // Work order of the prefill GEMMs: items (tile, column block) expert-major,
 // cut into 8 contiguous ranges, one per XCD (workgroups go to the XCDs
@@ -359,7 +422,7 @@ __device__ __forceinline__ int pf_asg_off(int w) { return (w >> 1) * kPfSlot + k
 
 template <bool GU, bool AG>
 __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
-  constexpr int kCopies = AG ? 6 : 7;
+  constexpr int kCopies = AG ? 7 : 8;
   int tile_idx, nblk;
   if (!pf_work_item(a, GU ? a.dff / 128 : a.d / 256, &tile_idx, &nblk)) return;
   const Tile tile = a.tiles[tile_idx];
@@ -368,7 +431,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy of the wave index
   const int wm = wu & 3, wn = wu >> 2;
   const int K = GU ? a.d : a.dff;
-  const int nsteps = K / 128, nq4 = (K + 511) / 512;
+  const int nsteps = K / 128;
 
   const bool shared = tile.ex >= a.E;
   const int sidx = tile.ex - a.E;
@@ -379,13 +442,11 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
   const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + tile.ex * ws_stride)
                          : (shared ? a.sdn_s + sidx * ws_stride : a.dn_s + tile.ex * ws_stride);
 
-  // the tile's 16 weight-row blocks (16 rows each): gate then up (gate_up), or
-  // 256 consecutive output rows (down)
+  // the tile's four packed 64-row groups 4*nblk .. 4*nblk+3: gate and up rows
+  // of h columns 32 apiece (gate_up, interleaved packing), or 256 consecutive
+  // output rows (down)
   const int c0 = GU ? nblk * 128 : nblk * 256;
-  auto wblk = [&](int j) -> int64_t {
-    if (GU) return j < 8 ? (c0 + 16 * j) / 16 : (a.dff + c0 + 16 * (j - 8)) / 16;
-    return (c0 + 16 * j) / 16;
-  };
+  const int64_t grp0 = 4 * int64_t(nblk);
   // activation row r of the tile; padding rows read the tile's first row
   auto src_row = [&](int r) -> int64_t {
     int row = tile.row_begin + r;
@@ -403,36 +464,30 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
     a_src[q] = (GU ? a.x_codes : a.h_codes) + src_row(rl) * K + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
   }
   const uint8_t* as_src = (GU ? a.x_scales : a.h_scales) + src_row(AG ? (64 * wu + lane) & 255 : 32 * wu + l32) * (K / 32);
-  const uint8_t* b_src[2];
-  const uint8_t* bs_src[2];
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    b_src[jj] = wc + wblk(2 * wu + jj) * nsteps * 1024 + 16 * lane;
-    bs_src[jj] = ws + wblk(2 * wu + jj) * nq4 * 256 + 4 * lane;
-  }
+  // weight chunks 2wu, 2wu+1 of the tile: group wu/2, blocks 2(wu%2) and +1;
+  // scale dwords of group wu%4 (waves w and w+4 copy the same 256 bytes)
+  const uint8_t* b_src = wc + ((grp0 + (wu >> 1)) * nsteps * 4 + 2 * (wu & 1)) * 1024 + 16 * lane;
+  const uint8_t* bs_src = ws + (grp0 + (wu & 3)) * nsteps * 256 + 4 * lane;
   const uint32_t lds0 = lds_addr(pf_lds);
 
-  // copies of step st into slot st % 3 (and of the weight scales of group
-  // st / 4 when st starts a group)
+  // copies of step st into slot st % 3 (and of the activation scales of
+  // group st / 4 when st starts a group)
   auto issue = [&](int st, bool group_start) {
     const uint32_t slot = lds0 + (st % 3) * kPfSlot;
 #pragma unroll
     for (int q = 0; q < 4; ++q) lds_copy16(a_src[q] + 128 * st, slot + kPfA + (32 * wu + 8 * q) * 128);
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) lds_copy16(b_src[jj] + st * 1024, slot + kPfB + (2 * wu + jj) * 1024);
+    for (int jj = 0; jj < 2; ++jj) lds_copy16(b_src + st * 4096 + jj * 1024, slot + kPfB + (2 * wu + jj) * 1024);
+    lds_copy4(bs_src + st * 256, slot + kPfBS + (wu & 3) * 256);
     if (!AG) lds_copy4(as_src + 4 * st, slot + kPfAS + wu * 256);
-    if (group_start) {
-      if (AG && wu < 4) lds_copy16(as_src + 16 * (st >> 2), lds0 + pf_asg_off(wu));
-      const int q = st >> 2;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        lds_copy4(bs_src[jj] + q * 256, lds0 + kPfBS + (q & 1) * 4096 + (2 * wu + jj) * 256);
-    }
+    if (group_start && AG && wu < 4) lds_copy16(as_src + 16 * (st >> 2), lds0 + pf_asg_off(wu));
   };
 
   // ---- per-lane LDS read offsets
-  // weight fragment p (32 rows) starts at chunk j0(p) of the tile's 16
-  auto j0 = [&](int p) -> int { return GU ? (p < 2 ? 4 * wn + 2 * p : 8 + 4 * wn + 2 * (p - 2)) : 8 * wn + 2 * p; };
+  // weight fragment p (32 rows) starts at chunk j0(p) of the tile's 16: for
+  // gate_up, gate rows of h columns c0 + 64wn + 32p (p < 2; group 2wn + p,
+  // blocks 0-1) and the up rows of the same columns (blocks 2-3)
+  auto j0 = [&](int p) -> int { return GU ? (p < 2 ? 8 * wn + 4 * p : 8 * wn + 4 * (p - 2) + 2) : 8 * wn + 2 * p; };
   const int b_lane = ((l32 >> 4) << 10) + 16 * (16 * g32 + (lane & 15));  // + j0*1024 + 512h
   // A fragment (row l32 of a 32-row block, K half h, piece c): chunk 4h+2c+g32
   int a_lane[2][2];
@@ -440,7 +495,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int c = 0; c < 2; ++c) a_lane[h][c] = l32 * 128 + 16 * ((4 * h + 2 * c + g32) ^ ((l32 >> 1) & 7));
-  const int bs_lane = ((l32 >> 4) << 8) + 4 * (16 * g32 + (lane & 15));   // + j0*256 + 128h
+  const int bs_lane = 4 * (16 * g32 + (lane & 15));   // + group*256 + 128h; byte = block in group
   const int rows_left = tile.row_end - tile.row_begin - 64 * wm;
   const int nact = rows_left <= 0 ? 0 : (rows_left <= 32 ? 1 : 2);   // active row blocks
 
@@ -452,20 +507,20 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
 
   auto main_loop = [&](auto nact_c) {
     constexpr int NACT = decltype(nact_c)::value;
-    uint32_t bsr[4][2];  // weight scale dwords of the current group
     uint4 asg[2];        // grouped activation scales of this lane's rows
 
     auto compute = [&](int st, auto ic) {
       constexpr int I = decltype(ic)::value;  // st % 4
       if (NACT == 0) return;
       const uint8_t* sb = pf_lds + (st % 3) * kPfSlot;
+      uint32_t bsr[4][2];  // weight scales of the fragments, in byte 0
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          bsr[pp][h] = *reinterpret_cast<const uint32_t*>(sb + kPfBS + (j0(pp) >> 2) * 256 + 128 * h + bs_lane) >>
+                       (8 * ((j0(pp) & 3) + (l32 >> 4)));
       if (I == 0) {
-        const uint8_t* bsb = pf_lds + kPfBS + ((st >> 2) & 1) * 4096 + bs_lane;
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            bsr[pp][h] = *reinterpret_cast<const uint32_t*>(bsb + j0(pp) * 256 + 128 * h);
         if (AG) {
 #pragma unroll
           for (int i = 0; i < NACT; ++i)
@@ -496,7 +551,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
         for (int i = 0; i < NACT; ++i) {
           const uint32_t sa = asr[i] >> (8 * (2 * h + g32));
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) acc[i][pp] = mfma32_mx<I>(av[h][i], bv[h][pp], acc[i][pp], sa, bsr[pp][h]);
+          for (int pp = 0; pp < 4; ++pp) acc[i][pp] = mfma32_mx<0>(av[h][i], bv[h][pp], acc[i][pp], sa, bsr[pp][h]);
         }
     };
 
@@ -506,12 +561,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
     auto stage = [&](int st, auto ic) {
       constexpr int I = decltype(ic)::value;
       if (st + 1 < nsteps) {
-        if (((I + 1) & 3) == 0) {
-          if (AG && wu < 4) PF_WAIT_VM(kCopies + 3);
-          else PF_WAIT_VM(kCopies + 2);
-        } else {
-          PF_WAIT_VM(kCopies);
-        }
+        if (AG && ((I + 1) & 3) == 0 && wu < 4) PF_WAIT_VM(kCopies + 1);
+        else PF_WAIT_VM(kCopies);
       } else {
         PF_WAIT_VM(0);
       }
@@ -637,13 +688,14 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+
 hipError_t launch_gemm_gate_up(const FwdArgs& a, hipStream_t st) {
-  if (a.bm == 16) return launch_dec<2, 2, true>(a, st);
+  if (a.bm <= kDecodeMaxRows) return launch_stream<true>(a, st);
   return launch_pf<true>(a, st);
 }
 
 hipError_t launch_gemm_down(const FwdArgs& a, hipStream_t st) {
-  if (a.bm == 16) return launch_dec<2, 1, false>(a, st);
+  if (a.bm <= kDecodeMaxRows) return launch_stream<false>(a, st);
   return launch_pf<false>(a, st);
 }
 

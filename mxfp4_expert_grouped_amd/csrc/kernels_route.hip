@@ -374,7 +374,8 @@ __device__ __forceinline__ float order_key_to_float(uint32_t key) {
 // 3. With one candidate per lane, the k-th largest key th is found by a
 //    one-slot radix select; keys > th are taken and keys == th fill the
 //    remaining places in ascending expert order (ties -> lower index).
-__device__ void topk_token(const FwdArgs& a, int t, int lane, uint2* cand) {
+// With s_ids non-null the chosen ids are also stored there (LDS, [t*k + j]).
+__device__ void topk_token(const FwdArgs& a, int t, int lane, uint2* cand, int* s_ids = nullptr) {
   const __amdgpu_buffer_rsrc_t rl =
       __builtin_amdgcn_make_buffer_rsrc(a.logits + int64_t(t) * a.E, static_cast<short>(0), a.E * 4, 0x00020000);
   uint32_t key[kMaxSlots];
@@ -451,6 +452,7 @@ __device__ void topk_token(const FwdArgs& a, int t, int lane, uint2* cand) {
     const int pos = __popcll(m & lt_mask);  // candidates are in ascending expert order
     a.topk_ids[int64_t(t) * a.k + pos] = cidx;
     a.topk_w[int64_t(t) * a.k + pos] = sig * inv;
+    if (s_ids) s_ids[t * a.k + pos] = cidx;
   }
 }
 
@@ -606,15 +608,71 @@ __global__ void __launch_bounds__(1024) k_permute_small(FwdArgs a) {
   permute_block(a, L);
 }
 
-// Few tokens: top-k of every token (one wave each) and the permutation in a
-// single workgroup; x was already quantised by the router launch.
+// Few tokens (router_small: T <= 32): top-k of every token (one wave each)
+// with the choices kept in LDS, then the permutation in the same workgroup:
+// per-expert counts and token bitmasks by LDS atomics, one scan of the packed
+// (rows | tiles << 16) per expert for row and tile starts, and each pair's
+// row = expert start + number of earlier tokens with that expert.  x was
+// already quantised by the router launch.
 __global__ void __launch_bounds__(1024) k_topk_permute_small(FwdArgs a) {
-  __shared__ PermLds L;
   __shared__ uint2 cand[16][64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int t = wv; t < a.T; t += 16) topk_token(a, t, lane, cand[wv]);
-  __syncthreads();  // top-k results (global memory) visible to the workgroup
-  permute_block(a, L);
+  __shared__ int s_ids[32 * 32];
+  __shared__ int cnt[1024];
+  __shared__ uint32_t mask[1024];
+  __shared__ int wave_tot[40];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid < a.E) { cnt[tid] = 0; mask[tid] = 0u; }
+  for (int t = wv; t < a.T; t += 16) topk_token(a, t, lane, cand[wv], s_ids);
+  __syncthreads();
+  const int npairs = a.T * a.k;
+  for (int p = tid; p < npairs; p += 1024) {
+    const int e = s_ids[p];
+    atomicAdd(&cnt[e], 1);
+    atomicOr(&mask[e], 1u << (p / a.k));
+  }
+  __syncthreads();
+  const int c = tid < a.E ? cnt[tid] : 0;
+  const int ntile = (c + a.bm - 1) / a.bm;
+  if (tid < a.E) cnt[tid] = c | (ntile << 16);
+  const int total = block_exclusive_scan(cnt, a.E, wave_tot);  // ends with a barrier
+  const int rtiles = total >> 16;
+  const int nts = (a.T + a.bm - 1) / a.bm;  // tiles per shared expert
+  if (tid < a.E) {
+    const int row0 = cnt[tid] & 0xFFFF, tile0 = cnt[tid] >> 16;
+    a.offsets[tid] = row0;
+    a.counts[tid] = c;
+    a.ex_tiles[tid] = tile0;
+    for (int i = 0; i < ntile; ++i) {
+      Tile tl;
+      tl.ex = tid;
+      tl.row_begin = row0 + i * a.bm;
+      tl.row_end = min(row0 + (i + 1) * a.bm, row0 + c);
+      tl.pad = 0;
+      a.tiles[tile0 + i] = tl;
+    }
+  }
+  if (tid < a.S * nts) {
+    const int sx = tid / nts, i = tid % nts;
+    const int rb = a.Rr + sx * a.T;
+    Tile tl;
+    tl.ex = a.E + sx;
+    tl.row_begin = rb + i * a.bm;
+    tl.row_end = min(rb + (i + 1) * a.bm, rb + a.T);
+    tl.pad = 0;
+    a.tiles[rtiles + tid] = tl;
+  }
+  if (tid <= a.S) a.ex_tiles[a.E + tid] = rtiles + tid * nts;
+  if (tid == 0) {
+    a.offsets[a.E] = a.Rr;
+    *a.tile_count = rtiles + a.S * nts;
+  }
+  for (int p = tid; p < npairs; p += 1024) {
+    const int t = p / a.k, e = s_ids[p];
+    const int row = (cnt[e] & 0xFFFF) + __popc(mask[e] & ((1u << t) - 1u));
+    a.row_src[row] = p;
+    a.row_token[row] = t;
+    a.token_row[p] = row;
+  }
 }
 
 // Large token counts: per-chunk masks and counts ...
@@ -711,19 +769,14 @@ hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
 // (fixed order: slots ascending = expert id ascending, then shared experts)
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256) k_combine(FwdArgs a) {
-  __shared__ int rows[32];
-  __shared__ float wts[32];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  if (tid < a.k) {
-    rows[tid] = a.token_row[int64_t(t) * a.k + tid];
-    wts[tid] = a.topk_w[int64_t(t) * a.k + tid];
-  }
-  __syncthreads();
-  const int c = blockIdx.y * 256 + tid;  // 4-column group
+// One thread per 4 output columns of one token; the k expert rows are read
+// in batches of 16 loads in flight, summed in slot order.
+__global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
+  const int t = blockIdx.x;
+  const int c = blockIdx.y * 64 + threadIdx.x;  // 4-column group
   if (c >= a.d / 4) return;
-  // o rows are fp32 after the 16-row-tile kernels, bf16 after the 128-row ones
-  const bool o16 = a.bm != 16;
+  // o rows are fp32 after the decode kernels, bf16 after the prefill ones
+  const bool o16 = a.bm > kDecodeMaxRows;
   auto load4 = [&](int64_t row) -> float4 {
     if (o16) {
       const uint2 u = reinterpret_cast<const uint2*>(a.o16 + row * a.d)[c];
@@ -732,30 +785,33 @@ __global__ void __launch_bounds__(256) k_combine(FwdArgs a) {
     }
     return reinterpret_cast<const float4*>(a.o + row * a.d)[c];
   };
+  const int* trow = a.token_row + int64_t(t) * a.k;
+  const float* tw = a.topk_w + int64_t(t) * a.k;
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-  int j = 0;
-  for (; j + 4 <= a.k; j += 4) {
-    float4 v[4];
+  for (int j0 = 0; j0 < a.k; j0 += 16) {
+    float4 v[16];
+    float w[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = load4(rows[j + u]);
+    for (int u = 0; u < 16; ++u)
+      if (j0 + u < a.k) {
+        v[u] = load4(trow[j0 + u]);
+        w[u] = tw[j0 + u];
+      }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = wts[j + u];
-      r.x = fmaf(w, v[u].x, r.x); r.y = fmaf(w, v[u].y, r.y);
-      r.z = fmaf(w, v[u].z, r.z); r.w = fmaf(w, v[u].w, r.w);
-    }
+    for (int u = 0; u < 16; ++u)
+      if (j0 + u < a.k) {
+        r.x = fmaf(w[u], v[u].x, r.x); r.y = fmaf(w[u], v[u].y, r.y);
+        r.z = fmaf(w[u], v[u].z, r.z); r.w = fmaf(w[u], v[u].w, r.w);
+      }
   }
-  for (; j < a.k; ++j) {
-    const float4 v = load4(rows[j]);
-    const float w = wts[j];
-    r.x = fmaf(w, v.x, r.x); r.y = fmaf(w, v.y, r.y);
-    r.z = fmaf(w, v.z, r.z); r.w = fmaf(w, v.w, r.w);
-  }
+  float4 sv[8];
+#pragma unroll
+  for (int sh = 0; sh < 8; ++sh)
+    if (sh < a.S) sv[sh] = load4(int64_t(a.Rr + sh * a.T + t));
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sh = 0; sh < a.S; ++sh) {
-    const float4 v = load4(int64_t(a.Rr + sh * a.T + t));
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-  }
+#pragma unroll
+  for (int sh = 0; sh < 8; ++sh)
+    if (sh < a.S) { s.x += sv[sh].x; s.y += sv[sh].y; s.z += sv[sh].z; s.w += sv[sh].w; }
   uint2 yb;
   yb.x = uint32_t(f32_to_bf16_rne(r.x + s.x)) | (uint32_t(f32_to_bf16_rne(r.y + s.y)) << 16);
   yb.y = uint32_t(f32_to_bf16_rne(r.z + s.z)) | (uint32_t(f32_to_bf16_rne(r.w + s.w)) << 16);
@@ -765,7 +821,7 @@ __global__ void __launch_bounds__(256) k_combine(FwdArgs a) {
 }
 
 hipError_t launch_combine(const FwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(a.T, (a.d / 4 + 255) / 256), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_combine, dim3(a.T, (a.d / 4 + 63) / 64), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -95,9 +95,9 @@ def packed_experts_device(cfg: I.LayerConfig, kind: str, count: int, layer: int 
                              I.stream_id(I.KIND_GU_SCALES, slot, layer), eb)
         gen_mx_matrix_device(tdc, tds, d, f, cfg.seed, I.stream_id(I.KIND_DN_CODES, slot, layer),
                              I.stream_id(I.KIND_DN_SCALES, slot, layer), eb)
-        M.moe_pack_mx4(tgc.data_ptr(), tgs.data_ptr(), 1, 2 * f, d, out[0][i].data_ptr(),
+        M.moe_pack_mx4(tgc.data_ptr(), tgs.data_ptr(), 1, 2 * f, d, 1, out[0][i].data_ptr(),
                        out[1][i].data_ptr(), st)
-        M.moe_pack_mx4(tdc.data_ptr(), tds.data_ptr(), 1, d, f, out[2][i].data_ptr(),
+        M.moe_pack_mx4(tdc.data_ptr(), tds.data_ptr(), 1, d, f, 0, out[2][i].data_ptr(),
                        out[3][i].data_ptr(), st)
     return out
 

@@ -79,7 +79,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_profile_end.restype = c_int
     lib.moe_packed_scale_bytes.argtypes = [c_int64, c_int64]
     lib.moe_packed_scale_bytes.restype = c_size_t
-    lib.moe_pack_mx4.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p,
+    lib.moe_pack_mx4.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int, c_void_p,
                                  c_void_p, c_void_p]
     lib.moe_pack_mx4.restype = c_int
     lib.moe_status_string.argtypes = [c_int]
@@ -147,6 +147,7 @@ def moe_packed_scale_bytes(rows: int, k: int) -> int:
     return load_library().moe_packed_scale_bytes(rows, k)
 
 
-def moe_pack_mx4(codes: int, scales: int, mats: int, rows: int, k: int, codes_p: int,
+def moe_pack_mx4(codes: int, scales: int, mats: int, rows: int, k: int, interleave: int, codes_p: int,
                  scales_p: int, stream: Optional[int] = None) -> None:
-    _check(load_library().moe_pack_mx4(codes, scales, mats, rows, k, codes_p, scales_p, stream))
+    _check(load_library().moe_pack_mx4(codes, scales, mats, rows, k, interleave, codes_p, scales_p,
+                                       stream))

@@ -162,16 +162,20 @@ def test_no_device_reports_device_error(M):
 def test_pack_sizes_and_argument_errors(M):
     assert M.moe_packed_scale_bytes(4096, 7168) == 4096 * 224
     assert M.moe_packed_scale_bytes(7168, 2048) == 7168 * 64
-    assert M.moe_packed_scale_bytes(256, 256) == 16 * 256  # K padded to 512
+    assert M.moe_packed_scale_bytes(256, 256) == 256 * 8
     assert M.moe_packed_scale_bytes(0, 128) == 0
+    assert M.moe_packed_scale_bytes(32, 256) == 0   # rows not a multiple of 64
+    assert M.moe_packed_scale_bytes(64, 192) == 0   # k not a multiple of 128
     fake = 1 << 20
-    M.moe_pack_mx4(None, None, 0, 32, 256, None, None)  # nothing to pack
+    M.moe_pack_mx4(None, None, 0, 64, 256, 0, None, None)  # nothing to pack
     for args, status in [
-        ((fake, fake, 1, 24, 256, fake, fake), M.MOE_ERR_UNSUPPORTED),
-        ((fake, fake, 1, 32, 192, fake, fake), M.MOE_ERR_UNSUPPORTED),
-        ((fake, fake, -1, 32, 256, fake, fake), M.MOE_ERR_INVALID_ARG),
-        ((None, fake, 1, 32, 256, fake, fake), M.MOE_ERR_INVALID_ARG),
-        ((fake + 8, fake, 1, 32, 256, fake, fake), M.MOE_ERR_INVALID_ARG),
+        ((fake, fake, 1, 24, 256, 0, fake, fake), M.MOE_ERR_UNSUPPORTED),
+        ((fake, fake, 1, 32, 256, 0, fake, fake), M.MOE_ERR_UNSUPPORTED),
+        ((fake, fake, 1, 64, 192, 0, fake, fake), M.MOE_ERR_UNSUPPORTED),
+        ((fake, fake, -1, 64, 256, 0, fake, fake), M.MOE_ERR_INVALID_ARG),
+        ((fake, fake, 1, 64, 256, 2, fake, fake), M.MOE_ERR_INVALID_ARG),
+        ((None, fake, 1, 64, 256, 1, fake, fake), M.MOE_ERR_INVALID_ARG),
+        ((fake + 8, fake, 1, 64, 256, 1, fake, fake), M.MOE_ERR_INVALID_ARG),
     ]:
         with pytest.raises(M.MoeError) as ei:
             M.moe_pack_mx4(*args)

@@ -46,43 +46,47 @@ def test_gpu_generator_matches_numpy_tiny_all_experts():
         assert np.array_equal(got.cpu().numpy(), want)
 
 
-def _pack_reference(codes, scales, rows, k):
+def _pack_reference(codes, scales, rows, k, interleave):
     """The packed tile order, written out with plain loops over its definition."""
-    nsteps, nq = k // 128, (k + 511) // 512
-    cp = np.zeros((rows // 16, nsteps, 64, 16), np.uint8)
-    sp = np.zeros((rows // 16, nq, 64, 4), np.uint8)
-    for b in range(rows // 16):
-        for lane in range(64):
-            g, r = lane // 16, lane % 16
-            for s in range(nsteps):
-                cp[b, s, lane] = codes[16 * b + r, 64 * s + 16 * g: 64 * s + 16 * g + 16]
-            for q in range(nq):
+    nsteps = k // 128
+    cp = np.zeros((rows // 64, nsteps, 4, 64, 16), np.uint8)
+    sp = np.zeros((rows // 64, nsteps, 64, 4), np.uint8)
+
+    def row(G, j, r):
+        if interleave:
+            return (j // 2) * (rows // 2) + 32 * G + 16 * (j % 2) + r
+        return 64 * G + 16 * j + r
+
+    for G in range(rows // 64):
+        for s in range(nsteps):
+            for lane in range(64):
+                g, r = lane // 16, lane % 16
                 for j in range(4):
-                    blk = 16 * q + 4 * j + g
-                    if blk < k // 32:
-                        sp[b, q, lane, j] = scales[16 * b + r, blk]
+                    cp[G, s, j, lane] = codes[row(G, j, r), 64 * s + 16 * g: 64 * s + 16 * g + 16]
+                    sp[G, s, lane, j] = scales[row(G, j, r), 4 * s + g]
     return cp.reshape(-1), sp.reshape(-1)
 
 
-@pytest.mark.parametrize("rows,k", [(32, 128), (16, 256), (48, 640), (64, 2048), (32, 7168)])
-def test_pack_mx4_layout(rows, k):
+@pytest.mark.parametrize("rows,k,interleave", [(64, 128, 0), (64, 256, 1), (128, 640, 0), (192, 2048, 1),
+                                               (64, 7168, 1)])
+def test_pack_mx4_layout(rows, k, interleave):
     from mxfp4_expert_grouped_amd import mxmoe as M
     rng = np.random.default_rng(rows + k)
     mats = 3
     codes = rng.integers(0, 256, size=(mats, rows, k // 2), dtype=np.uint8)
     scales = rng.integers(0, 255, size=(mats, rows, k // 32), dtype=np.uint8)
     sb = M.moe_packed_scale_bytes(rows, k)
-    assert sb == (rows // 16) * ((k + 511) // 512) * 256
+    assert sb == rows * k // 32
     cp = torch.empty(mats * rows * k // 2, dtype=torch.uint8, device="cuda")
     spk = torch.empty(mats * sb, dtype=torch.uint8, device="cuda")
-    M.moe_pack_mx4(None, None, 0, rows, k, None, None)  # zero matrices: no-op
+    M.moe_pack_mx4(None, None, 0, rows, k, interleave, None, None)  # zero matrices: no-op
     tc, ts = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
-    M.moe_pack_mx4(tc.data_ptr(), ts.data_ptr(), mats, rows, k, cp.data_ptr(), spk.data_ptr(),
+    M.moe_pack_mx4(tc.data_ptr(), ts.data_ptr(), mats, rows, k, interleave, cp.data_ptr(), spk.data_ptr(),
                    torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     cpn, spn = cp.cpu().numpy(), spk.cpu().numpy()
     for m in range(mats):
-        rc, rs = _pack_reference(codes[m], scales[m], rows, k)
+        rc, rs = _pack_reference(codes[m], scales[m], rows, k, interleave)
         assert np.array_equal(cpn[m * rows * k // 2:(m + 1) * rows * k // 2], rc)
         assert np.array_equal(spn[m * sb:(m + 1) * sb], rs)
 
