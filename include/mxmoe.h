@@ -173,6 +173,8 @@ typedef enum {
  * writes the summed milliseconds per stage to stage_ms[MOE_NUM_STAGES] (zero
  * for unrecorded stages) and the number of recorded calls to *calls, and stops
  * recording.  Host-side state of the plan; no device memory is allocated.
+ * Each timed event pair leaves the GPU idle for a few microseconds between the
+ * kernels it brackets, so calls being profiled are slower than plain ones.
  * Profiling a plan that is used by several threads at once is not supported. */
 moe_status moe_profile_begin(moe_plan_t *plan, uint32_t stage_mask, int32_t max_calls);
 moe_status moe_profile_end(moe_plan_t *plan, double *stage_ms, int32_t *calls);
