@@ -84,6 +84,28 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // s_waitcnt with vmcnt = n, lgkmcnt and expcnt left unconstrained
 #define PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
 
+// the same for a wave-uniform n in [0, 15] known only at run time
+__device__ __forceinline__ void wait_vm_upto15(int n) {
+  switch (n) {
+    case 0: PF_WAIT_VM(0); break;
+    case 1: PF_WAIT_VM(1); break;
+    case 2: PF_WAIT_VM(2); break;
+    case 3: PF_WAIT_VM(3); break;
+    case 4: PF_WAIT_VM(4); break;
+    case 5: PF_WAIT_VM(5); break;
+    case 6: PF_WAIT_VM(6); break;
+    case 7: PF_WAIT_VM(7); break;
+    case 8: PF_WAIT_VM(8); break;
+    case 9: PF_WAIT_VM(9); break;
+    case 10: PF_WAIT_VM(10); break;
+    case 11: PF_WAIT_VM(11); break;
+    case 12: PF_WAIT_VM(12); break;
+    case 13: PF_WAIT_VM(13); break;
+    case 14: PF_WAIT_VM(14); break;
+    default: PF_WAIT_VM(15); break;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decode variant (tiles of at most 8 rows: a few tokens per expert), weight
 // streaming.  A persistent grid of one 4-wave workgroup per CU walks the
@@ -91,15 +113,19 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // grid streams neighbouring groups of a few experts (DRAM-page friendly;
 // per-workgroup contiguous item ranges measured slower).  For gate_up a group
 // is the gate and up rows of 32 h columns (interleaved packing), for down 64
-// output columns.  Wave w takes the K steps w, w+4, w+8, ... of every item
-// (so the four waves' current elements are 16 KB of contiguous weights) and
-// streams them through a private ring of kDsS LDS slots filled by direct-to-LDS copies,
+// output columns.  With the K split (gate_up when there are fewer than 16
+// items per wave, so that whole items would leave a long tail) wave w takes
+// the K steps w, w+4, w+8, ... of every item of its workgroup (the four
+// waves' current elements are 16 KB of contiguous weights); otherwise every
+// wave takes whole items of its own, round-robin over all waves of the grid,
+// and needs no cross-wave reduction.  A wave streams its steps through a
+// private ring of kDsS LDS slots filled by direct-to-LDS copies,
 // kDsS - 1 elements (one K step of one item) ahead, across item boundaries;
 // the stream itself has no workgroup barrier.  After its last step of an
-// item a wave parks its partial sums in the slot it just consumed; between
-// two barriers every wave sums the four quarters in wave order for a quarter
-// of the output lanes and writes that part of the epilogue.  The MFMA's rows
-// 8-15 repeat rows 0-7 and are discarded.
+// item of gate_up a wave parks its partial sums in the slot it just consumed;
+// between two barriers every wave sums the four quarters in wave order for a
+// quarter of the output lanes and writes that part of the epilogue.  The
+// MFMA's rows 8-15 repeat rows 0-7 and are discarded.
 // Slot (5632 bytes): weights 4 KB (the group's step, as packed) | A 8 rows x
 // 128 B (16-byte chunks XOR-swizzled by (row/2)%4; only the tile's rows are
 // copied) | A scales (dword per row, lanes 0-7) | weight scales (the packed
@@ -134,18 +160,21 @@ __device__ __forceinline__ int sload1(const void* p) {
   return v;
 }
 
-template <bool GU>
+template <bool GU, bool KSPLIT>
 __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int wu = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = lane >> 4, r16 = lane & 15;
   const int K = GU ? a.d : a.dff;
   const int ns = K / 128;
-  auto wsteps = [&](int w) { return (ns - w + 3) / 4; };  // K steps of wave w per item: w, w+4, ...
+  // K steps per item of wave w: w, w+4, ... (split) or all of them
+  auto wsteps = [&](int w) { return KSPLIT ? (ns - w + 3) / 4 : ns; };
   const int nsw = wsteps(wu);
   const int ngrp = GU ? a.dff / 32 : a.d / 64;
   const int nitems = sload1(a.tile_count) * ngrp;
-  const int bid = blockIdx.x, nwg = gridDim.x;
+  // item walkers: workgroups (split) or single waves, round-robin
+  const int bid = KSPLIT ? blockIdx.x : blockIdx.x * 4 + wu;
+  const int nwg = KSPLIT ? gridDim.x : gridDim.x * 4;
   const int my_items = nitems > bid ? (nitems - bid + nwg - 1) / nwg : 0;
   const int nel = my_items * nsw;
   const int64_t wrows = GU ? 2 * a.dff : a.d;
@@ -153,9 +182,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   const uint32_t wbase = lds_addr(ds_lds) + wu * kDsWave;
   const uint8_t* wlds = ds_lds + wu * kDsWave;
   // item metadata, issue side -> epilogue: every wave writes its own queue;
-  // the epilogue reads wave 0's, the one wave with K steps whenever K >= 128
+  // with the K split the epilogue reads wave 0's, the one wave with K steps
+  // whenever K >= 128
   int* fifo = reinterpret_cast<int*>(ds_lds + kDsFifo) + wu * 32;
-  const int* fifo0 = reinterpret_cast<const int*>(ds_lds + kDsFifo);
+  const int* fifo_ep = reinterpret_cast<const int*>(ds_lds + kDsFifo) + (KSPLIT ? 0 : wu * 32);
 
   // ---- issue side: copy sources of the item being issued
   const uint8_t* w_src = nullptr;
@@ -211,7 +241,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   auto issue = [&](int el) {
     const int il = el / nsw, si = el - il * nsw;
     if (si == 0) item_setup(il);
-    const int st = wu + 4 * si;
+    const int st = KSPLIT ? wu + 4 * si : si;
     const uint32_t slot = wbase + (el % kDsS) * kDsSlot;
 #pragma unroll
     for (int j = 0; j < 4; ++j) lds_copy16(w_src + st * 4096 + j * 1024, slot + kDsW + j * 1024);
@@ -248,7 +278,52 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     const int sl = n > 0 ? ((il + 1) * n - 1) % kDsS : 0;
     return reinterpret_cast<const v4f*>(ds_lds + w * kDsWave + sl * kDsSlot);
   };
+  // gate_up epilogue of one output row: v[0..1] gate and v[2..3] up sums of h
+  // columns 32G + col and 32G + 16 + col (the 16 lanes with equal lane/16
+  // hold the row's 32 columns: one MXFP8 block)
+  auto gu_epilogue = [&](const float* v, int row, bool valid, int G, int col) {
+    float h[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      h[j] = v[j] / (1.0f + __expf(-v[j])) * v[2 + j];
+      if (valid && a.gu_acc) {
+        const int c = 32 * G + 16 * j + col;
+        a.gu_acc[int64_t(row) * 2 * a.dff + c] = v[j];
+        a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + c] = v[2 + j];
+      }
+    }
+    const int e = mx8_block_exp(group_max<16>(fmaxf(fabsf(h[0]), fabsf(h[1]))));
+    const float sc = exp2_int(-e);
+    const uint32_t codes = e4m3_cvt2(h[0] * sc, h[1] * sc);
+    if (valid) {
+      uint8_t* hc = a.h_codes + int64_t(row) * a.dff + 32 * G + col;
+      hc[0] = static_cast<uint8_t>(codes & 0xFFu);
+      hc[16] = static_cast<uint8_t>(codes >> 8);
+      if (col == 0) a.h_scales[int64_t(row) * (a.dff / 32) + G] = static_cast<uint8_t>(e + 127);
+    }
+  };
   auto item_end = [&](int il) {
+    if (!KSPLIT) {
+      // whole item in this wave: lane l holds rows 4(l/16) + i, column l%16
+      const int* md = fifo_ep + (il & 7) * 4;
+      const int t_rb = md[1], t_re = md[2], G = md[3];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = t_rb + 4 * g + i;
+        const bool valid = row < t_re;
+        if (GU) {
+          float v[4] = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+          gu_epilogue(v, row, valid, G, r16);
+        } else if (valid) {
+          float* orow = a.o + int64_t(row) * a.d + 64 * G + r16;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) orow[16 * j] = acc[j][i];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+      return;
+    }
     v4f* mine = const_cast<v4f*>(part_slot(wu, il));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -256,7 +331,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
       acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
-    const int* md = fifo0 + (il & 7) * 4;
+    const int* md = fifo_ep + (il & 7) * 4;
     const int t_rb = md[1], t_re = md[2], G = md[3];
     const int i = lane >> 4, col = lane & 15;
     const int row = t_rb + 4 * wu + i;
@@ -271,26 +346,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
       }
       const bool valid = row < t_re;
       if (GU) {
-        // blocks 0-1: gate rows of h columns 32G + 16j + col; blocks 2-3: up rows
-        float h[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          h[j] = v[j] / (1.0f + __expf(-v[j])) * v[2 + j];
-          if (valid && a.gu_acc) {
-            const int c = 32 * G + 16 * j + col;
-            a.gu_acc[int64_t(row) * 2 * a.dff + c] = v[j];
-            a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + c] = v[2 + j];
-          }
-        }
-        const int e = mx8_block_exp(group_max<16>(fmaxf(fabsf(h[0]), fabsf(h[1]))));
-        const float sc = exp2_int(-e);
-        const uint32_t codes = e4m3_cvt2(h[0] * sc, h[1] * sc);
-        if (valid) {
-          uint8_t* hc = a.h_codes + int64_t(row) * a.dff + 32 * G + col;
-          hc[0] = static_cast<uint8_t>(codes & 0xFFu);
-          hc[16] = static_cast<uint8_t>(codes >> 8);
-          if (col == 0) a.h_scales[int64_t(row) * (a.dff / 32) + G] = static_cast<uint8_t>(e + 127);
-        }
+        gu_epilogue(v, row, valid, G, col);
       } else if (valid) {
         float* orow = a.o + int64_t(row) * a.d + 64 * G + col;
 #pragma unroll
@@ -326,7 +382,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
 
 template <bool GU>
 static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm_stream<GU>), dim3(a.num_cus), dim3(256), 0, st, a);
+  // the item count is known on the device only; max_tiles bounds it
+  const int64_t max_items = int64_t(a.max_tiles) * (GU ? a.dff / 32 : a.d / 64);
+  if (GU && max_items < 16 * 4 * int64_t(a.num_cus))
+    hipLaunchKernelGGL((k_gemm_stream<GU, true>), dim3(a.num_cus), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm_stream<GU, false>), dim3(a.num_cus), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -353,9 +414,10 @@ static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
 //     rows' 16 bytes in registers for the group.
 //   * B scales, 1 KB: the step's packed scale dwords of the four groups (one
 //     byte per 16-row block).
-// Every wave issues its own share of the copies (4 A, 2 B, 1 B-scale and, per
-// step or per group, the A scales) and waits on its own copies before the
-// barrier that publishes a step.
+// Every wave issues its own share of the copies (up to 4 A -- an 8-row copy
+// wholly past the tile's end is skipped --, 2 B, 1 B-scale and, per step or
+// per group, the A scales) and waits on its own copies before the barrier
+// that publishes a step.
 //
 // Wave w computes rows 64(w%4) .. +63 (two 32-row blocks) against 128 of
 // the 256 weight rows: gate and up rows of the same 64 h columns for
@@ -380,8 +442,9 @@ struct IntC {
 constexpr int kPfSlot = 52224;                 // A 32 KB | B 16 KB | A scales 2 KB | B scales 1 KB
 constexpr int kPfA = 0, kPfB = 32768, kPfAS = 49152, kPfBS = 51200;
 constexpr int kPfLds = 3 * kPfSlot;            // 156672 bytes
-// copies per wave per step: 4 A + 2 B + 1 B-scale (+1 A-scale dword when
-// activation scales are not grouped); per group: 1 A-scale copy (waves 0-3)
+// copies per wave per step: na A (na <= 4: this wave's 8-row copies that hold
+// tile rows) + 2 B + 1 B-scale (+1 A-scale dword when activation scales are
+// not grouped); per group: 1 A-scale copy (waves 0-3)
 __shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 
 
@@ -422,7 +485,7 @@ __device__ __forceinline__ int pf_asg_off(int w) { return (w >> 1) * kPfSlot + k
 
 template <bool GU, bool AG>
 __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
-  constexpr int kCopies = AG ? 7 : 8;
+  constexpr int kFixedCopies = AG ? 3 : 4;
   int tile_idx, nblk;
   if (!pf_work_item(a, GU ? a.dff / 128 : a.d / 256, &tile_idx, &nblk)) return;
   const Tile tile = a.tiles[tile_idx];
@@ -472,10 +535,13 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
 
   // copies of step st into slot st % 3 (and of the activation scales of
   // group st / 4 when st starts a group)
+  const int na = min(4, max(0, (tile.row_end - tile.row_begin - 32 * wu + 7) >> 3));
+  const int ncopies = na + kFixedCopies;
   auto issue = [&](int st, bool group_start) {
     const uint32_t slot = lds0 + (st % 3) * kPfSlot;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lds_copy16(a_src[q] + 128 * st, slot + kPfA + (32 * wu + 8 * q) * 128);
+    for (int q = 0; q < 4; ++q)
+      if (q < na) lds_copy16(a_src[q] + 128 * st, slot + kPfA + (32 * wu + 8 * q) * 128);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) lds_copy16(b_src + st * 4096 + jj * 1024, slot + kPfB + (2 * wu + jj) * 1024);
     lds_copy4(bs_src + st * 256, slot + kPfBS + (wu & 3) * 256);
@@ -561,8 +627,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
     auto stage = [&](int st, auto ic) {
       constexpr int I = decltype(ic)::value;
       if (st + 1 < nsteps) {
-        if (AG && ((I + 1) & 3) == 0 && wu < 4) PF_WAIT_VM(kCopies + 1);
-        else PF_WAIT_VM(kCopies);
+        wait_vm_upto15(ncopies + (AG && ((I + 1) & 3) == 0 && wu < 4 ? 1 : 0));
       } else {
         PF_WAIT_VM(0);
       }

@@ -769,59 +769,88 @@ hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
 // (fixed order: slots ascending = expert id ascending, then shared experts)
 // ---------------------------------------------------------------------------
 
-// One thread per 4 output columns of one token; the k expert rows are read
-// in batches of 16 loads in flight, summed in slot order.
+// One thread per C output columns of one token (C = 4 for the fp32 o of the
+// decode kernels, 8 for the bf16 o of the prefill kernels: 16-byte loads
+// either way); the k expert rows are read in batches of 16 loads in flight
+// and summed in slot order, then the shared rows.
+template <bool O16>
 __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
+  constexpr int C = O16 ? 8 : 4;
   const int t = blockIdx.x;
-  const int c = blockIdx.y * 64 + threadIdx.x;  // 4-column group
-  if (c >= a.d / 4) return;
-  // o rows are fp32 after the decode kernels, bf16 after the prefill ones
-  const bool o16 = a.bm > kDecodeMaxRows;
-  auto load4 = [&](int64_t row) -> float4 {
-    if (o16) {
-      const uint2 u = reinterpret_cast<const uint2*>(a.o16 + row * a.d)[c];
-      return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                         __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+  const int c = blockIdx.y * 64 + threadIdx.x;  // column group
+  if (c >= a.d / C) return;
+  auto load = [&](int64_t row, float* v) {
+    if (O16) {
+      const uint4 u = reinterpret_cast<const uint4*>(a.o16 + row * a.d)[c];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+    } else {
+      const float4 f = reinterpret_cast<const float4*>(a.o + row * a.d)[c];
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     }
-    return reinterpret_cast<const float4*>(a.o + row * a.d)[c];
   };
   const int* trow = a.token_row + int64_t(t) * a.k;
   const float* tw = a.topk_w + int64_t(t) * a.k;
-  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+  float r[C], sh[C];
+#pragma unroll
+  for (int q = 0; q < C; ++q) r[q] = sh[q] = 0.f;
   for (int j0 = 0; j0 < a.k; j0 += 16) {
-    float4 v[16];
+    float v[16][C];
     float w[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u)
       if (j0 + u < a.k) {
-        v[u] = load4(trow[j0 + u]);
+        load(trow[j0 + u], v[u]);
         w[u] = tw[j0 + u];
       }
 #pragma unroll
     for (int u = 0; u < 16; ++u)
       if (j0 + u < a.k) {
-        r.x = fmaf(w[u], v[u].x, r.x); r.y = fmaf(w[u], v[u].y, r.y);
-        r.z = fmaf(w[u], v[u].z, r.z); r.w = fmaf(w[u], v[u].w, r.w);
+#pragma unroll
+        for (int q = 0; q < C; ++q) r[q] = fmaf(w[u], v[u][q], r[q]);
       }
   }
-  float4 sv[8];
+  {
+    float v[8][C];
 #pragma unroll
-  for (int sh = 0; sh < 8; ++sh)
-    if (sh < a.S) sv[sh] = load4(int64_t(a.Rr + sh * a.T + t));
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < 8; ++s)
+      if (s < a.S) load(int64_t(a.Rr + s * a.T + t), v[s]);
 #pragma unroll
-  for (int sh = 0; sh < 8; ++sh)
-    if (sh < a.S) { s.x += sv[sh].x; s.y += sv[sh].y; s.z += sv[sh].z; s.w += sv[sh].w; }
-  uint2 yb;
-  yb.x = uint32_t(f32_to_bf16_rne(r.x + s.x)) | (uint32_t(f32_to_bf16_rne(r.y + s.y)) << 16);
-  yb.y = uint32_t(f32_to_bf16_rne(r.z + s.z)) | (uint32_t(f32_to_bf16_rne(r.w + s.w)) << 16);
-  reinterpret_cast<uint2*>(a.y + int64_t(t) * a.d)[c] = yb;
-  if (a.y_routed) reinterpret_cast<float4*>(a.y_routed + int64_t(t) * a.d)[c] = r;
-  if (a.y_shared) reinterpret_cast<float4*>(a.y_shared + int64_t(t) * a.d)[c] = s;
+    for (int s = 0; s < 8; ++s)
+      if (s < a.S) {
+#pragma unroll
+        for (int q = 0; q < C; ++q) sh[q] += v[s][q];
+      }
+  }
+  uint32_t yb[C / 2];
+#pragma unroll
+  for (int q = 0; q < C / 2; ++q)
+    yb[q] = uint32_t(f32_to_bf16_rne(r[2 * q] + sh[2 * q])) |
+            (uint32_t(f32_to_bf16_rne(r[2 * q + 1] + sh[2 * q + 1])) << 16);
+  if (O16) reinterpret_cast<uint4*>(a.y + int64_t(t) * a.d)[c] = make_uint4(yb[0], yb[1], yb[2], yb[3]);
+  else reinterpret_cast<uint2*>(a.y + int64_t(t) * a.d)[c] = make_uint2(yb[0], yb[1]);
+  if (a.y_routed) {
+    float4* yr = reinterpret_cast<float4*>(a.y_routed + int64_t(t) * a.d) + (C / 4) * c;
+#pragma unroll
+    for (int q = 0; q < C / 4; ++q) yr[q] = make_float4(r[4 * q], r[4 * q + 1], r[4 * q + 2], r[4 * q + 3]);
+  }
+  if (a.y_shared) {
+    float4* ys = reinterpret_cast<float4*>(a.y_shared + int64_t(t) * a.d) + (C / 4) * c;
+#pragma unroll
+    for (int q = 0; q < C / 4; ++q) ys[q] = make_float4(sh[4 * q], sh[4 * q + 1], sh[4 * q + 2], sh[4 * q + 3]);
+  }
 }
 
 hipError_t launch_combine(const FwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(a.T, (a.d / 4 + 63) / 64), dim3(64), 0, st, a);
+  // o rows are fp32 after the decode kernels, bf16 after the prefill ones
+  if (a.bm > kDecodeMaxRows)
+    hipLaunchKernelGGL(k_combine<true>, dim3(a.T, (a.d / 8 + 63) / 64), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_combine<false>, dim3(a.T, (a.d / 4 + 63) / 64), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
