@@ -84,28 +84,6 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // s_waitcnt with vmcnt = n, lgkmcnt and expcnt left unconstrained
 #define PF_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
 
-// the same for a wave-uniform n in [0, 15] known only at run time
-__device__ __forceinline__ void wait_vm_upto15(int n) {
-  switch (n) {
-    case 0: PF_WAIT_VM(0); break;
-    case 1: PF_WAIT_VM(1); break;
-    case 2: PF_WAIT_VM(2); break;
-    case 3: PF_WAIT_VM(3); break;
-    case 4: PF_WAIT_VM(4); break;
-    case 5: PF_WAIT_VM(5); break;
-    case 6: PF_WAIT_VM(6); break;
-    case 7: PF_WAIT_VM(7); break;
-    case 8: PF_WAIT_VM(8); break;
-    case 9: PF_WAIT_VM(9); break;
-    case 10: PF_WAIT_VM(10); break;
-    case 11: PF_WAIT_VM(11); break;
-    case 12: PF_WAIT_VM(12); break;
-    case 13: PF_WAIT_VM(13); break;
-    case 14: PF_WAIT_VM(14); break;
-    default: PF_WAIT_VM(15); break;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Decode variant (tiles of at most 8 rows: a few tokens per expert), weight
 // streaming.  A persistent grid of one 4-wave workgroup per CU walks the
@@ -392,12 +370,12 @@ static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill variant: 256-row x 256-weight-row workgroup tiles, eight waves (two
-// per SIMD) on the 32x32x64 scaled MFMA.
+// Prefill variant: 256-row x 256-weight-row workgroup tiles, four waves (one
+// per SIMD), each computing 128 rows x 128 weight rows on the 32x32x64
+// scaled MFMA (sixteen 32x32 fp32 accumulators per wave).
 //
 // Operands move global -> LDS with direct-to-LDS copies (no registers stage
-// them) through a ring of three K-step slots, so two steps are in flight
-// while one is computed.  A slot holds
+// them) through a ring of three K-step slots.  A slot holds
 //   * A codes, 32 KB: row-major, 128 bytes per row, with the 16-byte chunks
 //     of row r XOR-swizzled by (r/2)%8.  One copy moves 8 whole rows (8
 //     lanes per row, each 128-byte line read once) and the MFMA fragment
@@ -406,31 +384,40 @@ static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
 //     1 KB chunks of 16 rows x 128 K); the FP4 operand of 32 rows x 64 K is a
 //     per-lane gather over two chunks that touches 16 consecutive bytes per
 //     lane group (conflict free);
-//   * A scales, 2 KB: one dword (the step's four block scales) per row, in
-//     eight 256-byte copies of 32 rows -- only when K is not a multiple of
-//     512.  Otherwise the activation scales of four steps (16 bytes per row)
-//     come once per group: waves 0-3 each copy 64 rows into 1 KB of the
+//   * A scales, 1 KB: one dword (the step's four block scales) per row -- only
+//     when K is not a multiple of 512.  Otherwise the activation scales of
+//     four steps (16 bytes per row) come once per group into 4 KB of the
 //     (then unused) A-scale areas of slots 0 and 1, and every wave keeps its
-//     rows' 16 bytes in registers for the group.
+//     rows' 16 bytes in registers for the group;
 //   * B scales, 1 KB: the step's packed scale dwords of the four groups (one
 //     byte per 16-row block).
-// Every wave issues its own share of the copies (up to 4 A -- an 8-row copy
-// wholly past the tile's end is skipped --, 2 B, 1 B-scale and, per step or
-// per group, the A scales) and waits on its own copies before the barrier
-// that publishes a step.
+// Wave w copies rows 64w .. 64w+63 (eight 8-row copies; one wholly past the
+// tile's end is skipped), the packed group w of the weights and its scales,
+// and its rows' activation scales.
 //
-// Wave w computes rows 64(w%4) .. +63 (two 32-row blocks) against 128 of
-// the 256 weight rows: gate and up rows of the same 64 h columns for
-// gate_up, 128 output columns for down.  Row blocks past the tile's end
-// skip their MFMAs.
+// Step st (K = 128) runs in two K halves of 64 with two register sets:
+//   LDS reads of half 1 into set 1;   MFMAs of half 0 from set 0;
+//   wait for those reads and for this wave's copies of step st+1; barrier
+//     (every wave is then done with slot st, and step st+1 is in LDS);
+//   copies of step st+3 into slot st%3;
+//   LDS reads of half 0 of step st+1 (and its scales) into set 0;
+//   MFMAs of half 1 from set 1.
+// The LDS reads always run under the other half's MFMAs, and every copy has
+// two steps to land.  Row blocks past the tile's end skip their reads and
+// MFMAs.  Scale bytes are picked by the MFMA's operand selects.
+//
+// Wave w computes rows 128(w%2) .. +127 (four 32-row blocks) against 128 of
+// the 256 weight rows (w/2 picks them): gate and up rows of the same 64 h
+// columns for gate_up, 128 output columns for down.
 // ---------------------------------------------------------------------------
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// A: FP8 E4M3 with its scale in byte 0; B: FP4 E2M1 with its scale in byte SB
-template <int SB>
+// A: FP8 E4M3 with its scale in byte SA of sa; B: FP4 E2M1 with its scale in
+// byte SB of sb
+template <int SA, int SB>
 __device__ __forceinline__ v16f mfma32_mx(const v8i& a, const v8i& b, v16f c, uint32_t sa, uint32_t sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, static_cast<int>(sa), SB,
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, SA, static_cast<int>(sa), SB,
                                                          static_cast<int>(sb));
 }
 
@@ -439,12 +426,18 @@ struct IntC {
   static constexpr int value = N;
 };
 
+// f(IntC<B>{}), f(IntC<B+1>{}), ..., f(IntC<E-1>{})
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 constexpr int kPfSlot = 52224;                 // A 32 KB | B 16 KB | A scales 2 KB | B scales 1 KB
 constexpr int kPfA = 0, kPfB = 32768, kPfAS = 49152, kPfBS = 51200;
 constexpr int kPfLds = 3 * kPfSlot;            // 156672 bytes
-// copies per wave per step: na A (na <= 4: this wave's 8-row copies that hold
-// tile rows) + 2 B + 1 B-scale (+1 A-scale dword when activation scales are
-// not grouped); per group: 1 A-scale copy (waves 0-3)
 __shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 
 
@@ -484,15 +477,14 @@ __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int*
 __device__ __forceinline__ int pf_asg_off(int w) { return (w >> 1) * kPfSlot + kPfAS + (w & 1) * 1024; }
 
 template <bool GU, bool AG>
-__global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
-  constexpr int kFixedCopies = AG ? 3 : 4;
+__global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   int tile_idx, nblk;
   if (!pf_work_item(a, GU ? a.dff / 128 : a.d / 256, &tile_idx, &nblk)) return;
   const Tile tile = a.tiles[tile_idx];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, g32 = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy of the wave index
-  const int wm = wu & 3, wn = wu >> 2;
+  const int wm = wu & 1, wn = wu >> 1;
   const int K = GU ? a.d : a.dff;
   const int nsteps = K / 128;
 
@@ -517,42 +509,50 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
     return GU ? (row < a.Rr ? a.row_token[row] : row - a.Rr - sidx * a.T) : row;
   };
 
-  // ---- copy sources of this wave: rows 32wu .. 32wu+31, weight blocks 2wu, 2wu+1.
-  // A copy q covers rows 32wu + 8q .. +7: lane l reads chunk (l%8) ^ swz(row)
-  // of row 32wu + 8q + l/8 and lands at LDS row*128 + 16(l%8).
-  const uint8_t* a_src[4];
+  // ---- copy sources of this wave.  A copy q covers rows 64wu + 8q .. +7:
+  // lane l reads chunk (l%8) ^ swz(row) of row 64wu + 8q + l/8 and lands at
+  // LDS row*128 + 16(l%8).
+  const uint8_t* a_src[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int rl = 32 * wu + 8 * q + (lane >> 3);
+  for (int q = 0; q < 8; ++q) {
+    const int rl = 64 * wu + 8 * q + (lane >> 3);
     a_src[q] = (GU ? a.x_codes : a.h_codes) + src_row(rl) * K + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
   }
-  const uint8_t* as_src = (GU ? a.x_scales : a.h_scales) + src_row(AG ? (64 * wu + lane) & 255 : 32 * wu + l32) * (K / 32);
-  // weight chunks 2wu, 2wu+1 of the tile: group wu/2, blocks 2(wu%2) and +1;
-  // scale dwords of group wu%4 (waves w and w+4 copy the same 256 bytes)
-  const uint8_t* b_src = wc + ((grp0 + (wu >> 1)) * nsteps * 4 + 2 * (wu & 1)) * 1024 + 16 * lane;
-  const uint8_t* bs_src = ws + (grp0 + (wu & 3)) * nsteps * 256 + 4 * lane;
+  const uint8_t* as_src = (GU ? a.x_scales : a.h_scales) + src_row(64 * wu + lane) * (K / 32);
+  const uint8_t* b_src = wc + (grp0 + wu) * nsteps * 4096 + 16 * lane;
+  const uint8_t* bs_src = ws + (grp0 + wu) * nsteps * 256 + 4 * lane;
   const uint32_t lds0 = lds_addr(pf_lds);
 
-  // copies of step st into slot st % 3 (and of the activation scales of
-  // group st / 4 when st starts a group)
-  const int na = min(4, max(0, (tile.row_end - tile.row_begin - 32 * wu + 7) >> 3));
-  const int ncopies = na + kFixedCopies;
-  auto issue = [&](int st, bool group_start) {
+  // Copies of step st into slot st % 3 (and of the activation scales of
+  // group st / 4 when st starts a group).  Their number per step is fixed --
+  // an 8-row copy past the tile's end reads the tile's first row, and a step
+  // past K re-reads step 0 into a slot that is not read again -- so that every
+  // wait on them is a constant and a step has no branches.  They come in two
+  // parts: the 8 activation copies (copy_a) and the weights, weight scales
+  // and activation scales (copy_w, items 0-5).
+  constexpr auto ncop = [](int st) -> int { return 13 + (AG ? ((st & 3) == 0 ? 1 : 0) : 1); };
+  auto copy_a = [&](int st, auto qc) {
+    constexpr int q = decltype(qc)::value;
+    const int ss = st < nsteps ? st : 0;
+    lds_copy16(a_src[q] + 128 * ss, lds0 + (st % 3) * kPfSlot + kPfA + (64 * wu + 8 * q) * 128);
+  };
+  // item m of step st; GS: st starts a group of four steps
+  auto copy_w = [&](int st, auto mc, auto gsc) {
+    constexpr int m = decltype(mc)::value;
+    constexpr bool GS = decltype(gsc)::value != 0;
+    const int ss = st < nsteps ? st : 0;
     const uint32_t slot = lds0 + (st % 3) * kPfSlot;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (q < na) lds_copy16(a_src[q] + 128 * st, slot + kPfA + (32 * wu + 8 * q) * 128);
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) lds_copy16(b_src + st * 4096 + jj * 1024, slot + kPfB + (2 * wu + jj) * 1024);
-    lds_copy4(bs_src + st * 256, slot + kPfBS + (wu & 3) * 256);
-    if (!AG) lds_copy4(as_src + 4 * st, slot + kPfAS + wu * 256);
-    if (group_start && AG && wu < 4) lds_copy16(as_src + 16 * (st >> 2), lds0 + pf_asg_off(wu));
+    if constexpr (m < 4) lds_copy16(b_src + ss * 4096 + m * 1024, slot + kPfB + (4 * wu + m) * 1024);
+    if constexpr (m == 4) lds_copy4(bs_src + ss * 256, slot + kPfBS + wu * 256);
+    if constexpr (m == 5 && !AG) lds_copy4(as_src + 4 * ss, slot + kPfAS + wu * 256);
+    if constexpr (m == 5 && AG && GS) lds_copy16(as_src + 16 * (ss >> 2), lds0 + pf_asg_off(wu));
   };
 
   // ---- per-lane LDS read offsets
   // weight fragment p (32 rows) starts at chunk j0(p) of the tile's 16: for
   // gate_up, gate rows of h columns c0 + 64wn + 32p (p < 2; group 2wn + p,
-  // blocks 0-1) and the up rows of the same columns (blocks 2-3)
+  // blocks 0-1) and the up rows of the same columns (blocks 2-3).  Its scale
+  // dword lies in group 2wn + pg(p), byte j0(p)%4 (+1 for rows 16-31).
   auto j0 = [&](int p) -> int { return GU ? (p < 2 ? 8 * wn + 4 * p : 8 * wn + 4 * (p - 2) + 2) : 8 * wn + 2 * p; };
   const int b_lane = ((l32 >> 4) << 10) + 16 * (16 * g32 + (lane & 15));  // + j0*1024 + 512h
   // A fragment (row l32 of a 32-row block, K half h, piece c): chunk 4h+2c+g32
@@ -561,111 +561,187 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int c = 0; c < 2; ++c) a_lane[h][c] = l32 * 128 + 16 * ((4 * h + 2 * c + g32) ^ ((l32 >> 1) & 7));
-  const int bs_lane = 4 * (16 * g32 + (lane & 15));   // + group*256 + 128h; byte = block in group
-  const int rows_left = tile.row_end - tile.row_begin - 64 * wm;
-  const int nact = rows_left <= 0 ? 0 : (rows_left <= 32 ? 1 : 2);   // active row blocks
+  const int bs_lane = 4 * (16 * g32 + (lane & 15)) + (2 * wn) * 256;  // + 256*group + 128h
+  const int rows_left = tile.row_end - tile.row_begin - 128 * wm;
+  const int nact = rows_left <= 0 ? 0 : min(4, (rows_left + 31) >> 5);   // active row blocks
 
-  v16f acc[2][4];
+  v16f acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[i][p] = v16f{};
 
   auto main_loop = [&](auto nact_c) {
     constexpr int NACT = decltype(nact_c)::value;
-    uint4 asg[2];        // grouped activation scales of this lane's rows
+    uint4 asg[4];               // grouped activation scales of this lane's rows
+    uint32_t asr[2][4];         // A scale dwords (shifted by 8*g32) of the current / next step
+    uint32_t bsd[2][2][2];      // B scale dwords [buffer][group 2wn+gi][half] (shifted by 8*(l32/16))
+    v8i av[2][4], bv[2][4];     // operand sets of K half 0 and 1
 
-    auto compute = [&](int st, auto ic) {
-      constexpr int I = decltype(ic)::value;  // st % 4
+    // operand reads (slot byte offset so): A fragment of row block I_, B
+    // fragment P, K half H
+    auto read_a = [&](int so, auto hc, auto ic_) {
+      constexpr int H = decltype(hc)::value, I_ = decltype(ic_)::value;
+      if (I_ >= NACT) return;
+      const uint8_t* pa = pf_lds + so + kPfA + (4 * wm + I_) * 4096;
+      av[H][I_] = make_a(ld16(pa + a_lane[H][0]), ld16(pa + a_lane[H][1]));
+    };
+    auto read_b = [&](int so, auto hc, auto pc) {
+      constexpr int H = decltype(hc)::value, P = decltype(pc)::value;
+      if (NACT == 0) return;
+      bv[H][P] = make_b(ld16(pf_lds + so + kPfB + j0(P) * 1024 + 512 * H + b_lane));
+    };
+    // scales of step st (st % 4 == I): raw loads, then (once later LDS reads
+    // are in flight) the shifts into buffer B
+    uint32_t bs_raw[2][2], as_raw[4];
+    auto load_scales = [&](int st, auto ic) {
+      constexpr int I = decltype(ic)::value;
       if (NACT == 0) return;
       const uint8_t* sb = pf_lds + (st % 3) * kPfSlot;
-      uint32_t bsr[4][2];  // weight scales of the fragments, in byte 0
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp)
+      for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          bsr[pp][h] = *reinterpret_cast<const uint32_t*>(sb + kPfBS + (j0(pp) >> 2) * 256 + 128 * h + bs_lane) >>
-                       (8 * ((j0(pp) & 3) + (l32 >> 4)));
-      if (I == 0) {
-        if (AG) {
+          bs_raw[gi][h] = *reinterpret_cast<const uint32_t*>(sb + kPfBS + gi * 256 + 128 * h + bs_lane);
+      if (AG) {
+        if (I == 0) {
 #pragma unroll
           for (int i = 0; i < NACT; ++i)
-            asg[i] = *reinterpret_cast<const uint4*>(pf_lds + pf_asg_off(wm) + (32 * i + l32) * 16);
+            asg[i] = *reinterpret_cast<const uint4*>(pf_lds + pf_asg_off(2 * wm + (i >> 1)) + (32 * (i & 1) + l32) * 16);
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NACT; ++i)
+          as_raw[i] = *reinterpret_cast<const uint32_t*>(sb + kPfAS + (128 * wm + 32 * i + l32) * 4);
       }
-      uint32_t asr[2];
-      v8i av[2][2];
-      v8i bv[2][4];
+    };
+    auto shift_scales = [&](auto ic, auto bc) {
+      constexpr int I = decltype(ic)::value, B = decltype(bc)::value;
+      if (NACT == 0) return;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bsd[B][gi][h] = bs_raw[gi][h] >> (8 * (l32 >> 4));
 #pragma unroll
       for (int i = 0; i < NACT; ++i) {
-        if (AG) asr[i] = I == 0 ? asg[i].x : I == 1 ? asg[i].y : I == 2 ? asg[i].z : asg[i].w;
-        else asr[i] = *reinterpret_cast<const uint32_t*>(sb + kPfAS + (2 * wm + i) * 256 + 4 * l32);
+        const uint32_t v = AG ? (I == 0 ? asg[i].x : I == 1 ? asg[i].y : I == 2 ? asg[i].z : asg[i].w) : as_raw[i];
+        asr[B][i] = v >> (8 * g32);
       }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int i = 0; i < NACT; ++i) {
-          const uint8_t* pa = sb + kPfA + (2 * wm + i) * 4096;
-          av[h][i] = make_a(ld16(pa + a_lane[h][0]), ld16(pa + a_lane[h][1]));
-        }
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) bv[h][pp] = make_b(ld16(sb + kPfB + j0(pp) * 1024 + 512 * h + b_lane));
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < NACT; ++i) {
-          const uint32_t sa = asr[i] >> (8 * (2 * h + g32));
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) acc[i][pp] = mfma32_mx<0>(av[h][i], bv[h][pp], acc[i][pp], sa, bsr[pp][h]);
-        }
+    };
+    // MFMA k of K half H (row block k/4, fragment k%4) with scale buffer B;
+    // fragment p's weight scale: group 2wn + gi, byte sel
+    auto mf = [&](auto hc, auto bc, auto kc) {
+      constexpr int H = decltype(hc)::value, B = decltype(bc)::value, Kk = decltype(kc)::value;
+      constexpr int I_ = Kk >> 2, P = Kk & 3;
+      constexpr int GI = GU ? (P & 1) : (P >> 1);
+      constexpr int SB = GU ? (P >= 2 ? 2 : 0) : ((P & 1) ? 2 : 0);
+      if (I_ < NACT)
+        acc[I_][P] = mfma32_mx<2 * H, SB>(av[H][I_], bv[H][P], acc[I_][P], asr[B][I_], bsd[B][GI][H]);
     };
 
-    // step st: wait for this wave's copies of st (the next step's may stay
-    // in flight), publish with a barrier, refill the slot of step st-1 with
-    // step st+2, then compute
-    auto stage = [&](int st, auto ic) {
-      constexpr int I = decltype(ic)::value;
-      if (st + 1 < nsteps) {
-        wait_vm_upto15(ncopies + (AG && ((I + 1) & 3) == 0 && wu < 4 ? 1 : 0));
-      } else {
-        PF_WAIT_VM(0);
-      }
+    // step st: the memory work of the step sits between its MFMAs in a fixed
+    // order (one scheduling region per MFMA), so the copies and LDS reads
+    // issue while the matrix core is busy, spread over the step so the four
+    // waves do not queue their copies at once
+    auto step = [&](int st, auto ic) {
+      constexpr int I = decltype(ic)::value;   // st % 4
+      constexpr int B = I & 1;                 // scale buffer of step st
+      const int s0 = (st % 3) * kPfSlot;
+      // half 0 from set 0; between the MFMAs: reads of half 1 into set 1 and
+      // the weight copies of step st+2 (its slot was freed in step st-1)
+      static_for<0, 16>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        mf(IntC<0>{}, IntC<B>{}, kc);
+        if constexpr (k % 2 == 1) {
+          if constexpr (k / 2 < 4) read_a(s0, IntC<1>{}, IntC<k / 2>{});
+          else read_b(s0, IntC<1>{}, IntC<k / 2 - 4>{});
+        } else if constexpr (k / 2 < 6) {
+          copy_w(st + 2, IntC<k / 2>{}, IntC<((I + 2) & 3) == 0>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // (after the last step the reads below fetch a stale slot whose values
+      // go unused: one code path keeps the accumulators in place)
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave is done reading slot st
+      PF_WAIT_VM(ncop(I + 2));                 // its copies of step st+1 have landed
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      if (st + 2 < nsteps) issue(st + 2, ((I + 2) & 3) == 0);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(st, ic);
+      const int s1 = ((st + 1) % 3) * kPfSlot;
+      // half 1 from set 1; between the MFMAs: the scales and half 0 of step
+      // st+1 (into set 0), then the activation copies of step st+3 into slot st
+      static_for<0, 16>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        mf(IntC<1>{}, IntC<B>{}, kc);
+        if constexpr (k == 0) { load_scales(st + 1, IntC<(I + 1) & 3>{}); read_a(s1, IntC<0>{}, IntC<0>{}); }
+        if constexpr (k == 1) { read_b(s1, IntC<0>{}, IntC<0>{}); read_b(s1, IntC<0>{}, IntC<1>{}); }
+        if constexpr (k == 2) read_a(s1, IntC<0>{}, IntC<1>{});
+        if constexpr (k == 3) { read_b(s1, IntC<0>{}, IntC<2>{}); read_b(s1, IntC<0>{}, IntC<3>{}); }
+        if constexpr (k == 4) read_a(s1, IntC<0>{}, IntC<2>{});
+        if constexpr (k == 5) read_a(s1, IntC<0>{}, IntC<3>{});
+        if constexpr (k >= 6 && k <= 13) copy_a(st + 3, IntC<k - 6>{});
+        if constexpr (k == 8) shift_scales(IntC<(I + 1) & 3>{}, IntC<B ^ 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(0, true);
-    if (1 < nsteps) issue(1, false);
-    for (int st0 = 0; st0 < nsteps; st0 += 4) {
-      stage(st0, IntC<0>{});
-      if (st0 + 1 < nsteps) stage(st0 + 1, IntC<1>{});
-      if (st0 + 2 < nsteps) stage(st0 + 2, IntC<2>{});
-      if (st0 + 3 < nsteps) stage(st0 + 3, IntC<3>{});
+    // prologue: steps 0 and 1, and the activation copies of step 2 (its
+    // weight copies come in step 0)
+    static_for<0, 8>([&](auto qc) { copy_a(0, qc); });
+    static_for<0, 6>([&](auto mc) { copy_w(0, mc, IntC<1>{}); });
+    static_for<0, 8>([&](auto qc) { copy_a(1, qc); });
+    static_for<0, 6>([&](auto mc) { copy_w(1, mc, IntC<0>{}); });
+    static_for<0, 8>([&](auto qc) { copy_a(2, qc); });
+    PF_WAIT_VM(ncop(1) + 8);                   // step 0 has landed
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    load_scales(0, IntC<0>{});
+    shift_scales(IntC<0>{}, IntC<0>{});
+    static_for<0, 4>([&](auto ic_) { read_a(0, IntC<0>{}, ic_); read_b(0, IntC<0>{}, ic_); });
+    // one branch-free block per loop body (K % 512 == 0 with grouped scales)
+    if (AG) {
+      for (int st0 = 0; st0 < nsteps; st0 += 4) {
+        step(st0, IntC<0>{});
+        step(st0 + 1, IntC<1>{});
+        step(st0 + 2, IntC<2>{});
+        step(st0 + 3, IntC<3>{});
+      }
+    } else {
+      int st0 = 0;
+      for (; st0 + 1 < nsteps; st0 += 2) {
+        step(st0, IntC<0>{});
+        step(st0 + 1, IntC<1>{});
+      }
+      if (st0 < nsteps) step(st0, IntC<0>{});
     }
   };
-  if (nact == 2) main_loop(IntC<2>{});
-  else if (nact == 1) main_loop(IntC<1>{});
-  else main_loop(IntC<0>{});
+  switch (nact) {
+    case 4: main_loop(IntC<4>{}); break;
+    case 3: main_loop(IntC<3>{}); break;
+    case 2: main_loop(IntC<2>{}); break;
+    case 1: main_loop(IntC<1>{}); break;
+    default: main_loop(IntC<0>{}); break;
+  }
 
-  // ---- epilogue through LDS: every wave is past its last operand read
-  // after this barrier, and each wave then owns a private stage region.
-  // acc[i][p] register r holds tile row 64wm + 32i + 8(r/4) + 4 g32 + r%4
+  // ---- epilogue through LDS: after this wave's last copies have landed and
+  // the barrier, every wave is past its last operand read and each wave then
+  // owns a private stage region.
+  // acc[i][p] register r holds tile row 128wm + 32i + 8(r/4) + 4 g32 + r%4
   // and column l32 of weight fragment p.
+  PF_WAIT_VM(0);
   __syncthreads();
   if (nact == 0) return;
   if (GU) {
-    // h = silu(gate) * up as fp32 [64 rows][64 h columns] (row stride 68)
-    float* hs = reinterpret_cast<float*>(pf_lds) + wu * (64 * 68);
+    // h = silu(gate) * up as fp32 [128 rows][64 h columns] (row stride 68)
+    float* hs = reinterpret_cast<float*>(pf_lds) + wu * (128 * 68);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       if (i >= nact) break;
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp)
@@ -675,7 +751,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
           const float gt = acc[i][pp][r], up = acc[i][pp + 2][r];
           hs[rl * 68 + 32 * pp + l32] = gt / (1.0f + __expf(-gt)) * up;
           if (a.gu_acc) {
-            const int row = tile.row_begin + 64 * wm + rl;
+            const int row = tile.row_begin + 128 * wm + rl;
             if (row < tile.row_end) {
               const int col = c0 + 64 * wn + 32 * pp + l32;
               a.gu_acc[int64_t(row) * 2 * a.dff + col] = gt;
@@ -684,40 +760,44 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
           }
         }
     }
-    // lane l quantises row l: two MXFP8 blocks of 32 h values
-    const int row = tile.row_begin + 64 * wm + lane;
-    if (row < tile.row_end) {
+    // lane l quantises rows l and l + 64: two MXFP8 blocks of 32 h values each
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const float4* src = reinterpret_cast<const float4*>(hs + lane * 68 + 32 * blk);
-        float v[32];
+    for (int half = 0; half < 2; ++half) {
+      const int rl = 64 * half + lane;
+      const int row = tile.row_begin + 128 * wm + rl;
+      if (row < tile.row_end) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 t = src[q];
-          v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+        for (int blk = 0; blk < 2; ++blk) {
+          const float4* src = reinterpret_cast<const float4*>(hs + rl * 68 + 32 * blk);
+          float v[32];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float4 t = src[q];
+            v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+          }
+          float amax = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
+          const int e = mx8_block_exp(amax);
+          const float sc = exp2_int(-e);
+          uint32_t w[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            w[q] = e4m3_cvt4(v[4 * q] * sc, v[4 * q + 1] * sc, v[4 * q + 2] * sc, v[4 * q + 3] * sc);
+          const int col = c0 + 64 * wn + 32 * blk;
+          uint4* dst = reinterpret_cast<uint4*>(a.h_codes + int64_t(row) * a.dff + col);
+          dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+          a.h_scales[int64_t(row) * (a.dff / 32) + (col >> 5)] = static_cast<uint8_t>(e + 127);
         }
-        float amax = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
-        const int e = mx8_block_exp(amax);
-        const float sc = exp2_int(-e);
-        uint32_t w[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          w[q] = e4m3_cvt4(v[4 * q] * sc, v[4 * q + 1] * sc, v[4 * q + 2] * sc, v[4 * q + 3] * sc);
-        const int col = c0 + 64 * wn + 32 * blk;
-        uint4* dst = reinterpret_cast<uint4*>(a.h_codes + int64_t(row) * a.dff + col);
-        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        a.h_scales[int64_t(row) * (a.dff / 32) + (col >> 5)] = static_cast<uint8_t>(e + 127);
       }
     }
   } else {
-    // bf16 outputs [64 rows][128 columns] (row stride 136 halves), then
-    // 16-byte row chunks: 16 per row, 1024 per wave, 16 per lane
-    uint16_t* os = reinterpret_cast<uint16_t*>(pf_lds) + wu * (64 * 136);
+    // bf16 outputs [128 rows][128 columns] (row stride 136 halves), then
+    // 16-byte row chunks: 16 per row, 2048 per wave, 32 per lane
+    uint16_t* os = reinterpret_cast<uint16_t*>(pf_lds) + wu * (128 * 136);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       if (i >= nact) break;
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp)
@@ -727,11 +807,11 @@ __global__ void __launch_bounds__(512, 1) k_gemm_pf(FwdArgs a) {
           os[rl * 136 + 32 * pp + l32] = f32_to_bf16_rne(acc[i][pp][r]);
         }
     }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
       const int ch = q * 64 + lane;          // chunk: row ch / 16, 8 columns at 8 (ch % 16)
       const int rl = ch >> 4, cc = 8 * (ch & 15);
-      const int row = tile.row_begin + 64 * wm + rl;
+      const int row = tile.row_begin + 128 * wm + rl;
       if (row < tile.row_end) {
         const uint4 t = *reinterpret_cast<const uint4*>(os + rl * 136 + cc);
         *reinterpret_cast<uint4*>(a.o16 + int64_t(row) * a.d + c0 + 128 * wn + cc) = t;
@@ -747,9 +827,9 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
   const int K = GU ? a.d : a.dff;
   const dim3 grid(8 * ((items + 7) / 8));
   if (K % 512 == 0)
-    hipLaunchKernelGGL((k_gemm_pf<GU, true>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_pf<GU, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_pf<GU, false>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_pf<GU, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

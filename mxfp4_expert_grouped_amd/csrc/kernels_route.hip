@@ -105,9 +105,9 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int e = blockIdx.x;
   const int d = a.d, T = a.T;
+  const int nb = d / 32;
   // fused MXFP8 quantisation of x: 8 threads per 32-element block, 32 blocks
   // per workgroup (workgroup e takes blocks 32e .. 32e+31 of all T*d/32)
-  const int nb = d / 32;
   {
     const int b = 32 * e + (tid >> 3), j = tid & 7;
     if (b < T * nb) {
@@ -117,8 +117,8 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
                     __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u)};
       const float amax = group_max<8>(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
       const int ex = mx8_block_exp(amax);
-      const uint32_t w = mx8_encode(v[0], ex) | (mx8_encode(v[1], ex) << 8) |
-                         (mx8_encode(v[2], ex) << 16) | (mx8_encode(v[3], ex) << 24);
+      const float sc = exp2_int(-ex);
+      const uint32_t w = e4m3_cvt4(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
       *reinterpret_cast<uint32_t*>(a.x_codes + int64_t(t) * d + c * 32 + 4 * j) = w;
       if (j == 0) a.x_scales[int64_t(t) * nb + c] = static_cast<uint8_t>(ex + 127);
     }
