@@ -456,14 +456,10 @@ __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int*
   const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
   const int w = xcd * per_xcd + i;
   if (i >= per_xcd || w >= total) return false;
-  // expert e: the last with ex_tiles[e] <= w / nblocks
-  const int q = w / nblocks;
-  int lo = 0, hi = a.E + a.S;  // ex_tiles[lo] <= q < ex_tiles[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.ex_tiles[mid] <= q) lo = mid; else hi = mid;
-  }
-  const int t0 = a.ex_tiles[lo], nt = a.ex_tiles[lo + 1] - t0;
+  // the expert owning items w: tiles are expert-major and an expert's items
+  // span its tiles, so tile w / nblocks belongs to it
+  const int ex = a.tiles[w / nblocks].ex;
+  const int t0 = a.ex_tiles[ex], nt = a.ex_tiles[ex + 1] - t0;
   const int local = w - t0 * nblocks;
   const int tg = local / (kPfGroupTiles * nblocks);           // tile group
   const int gsize = min(kPfGroupTiles, nt - tg * kPfGroupTiles);
