@@ -789,6 +789,16 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
       }
     }
   } else {
+    // o rows are stored in (token, slot) order: routed row r goes to its pair
+    // index row_src[r] (token-major, so the combine reads a token's rows
+    // back to back), shared rows keep their place.  Destinations of this
+    // wave's 128 rows into an LDS table after the four staging areas.
+    int* dst_tab = reinterpret_cast<int*>(pf_lds + 4 * (128 * 136 * 2)) + wu * 128;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = tile.row_begin + 128 * wm + 64 * hh + lane;
+      dst_tab[64 * hh + lane] = row < tile.row_end && row < a.Rr ? a.row_src[row] : row;
+    }
     // bf16 outputs [128 rows][128 columns] (row stride 136 halves), then
     // 16-byte row chunks: 16 per row, 2048 per wave, 32 per lane
     uint16_t* os = reinterpret_cast<uint16_t*>(pf_lds) + wu * (128 * 136);
@@ -810,7 +820,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
       const int row = tile.row_begin + 128 * wm + rl;
       if (row < tile.row_end) {
         const uint4 t = *reinterpret_cast<const uint4*>(os + rl * 136 + cc);
-        *reinterpret_cast<uint4*>(a.o16 + int64_t(row) * a.d + c0 + 128 * wn + cc) = t;
+        *reinterpret_cast<uint4*>(a.o16 + int64_t(dst_tab[rl]) * a.d + c0 + 128 * wn + cc) = t;
       }
     }
   }

@@ -772,7 +772,9 @@ hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
 // One thread per C output columns of one token (C = 4 for the fp32 o of the
 // decode kernels, 8 for the bf16 o of the prefill kernels: 16-byte loads
 // either way); the k expert rows are read in batches of 16 loads in flight
-// and summed in slot order, then the shared rows.
+// and summed in slot order, then the shared rows.  The decode kernels leave
+// o in permuted-row order (found through token_row); the prefill kernels
+// store it in (token, slot) order, so a token's k rows are contiguous.
 template <bool O16>
 __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   constexpr int C = O16 ? 8 : 4;
@@ -804,7 +806,7 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
 #pragma unroll
     for (int u = 0; u < 16; ++u)
       if (j0 + u < a.k) {
-        load(trow[j0 + u], v[u]);
+        load(O16 ? int64_t(t) * a.k + j0 + u : int64_t(trow[j0 + u]), v[u]);
         w[u] = tw[j0 + u];
       }
 #pragma unroll
