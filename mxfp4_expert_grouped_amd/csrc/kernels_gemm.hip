@@ -441,31 +441,28 @@ constexpr int kPfLds = 3 * kPfSlot;            // 156672 bytes
 __shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 
 
-// Work order of the prefill GEMMs: items (tile, column block) expert-major,
-// cut into 8 contiguous ranges, one per XCD (workgroups go to the XCDs
-// round-robin by linear id).  Inside an expert the items run in groups of
-// kPfGroupTiles tiles, column block next and tile fastest, so the workgroups
-// an XCD runs at once cover a few tiles x several column blocks: every
-// activation window and every weight window they read in the same K step is
-// shared by several of them and comes from that XCD's L2.  Returns false for
-// a workgroup with no item.
+// Work order of the prefill GEMMs: items (tile, column block) in tile order
+// (tiles are expert-major), cut into 8 contiguous ranges, one per XCD
+// (workgroups go to the XCDs round-robin by linear id).  Items run in groups
+// of kPfGroupTiles consecutive tiles, column block next and tile fastest, so
+// the workgroups an XCD runs at once cover a few tiles x several column
+// blocks: every activation window and every weight window they read in the
+// same K step is shared by several of them and comes from that XCD's L2.
+// The mapping needs only the tile count.  Returns false for a workgroup with
+// no item.
 constexpr int kPfGroupTiles = 4;
 __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int* tile_out, int* blk_out) {
-  const int total = *a.tile_count * nblocks;
+  const int ntiles = *a.tile_count;
+  const int total = ntiles * nblocks;
   const int per_xcd = (total + 7) / 8;
   const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
   const int w = xcd * per_xcd + i;
   if (i >= per_xcd || w >= total) return false;
-  // the expert owning items w: tiles are expert-major and an expert's items
-  // span its tiles, so tile w / nblocks belongs to it
-  const int ex = a.tiles[w / nblocks].ex;
-  const int t0 = a.ex_tiles[ex], nt = a.ex_tiles[ex + 1] - t0;
-  const int local = w - t0 * nblocks;
-  const int tg = local / (kPfGroupTiles * nblocks);           // tile group
-  const int gsize = min(kPfGroupTiles, nt - tg * kPfGroupTiles);
-  const int rem = local - tg * kPfGroupTiles * nblocks;
+  const int tg = w / (kPfGroupTiles * nblocks);                // tile group
+  const int gsize = min(kPfGroupTiles, ntiles - tg * kPfGroupTiles);
+  const int rem = w - tg * kPfGroupTiles * nblocks;
   *blk_out = rem / gsize;
-  *tile_out = t0 + tg * kPfGroupTiles + rem % gsize;
+  *tile_out = tg * kPfGroupTiles + rem % gsize;
   return true;
 }
 

@@ -234,7 +234,7 @@ def test_tiny_layer_all_taps():
     assert not differ
 
 
-@pytest.mark.parametrize("T", [1, 3, 13, 64, 65, 200, 256, 1100, 1500])
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 13, 64, 65, 200, 256, 1100, 1500])
 def test_ragged_token_counts(T):
     # 256 and above use 64-row tiles (>= 24 rows per expert on average);
     # above 1024 tokens the multi-kernel permutation path runs
