@@ -406,9 +406,10 @@ static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
 // two steps to land.  Row blocks past the tile's end skip their reads and
 // MFMAs.  Scale bytes are picked by the MFMA's operand selects.
 //
-// Wave w computes rows 128(w%2) .. +127 (four 32-row blocks) against 128 of
-// the 256 weight rows (w/2 picks them): gate and up rows of the same 64 h
-// columns for gate_up, 128 output columns for down.
+// The two waves with the same w/2 split the tile's 32-row blocks evenly
+// (up to four each, the first ones to w%2 == 0) and compute them against
+// 128 of the 256 weight rows (w/2 picks them): gate and up rows of the same
+// 64 h columns for gate_up, 128 output columns for down.
 // ---------------------------------------------------------------------------
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -555,8 +556,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) a_lane[h][c] = l32 * 128 + 16 * ((4 * h + 2 * c + g32) ^ ((l32 >> 1) & 7));
   const int bs_lane = 4 * (16 * g32 + (lane & 15)) + (2 * wn) * 256;  // + 256*group + 128h
-  const int rows_left = tile.row_end - tile.row_begin - 128 * wm;
-  const int nact = rows_left <= 0 ? 0 : min(4, (rows_left + 31) >> 5);   // active row blocks
+  // the tile's 32-row blocks split evenly between the two row halves (a
+  // step lasts as long as its busiest wave): wave half wm takes blocks
+  // rb0 .. rb0 + nact - 1
+  const int nb = (tile.row_end - tile.row_begin + 31) >> 5;
+  const int rb0 = wm ? (nb + 1) >> 1 : 0;
+  const int nact = wm ? nb >> 1 : (nb + 1) >> 1;                        // active row blocks
+  const int wrow0 = 32 * rb0;                                            // first tile row of this wave
 
   v16f acc[4][4];
 #pragma unroll
@@ -576,7 +582,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
     auto read_a = [&](int so, auto hc, auto ic_) {
       constexpr int H = decltype(hc)::value, I_ = decltype(ic_)::value;
       if (I_ >= NACT) return;
-      const uint8_t* pa = pf_lds + so + kPfA + (4 * wm + I_) * 4096;
+      const uint8_t* pa = pf_lds + so + kPfA + (rb0 + I_) * 4096;
       av[H][I_] = make_a(ld16(pa + a_lane[H][0]), ld16(pa + a_lane[H][1]));
     };
     auto read_b = [&](int so, auto hc, auto pc) {
@@ -600,12 +606,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
         if (I == 0) {
 #pragma unroll
           for (int i = 0; i < NACT; ++i)
-            asg[i] = *reinterpret_cast<const uint4*>(pf_lds + pf_asg_off(2 * wm + (i >> 1)) + (32 * (i & 1) + l32) * 16);
+            asg[i] = *reinterpret_cast<const uint4*>(pf_lds + pf_asg_off((rb0 + i) >> 1) + (32 * ((rb0 + i) & 1) + l32) * 16);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < NACT; ++i)
-          as_raw[i] = *reinterpret_cast<const uint32_t*>(sb + kPfAS + (128 * wm + 32 * i + l32) * 4);
+          as_raw[i] = *reinterpret_cast<const uint32_t*>(sb + kPfAS + (wrow0 + 32 * i + l32) * 4);
       }
     };
     auto shift_scales = [&](auto ic, auto bc) {
@@ -725,7 +731,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   // ---- epilogue through LDS: after this wave's last copies have landed and
   // the barrier, every wave is past its last operand read and each wave then
   // owns a private stage region.
-  // acc[i][p] register r holds tile row 128wm + 32i + 8(r/4) + 4 g32 + r%4
+  // acc[i][p] register r holds tile row wrow0 + 32i + 8(r/4) + 4 g32 + r%4
   // and column l32 of weight fragment p.
   PF_WAIT_VM(0);
   __syncthreads();
@@ -744,7 +750,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
           const float gt = acc[i][pp][r], up = acc[i][pp + 2][r];
           hs[rl * 68 + 32 * pp + l32] = gt / (1.0f + __expf(-gt)) * up;
           if (a.gu_acc) {
-            const int row = tile.row_begin + 128 * wm + rl;
+            const int row = tile.row_begin + wrow0 + rl;
             if (row < tile.row_end) {
               const int col = c0 + 64 * wn + 32 * pp + l32;
               a.gu_acc[int64_t(row) * 2 * a.dff + col] = gt;
@@ -757,8 +763,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int rl = 64 * half + lane;
-      const int row = tile.row_begin + 128 * wm + rl;
-      if (row < tile.row_end) {
+      const int row = tile.row_begin + wrow0 + rl;
+      if (rl < 32 * nact && row < tile.row_end) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
           const float4* src = reinterpret_cast<const float4*>(hs + rl * 68 + 32 * blk);
@@ -793,7 +799,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
     int* dst_tab = reinterpret_cast<int*>(pf_lds + 4 * (128 * 136 * 2)) + wu * 128;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int row = tile.row_begin + 128 * wm + 64 * hh + lane;
+      const int row = tile.row_begin + wrow0 + 64 * hh + lane;
       dst_tab[64 * hh + lane] = row < tile.row_end && row < a.Rr ? a.row_src[row] : row;
     }
     // bf16 outputs [128 rows][128 columns] (row stride 136 halves), then
@@ -814,8 +820,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
     for (int q = 0; q < 32; ++q) {
       const int ch = q * 64 + lane;          // chunk: row ch / 16, 8 columns at 8 (ch % 16)
       const int rl = ch >> 4, cc = 8 * (ch & 15);
-      const int row = tile.row_begin + 128 * wm + rl;
-      if (row < tile.row_end) {
+      const int row = tile.row_begin + wrow0 + rl;
+      if (rl < 32 * nact && row < tile.row_end) {
         const uint4 t = *reinterpret_cast<const uint4*>(os + rl * 136 + cc);
         *reinterpret_cast<uint4*>(a.o16 + int64_t(dst_tab[rl]) * a.d + c0 + 128 * wn + cc) = t;
       }
