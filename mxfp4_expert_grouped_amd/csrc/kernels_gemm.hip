@@ -150,10 +150,23 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   const int nsw = wsteps(wu);
   const int ngrp = GU ? a.dff / 32 : a.d / 64;
   const int nitems = sload1(a.tile_count) * ngrp;
-  // item walkers: workgroups (split) or single waves, round-robin
-  const int bid = KSPLIT ? blockIdx.x : blockIdx.x * 4 + wu;
-  const int nwg = KSPLIT ? gridDim.x : gridDim.x * 4;
-  const int my_items = nitems > bid ? (nitems - bid + nwg - 1) / nwg : 0;
+  // item walkers: workgroups (split) or single waves, round-robin.  With
+  // many items per walker (16+) the items are first cut into 8 contiguous
+  // ranges, one per XCD (workgroups go to the XCDs round-robin), and an
+  // XCD's walkers take its range round-robin: the column groups of a tile
+  // then share its activation rows in one L2 while every XCD streams
+  // neighbouring weight groups.  With few items plain round-robin keeps the
+  // whole grid on one contiguous stretch of weights, which measured faster.
+  const int walkers = KSPLIT ? gridDim.x : gridDim.x * 4;
+  const bool by_xcd = nitems >= 16 * walkers;
+  const int xcd = by_xcd ? blockIdx.x & 7 : 0;
+  const int xw = by_xcd ? blockIdx.x >> 3 : blockIdx.x;
+  const int nxw = by_xcd ? gridDim.x >> 3 : gridDim.x;
+  const int bid = KSPLIT ? xw : xw * 4 + wu;
+  const int nwg = KSPLIT ? nxw : nxw * 4;
+  const int per_xcd = by_xcd ? (nitems + 7) / 8 : nitems;
+  const int xbase = xcd * per_xcd, xn = max(0, min(per_xcd, nitems - xbase));
+  const int my_items = xn > bid ? (xn - bid + nwg - 1) / nwg : 0;
   const int nel = my_items * nsw;
   const int64_t wrows = GU ? 2 * a.dff : a.d;
   const int64_t wc_stride = wrows * (K / 2), ws_stride = packed_scale_bytes(wrows, K);
@@ -174,7 +187,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   const int achunk = (lane & 7) ^ ((ar >> 1) & 3);    // global chunk landing at chunk lane&7
   int cur_tile = -1, ex = 0, rb = 0, nr = 0;
   auto item_setup = [&](int il) {
-    const int item = bid + il * nwg;
+    const int item = xbase + bid + il * nwg;
     const int tidx = item / ngrp, G = item - tidx * ngrp;
     const bool new_tile = tidx != cur_tile;
     if (new_tile) {
@@ -362,10 +375,12 @@ template <bool GU>
 static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
   // the item count is known on the device only; max_tiles bounds it
   const int64_t max_items = int64_t(a.max_tiles) * (GU ? a.dff / 32 : a.d / 64);
+  // persistent: one workgroup per CU, a multiple of 8 (one share per XCD)
+  const unsigned grid = 8u * static_cast<unsigned>(a.num_cus >= 16 ? a.num_cus / 8 : 1);
   if (GU && max_items < 16 * 4 * int64_t(a.num_cus))
-    hipLaunchKernelGGL((k_gemm_stream<GU, true>), dim3(a.num_cus), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_stream<GU, true>), dim3(grid), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_stream<GU, false>), dim3(a.num_cus), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_stream<GU, false>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
