@@ -24,13 +24,14 @@ __device__ __forceinline__ uint32_t quant_block32(const float* v, uint8_t* codes
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int e = mx8_block_exp(amax);
+  const int e = mx8_block_exp(amax);
+  // v / 2^e is exact (a power-of-two scale; a product below the fp32 normal
+  // range encodes to a signed zero either way), then the hardware E4M3
+  // conversion with the +-448 clamp
+  const float sc = exp2_int(-e);
   uint32_t w[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    w[i] = mx8_encode(v[4 * i], e) | (mx8_encode(v[4 * i + 1], e) << 8) |
-           (mx8_encode(v[4 * i + 2], e) << 16) | (mx8_encode(v[4 * i + 3], e) << 24);
-  }
+  for (int i = 0; i < 8; ++i) w[i] = e4m3_cvt4(v[4 * i] * sc, v[4 * i + 1] * sc, v[4 * i + 2] * sc, v[4 * i + 3] * sc);
   uint4* dst = reinterpret_cast<uint4*>(codes);
   dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
   dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
