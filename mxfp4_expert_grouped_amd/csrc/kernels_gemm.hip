@@ -103,18 +103,19 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // item of gate_up a wave parks its partial sums in the slot it just consumed;
 // between two barriers every wave sums the four quarters in wave order for a
 // quarter of the output lanes and writes that part of the epilogue.  The
-// MFMA's rows 8-15 repeat rows 0-7 and are discarded.
-// Slot (5632 bytes): weights 4 KB (the group's step, as packed) | A 8 rows x
-// 128 B (16-byte chunks XOR-swizzled by (row/2)%4; only the tile's rows are
-// copied) | A scales (dword per row, lanes 0-7) | weight scales (the packed
-// dword of each lane, byte = block).
+// MFMA's rows 8-15 repeat rows 0-7 and are discarded.  With many items (16+
+// per wave) a down item covers two groups (128 output columns): one A copy
+// then feeds eight MFMAs and the per-item work halves, through a shallower
+// ring of larger slots.
+// Slot (5632 bytes; 9984 for two-group items): weights 4 KB per group (the
+// group's step, as packed) | A 8 rows x 128 B (16-byte chunks XOR-swizzled by
+// (row/2)%4; only the tile's rows are copied) | A scales (dword per row, lanes
+// 0-7) | weight scales per group (the packed dword of each lane, byte = block).
 // ---------------------------------------------------------------------------
-constexpr int kDsS = 7;                        // ring slots per wave
-constexpr int kDsNC = 7;                       // copies per element: 4 weights, A, A scales, weight scales
-constexpr int kDsW = 0, kDsA = 4096, kDsAS = 5120, kDsBS = 5376, kDsSlot = 5632;
-constexpr int kDsWave = kDsS * kDsSlot;
-constexpr int kDsFifo = 4 * kDsWave;           // per wave: 8 x {ex, row_begin, row_end, group}
-constexpr int kDsLds = kDsFifo + 4 * 8 * 16;   // 158208 bytes
+constexpr int kDsS = 7;                        // ring slots per wave (5632-byte slots)
+constexpr int kDsSWide = 4;                    // ring slots per wave of wide items (9984 bytes)
+// LDS: four waves' rings, then per wave 8 x {ex, row_begin, row_end, group}
+constexpr int kDsLds = 4 * kDsSWide * 9984 + 4 * 8 * 16;   // 160256 bytes (the larger ring)
 __shared__ __attribute__((aligned(1024))) uint8_t ds_lds[kDsLds];
 
 typedef int v4i_s __attribute__((ext_vector_type(4)));
@@ -138,8 +139,16 @@ __device__ __forceinline__ int sload1(const void* p) {
   return v;
 }
 
-template <bool GU, bool KSPLIT>
+template <bool GU, bool KSPLIT, bool WIDE>
 __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
+  // ring geometry: WIDE items (down only) cover two 64-row groups
+  constexpr int GPI = WIDE ? 2 : 1;                 // packed groups per item
+  constexpr int S = WIDE ? kDsSWide : kDsS;         // ring slots per wave
+  constexpr int NC = 4 * GPI + 2 + GPI;             // copies per element
+  constexpr int SW = 0, SA = 4096 * GPI, SAS = SA + 1024, SBS = SAS + 256, SLOT = SBS + 256 * GPI;
+  constexpr int WAVE = S * SLOT, FIFO = 4 * WAVE;
+  static_assert(FIFO + 4 * 8 * 16 <= kDsLds, "ring does not fit");
+  static_assert(!(WIDE && (GU || KSPLIT)), "wide items are for the down GEMM");
   const int lane = threadIdx.x & 63;
   const int wu = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = lane >> 4, r16 = lane & 15;
@@ -148,7 +157,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   // K steps per item of wave w: w, w+4, ... (split) or all of them
   auto wsteps = [&](int w) { return KSPLIT ? (ns - w + 3) / 4 : ns; };
   const int nsw = wsteps(wu);
-  const int ngrp = GU ? a.dff / 32 : a.d / 64;
+  const int ngrp = (GU ? a.dff / 32 : a.d / 64) / GPI;   // items per tile
   const int nitems = sload1(a.tile_count) * ngrp;
   // item walkers: workgroups (split) or single waves, round-robin.  With
   // many items per walker (16+) the items are first cut into 8 contiguous
@@ -170,13 +179,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   const int nel = my_items * nsw;
   const int64_t wrows = GU ? 2 * a.dff : a.d;
   const int64_t wc_stride = wrows * (K / 2), ws_stride = packed_scale_bytes(wrows, K);
-  const uint32_t wbase = lds_addr(ds_lds) + wu * kDsWave;
-  const uint8_t* wlds = ds_lds + wu * kDsWave;
+  const uint32_t wbase = lds_addr(ds_lds) + wu * WAVE;
+  const uint8_t* wlds = ds_lds + wu * WAVE;
   // item metadata, issue side -> epilogue: every wave writes its own queue;
   // with the K split the epilogue reads wave 0's, the one wave with K steps
   // whenever K >= 128
-  int* fifo = reinterpret_cast<int*>(ds_lds + kDsFifo) + wu * 32;
-  const int* fifo_ep = reinterpret_cast<const int*>(ds_lds + kDsFifo) + (KSPLIT ? 0 : wu * 32);
+  int* fifo = reinterpret_cast<int*>(ds_lds + FIFO) + wu * 32;
+  const int* fifo_ep = reinterpret_cast<const int*>(ds_lds + FIFO) + (KSPLIT ? 0 : wu * 32);
 
   // ---- issue side: copy sources of the item being issued
   const uint8_t* w_src = nullptr;
@@ -204,8 +213,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
                            : (shared ? a.sdn_c + sidx * wc_stride : a.dn_c + ex * wc_stride);
     const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + ex * ws_stride)
                            : (shared ? a.sdn_s + sidx * ws_stride : a.dn_s + ex * ws_stride);
-    w_src = wc + int64_t(G) * ns * 4096 + 16 * lane;
-    bs_src = ws + int64_t(G) * ns * 256 + 4 * lane;
+    w_src = wc + int64_t(G) * GPI * ns * 4096 + 16 * lane;
+    bs_src = ws + int64_t(G) * GPI * ns * 256 + 4 * lane;
     if (!new_tile) return;
     // activation rows of the tile (rows past the end repeat the first)
     int src_a, src_s;
@@ -233,32 +242,39 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     const int il = el / nsw, si = el - il * nsw;
     if (si == 0) item_setup(il);
     const int st = KSPLIT ? wu + 4 * si : si;
-    const uint32_t slot = wbase + (el % kDsS) * kDsSlot;
+    const uint32_t slot = wbase + (el % S) * SLOT;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_copy16(w_src + st * 4096 + j * 1024, slot + kDsW + j * 1024);
+    for (int g2 = 0; g2 < GPI; ++g2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        lds_copy16(w_src + int64_t(g2) * ns * 4096 + st * 4096 + j * 1024, slot + SW + g2 * 4096 + j * 1024);
     // only the tile's rows (tiles are never empty, so the copy is always
-    // issued and every element counts kDsNC copies)
-    if (lane < 8 * nr) lds_copy16(a_src + 128 * st, slot + kDsA);
-    lds_copy4(as_src + 4 * st, slot + kDsAS);
-    lds_copy4(bs_src + st * 256, slot + kDsBS);
+    // issued and every element counts NC copies)
+    if (lane < 8 * nr) lds_copy16(a_src + 128 * st, slot + SA);
+    lds_copy4(as_src + 4 * st, slot + SAS);
+#pragma unroll
+    for (int g2 = 0; g2 < GPI; ++g2) lds_copy4(bs_src + int64_t(g2) * ns * 256 + st * 256, slot + SBS + g2 * 256);
   };
 
   // ---- consume side
   const int arow = r16 & 7;
   const int a_off0 = arow * 128 + 16 * (g ^ ((arow >> 1) & 3));
   const int a_off1 = arow * 128 + 16 * ((4 + g) ^ ((arow >> 1) & 3));
-  v4f acc[4];
+  v4f acc[4 * GPI];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4 * GPI; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int el) {
-    const uint8_t* sl = wlds + (el % kDsS) * kDsSlot;
-    const v8i av = make_a(ld16(sl + kDsA + a_off0), ld16(sl + kDsA + a_off1));
-    const uint32_t sa = *reinterpret_cast<const uint32_t*>(sl + kDsAS + 4 * arow) >> (8 * g);
-    const uint32_t sbw = *reinterpret_cast<const uint32_t*>(sl + kDsBS + 4 * lane);
+    const uint8_t* sl = wlds + (el % S) * SLOT;
+    const v8i av = make_a(ld16(sl + SA + a_off0), ld16(sl + SA + a_off1));
+    const uint32_t sa = *reinterpret_cast<const uint32_t*>(sl + SAS + 4 * arow) >> (8 * g);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v8i bv = make_b(ld16(sl + kDsW + j * 1024 + 16 * lane));
-      acc[j] = mfma_mx(av, bv, acc[j], sa, sbw >> (8 * j));
+    for (int g2 = 0; g2 < GPI; ++g2) {
+      const uint32_t sbw = *reinterpret_cast<const uint32_t*>(sl + SBS + g2 * 256 + 4 * lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v8i bv = make_b(ld16(sl + SW + g2 * 4096 + j * 1024 + 16 * lane));
+        acc[4 * g2 + j] = mfma_mx(av, bv, acc[4 * g2 + j], sa, sbw >> (8 * j));
+      }
     }
   };
   // end of item il: partial sums into the slot just consumed (a wave without
@@ -266,8 +282,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   // 16w .. 16w+15 (tile rows 4w .. 4w+3) in wave order and writes them
   auto part_slot = [&](int w, int il) -> const v4f* {
     const int n = wsteps(w);
-    const int sl = n > 0 ? ((il + 1) * n - 1) % kDsS : 0;
-    return reinterpret_cast<const v4f*>(ds_lds + w * kDsWave + sl * kDsSlot);
+    const int sl = n > 0 ? ((il + 1) * n - 1) % S : 0;
+    return reinterpret_cast<const v4f*>(ds_lds + w * WAVE + sl * SLOT);
   };
   // gate_up epilogue of one output row: v[0..1] gate and v[2..3] up sums of h
   // columns 32G + col and 32G + 16 + col (the 16 lanes with equal lane/16
@@ -306,13 +322,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
           float v[4] = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
           gu_epilogue(v, row, valid, G, r16);
         } else if (valid) {
-          float* orow = a.o + int64_t(row) * a.d + 64 * G + r16;
+          float* orow = a.o + int64_t(row) * a.d + 64 * GPI * G + r16;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) orow[16 * j] = acc[j][i];
+          for (int j = 0; j < 4 * GPI; ++j) orow[16 * j] = acc[j][i];
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4 * GPI; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
       return;
     }
     v4f* mine = const_cast<v4f*>(part_slot(wu, il));
@@ -348,7 +364,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   };
 
   int iss = 0;
-  for (; iss < nel && iss < kDsS - 1; ++iss) issue(iss);
+  for (; iss < nel && iss < S - 1; ++iss) issue(iss);
   int el = 0;
   for (int il = 0; il < my_items; ++il) {
     for (int k = 0; k < nsw; ++k, ++el) {
@@ -356,12 +372,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
       // copies issued after element el are still allowed in flight
       switch (iss - 1 - el) {
         case 0: PF_WAIT_VM(0); break;
-        case 1: PF_WAIT_VM(kDsNC); break;
-        case 2: PF_WAIT_VM(2 * kDsNC); break;
-        case 3: PF_WAIT_VM(3 * kDsNC); break;
-        case 4: PF_WAIT_VM(4 * kDsNC); break;
-        case 5: PF_WAIT_VM(5 * kDsNC); break;
-        default: PF_WAIT_VM(6 * kDsNC); break;
+        case 1: PF_WAIT_VM(NC); break;
+        case 2: PF_WAIT_VM(2 * NC); break;
+        case 3: PF_WAIT_VM(3 * NC); break;
+        case 4: PF_WAIT_VM(4 * NC); break;
+        case 5: PF_WAIT_VM(5 * NC); break;
+        default: PF_WAIT_VM(6 * NC); break;
       }
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
@@ -377,10 +393,18 @@ static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
   const int64_t max_items = int64_t(a.max_tiles) * (GU ? a.dff / 32 : a.d / 64);
   // persistent: one workgroup per CU, a multiple of 8 (one share per XCD)
   const unsigned grid = 8u * static_cast<unsigned>(a.num_cus >= 16 ? a.num_cus / 8 : 1);
-  if (GU && max_items < 16 * 4 * int64_t(a.num_cus))
-    hipLaunchKernelGGL((k_gemm_stream<GU, true>), dim3(grid), dim3(256), 0, st, a);
+  // few items per wave (< 16): gate_up splits K across a workgroup's waves,
+  // down keeps one-group items and the deeper ring; many: whole items per
+  // wave, two groups per down item
+  const bool few = max_items < 16 * 4 * int64_t(a.num_cus);
+  if (!GU && !few)
+    hipLaunchKernelGGL((k_gemm_stream<false, false, true>), dim3(grid), dim3(256), 0, st, a);
+  else if (!GU)
+    hipLaunchKernelGGL((k_gemm_stream<false, false, false>), dim3(grid), dim3(256), 0, st, a);
+  else if (few)
+    hipLaunchKernelGGL((k_gemm_stream<true, true, false>), dim3(grid), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_stream<GU, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_stream<true, false, false>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
