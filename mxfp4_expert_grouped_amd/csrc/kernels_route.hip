@@ -107,23 +107,19 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
   const int e = blockIdx.x;
   const int d = a.d, T = a.T;
   const int nb = d / 32;
-  // fused MXFP8 quantisation of x: 8 threads per 32-element block, 32 blocks
-  // per workgroup (workgroup e takes blocks 32e .. 32e+31 of all T*d/32)
-  {
-    const int b = 32 * e + (tid >> 3), j = tid & 7;
-    if (b < T * nb) {
-      const int t = b / nb, c = b - t * nb;
-      const uint2 raw = *reinterpret_cast<const uint2*>(a.x + int64_t(t) * d + c * 32 + 4 * j);
-      float v[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
-                    __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u)};
-      const float amax = group_max<8>(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-      const int ex = mx8_block_exp(amax);
-      const float sc = exp2_int(-ex);
-      const uint32_t w = e4m3_cvt4(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
-      *reinterpret_cast<uint32_t*>(a.x_codes + int64_t(t) * d + c * 32 + 4 * j) = w;
-      if (j == 0) a.x_scales[int64_t(t) * nb + c] = static_cast<uint8_t>(ex + 127);
-    }
-  }
+  // Loads are never made conditional: indices past the end are clamped to a
+  // valid element and the value is masked afterwards.  A load under a
+  // per-lane condition would be placed in its own branch with a full wait,
+  // one memory round trip after another.
+  // MXFP8 quantisation of x, 8 threads per 32-element block, 32 blocks per
+  // workgroup (workgroup e takes blocks 32e .. 32e+31 of all T*d/32): its
+  // operand is loaded with the first router weights and used after the dot
+  // products (loaded before the loop it would be waited for at the loop head).
+  const int qb = 32 * e + (tid >> 3), qj = tid & 7;
+  const bool qok = qb < T * nb;
+  const int qt = qok ? qb / nb : 0, qc = qok ? qb - qt * nb : 0;
+  uint2 qraw = make_uint2(0u, 0u);
+
   const float4* w4 = reinterpret_cast<const float4*>(a.wr + int64_t(e) * d);
   const int n4 = d / 4;
   const float bias = a.br ? a.br[e] : 0.f;
@@ -132,25 +128,33 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int base = 0; base < n4; base += 256 * 8) {
       float4 w[8];
+      uint32_t ok[8];  // all ones for columns inside the row
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int c = base + tid + 256 * i;
-        w[i] = c < n4 ? w4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        ok[i] = c < n4 ? ~0u : 0u;
+        w[i] = w4[c < n4 ? c : 0];
       }
+      if (t0 == 0 && base == 0)
+        qraw = *reinterpret_cast<const uint2*>(a.x + int64_t(qt) * d + qc * 32 + 4 * qj);
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
-        if (tt < nt) {
+        if (tt < nt) {  // the same in every lane
           const uint2* xr = reinterpret_cast<const uint2*>(a.x + int64_t(t0 + tt) * d);
+          uint2 xb[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int c = base + tid + 256 * i;
-            if (c < n4) {
-              uint2 xb = xr[c];
-              acc[tt] = fmaf(__uint_as_float(xb.x << 16), w[i].x, acc[tt]);
-              acc[tt] = fmaf(__uint_as_float(xb.x & 0xFFFF0000u), w[i].y, acc[tt]);
-              acc[tt] = fmaf(__uint_as_float(xb.y << 16), w[i].z, acc[tt]);
-              acc[tt] = fmaf(__uint_as_float(xb.y & 0xFFFF0000u), w[i].w, acc[tt]);
-            }
+            xb[i] = xr[c < n4 ? c : 0];
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            // masked bf16 pairs: columns past the row contribute 0 * w
+            const uint32_t x0 = xb[i].x & ok[i], x1 = xb[i].y & ok[i];
+            acc[tt] = fmaf(__uint_as_float(x0 << 16), w[i].x, acc[tt]);
+            acc[tt] = fmaf(__uint_as_float(x0 & 0xFFFF0000u), w[i].y, acc[tt]);
+            acc[tt] = fmaf(__uint_as_float(x1 << 16), w[i].z, acc[tt]);
+            acc[tt] = fmaf(__uint_as_float(x1 & 0xFFFF0000u), w[i].w, acc[tt]);
           }
         }
       }
@@ -166,6 +170,19 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
     if (tid < nt) a.logits[int64_t(t0 + tid) * a.E + e] =
         ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) + bias;
     __syncthreads();
+  }
+
+  {
+    float v[4] = {__uint_as_float(qraw.x << 16), __uint_as_float(qraw.x & 0xFFFF0000u),
+                  __uint_as_float(qraw.y << 16), __uint_as_float(qraw.y & 0xFFFF0000u)};
+    const float amax = group_max<8>(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    const int ex = mx8_block_exp(amax);
+    const float sc = exp2_int(-ex);
+    const uint32_t wq = e4m3_cvt4(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
+    if (qok) {
+      *reinterpret_cast<uint32_t*>(a.x_codes + int64_t(qt) * d + qc * 32 + 4 * qj) = wq;
+      if (qj == 0) a.x_scales[int64_t(qt) * nb + qc] = static_cast<uint8_t>(ex + 127);
+    }
   }
 }
 
@@ -377,14 +394,20 @@ __device__ __forceinline__ float order_key_to_float(uint32_t key) {
 //    remaining places in ascending expert order (ties -> lower index).
 // With s_ids non-null the chosen ids are also stored there (LDS, [t*k + j]).
 __device__ void topk_token(const FwdArgs& a, int t, int lane, uint2* cand, int* s_ids = nullptr) {
+  // t is the same in every lane: saying so keeps the buffer resource in
+  // scalar registers, so the 16 loads below go out together (a lane-varying
+  // resource would get one waterfall loop with a full wait per load)
+  t = __builtin_amdgcn_readfirstlane(t);
   const __amdgpu_buffer_rsrc_t rl =
       __builtin_amdgcn_make_buffer_rsrc(a.logits + int64_t(t) * a.E, static_cast<short>(0), a.E * 4, 0x00020000);
+  // every load is issued before any is used (offsets past the row read 0
+  // through the resource's bound); slots past E get key 0
   uint32_t key[kMaxSlots];
 #pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) {
-    const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * (lane + 64 * i), 0, 0));
-    key[i] = (lane + 64 * i < a.E) ? float_order_key(v) : 0u;
-  }
+  for (int i = 0; i < kMaxSlots; ++i) key[i] = __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * (lane + 64 * i), 0, 0);
+#pragma unroll
+  for (int i = 0; i < kMaxSlots; ++i)
+    key[i] = float_order_key(__builtin_bit_cast(float, key[i])) & (lane + 64 * i < a.E ? ~0u : 0u);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t lmax = 0;
 #pragma unroll
@@ -801,33 +824,35 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   float r[C], sh[C];
 #pragma unroll
   for (int q = 0; q < C; ++q) r[q] = sh[q] = 0.f;
+  // Every load is issued unconditionally (slots past k re-read slot 0 with
+  // weight 0, shared experts past S re-read the last one, masked to 0), so
+  // the 16 + 8 loads go out together instead of one branch and one full wait
+  // per load.
   for (int j0 = 0; j0 < a.k; j0 += 16) {
     float v[16][C];
     float w[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (j0 + u < a.k) {
-        load(O16 ? int64_t(t) * a.k + j0 + u : int64_t(trow[j0 + u]), v[u]);
-        w[u] = tw[j0 + u];
-      }
+    for (int u = 0; u < 16; ++u) {
+      const bool ok = j0 + u < a.k;
+      const int j = ok ? j0 + u : 0;
+      load(O16 ? int64_t(t) * a.k + j : int64_t(trow[j]), v[u]);
+      w[u] = __uint_as_float(__float_as_uint(tw[j]) & (ok ? ~0u : 0u));
+    }
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      if (j0 + u < a.k) {
 #pragma unroll
-        for (int q = 0; q < C; ++q) r[q] = fmaf(w[u], v[u][q], r[q]);
-      }
+      for (int q = 0; q < C; ++q) r[q] = fmaf(w[u], v[u][q], r[q]);
   }
-  {
+  if (a.S > 0) {
     float v[8][C];
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      if (s < a.S) load(int64_t(a.Rr + s * a.T + t), v[s]);
+    for (int s = 0; s < 8; ++s) load(int64_t(a.Rr + (s < a.S ? s : a.S - 1) * a.T + t), v[s]);
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      if (s < a.S) {
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t m = s < a.S ? ~0u : 0u;
 #pragma unroll
-        for (int q = 0; q < C; ++q) sh[q] += v[s][q];
-      }
+      for (int q = 0; q < C; ++q) sh[q] += __uint_as_float(__float_as_uint(v[s][q]) & m);
+    }
   }
   uint32_t yb[C / 2];
 #pragma unroll

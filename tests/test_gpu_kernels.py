@@ -281,3 +281,54 @@ def test_deterministic_and_workspace_independent():
     c = P.run_gpu(cfg, W, x, taps=True, workspace_fill=0x5A)["y"]
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [1, 40])
+def test_graph_replay_matches_eager(T):
+    # a captured forward (T = 1: few-token router with the fused x
+    # quantisation and the one-workgroup top-k/permutation; T = 40: MFMA
+    # router, top-k launch, permutation launch) replays several times, with
+    # eager forwards of other inputs in between, and every replay equals the
+    # eager result bit for bit
+    from mxfp4_expert_grouped_amd.layer import MoeLayer
+    cfg = I.LayerConfig("graph", T, 256, 16, 2, 128, 2, seed=20 + T)
+    W = P.IG.device_weights(cfg)
+    layer = MoeLayer(cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k, cfg.num_shared, T, W)
+    xs = [P.IG.device_x(cfg, layer=i) for i in range(2)]
+    ws = torch.empty(layer.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    refs = [layer.forward(x, workspace=ws).clone() for x in xs]
+    torch.cuda.synchronize()
+    assert not torch.equal(refs[0].view(torch.int16), refs[1].view(torch.int16))
+    x_static = xs[0].clone()
+    y_static = torch.empty_like(x_static)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward(x_static, y=y_static, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x_static, y=y_static, workspace=ws)
+    y_eager = torch.empty_like(x_static)
+    for i in range(4):
+        x_static.copy_(xs[i % 2])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_static.view(torch.int16), refs[i % 2].view(torch.int16)), f"replay {i}"
+        layer.forward(xs[(i + 1) % 2], y=y_eager, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y_eager.view(torch.int16), refs[(i + 1) % 2].view(torch.int16)), f"eager {i}"
+
+
+def test_forward_on_a_non_default_caller_stream():
+    # every launch of the forward goes to the caller's stream
+    cfg = I.LayerConfig("stream", 3, 256, 16, 2, 128, 2, seed=31)
+    W = P.IG.device_weights(cfg)
+    x = P.IG.device_x(cfg)
+    ref = P.run_gpu(cfg, W, x, taps=False)["y"]
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        got = P.run_gpu(cfg, W, x, taps=False)["y"]
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
