@@ -481,26 +481,32 @@ constexpr int kPfLds = 3 * kPfSlot;            // 156672 bytes
 __shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 
 
-// Work order of the prefill GEMMs: items (tile, column block) in tile order
-// (tiles are expert-major), cut into 8 contiguous ranges, one per XCD
-// (workgroups go to the XCDs round-robin by linear id).  Items run in groups
-// of kPfGroupTiles consecutive tiles, column block next and tile fastest, so
-// the workgroups an XCD runs at once cover a few tiles x several column
-// blocks: every activation window and every weight window they read in the
-// same K step is shared by several of them and comes from that XCD's L2.
-// The mapping needs only the tile count.  Returns false for a workgroup with
-// no item.
+// Work order of the prefill GEMMs.  Items (tile, column block) run in groups
+// of kPfGroupTiles consecutive tiles (tiles are expert-major), column block
+// next and tile fastest, so the workgroups an XCD runs at once cover a few
+// tiles x several column blocks: every activation window and every weight
+// window they read in the same K step is shared by several of them and comes
+// from that XCD's L2.  Whole groups are dealt to the XCDs round-robin
+// (workgroups go to the XCDs round-robin by linear id), taken alternately
+// from the two ends of the group list: the first, the last, the second, ...
+// With skewed routing the list starts with the busiest experts (full tiles,
+// MFMA-bound) and ends with experts of a few rows (one mostly empty tile that
+// streams a whole weight tile, HBM-bound); alternating spreads the two kinds
+// over all XCDs and over the run, so the weight streaming of the sparse
+// tiles overlaps the MFMA work of the full ones.  The mapping needs only the
+// tile count.  Returns false for a workgroup with no item.
 constexpr int kPfGroupTiles = 4;
 __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int* tile_out, int* blk_out) {
   const int ntiles = *a.tile_count;
-  const int total = ntiles * nblocks;
-  const int per_xcd = (total + 7) / 8;
+  const int ngroups = (ntiles + kPfGroupTiles - 1) / kPfGroupTiles;
   const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
-  const int w = xcd * per_xcd + i;
-  if (i >= per_xcd || w >= total) return false;
-  const int tg = w / (kPfGroupTiles * nblocks);                // tile group
+  const int gitems = kPfGroupTiles * nblocks;                  // items of a full group
+  const int j = i / gitems, rem = i - j * gitems;
+  const int p = 8 * j + xcd;                                   // place in the alternating order
+  if (p >= ngroups) return false;
+  const int tg = (p & 1) ? ngroups - 1 - (p >> 1) : (p >> 1);  // tile group
   const int gsize = min(kPfGroupTiles, ntiles - tg * kPfGroupTiles);
-  const int rem = w - tg * kPfGroupTiles * nblocks;
+  if (rem >= gsize * nblocks) return false;
   *blk_out = rem / gsize;
   *tile_out = tg * kPfGroupTiles + rem % gsize;
   return true;
@@ -871,9 +877,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 template <bool GU>
 static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
   const int64_t N = GU ? a.dff / 128 : a.d / 256;
-  const int64_t items = int64_t(a.max_tiles) * N;
+  // room for the most groups one XCD can get (the tile count is known on the
+  // device only; max_tiles bounds it)
+  const int64_t max_groups = (int64_t(a.max_tiles) + kPfGroupTiles - 1) / kPfGroupTiles;
+  const int64_t per_xcd = (max_groups + 7) / 8 * kPfGroupTiles * N;
   const int K = GU ? a.d : a.dff;
-  const dim3 grid(8 * ((items + 7) / 8));
+  const dim3 grid(static_cast<unsigned>(8 * per_xcd));
   if (K % 512 == 0)
     hipLaunchKernelGGL((k_gemm_pf<GU, true>), grid, dim3(256), 0, st, a);
   else
