@@ -486,15 +486,15 @@ __shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 // next and tile fastest, so the workgroups an XCD runs at once cover a few
 // tiles x several column blocks: every activation window and every weight
 // window they read in the same K step is shared by several of them and comes
-// from that XCD's L2.  Whole groups are dealt to the XCDs round-robin
-// (workgroups go to the XCDs round-robin by linear id), taken alternately
-// from the two ends of the group list: the first, the last, the second, ...
-// With skewed routing the list starts with the busiest experts (full tiles,
-// MFMA-bound) and ends with experts of a few rows (one mostly empty tile that
-// streams a whole weight tile, HBM-bound); alternating spreads the two kinds
-// over all XCDs and over the run, so the weight streaming of the sparse
-// tiles overlaps the MFMA work of the full ones.  The mapping needs only the
-// tile count.  Returns false for a workgroup with no item.
+// from that XCD's L2.  Whole groups are dealt to the XCDs round-robin in list
+// order (workgroups go to the XCDs round-robin by linear id), so at any time
+// the eight XCDs work on neighbouring groups -- mostly the same expert, whose
+// weight tiles they then share through the memory-side cache -- and the
+// sparse tiles of lightly loaded experts are spread over all XCDs instead of
+// piling up on the last ones (measured faster than cutting the list into
+// eight contiguous ranges, and than taking groups alternately from its two
+// ends).  The mapping needs only the tile count.  Returns false for a
+// workgroup with no item.
 constexpr int kPfGroupTiles = 4;
 __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int* tile_out, int* blk_out) {
   const int ntiles = *a.tile_count;
@@ -502,9 +502,8 @@ __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int*
   const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
   const int gitems = kPfGroupTiles * nblocks;                  // items of a full group
   const int j = i / gitems, rem = i - j * gitems;
-  const int p = 8 * j + xcd;                                   // place in the alternating order
-  if (p >= ngroups) return false;
-  const int tg = (p & 1) ? ngroups - 1 - (p >> 1) : (p >> 1);  // tile group
+  const int tg = 8 * j + xcd;                                  // tile group
+  if (tg >= ngroups) return false;
   const int gsize = min(kPfGroupTiles, ntiles - tg * kPfGroupTiles);
   if (rem >= gsize * nblocks) return false;
   *blk_out = rem / gsize;
