@@ -205,13 +205,18 @@ typedef float v16f_r __attribute__((ext_vector_type(16)));
 constexpr int kRtRow = 80;                   // bytes per LDS row (32 bf16 + pad)
 constexpr int kRtPlane = 128 * kRtRow;       // one 128-row operand plane
 constexpr int kRtStage = 4 * kRtPlane;       // x, w_hi, w_mid, w_lo
+constexpr int kRtDepth = 4;                  // K steps in flight (register sets)
+template <int N>
+struct RtSlot {
+  static constexpr int value = N;
+};
 
 __device__ __forceinline__ uint32_t pack_bf16_hi(float a, float b) {
   // upper halves of two floats whose low 16 bits are zero: (b, a) bf16 pair
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
 }
 
-__global__ void __launch_bounds__(256) k_router_mfma(FwdArgs a) {
+__global__ void __launch_bounds__(256, 1) k_router_mfma(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kRtStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -224,25 +229,34 @@ __global__ void __launch_bounds__(256) k_router_mfma(FwdArgs a) {
   const int lr = tid >> 1, lk = 16 * (tid & 1);
   const uint16_t* xp = a.x + int64_t(min(t0 + lr, a.T - 1)) * a.d + kb + lk;
   const float* wp = a.wr + int64_t(min(e0 + lr, a.E - 1)) * a.d + kb + lk;
-  uint4 xr[2];
-  float4 wr4[4];
-  auto load = [&](int st) {
-    const uint4* xs = reinterpret_cast<const uint4*>(xp + 32 * st);
-    xr[0] = xs[0];
-    xr[1] = xs[1];
-    const float4* ws = reinterpret_cast<const float4*>(wp + 32 * st);
+  // kRtDepth register sets: step st's global loads go out kRtDepth - 1 steps
+  // before its data is split and stored to LDS (one step ahead left the load
+  // latency exposed at every step)
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  typedef float v4f_r __attribute__((ext_vector_type(4)));
+  v4u xr[kRtDepth][2];
+  v4f_r wr4[kRtDepth][4];
+  auto load = [&](int st, auto S) __attribute__((always_inline)) {
+    constexpr int slot = decltype(S)::value;
+    const v4u* xs = reinterpret_cast<const v4u*>(xp + 32 * st);
+    xr[slot][0] = xs[0];
+    xr[slot][1] = xs[1];
+    const v4f_r* ws = reinterpret_cast<const v4f_r*>(wp + 32 * st);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wr4[q] = ws[q];
+    for (int q = 0; q < 4; ++q) wr4[slot][q] = ws[q];
   };
-  // split the weights into three bf16 planes and store the step to LDS buffer b
-  auto store = [&](int b) {
+  // split the weights of register set `slot` into three bf16 planes and store
+  // the step to LDS buffer b
+  auto store = [&](int b, auto S) __attribute__((always_inline)) {
+    constexpr int slot = decltype(S)::value;
     uint8_t* base = lds + b * kRtStage + lr * kRtRow + 2 * lk;
-    *reinterpret_cast<uint4*>(base) = xr[0];
-    *reinterpret_cast<uint4*>(base + 16) = xr[1];
+    *reinterpret_cast<v4u*>(base) = xr[slot][0];
+    *reinterpret_cast<v4u*>(base + 16) = xr[slot][1];
     float w[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      w[4 * q] = wr4[q].x; w[4 * q + 1] = wr4[q].y; w[4 * q + 2] = wr4[q].z; w[4 * q + 3] = wr4[q].w;
+      w[4 * q] = wr4[slot][q].x; w[4 * q + 1] = wr4[slot][q].y;
+      w[4 * q + 2] = wr4[slot][q].z; w[4 * q + 3] = wr4[slot][q].w;
     }
     uint32_t hi[8], mid[8], lo[8];
 #pragma unroll
@@ -278,7 +292,7 @@ __global__ void __launch_bounds__(256) k_router_mfma(FwdArgs a) {
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f_r{};
   // fragment lane: row l%32 of a 32-row block, K elements 8(l/32) .. +7 of a 16-chunk
   const int frag = (lane & 31) * kRtRow + 16 * (lane >> 5);
-  auto compute = [&](int b) {
+  auto compute = [&](int b) __attribute__((always_inline)) {
     const uint8_t* base = lds + b * kRtStage;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -303,16 +317,35 @@ __global__ void __launch_bounds__(256) k_router_mfma(FwdArgs a) {
   };
 
   if (nsteps > 0) {
-    load(0);
-    store(0);
+    // steps 0 .. kRtDepth-2 in flight; step s lives in register set s % kRtDepth
+    load(0, RtSlot<0>{});
+    load(min(1, nsteps - 1), RtSlot<1>{});
+    load(min(2, nsteps - 1), RtSlot<2>{});
+    store(0, RtSlot<0>{});
     __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-      const int cur = st & 1;
-      if (st + 1 < nsteps) load(st + 1);
-      compute(cur);
-      if (st + 1 < nsteps) store(cur ^ 1);
+    // one step; U (a compile-time constant) picks the register sets
+    auto step = [&](int st, auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      // past the last step the last one is loaded again (never stored)
+      load(min(st + kRtDepth - 1, nsteps - 1), RtSlot<(u + kRtDepth - 1) % kRtDepth>{});
+      compute(st & 1);
+      if (st + 1 < nsteps) store((st + 1) & 1, RtSlot<(u + 1) % kRtDepth>{});
       __syncthreads();
+    };
+    static_assert(kRtDepth == 4, "the step sequence below is written for four register sets");
+    // whole groups of four steps without conditions (conditional copies of
+    // the step were merged by the compiler into one with a run-time register
+    // set, i.e. private memory), then at most three more
+    int st0 = 0;
+    for (; st0 + kRtDepth <= nsteps; st0 += kRtDepth) {
+      step(st0, RtSlot<0>{});
+      step(st0 + 1, RtSlot<1>{});
+      step(st0 + 2, RtSlot<2>{});
+      step(st0 + 3, RtSlot<3>{});
     }
+    if (st0 < nsteps) step(st0, RtSlot<0>{});  // conditions are the same in every lane
+    if (st0 + 1 < nsteps) step(st0 + 1, RtSlot<1>{});
+    if (st0 + 2 < nsteps) step(st0 + 2, RtSlot<2>{});
   }
 
   // acc[i][j] register r: token 64wm + 32i + 8(r/4) + 4(lane/32) + r%4,
