@@ -210,6 +210,14 @@ template <int N>
 struct RtSlot {
   static constexpr int value = N;
 };
+// f(RtSlot<B>{}), ..., f(RtSlot<E-1>{})
+template <int B, int E, typename F>
+__device__ __forceinline__ void rt_for(F&& f) {
+  if constexpr (B < E) {
+    f(RtSlot<B>{});
+    rt_for<B + 1, E>(f);
+  }
+}
 
 __device__ __forceinline__ uint32_t pack_bf16_hi(float a, float b) {
   // upper halves of two floats whose low 16 bits are zero: (b, a) bf16 pair
@@ -318,9 +326,7 @@ __global__ void __launch_bounds__(256, 1) k_router_mfma(FwdArgs a) {
 
   if (nsteps > 0) {
     // steps 0 .. kRtDepth-2 in flight; step s lives in register set s % kRtDepth
-    load(0, RtSlot<0>{});
-    load(min(1, nsteps - 1), RtSlot<1>{});
-    load(min(2, nsteps - 1), RtSlot<2>{});
+    rt_for<0, kRtDepth - 1>([&](auto U) { load(min(decltype(U)::value, nsteps - 1), U); });
     store(0, RtSlot<0>{});
     __syncthreads();
     // one step; U (a compile-time constant) picks the register sets
@@ -332,20 +338,15 @@ __global__ void __launch_bounds__(256, 1) k_router_mfma(FwdArgs a) {
       if (st + 1 < nsteps) store((st + 1) & 1, RtSlot<(u + 1) % kRtDepth>{});
       __syncthreads();
     };
-    static_assert(kRtDepth == 4, "the step sequence below is written for four register sets");
-    // whole groups of four steps without conditions (conditional copies of
-    // the step were merged by the compiler into one with a run-time register
-    // set, i.e. private memory), then at most three more
+    // whole groups of kRtDepth steps without conditions (conditional copies
+    // of the step were merged by the compiler into one with a run-time
+    // register set, i.e. private memory), then at most kRtDepth - 1 more
     int st0 = 0;
-    for (; st0 + kRtDepth <= nsteps; st0 += kRtDepth) {
-      step(st0, RtSlot<0>{});
-      step(st0 + 1, RtSlot<1>{});
-      step(st0 + 2, RtSlot<2>{});
-      step(st0 + 3, RtSlot<3>{});
-    }
-    if (st0 < nsteps) step(st0, RtSlot<0>{});  // conditions are the same in every lane
-    if (st0 + 1 < nsteps) step(st0 + 1, RtSlot<1>{});
-    if (st0 + 2 < nsteps) step(st0 + 2, RtSlot<2>{});
+    for (; st0 + kRtDepth <= nsteps; st0 += kRtDepth)
+      rt_for<0, kRtDepth>([&](auto U) { step(st0 + decltype(U)::value, U); });
+    rt_for<0, kRtDepth - 1>([&](auto U) {  // conditions are the same in every lane
+      if (st0 + decltype(U)::value < nsteps) step(st0 + decltype(U)::value, U);
+    });
   }
 
   // acc[i][j] register r: token 64wm + 32i + 8(r/4) + 4(lane/32) + r%4,

@@ -243,6 +243,14 @@ def test_ragged_token_counts(T):
     _layer_case(cfg, tokens=tokens)
 
 
+def test_prefill_tiles_over_many_groups():
+    # 256-row tiles (about 130 rows per expert): 63 routed tiles + 8 shared
+    # ones = 71 tiles, i.e. 18 groups of up to four tiles dealt to the eight
+    # XCDs, the last group partial; two column blocks in both GEMMs
+    cfg = I.LayerConfig("groups", 2048, 512, 63, 4, 256, 1, seed=41)
+    _layer_case(cfg, tokens=list(range(0, 2048, 37)) + [2047])
+
+
 def test_medium_layer_k4_two_shared():
     cfg = I.LayerConfig("mid", 96, 1024, 32, 4, 512, 2, seed=7)
     _layer_case(cfg)
