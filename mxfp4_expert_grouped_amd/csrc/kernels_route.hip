@@ -101,6 +101,8 @@ hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t 
 // loads in flight per thread) once per 8 tokens.  The same launch quantises x
 // to MXFP8: workgroup e handles activation blocks e, e + E, e + 2E, ...
 
+typedef float v4f_nt __attribute__((ext_vector_type(4)));
+
 __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
   __shared__ float part[4][8];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -133,7 +135,9 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
       for (int i = 0; i < 8; ++i) {
         const int c = base + tid + 256 * i;
         ok[i] = c < n4 ? ~0u : 0u;
-        w[i] = w4[c < n4 ? c : 0];
+        // router weights are read once per forward: non-temporal
+        const v4f_nt wv = __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(w4 + (c < n4 ? c : 0)));
+        w[i] = make_float4(wv.x, wv.y, wv.z, wv.w);
       }
       if (t0 == 0 && base == 0)
         qraw = *reinterpret_cast<const uint2*>(a.x + int64_t(qt) * d + qc * 32 + 4 * qj);
