@@ -837,6 +837,8 @@ hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
 // and summed in slot order, then the shared rows.  The decode kernels leave
 // o in permuted-row order (found through token_row); the prefill kernels
 // store it in (token, slot) order, so a token's k rows are contiguous.
+typedef uint32_t v4u_nt __attribute__((ext_vector_type(4)));
+
 template <bool O16>
 __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   constexpr int C = O16 ? 8 : 4;
@@ -844,8 +846,9 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   const int c = blockIdx.y * 64 + threadIdx.x;  // column group
   if (c >= a.d / C) return;
   auto load = [&](int64_t row, float* v) {
+    // o rows are read once: non-temporal loads
     if (O16) {
-      const uint4 u = reinterpret_cast<const uint4*>(a.o16 + row * a.d)[c];
+      const v4u_nt u = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt*>(a.o16 + row * a.d) + c);
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -853,7 +856,7 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
         v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
       }
     } else {
-      const float4 f = reinterpret_cast<const float4*>(a.o + row * a.d)[c];
+      const v4f_nt f = __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(a.o + row * a.d) + c);
       v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     }
   };
