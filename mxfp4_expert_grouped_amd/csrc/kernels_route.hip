@@ -97,9 +97,10 @@ hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t 
 // Router logits  l[t][e] = sum_i x[t][i] W_r[e][i] + b[e]   (fp32 accumulate)
 // ---------------------------------------------------------------------------
 
-// Few tokens: one 256-thread workgroup per expert streams its W_r row (8 float4
-// loads in flight per thread) once per 8 tokens.  The same launch quantises x
-// to MXFP8: workgroup e handles activation blocks e, e + E, e + 2E, ...
+// Few tokens: one 256-thread workgroup per expert streams its W_r row (up to 8
+// float4 loads in flight per thread, non-temporal: read once per forward) once
+// per 8 tokens.  The same launch quantises x to MXFP8: workgroup e takes the
+// 32 consecutive activation blocks 32e .. 32e+31 of all T*d/32.
 
 typedef float v4f_nt __attribute__((ext_vector_type(4)));
 
