@@ -539,6 +539,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   int tile_idx, nblk;
   if (!pf_work_item(a, GU ? a.dff / 128 : a.d / 256, &tile_idx, &nblk)) return;
   const Tile tile = a.tiles[tile_idx];
+  // the tile's expert has no other tile: its weights are read once
+  const bool w_once = a.ex_tiles[tile.ex + 1] - a.ex_tiles[tile.ex] == 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, g32 = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy of the wave index
@@ -595,13 +597,19 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
     lds_copy16(a_src[q] + 128 * ss, lds0 + (st % 3) * kPfSlot + kPfA + (64 * wu + 8 * q) * 128);
   };
   // item m of step st; GS: st starts a group of four steps
-  auto copy_w = [&](int st, auto mc, auto gsc) {
+  // WNT: the weights are read by this tile only (its expert has one tile),
+  // so their copies carry the non-temporal hint; an expert with several tiles
+  // keeps its weight tiles cacheable for the others
+  auto copy_w = [&](int st, auto mc, auto gsc, auto wntc) {
+    constexpr bool WNT = decltype(wntc)::value != 0;
     constexpr int m = decltype(mc)::value;
     constexpr bool GS = decltype(gsc)::value != 0;
     const int ss = st < nsteps ? st : 0;
     const uint32_t slot = lds0 + (st % 3) * kPfSlot;
-    if constexpr (m < 4) lds_copy16(b_src + ss * 4096 + m * 1024, slot + kPfB + (4 * wu + m) * 1024);
-    if constexpr (m == 4) lds_copy4(bs_src + ss * 256, slot + kPfBS + wu * 256);
+    if constexpr (m < 4 && WNT) lds_copy16_nt(b_src + ss * 4096 + m * 1024, slot + kPfB + (4 * wu + m) * 1024);
+    if constexpr (m < 4 && !WNT) lds_copy16(b_src + ss * 4096 + m * 1024, slot + kPfB + (4 * wu + m) * 1024);
+    if constexpr (m == 4 && WNT) lds_copy4_nt(bs_src + ss * 256, slot + kPfBS + wu * 256);
+    if constexpr (m == 4 && !WNT) lds_copy4(bs_src + ss * 256, slot + kPfBS + wu * 256);
     if constexpr (m == 5 && !AG) lds_copy4(as_src + 4 * ss, slot + kPfAS + wu * 256);
     if constexpr (m == 5 && AG && GS) lds_copy16(as_src + 16 * (ss >> 2), lds0 + pf_asg_off(wu));
   };
@@ -634,7 +642,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[i][p] = v16f{};
 
-  auto main_loop = [&](auto nact_c) {
+  auto main_loop = [&](auto nact_c, auto wnt_c) {
     constexpr int NACT = decltype(nact_c)::value;
     uint4 asg[4];               // grouped activation scales of this lane's rows
     uint32_t asr[2][4];         // A scale dwords (shifted by 8*g32) of the current / next step
@@ -719,7 +727,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
           if constexpr (k / 2 < 4) read_a(s0, IntC<1>{}, IntC<k / 2>{});
           else read_b(s0, IntC<1>{}, IntC<k / 2 - 4>{});
         } else if constexpr (k / 2 < 6) {
-          copy_w(st + 2, IntC<k / 2>{}, IntC<((I + 2) & 3) == 0>{});
+          copy_w(st + 2, IntC<k / 2>{}, IntC<((I + 2) & 3) == 0>{}, wnt_c);
         }
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -754,9 +762,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
     // prologue: steps 0 and 1, and the activation copies of step 2 (its
     // weight copies come in step 0)
     static_for<0, 8>([&](auto qc) { copy_a(0, qc); });
-    static_for<0, 6>([&](auto mc) { copy_w(0, mc, IntC<1>{}); });
+    static_for<0, 6>([&](auto mc) { copy_w(0, mc, IntC<1>{}, wnt_c); });
     static_for<0, 8>([&](auto qc) { copy_a(1, qc); });
-    static_for<0, 6>([&](auto mc) { copy_w(1, mc, IntC<0>{}); });
+    static_for<0, 6>([&](auto mc) { copy_w(1, mc, IntC<0>{}, wnt_c); });
     static_for<0, 8>([&](auto qc) { copy_a(2, qc); });
     PF_WAIT_VM(ncop(1) + 8);                   // step 0 has landed
     __builtin_amdgcn_sched_barrier(0);
@@ -785,11 +793,11 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
     }
   };
   switch (nact) {
-    case 4: main_loop(IntC<4>{}); break;
-    case 3: main_loop(IntC<3>{}); break;
-    case 2: main_loop(IntC<2>{}); break;
-    case 1: main_loop(IntC<1>{}); break;
-    default: main_loop(IntC<0>{}); break;
+    case 4: w_once ? main_loop(IntC<4>{}, IntC<1>{}) : main_loop(IntC<4>{}, IntC<0>{}); break;
+    case 3: w_once ? main_loop(IntC<3>{}, IntC<1>{}) : main_loop(IntC<3>{}, IntC<0>{}); break;
+    case 2: w_once ? main_loop(IntC<2>{}, IntC<1>{}) : main_loop(IntC<2>{}, IntC<0>{}); break;
+    case 1: w_once ? main_loop(IntC<1>{}, IntC<1>{}) : main_loop(IntC<1>{}, IntC<0>{}); break;
+    default: main_loop(IntC<0>{}, IntC<0>{}); break;
   }
 
   // ---- epilogue through LDS: after this wave's last copies have landed and
