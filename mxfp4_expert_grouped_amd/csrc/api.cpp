@@ -119,7 +119,7 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.ex_tiles = take((E + S + 1) * 4);
   L.h_codes = take(R * f);
   L.h_scales = take(R * f / 32);
-  L.o = take(R * d * (L.bm <= kDecodeMaxRows ? 4 : 2));
+  L.o = take(R * d * 2);
   L.total = off;
   return L;
 }
@@ -318,7 +318,6 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
   a.ex_tiles = reinterpret_cast<int32_t*>(ws + L.ex_tiles);
   a.h_codes = pick(tp.h_codes, L.h_codes, static_cast<uint8_t*>(nullptr));
   a.h_scales = pick(tp.h_scales, L.h_scales, static_cast<uint8_t*>(nullptr));
-  a.o = reinterpret_cast<float*>(ws + L.o);
   a.o16 = reinterpret_cast<uint16_t*>(ws + L.o);
   a.gu_acc = tp.gu_acc;
   a.y_routed = tp.y_routed;

@@ -45,8 +45,8 @@ struct FwdArgs {
   int32_t* ex_tiles;    // [E+S+1] first tile of each expert (prefix over tile counts)
   uint8_t* h_codes;     // [R][dff]
   uint8_t* h_scales;    // [R][dff/32]
-  float* o;             // [R][d] fp32 (16-row tiles)
-  uint16_t* o16;        // [R][d] bf16 (128-row tiles); same workspace region as o
+  uint16_t* o16;        // [R][d] bf16 down outputs: permuted-row order after the
+                        // decode kernels, (token, slot) order after the prefill ones
   // optional taps (null = skip)
   float* gu_acc;        // [R][2*dff]
   float* y_routed;      // [T][d]

@@ -160,6 +160,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   constexpr int WAVE = S * SLOT, FIFO = 4 * WAVE;
   static_assert(FIFO + 4 * 8 * 16 <= kDsLds, "ring does not fit");
   static_assert(!(WIDE && (GU || KSPLIT)), "wide items are for the down GEMM");
+  static_assert(GU || !KSPLIT, "the K split is for the gate_up GEMM");
   const int lane = threadIdx.x & 63;
   const int wu = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int g = lane >> 4, r16 = lane & 15;
@@ -329,22 +330,35 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
       if (col == 0) a.h_scales[int64_t(row) * (a.dff / 32) + G] = static_cast<uint8_t>(e + 127);
     }
   };
-  auto item_end = [&](int il) {
+  auto item_end = [&](int il, int el_last) {
     if (!KSPLIT) {
       // whole item in this wave: lane l holds rows 4(l/16) + i, column l%16
       const int* md = fifo_ep + (il & 7) * 4;
       const int t_rb = md[1], t_re = md[2], G = md[3];
+      if (GU) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = t_rb + 4 * g + i;
-        const bool valid = row < t_re;
-        if (GU) {
+        for (int i = 0; i < 4; ++i) {
+          const int row = t_rb + 4 * g + i;
           float v[4] = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-          gu_epilogue(v, row, valid, G, r16);
-        } else if (valid) {
-          float* orow = a.o + int64_t(row) * a.d + 64 * GPI * G + r16;
+          gu_epilogue(v, row, row < t_re, G, r16);
+        }
+      } else {
+        // o rows [8][64*GPI] as bf16 (RNE), staged in the slot of the item's
+        // last element (no copy lands there before the next element is
+        // issued) and written in 16-byte chunks of 8 columns
+        constexpr int OC = 64 * GPI;
+        uint16_t* stg = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(wlds) + (el_last % S) * SLOT);
 #pragma unroll
-          for (int j = 0; j < 4 * GPI; ++j) orow[16 * j] = acc[j][i];
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4 * GPI; ++j) stg[(4 * g + i) * OC + 16 * j + r16] = f32_to_bf16_rne(acc[j][i]);
+#pragma unroll
+        for (int q = 0; q < GPI; ++q) {
+          const int ch = 64 * q + lane;             // chunk: row ch / (OC/8), columns 8 (ch % (OC/8))
+          const int rl = ch / (OC / 8), c8 = ch - rl * (OC / 8);
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + rl * OC + 8 * c8);
+          if (t_rb + rl < t_re)
+            *reinterpret_cast<uint4*>(a.o16 + int64_t(t_rb + rl) * a.d + OC * G + 8 * c8) = v;
         }
       }
 #pragma unroll
@@ -371,14 +385,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
         for (int w = 0; w < 4; ++w) sum += part_slot(w, il)[j * 64 + 16 * wu + col][i];
         v[j] = sum;
       }
-      const bool valid = row < t_re;
-      if (GU) {
-        gu_epilogue(v, row, valid, G, col);
-      } else if (valid) {
-        float* orow = a.o + int64_t(row) * a.d + 64 * G + col;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) orow[16 * j] = v[j];
-      }
+      gu_epilogue(v, row, row < t_re, G, col);
     }
     __syncthreads();  // the parked partials are read: their slots may be refilled
   };
@@ -403,7 +410,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
       asm volatile("" ::: "memory");
       compute(el);
     }
-    item_end(il);
+    item_end(il, el - 1);
   }
 }
 

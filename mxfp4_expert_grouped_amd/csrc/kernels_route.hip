@@ -832,33 +832,27 @@ hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
 // (fixed order: slots ascending = expert id ascending, then shared experts)
 // ---------------------------------------------------------------------------
 
-// One thread per C output columns of one token (C = 4 for the fp32 o of the
-// decode kernels, 8 for the bf16 o of the prefill kernels: 16-byte loads
-// either way); the k expert rows are read in batches of 16 loads in flight
-// and summed in slot order, then the shared rows.  The decode kernels leave
-// o in permuted-row order (found through token_row); the prefill kernels
-// store it in (token, slot) order, so a token's k rows are contiguous.
+// One thread per 8 output columns of one token (one 16-byte load of bf16 o
+// per row); the k expert rows are read in batches of 16 loads in flight and
+// summed in slot order, then the shared rows.  The decode kernels leave o in
+// permuted-row order (found through token_row); the prefill kernels store it
+// in (token, slot) order (TOKMAJOR), so a token's k rows are contiguous.
 typedef uint32_t v4u_nt __attribute__((ext_vector_type(4)));
 
-template <bool O16>
+template <bool TOKMAJOR>
 __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
-  constexpr int C = O16 ? 8 : 4;
+  constexpr int C = 8;
   const int t = blockIdx.x;
   const int c = blockIdx.y * 64 + threadIdx.x;  // column group
   if (c >= a.d / C) return;
   auto load = [&](int64_t row, float* v) {
     // o rows are read once: non-temporal loads
-    if (O16) {
-      const v4u_nt u = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt*>(a.o16 + row * a.d) + c);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const v4u_nt u = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt*>(a.o16 + row * a.d) + c);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[2 * q] = __uint_as_float(w[q] << 16);
-        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-      }
-    } else {
-      const v4f_nt f = __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(a.o + row * a.d) + c);
-      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
     }
   };
   const int* trow = a.token_row + int64_t(t) * a.k;
@@ -877,7 +871,7 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
     for (int u = 0; u < 16; ++u) {
       const bool ok = j0 + u < a.k;
       const int j = ok ? j0 + u : 0;
-      load(O16 ? int64_t(t) * a.k + j : int64_t(trow[j]), v[u]);
+      load(TOKMAJOR ? int64_t(t) * a.k + j : int64_t(trow[j]), v[u]);
       w[u] = __uint_as_float(__float_as_uint(tw[j]) & (ok ? ~0u : 0u));
     }
 #pragma unroll
@@ -901,8 +895,7 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   for (int q = 0; q < C / 2; ++q)
     yb[q] = uint32_t(f32_to_bf16_rne(r[2 * q] + sh[2 * q])) |
             (uint32_t(f32_to_bf16_rne(r[2 * q + 1] + sh[2 * q + 1])) << 16);
-  if (O16) reinterpret_cast<uint4*>(a.y + int64_t(t) * a.d)[c] = make_uint4(yb[0], yb[1], yb[2], yb[3]);
-  else reinterpret_cast<uint2*>(a.y + int64_t(t) * a.d)[c] = make_uint2(yb[0], yb[1]);
+  reinterpret_cast<uint4*>(a.y + int64_t(t) * a.d)[c] = make_uint4(yb[0], yb[1], yb[2], yb[3]);
   if (a.y_routed) {
     float4* yr = reinterpret_cast<float4*>(a.y_routed + int64_t(t) * a.d) + (C / 4) * c;
 #pragma unroll
@@ -916,11 +909,12 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
 }
 
 hipError_t launch_combine(const FwdArgs& a, hipStream_t st) {
-  // o rows are fp32 after the decode kernels, bf16 after the prefill ones
+  // o rows in (token, slot) order after the prefill kernels, in permuted-row
+  // order after the decode ones
   if (a.bm > kDecodeMaxRows)
     hipLaunchKernelGGL(k_combine<true>, dim3(a.T, (a.d / 8 + 63) / 64), dim3(64), 0, st, a);
   else
-    hipLaunchKernelGGL(k_combine<false>, dim3(a.T, (a.d / 4 + 63) / 64), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_combine<false>, dim3(a.T, (a.d / 8 + 63) / 64), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
