@@ -842,8 +842,12 @@ typedef uint32_t v4u_nt __attribute__((ext_vector_type(4)));
 template <bool TOKMAJOR>
 __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   constexpr int C = 8;
-  const int t = blockIdx.x;
-  const int c = blockIdx.y * 64 + threadIdx.x;  // column group
+  // workgroup = (token, 512-column block), blocks of a token adjacent: the
+  // workgroups in flight read whole o rows rather than one 1 KB piece of
+  // every row
+  const int nblk = (a.d / C + 63) / 64;
+  const int t = blockIdx.x / nblk;
+  const int c = (blockIdx.x - t * nblk) * 64 + threadIdx.x;  // column group
   if (c >= a.d / C) return;
   auto load = [&](int64_t row, float* v) {
     // o rows are read once: non-temporal loads
@@ -911,10 +915,11 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
 hipError_t launch_combine(const FwdArgs& a, hipStream_t st) {
   // o rows in (token, slot) order after the prefill kernels, in permuted-row
   // order after the decode ones
+  const unsigned grid = static_cast<unsigned>(a.T) * static_cast<unsigned>((a.d / 8 + 63) / 64);
   if (a.bm > kDecodeMaxRows)
-    hipLaunchKernelGGL(k_combine<true>, dim3(a.T, (a.d / 8 + 63) / 64), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_combine<true>, dim3(grid), dim3(64), 0, st, a);
   else
-    hipLaunchKernelGGL(k_combine<false>, dim3(a.T, (a.d / 8 + 63) / 64), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_combine<false>, dim3(grid), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
