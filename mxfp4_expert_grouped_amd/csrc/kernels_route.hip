@@ -839,7 +839,7 @@ hipError_t launch_permute(const FwdArgs& a, hipStream_t st) {
 // in (token, slot) order (TOKMAJOR), so a token's k rows are contiguous.
 typedef uint32_t v4u_nt __attribute__((ext_vector_type(4)));
 
-template <bool TOKMAJOR>
+template <bool TOKMAJOR, int NSH>
 __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   constexpr int C = 8;
   // workgroup = (token, 512-column block), blocks of a token adjacent: the
@@ -866,7 +866,7 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   for (int q = 0; q < C; ++q) r[q] = sh[q] = 0.f;
   // Every load is issued unconditionally (slots past k re-read slot 0 with
   // weight 0, shared experts past S re-read the last one, masked to 0), so
-  // the 16 + 8 loads go out together instead of one branch and one full wait
+  // the 16 + NSH loads go out together instead of one branch and one full wait
   // per load.
   for (int j0 = 0; j0 < a.k; j0 += 16) {
     float v[16][C];
@@ -884,11 +884,11 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
       for (int q = 0; q < C; ++q) r[q] = fmaf(w[u], v[u][q], r[q]);
   }
   if (a.S > 0) {
-    float v[8][C];
+    float v[NSH][C];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) load(int64_t(a.Rr + (s < a.S ? s : a.S - 1) * a.T + t), v[s]);
+    for (int s = 0; s < NSH; ++s) load(int64_t(a.Rr + (s < a.S ? s : a.S - 1) * a.T + t), v[s]);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < NSH; ++s) {
       const uint32_t m = s < a.S ? ~0u : 0u;
 #pragma unroll
       for (int q = 0; q < C; ++q) sh[q] += __uint_as_float(__float_as_uint(v[s][q]) & m);
@@ -916,10 +916,16 @@ hipError_t launch_combine(const FwdArgs& a, hipStream_t st) {
   // o rows in (token, slot) order after the prefill kernels, in permuted-row
   // order after the decode ones
   const unsigned grid = static_cast<unsigned>(a.T) * static_cast<unsigned>((a.d / 8 + 63) / 64);
-  if (a.bm > kDecodeMaxRows)
-    hipLaunchKernelGGL(k_combine<true>, dim3(grid), dim3(64), 0, st, a);
+  // shared rows: two loads cover the usual S <= 2, eight any S (unused
+  // ones re-read the last row and are masked)
+  if (a.bm > kDecodeMaxRows && a.S <= 2)
+    hipLaunchKernelGGL((k_combine<true, 2>), dim3(grid), dim3(64), 0, st, a);
+  else if (a.bm > kDecodeMaxRows)
+    hipLaunchKernelGGL((k_combine<true, 8>), dim3(grid), dim3(64), 0, st, a);
+  else if (a.S <= 2)
+    hipLaunchKernelGGL((k_combine<false, 2>), dim3(grid), dim3(64), 0, st, a);
   else
-    hipLaunchKernelGGL(k_combine<false>, dim3(grid), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((k_combine<false, 8>), dim3(grid), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -251,6 +251,14 @@ def test_prefill_tiles_over_many_groups():
     _layer_case(cfg, tokens=list(range(0, 2048, 37)) + [2047])
 
 
+@pytest.mark.parametrize("T", [5, 300])
+def test_more_than_two_shared_experts(T):
+    # the combine reads up to eight shared rows per token once S > 2; both
+    # the permuted-row (decode) and the (token, slot) (prefill) o layouts
+    cfg = I.LayerConfig("shared5", T, 256, 16, 2, 128, 5, seed=50 + T)
+    _layer_case(cfg, tokens=None if T <= 64 else list(range(0, T, 7)) + [T - 1])
+
+
 def test_medium_layer_k4_two_shared():
     cfg = I.LayerConfig("mid", 96, 1024, 32, 4, 512, 2, seed=7)
     _layer_case(cfg)
