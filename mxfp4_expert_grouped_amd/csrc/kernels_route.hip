@@ -847,51 +847,66 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   // every row
   const int nblk = (a.d / C + 63) / 64;
   const int t = blockIdx.x / nblk;
-  const int c = (blockIdx.x - t * nblk) * 64 + threadIdx.x;  // column group
-  if (c >= a.d / C) return;
-  auto load = [&](int64_t row, float* v) {
-    // o rows are read once: non-temporal loads
-    const v4u_nt u = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt*>(a.o16 + row * a.d) + c);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  const int cg = (blockIdx.x - t * nblk) * 64 + threadIdx.x;  // column group
+  // every lane stays to the end (lanes 0..15 hand the slot weights to the
+  // others); lanes past the row load column group 0 and store nothing
+  const bool live = cg < a.d / C;
+  const int c = live ? cg : 0;
+  // o rows are read once: non-temporal loads, kept raw until every load of
+  // the pass is out (a conversion right after each load would make the
+  // compiler wait on it)
+  auto load = [&](int64_t row) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4u_nt*>(a.o16 + row * a.d) + c);
+  };
+  auto add = [&](const v4u_nt& u, float w, float* acc) {
+    const uint32_t q4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      v[2 * q] = __uint_as_float(w[q] << 16);
-      v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+      acc[2 * q] = fmaf(w, __uint_as_float(q4[q] << 16), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(w, __uint_as_float(q4[q] & 0xFFFF0000u), acc[2 * q + 1]);
     }
   };
-  const int* trow = a.token_row + int64_t(t) * a.k;
-  const float* tw = a.topk_w + int64_t(t) * a.k;
   float r[C], sh[C];
 #pragma unroll
   for (int q = 0; q < C; ++q) r[q] = sh[q] = 0.f;
-  // Every load is issued unconditionally (slots past k re-read slot 0 with
-  // weight 0, shared experts past S re-read the last one, masked to 0), so
-  // the 16 + NSH loads go out together instead of one branch and one full wait
-  // per load.
+  // Lane l < 32 first reads slot l's weight and row (clamped into the
+  // token's k entries; slots past k get weight 0), and every lane takes the
+  // values from those lanes: one load each, issued before any o row so that
+  // waiting for it waits for nothing else.  Every o load is unconditional
+  // (slots past k re-read slot k-1 with weight 0; shared experts past S
+  // re-read the last one, or with S = 0 a routed row, masked to 0), so the
+  // NSH + 16 row loads go out together instead of one branch and one full
+  // wait per load.  Sums run in slot order, then shared-expert order.
+  const int lane = threadIdx.x;
+  const int jl = min(lane & 31, a.k - 1);
+  const uint32_t wl = __float_as_uint(a.topk_w[int64_t(t) * a.k + jl]);
+  const int rl = TOKMAJOR ? 0 : a.token_row[int64_t(t) * a.k + jl];
+  __builtin_amdgcn_sched_barrier(0);
+  v4u_nt us[NSH];
+#pragma unroll
+  for (int s = 0; s < NSH; ++s) us[s] = load(int64_t(a.Rr + (s < a.S ? s : a.S - 1) * a.T + t));
   for (int j0 = 0; j0 < a.k; j0 += 16) {
-    float v[16][C];
+    v4u_nt u[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int j = j0 + k < a.k ? j0 + k : a.k - 1;
+      u[k] = load(TOKMAJOR ? int64_t(t) * a.k + j : int64_t(__builtin_amdgcn_readlane(rl, j)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float w[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const bool ok = j0 + u < a.k;
-      const int j = ok ? j0 + u : 0;
-      load(TOKMAJOR ? int64_t(t) * a.k + j : int64_t(trow[j]), v[u]);
-      w[u] = __uint_as_float(__float_as_uint(tw[j]) & (ok ? ~0u : 0u));
-    }
+    for (int k = 0; k < 16; ++k) w[k] = __uint_as_float(__builtin_amdgcn_readlane(wl, j0 + k) & (j0 + k < a.k ? ~0u : 0u));
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-#pragma unroll
-      for (int q = 0; q < C; ++q) r[q] = fmaf(w[u], v[u][q], r[q]);
+    for (int k = 0; k < 16; ++k) add(u[k], w[k], r);
   }
-  if (a.S > 0) {
-    float v[NSH][C];
 #pragma unroll
-    for (int s = 0; s < NSH; ++s) load(int64_t(a.Rr + (s < a.S ? s : a.S - 1) * a.T + t), v[s]);
+  for (int s = 0; s < NSH; ++s) {
+    const uint32_t m = s < a.S ? ~0u : 0u;
+    const uint32_t q4[4] = {us[s].x & m, us[s].y & m, us[s].z & m, us[s].w & m};
 #pragma unroll
-    for (int s = 0; s < NSH; ++s) {
-      const uint32_t m = s < a.S ? ~0u : 0u;
-#pragma unroll
-      for (int q = 0; q < C; ++q) sh[q] += __uint_as_float(__float_as_uint(v[s][q]) & m);
+    for (int q = 0; q < 4; ++q) {
+      sh[2 * q] += __uint_as_float(q4[q] << 16);
+      sh[2 * q + 1] += __uint_as_float(q4[q] & 0xFFFF0000u);
     }
   }
   uint32_t yb[C / 2];
@@ -899,6 +914,7 @@ __global__ void __launch_bounds__(64) k_combine(FwdArgs a) {
   for (int q = 0; q < C / 2; ++q)
     yb[q] = uint32_t(f32_to_bf16_rne(r[2 * q] + sh[2 * q])) |
             (uint32_t(f32_to_bf16_rne(r[2 * q + 1] + sh[2 * q + 1])) << 16);
+  if (!live) return;
   reinterpret_cast<uint4*>(a.y + int64_t(t) * a.d)[c] = make_uint4(yb[0], yb[1], yb[2], yb[3]);
   if (a.y_routed) {
     float4* yr = reinterpret_cast<float4*>(a.y_routed + int64_t(t) * a.d) + (C / 4) * c;
