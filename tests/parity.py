@@ -130,12 +130,31 @@ def rel_err(got: np.ndarray, ref: np.ndarray):
     return rel, np.abs(diff).max() / max(rms, 1e-300)
 
 
-def check_outputs(name: str, got: np.ndarray, ref: np.ndarray):
+def check_outputs(name: str, got: np.ndarray, ref: np.ndarray, allow: Optional[np.ndarray] = None):
+    """Relative L2 over everything, and elementwise |got - ref| <=
+    MAX_ERR_RMS * rms(ref) + allow, where `allow` (same shape, default 0) is
+    the exact effect of the h bytes that differ from the oracle's: a code on
+    the other side of a rounding boundary moves the output by that element's
+    change times its W_dn column, which for one FP8 step of a large element
+    is a sizeable fraction of rms(ref)."""
     rel, mx = rel_err(got, ref)
-    log(f"{name}: rel_l2={rel:.3e} max_err/rms={mx:.3e}")
+    if allow is not None:
+        rms = max(np.sqrt(np.mean(ref ** 2)), 1e-300)
+        mx = float(np.max((np.abs(got - ref) - allow) / rms))
+        log(f"{name}: rel_l2={rel:.3e} (max_err - h flip effect)/rms={mx:.3e} "
+            f"(largest flip effect {np.max(allow) / rms:.3e} rms)")
+    else:
+        log(f"{name}: rel_l2={rel:.3e} max_err/rms={mx:.3e}")
     assert rel <= REL_L2, f"{name}: relative L2 error {rel}"
     assert mx <= MAX_ERR_RMS, f"{name}: max error {mx} x rms"
     return rel, mx
+
+
+def _dn_columns(dn_codes: np.ndarray, dn_scales: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """Decoded columns `cols` of an MXFP4 W_dn [d, d_ff] (canonical layout:
+    element 2i in the low nibble of byte i, one scale per 32 along d_ff)."""
+    nib = (dn_codes[:, cols // 2] >> (4 * (cols % 2))[None, :]) & 0xF
+    return OX.decode_e2m1(nib) * OX.decode_e8m0(dn_scales[:, cols // 32])
 
 
 def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g,
@@ -171,6 +190,18 @@ def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g,
     nbytes = nflip = 0
     sflip = 0
     hdiff = []
+    pos = {int(t): i for i, t in enumerate(toks)}
+    d = res.y.shape[1]
+    # exact effect of the differing h bytes on y_routed and y_shared
+    allow_r = np.zeros((len(toks), d))
+    allow_s = np.zeros((len(toks), d))
+
+    def flip_effect(gh, oh, dn):
+        cols = np.nonzero(gh != oh)[0]
+        if cols.size == 0:
+            return 0.0
+        return np.abs(_dn_columns(dn[2], dn[3], cols)) @ np.abs(gh[cols] - oh[cols])
+
     for t in ok:
         for j in range(cfg.top_k):
             r = int(g["token_row"][t, j])
@@ -179,14 +210,22 @@ def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g,
             nbytes += hc.size
             nflip += int(np.sum(g["h_codes"][r] != hc))
             sflip += int(np.sum(g["h_scales"][r] != hs))
-            hdiff.append((OX.mx_decode(g["h_codes"][r:r + 1], g["h_scales"][r:r + 1], "e4m3"),
-                          OX.mx_decode(hc[None], hs[None], "e4m3")))
+            gh = OX.mx_decode(g["h_codes"][r:r + 1], g["h_scales"][r:r + 1], "e4m3")
+            oh = OX.mx_decode(hc[None], hs[None], "e4m3")
+            hdiff.append((gh, oh))
+            if not np.array_equal(gh, oh):
+                e = int(res.topk_ids[t, j])
+                allow_r[pos[int(t)]] += res.topk_w[t, j] * flip_effect(gh[0], oh[0], weights("routed", e))
         for s in range(cfg.num_shared):
             r = T * cfg.top_k + s * T + int(t)
             hc, hs = res.h_shared[(s, int(t))]
             nbytes += hc.size
             nflip += int(np.sum(g["h_codes"][r] != hc))
             sflip += int(np.sum(g["h_scales"][r] != hs))
+            gh = OX.mx_decode(g["h_codes"][r:r + 1], g["h_scales"][r:r + 1], "e4m3")[0]
+            oh = OX.mx_decode(hc[None], hs[None], "e4m3")[0]
+            if not np.array_equal(gh, oh):
+                allow_s[pos[int(t)]] += flip_effect(gh, oh, weights("shared", s))
     rate = nflip / max(nbytes, 1)
     log(f"h codes differing: {nflip}/{nbytes} ({rate:.2e}); scale bytes differing {sflip}")
     assert rate <= 5e-3
@@ -196,11 +235,10 @@ def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g,
         log(f"routed h decoded rel_l2 {hrel:.2e}")
         assert hrel < 1e-2
     # outputs on the tokens routed identically
-    pos = {int(t): i for i, t in enumerate(toks)}
     sel = [pos[int(t)] for t in ok]
     if sel:
-        check_outputs("y_routed", g["y_routed"][ok].astype(np.float64), res.y_routed[sel])
-        check_outputs("y_shared", g["y_shared"][ok].astype(np.float64), res.y_shared[sel])
+        check_outputs("y_routed", g["y_routed"][ok].astype(np.float64), res.y_routed[sel], allow_r[sel])
+        check_outputs("y_shared", g["y_shared"][ok].astype(np.float64), res.y_shared[sel], allow_s[sel])
         y_gpu = bf16_bits_to_f64(g["y"])[ok]
-        check_outputs("y", y_gpu, res.y[sel])
+        check_outputs("y", y_gpu, res.y[sel], allow_r[sel] + allow_s[sel])
     return res, differ

@@ -259,6 +259,14 @@ def test_more_than_two_shared_experts(T):
     _layer_case(cfg, tokens=None if T <= 64 else list(range(0, T, 7)) + [T - 1])
 
 
+@pytest.mark.parametrize("T", [3, 300])
+def test_top_k_above_16(T):
+    # 20 of 48 experts: top-k keeps more than 16 candidates and the combine
+    # sums its slots in two passes of 16
+    cfg = I.LayerConfig("k20", T, 256, 48, 20, 128, 1, seed=60 + T)
+    _layer_case(cfg, tokens=None if T <= 64 else list(range(0, T, 7)) + [T - 1])
+
+
 def test_medium_layer_k4_two_shared():
     cfg = I.LayerConfig("mid", 96, 1024, 32, 4, 512, 2, seed=7)
     _layer_case(cfg)
