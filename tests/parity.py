@@ -7,8 +7,10 @@ Bars (from the layer's contract):
   whose oracle gap between the k-th and (k+1)-th logit is below TAU: there a
   different set is accepted if every swapped expert's logit lies within TAU of
   the k-th logit (fp32 accumulation over d=7168 gives ~1e-5 logit error);
-* y_routed, y_shared and y, each: relative L2 error <= 5e-3 and max |err| <=
-  5e-2 * rms(reference);
+* y_routed, y_shared and y, each: relative L2 error <= 5e-3 and, per
+  element, |err| <= 5e-2 * rms(reference) + the exact effect of the h bytes
+  that differ (their change times their W_dn column, times the routing
+  weight for routed rows);
 * h bytes: a small fraction may differ by one rounding step (the GPU's fp32 h
   and the oracle's fp64 h can fall on either side of a rounding boundary).
 """
