@@ -32,9 +32,15 @@
  *     W_dn  [d_model][d_ff]
  *   each as codes u8 [rows][K/2] (E2M1 pairs, element 2i in the low nibble of
  *   byte i) and scales u8 [rows][K/32] (E8M0), K the reduction width.
- *   moe_forward takes them in the packed tile order made by moe_pack_mx4
- *   (below): gu_codes/gu_scales hold E packed W_gu matrices back to back,
- *   dn_codes/dn_scales E packed W_dn matrices, sgu_* / sdn_* the shared ones.
+ *   moe_forward takes them only in the packed tile order made by
+ *   moe_pack_mx4 (below): gu_codes/gu_scales hold E packed W_gu matrices back
+ *   to back, dn_codes/dn_scales E packed W_dn matrices, sgu_* / sdn_* the
+ *   shared ones.  The caller says so by setting moe_weights.layout to
+ *   MOE_WEIGHTS_PACKED; a weight set without that tag (for example a
+ *   zero-initialised struct pointing at canonical matrices) is rejected with
+ *   MOE_ERR_INVALID_ARG before anything is enqueued.  Packing is a one-time
+ *   load-time conversion: the canonical order would cost the decode kernels
+ *   strided 2-byte scale loads and the prefill kernels a re-layout per tile.
  *
  * Errors: every argument is checked on the host before anything is enqueued;
  * on an error nothing is written and the call returns a non-zero status
@@ -76,18 +82,25 @@ typedef struct {
  * moe_plan (only the optional profiling state below changes). */
 typedef struct moe_plan_s moe_plan_t;
 
+/* Layout tags of moe_weights.layout. */
+#define MOE_WEIGHTS_CANONICAL 0u          /* not accepted by moe_forward */
+#define MOE_WEIGHTS_PACKED 0x3450584Du    /* every expert matrix made by moe_pack_mx4 */
+
 typedef struct {
   const uint8_t *gu_codes, *gu_scales, *dn_codes, *dn_scales;
   const uint8_t *sgu_codes, *sgu_scales, *sdn_codes, *sdn_scales; /* NULL if num_shared==0 */
   const float *router_w;
   const float *router_b; /* may be NULL */
+  uint32_t layout;       /* MOE_WEIGHTS_PACKED (required) */
 } moe_weights;
 
 /* Optional device outputs for inspection; each NULL pointer is skipped.
  * Permuted rows: R = T*top_k routed rows (expert-major, tokens ascending)
  * followed by num_shared blocks of T rows (shared expert s, token t at
  * T*top_k + s*T + t). */
-/* Alignment: x_codes and h_codes 16 bytes, every other tap 4 bytes. */
+/* Alignment: x_codes, x_scales, h_codes, h_scales, y_routed and y_shared
+ * 16 bytes (the kernels move them in 16-byte pieces), every other tap 4
+ * bytes; a misaligned tap is rejected with MOE_ERR_INVALID_ARG. */
 typedef struct {
   float *logits;          /* [T][E]   router logits incl. bias (fp32)        */
   int32_t *topk_ids;      /* [T][top_k] selected experts, ascending          */

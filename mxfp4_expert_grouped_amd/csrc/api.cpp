@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -42,34 +43,34 @@ moe_status fail(moe_status s, const char* fmt, ...) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Checked once per device: a visible gfx950 device is current.  Also gives
-// its compute-unit count.
+// its compute-unit count.  The per-device cache holds the compute-unit count
+// (0 = not yet checked) in one atomic word, so threads that check the same
+// device at once at worst both query it and store the same value.
 moe_status check_device(int* num_cus = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
     (void)hipGetLastError();
     return fail(MOE_ERR_DEVICE, "no HIP device available");
   }
-  static int checked[64] = {0};  // 0 unknown, 1 ok, 2 bad
-  static int cus[64] = {0};
-  if (dev < 64 && checked[dev] == 1) {
-    if (num_cus) *num_cus = cus[dev];
-    return MOE_OK;
+  static std::atomic<int> cus[64];  // zero-initialised (static storage)
+  if (dev < 64) {
+    const int c = cus[dev].load(std::memory_order_acquire);
+    if (c > 0) {
+      if (num_cus) *num_cus = c;
+      return MOE_OK;
+    }
   }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
     (void)hipGetLastError();
     return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
   }
-  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
-    if (dev < 64) checked[dev] = 2;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(MOE_ERR_DEVICE, "device %d is %s, the kernels are built for gfx950", dev,
                 prop.gcnArchName);
-  }
-  if (dev < 64) {
-    checked[dev] = 1;
-    cus[dev] = prop.multiProcessorCount;
-  }
-  if (num_cus) *num_cus = prop.multiProcessorCount;
+  const int c = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  if (dev < 64) cus[dev].store(c, std::memory_order_release);
+  if (num_cus) *num_cus = c;
   return MOE_OK;
 }
 
@@ -110,7 +111,9 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
   L.row_src = take(Rr * 4);
-  L.row_token = take(Rr * 4);
+  // eight spare entries: the decode GEMM loads a tile's eight row-token
+  // entries with one scalar load, past the last routed row for the last tile
+  L.row_token = take((Rr + 8) * 4);
   L.token_row = take(T * k * 4);
   L.chunk_mask = take(size_t(L.nchunks) * E * 8);
   L.chunk_base = take(size_t(L.nchunks) * E * 4);
@@ -249,6 +252,11 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
                 static_cast<long long>(num_tokens), static_cast<long long>(c.max_tokens));
   if (num_tokens == 0) return MOE_OK;
   if (!w || !x_bf16 || !y_bf16) return fail(MOE_ERR_INVALID_ARG, "weights, x or y is NULL");
+  if (w->layout != MOE_WEIGHTS_PACKED)
+    return fail(MOE_ERR_INVALID_ARG,
+                "weights.layout is 0x%x: moe_forward reads only expert matrices packed by "
+                "moe_pack_mx4, tagged MOE_WEIGHTS_PACKED (0x%x)",
+                w->layout, MOE_WEIGHTS_PACKED);
   if (!w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales || !w->router_w)
     return fail(MOE_ERR_INVALID_ARG, "routed-expert or router weight pointer is NULL");
   if (c.num_shared > 0 && (!w->sgu_codes || !w->sgu_scales || !w->sdn_codes || !w->sdn_scales))
@@ -268,8 +276,8 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
   if (taps) {
     if ((taps->x_codes && !aligned(taps->x_codes, 16)) ||
         (taps->h_codes && !aligned(taps->h_codes, 16)) ||
-        (taps->x_scales && !aligned(taps->x_scales, 4)) ||
-        (taps->h_scales && !aligned(taps->h_scales, 4)) ||
+        (taps->x_scales && !aligned(taps->x_scales, 16)) ||
+        (taps->h_scales && !aligned(taps->h_scales, 16)) ||
         (taps->y_routed && !aligned(taps->y_routed, 16)) ||
         (taps->y_shared && !aligned(taps->y_shared, 16)) ||
         (taps->logits && !aligned(taps->logits, 4)) || (taps->topk_w && !aligned(taps->topk_w, 4)) ||

@@ -14,9 +14,10 @@
 //   * the scale byte of lane (r, g) applies to logical block g (k = 32g..32g+31)
 //     of row r; the result of lane l, register i is D[4(l/16)+i][l%16].
 // MFMA step s covers K = 128s .. 128s+127 in natural order.  Weights arrive
-// packed (moe_pack_mx4): the FP4 operand of one 16-row block and step is 1 KB
-// contiguous in lane order, and the block scales of four steps one dword per
-// lane (byte j for step 4q + j).
+// packed (moe_pack_mx4): the FP4 operands of the four 16-row blocks of a
+// 64-row group and one step are 4 KB contiguous in lane order (1 KB per
+// block), and their block scales one dword per lane, byte j holding the scale
+// of block j for that lane's row and 32-wide K group.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -238,7 +239,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
       src_a = rb - a.Rr - sidx * a.T + r_a;
       src_s = rb - a.Rr - sidx * a.T + r_s;
     } else {
-      const v8i_s rt = sload8(a.row_token + rb);     // may read past Rr: only rows < nr are used
+      // eight entries (the workspace pads row_token by eight past the last
+      // routed row); only rows < nr are used
+      const v8i_s rt = sload8(a.row_token + rb);
       src_a = rt[0];
       src_s = rt[0];
 #pragma unroll

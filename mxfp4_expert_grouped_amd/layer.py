@@ -31,7 +31,7 @@ class DeviceWeights:
         return M.MoeWeights(p(self.gu_codes), p(self.gu_scales), p(self.dn_codes),
                             p(self.dn_scales), p(self.sgu_codes), p(self.sgu_scales),
                             p(self.sdn_codes), p(self.sdn_scales), p(self.router_w),
-                            p(self.router_b))
+                            p(self.router_b), M.MOE_WEIGHTS_PACKED)
 
 
 class MoeLayer:

@@ -36,10 +36,16 @@ class MoeConfig(ctypes.Structure):
                 ("flags", c_uint32)]
 
 
+MOE_WEIGHTS_CANONICAL = 0
+MOE_WEIGHTS_PACKED = 0x3450584D
+
+
 class MoeWeights(ctypes.Structure):
+    """Device pointers of the layer's weights.  ``layout`` must be
+    MOE_WEIGHTS_PACKED (expert matrices made by moe_pack_mx4)."""
     _fields_ = [(n, c_void_p) for n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales",
                                          "sgu_codes", "sgu_scales", "sdn_codes", "sdn_scales",
-                                         "router_w", "router_b")]
+                                         "router_w", "router_b")] + [("layout", c_uint32)]
 
 
 TAP_FIELDS = ("logits", "topk_ids", "topk_w", "expert_offsets", "row_src", "token_row",

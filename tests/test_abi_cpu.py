@@ -99,7 +99,7 @@ def test_workspace_bytes(M):
 def test_forward_argument_errors_before_any_device_call(M):
     p = M.moe_plan(256, 128, 16, 2, 1, 8)
     fake = 1 << 20  # never dereferenced: every call below fails validation first
-    W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None)
+    W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, M.MOE_WEIGHTS_PACKED)
     ws = M.moe_workspace_bytes(p, 8)
     try:
         # T == 0 is a no-op even with null buffers
@@ -121,10 +121,51 @@ def test_forward_argument_errors_before_any_device_call(M):
                               args["workspace"] or None, args["workspace_bytes"])
             assert ei.value.status == status, (over, ei.value)
         # missing shared weights
-        W2 = M.MoeWeights(fake, fake, fake, fake, None, None, None, None, fake, None)
+        W2 = M.MoeWeights(fake, fake, fake, fake, None, None, None, None, fake, None, M.MOE_WEIGHTS_PACKED)
         with pytest.raises(M.MoeError) as ei:
             M.moe_forward(p, W2, fake, 8, fake, fake, ws)
         assert ei.value.status == M.MOE_ERR_INVALID_ARG
+    finally:
+        M.moe_plan_destroy(p)
+
+
+def test_forward_rejects_weights_not_tagged_packed(M):
+    # moe_forward reads only packed expert matrices: a weight set without the
+    # MOE_WEIGHTS_PACKED tag (canonical matrices, or a zero-initialised
+    # struct) fails before anything is enqueued, whatever else is valid
+    p = M.moe_plan(256, 128, 16, 2, 1, 8)
+    fake = 1 << 20
+    ws = M.moe_workspace_bytes(p, 8)
+    try:
+        for tag in (M.MOE_WEIGHTS_CANONICAL, M.MOE_WEIGHTS_PACKED + 1, 1):
+            W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, tag)
+            with pytest.raises(M.MoeError) as ei:
+                M.moe_forward(p, W, fake, 8, fake, fake, ws)
+            assert ei.value.status == M.MOE_ERR_INVALID_ARG
+            assert "MOE_WEIGHTS_PACKED" in ei.value.detail
+        # the default of the binding's struct is the canonical (rejected) tag
+        W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None)
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_forward(p, W, fake, 8, fake, fake, ws)
+        assert ei.value.status == M.MOE_ERR_INVALID_ARG
+    finally:
+        M.moe_plan_destroy(p)
+
+
+def test_forward_rejects_misaligned_scale_taps(M):
+    # x_scales and h_scales taps are read back by the prefill GEMM in
+    # 16-byte pieces: a 4-byte-aligned tap is refused
+    p = M.moe_plan(256, 128, 16, 2, 1, 8)
+    fake = 1 << 20
+    ws = M.moe_workspace_bytes(p, 8)
+    W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, M.MOE_WEIGHTS_PACKED)
+    try:
+        for name in ("x_scales", "h_scales", "y_routed", "y_shared", "x_codes", "h_codes"):
+            taps = M.MoeTaps(**{name: fake + 4})
+            with pytest.raises(M.MoeError) as ei:
+                M.moe_forward(p, W, fake, 8, fake, fake, ws, taps)
+            assert ei.value.status == M.MOE_ERR_INVALID_ARG, name
+            assert "tap" in ei.value.detail
     finally:
         M.moe_plan_destroy(p)
 
@@ -150,7 +191,7 @@ def test_no_device_reports_device_error(M):
         pytest.skip("a GPU is present")
     p = M.moe_plan(256, 128, 16, 2, 1, 8)
     fake = 1 << 20
-    W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None)
+    W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, M.MOE_WEIGHTS_PACKED)
     try:
         with pytest.raises(M.MoeError) as ei:
             M.moe_forward(p, W, fake, 8, fake, fake, M.moe_workspace_bytes(p, 8))
