@@ -147,20 +147,32 @@ def permute(ids, num_experts: int):
 
 def silu(g):
     g = np.asarray(g, dtype=np.float64)
-    return g / (1.0 + np.exp(-g))
+    with np.errstate(over="ignore"):  # exp(-g) = inf for g < -709: the quotient is then -0
+        return g / (1.0 + np.exp(-g))
 
 
-def expert_mlp(a_codes, a_scales, gu_codes, gu_scales, dn_codes, dn_scales, d_ff: int):
+def expert_mlp(a_codes, a_scales, gu_codes, gu_scales, dn_codes, dn_scales, d_ff: int,
+               intermediates: Optional[dict] = None):
     """One expert on a set of MXFP8 rows.
 
     A = decoded MXFP8 rows [n, d]; [g | u] = A W_gu^T with W_gu [2 d_ff, d]
     (rows [0, d_ff) gate, [d_ff, 2 d_ff) up); h = silu(g) * u; h quantised to
     MXFP8 along d_ff; o = dec(h_q) W_dn^T with W_dn [d, d_ff].
     Returns (h_codes [n, d_ff], h_scales [n, d_ff/32], o [n, d] float64).
+
+    With a dict ``intermediates`` it also receives the float64 values the
+    definition passes through: "gu" ([g | u], [n, 2 d_ff]), "h" (before its
+    quantisation, [n, d_ff]), and the magnitudes of the terms of each dot
+    product, "gu_abs" = |A| |W_gu|^T and "o_abs" = |dec(h_q)| |W_dn|^T (the
+    scale of the rounding error any finite-precision evaluation of those sums
+    can make).
     """
     a = mx.mx_decode(a_codes, a_scales, "e4m3")
     wgu = mx.mx_decode(gu_codes, gu_scales, "e2m1")
     gu = a @ wgu.T
+    if intermediates is not None:
+        intermediates["gu"] = gu
+        intermediates["gu_abs"] = np.abs(a) @ np.abs(wgu).T
     del wgu
     g, u = gu[:, :d_ff], gu[:, d_ff:]
     h = silu(g) * u
@@ -168,7 +180,19 @@ def expert_mlp(a_codes, a_scales, gu_codes, gu_scales, dn_codes, dn_scales, d_ff
     hq = mx.mx_decode(h_codes, h_scales, "e4m3")
     wdn = mx.mx_decode(dn_codes, dn_scales, "e2m1")
     o = hq @ wdn.T
+    if intermediates is not None:
+        intermediates["h"] = h
+        intermediates["o_abs"] = np.abs(hq) @ np.abs(wdn).T
     return h_codes, h_scales, o
+
+
+def _expert_job(job):
+    """expert_mlp of one expert on its rows: job = (weights, kind, index,
+    a_codes, a_scales, d_ff, intermediates) -> (h_codes, h_scales, o, mid)."""
+    weights, kind, index, a_codes, a_scales, d_ff, intermediates = job
+    mid = {} if intermediates else None
+    h_c, h_s, o = expert_mlp(a_codes, a_scales, *weights(kind, index), d_ff=d_ff, intermediates=mid)
+    return h_c, h_s, o, mid
 
 
 # --------------------------------------------------------------------------
@@ -200,20 +224,46 @@ class LayerResult:
     h_rows: Dict[int, Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict)
     # shared-expert h for the computed tokens: {(s, t): (codes, scales)}
     h_shared: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict)
+    # with intermediates=True: per routed row / per (s, t) the float64 values
+    # of expert_mlp's intermediates dict ("gu", "gu_abs", "h", "o_abs", and
+    # "o", the row's down-projection output), one row each
+    mid_rows: Dict[int, Dict[str, np.ndarray]] = field(default_factory=dict)
+    mid_shared: Dict[Tuple[int, int], Dict[str, np.ndarray]] = field(default_factory=dict)
 
 
 def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: int,
-            num_shared: int, d_ff: int, tokens: Optional[Sequence[int]] = None) -> LayerResult:
+            num_shared: int, d_ff: int, tokens: Optional[Sequence[int]] = None,
+            topk_ids=None, intermediates: bool = False, logits=None,
+            expert_map=map) -> LayerResult:
     """Full layer.  Routing, permutation and the MXFP8 quantisation of x are
     computed for every token; expert outputs only for ``tokens`` (all when
     None).  Each token's output depends only on its own row, so a subset gives
     exactly the rows the full computation would.  Experts are visited one at a
     time so the decoded float64 weights of only one expert are live.
+
+    ``topk_ids`` ([T, top_k] expert ids, ascending per row), when given,
+    replaces the selection: the layer is evaluated for that routing (weights
+    sigmoid(l)/sum sigmoid(l) over those experts, their permutation, their
+    experts), as for a token whose k-th and (k+1)-th logits are so close that
+    another evaluation of the logits may legitimately pick the other expert.
+    ``gap`` is still the one of the layer's own selection.  ``logits``, when
+    given, must be this function's own router_logits(x_bf16, w_r, b) from an
+    earlier call (it saves recomputing them for another subset of tokens).
+    ``expert_map(fn, jobs)`` evaluates the independent per-expert jobs (the
+    builtin map: one after another here; a process pool's map runs them side
+    by side); results are used in job order.
     """
     x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
     t_count, d = x_bf16.shape
-    logits = router_logits(x_bf16, w_r, b)
+    if logits is None:
+        logits = router_logits(x_bf16, w_r, b)
     ids, gap = topk_select(logits, top_k)
+    if topk_ids is not None:
+        given = np.asarray(topk_ids, dtype=np.int64)
+        assert given.shape == ids.shape
+        assert np.all((given >= 0) & (given < num_experts))
+        assert np.all(np.diff(given, axis=1) > 0), "ids must be distinct and ascending per row"
+        ids = given.astype(np.int32)
     w = routing_weights(logits, ids)
     counts, offsets, row_src, token_row = permute(ids, num_experts)
 
@@ -225,32 +275,46 @@ def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: i
     y_shared = np.zeros((len(toks), d))
     res_h: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
     res_hs: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]] = {}
+    res_mid: Dict[int, Dict[str, np.ndarray]] = {}
+    res_mids: Dict[Tuple[int, int], Dict[str, np.ndarray]] = {}
 
+    # one job per expert with rows among the computed tokens: the routed
+    # experts in order, then the shared experts on every computed token
     want = np.zeros(t_count, dtype=bool)
     want[toks] = True
+    jobs, placement = [], []
     for e in range(num_experts):
         rows = np.arange(offsets[e], offsets[e + 1])
         rows = rows[want[row_src[rows] // top_k]]
         if rows.size == 0:
             continue
         pairs = row_src[rows]
-        tk = pairs // top_k
-        jj = pairs % top_k
-        xi = np.array([pos[int(t)] for t in tk])
-        h_c, h_s, o = expert_mlp(x_codes[xi], x_scales[xi], *weights("routed", e), d_ff=d_ff)
-        for i in range(rows.size):
-            res_h[int(rows[i])] = (h_c[i], h_s[i])
-            y_routed[pos[int(tk[i])]] += w[tk[i], jj[i]] * o[i]
+        xi = np.array([pos[int(t)] for t in pairs // top_k])
+        jobs.append((weights, "routed", e, x_codes[xi], x_scales[xi], d_ff, intermediates))
+        placement.append(("routed", e, rows, pairs // top_k, pairs % top_k))
     for s in range(num_shared):
-        h_c, h_s, o = expert_mlp(x_codes, x_scales, *weights("shared", s), d_ff=d_ff)
-        for i, t in enumerate(toks):
-            res_hs[(s, int(t))] = (h_c[i], h_s[i])
-        y_shared += o
+        jobs.append((weights, "shared", s, x_codes, x_scales, d_ff, intermediates))
+        placement.append(("shared", s, None, toks, None))
+    # expert_map only decides where the jobs run (default: here, in order);
+    # the results are summed below in job order either way
+    for (kind, e, rows, tk, jj), (h_c, h_s, o, mid) in zip(placement, expert_map(_expert_job, jobs)):
+        if kind == "routed":
+            for i in range(rows.size):
+                res_h[int(rows[i])] = (h_c[i], h_s[i])
+                y_routed[pos[int(tk[i])]] += w[tk[i], jj[i]] * o[i]
+                if intermediates:
+                    res_mid[int(rows[i])] = dict({k: v[i] for k, v in mid.items()}, o=o[i])
+        else:
+            for i, t in enumerate(toks):
+                res_hs[(e, int(t))] = (h_c[i], h_s[i])
+                if intermediates:
+                    res_mids[(e, int(t))] = dict({k: v[i] for k, v in mid.items()}, o=o[i])
+            y_shared += o
     return LayerResult(logits=logits, gap=gap, topk_ids=ids, topk_w=w, counts=counts,
                        offsets=offsets, row_src=row_src, token_row=token_row,
                        x_codes=x_codes, x_scales=x_scales, tokens=toks,
                        y_routed=y_routed, y_shared=y_shared, y=y_routed + y_shared,
-                       h_rows=res_h, h_shared=res_hs)
+                       h_rows=res_h, h_shared=res_hs, mid_rows=res_mid, mid_shared=res_mids)
 
 
 def forward_dense(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: int,

@@ -158,3 +158,86 @@ def test_layer_outputs_nontrivial_tiny():
     assert len(set(res.topk_ids.reshape(-1).tolist())) >= 6  # several experts touched
     assert np.all(np.isfinite(res.y)) and res.y.std() > 0
     assert len(res.h_rows) == 16 and len(res.h_shared) == 8
+
+
+def test_given_routing_equals_dense_masked_sum():
+    # the layer evaluated for a routing it did not choose itself (what the
+    # parity tests do for near-tie tokens): every token's output must be the
+    # dense sum over all experts with weights that are zero off the given
+    # set and sigmoid-renormalised on it (weights here through torch's softmax
+    # of log-sigmoid, expert outputs without any permutation)
+    cfg = I.LayerConfig("given", 10, 128, 12, 3, 64, 1, seed=13)
+    x, wr = I.gen_x(cfg), I.gen_router_w(cfg)
+    W = I.ExpertWeights(cfg)
+    rng = np.random.default_rng(14)
+    given = np.stack([np.sort(rng.choice(cfg.num_experts, cfg.top_k, replace=False))
+                      for _ in range(cfg.tokens)]).astype(np.int32)
+    own, _ = moe.topk_select(moe.router_logits(x, wr), cfg.top_k)
+    assert not np.array_equal(given, own)
+    res = moe.forward(x, wr, None, W, num_experts=12, top_k=3, num_shared=1, d_ff=64,
+                      topk_ids=given)
+    assert np.array_equal(res.topk_ids, given)
+    logits = moe.router_logits(x, wr)
+    sel = torch.from_numpy(np.take_along_axis(logits, given.astype(np.int64), 1))
+    wts = torch.softmax(torch.nn.functional.logsigmoid(sel), dim=1).numpy()
+    dense_w = np.zeros((cfg.tokens, cfg.num_experts))
+    np.put_along_axis(dense_w, given.astype(np.int64), wts, axis=1)
+    xc, xs = mx.mx_quantize(moe.bf16_to_f64(x), "e4m3")
+    y_r = np.zeros((cfg.tokens, cfg.d_model))
+    for e in range(cfg.num_experts):
+        y_r += dense_w[:, e:e + 1] * moe.expert_mlp(xc, xs, *W("routed", e), d_ff=64)[2]
+    y_s = moe.expert_mlp(xc, xs, *W("shared", 0), d_ff=64)[2]
+    assert np.allclose(res.y_routed, y_r, rtol=1e-12, atol=1e-14 * np.abs(y_r).max())
+    assert np.allclose(res.y_shared, y_s, rtol=0, atol=0)
+    # its permutation is the one of the given ids
+    c, o, rs, tr = moe.permute(given, cfg.num_experts)
+    assert np.array_equal(res.row_src, rs) and np.array_equal(res.token_row, tr)
+
+
+def test_intermediates_exact_on_integer_operands():
+    # integer-valued MXFP8 rows and weight codes whose values are integers
+    # (E2M1 codes 2, 4, 5, 6, 7 with scale 2^0 are 1, 2, 3, 4, 6): [g|u] must
+    # be the exact integer matmul, h = silu(g) u from torch, and with all
+    # operands non-negative the term magnitudes equal the sums themselves
+    rng = np.random.default_rng(15)
+    d, f, n = 64, 32, 5
+    xi = rng.integers(0, 9, size=(n, d)).astype(np.float64)
+    xi[:, ::32] = 16.0  # every block's amax is 16: scale 2^-4, codes exact
+    a_codes, a_scales = mx.mx_quantize(xi, "e4m3")
+    assert np.array_equal(mx.mx_decode(a_codes, a_scales, "e4m3"), xi)
+    value_code = {1: 2, 2: 4, 3: 5, 4: 6, 6: 7}
+    wg = rng.choice([1, 2, 3, 4, 6], size=(2 * f, d))
+    wd = rng.choice([1, 2, 3, 4, 6], size=(d, f))
+    enc = np.vectorize(value_code.get)
+    guc, gus = mx.pack_fp4(enc(wg).astype(np.uint8)), np.full((2 * f, d // 32), 127, np.uint8)
+    dnc, dns = mx.pack_fp4(enc(wd).astype(np.uint8)), np.full((d, f // 32), 127, np.uint8)
+    mid = {}
+    hc, hs, o = moe.expert_mlp(a_codes, a_scales, guc, gus, dnc, dns, d_ff=f, intermediates=mid)
+    want = xi.astype(np.int64) @ wg.T.astype(np.int64)
+    assert np.array_equal(mid["gu"], want.astype(np.float64))
+    assert np.array_equal(mid["gu_abs"], mid["gu"])
+    g, u = torch.from_numpy(want[:, :f].astype(np.float64)), torch.from_numpy(want[:, f:].astype(np.float64))
+    assert np.allclose(mid["h"], (torch.nn.functional.silu(g) * u).numpy(), rtol=1e-15, atol=0)
+    assert np.all(mid["h"] >= 0)
+    assert np.allclose(mid["o_abs"], o, rtol=1e-15, atol=0)
+    # a row with mixed signs: the magnitudes bound the sums
+    mid2 = {}
+    moe.expert_mlp(a_codes, a_scales, guc | 0x88, gus, dnc, dns, d_ff=f, intermediates=mid2)
+    assert np.array_equal(mid2["gu"], -mid["gu"]) and np.array_equal(mid2["gu_abs"], mid["gu_abs"])
+
+
+def test_forward_intermediates_match_rows():
+    cfg = I.CONFIGS["tiny"]
+    x, wr = I.gen_x(cfg), I.gen_router_w(cfg)
+    W = I.ExpertWeights(cfg)
+    res = moe.forward(x, wr, None, W, num_experts=16, top_k=2, num_shared=1, d_ff=128,
+                      intermediates=True)
+    assert set(res.mid_rows) == set(res.h_rows) and set(res.mid_shared) == set(res.h_shared)
+    for r, m in res.mid_rows.items():
+        assert np.all(m["gu_abs"] >= np.abs(m["gu"]))
+        hc, hs = mx.mx_quantize(m["h"][None], "e4m3")
+        assert np.array_equal(hc[0], res.h_rows[r][0]) and np.array_equal(hs[0], res.h_rows[r][1])
+    t = 3
+    y_r = sum(res.topk_w[t, j] * res.mid_rows[int(res.token_row[t, j])]["o"] for j in range(2))
+    assert np.allclose(y_r, res.y_routed[t], rtol=1e-13, atol=0)
+    assert np.allclose(res.mid_shared[(0, t)]["o"], res.y_shared[t], rtol=0, atol=0)
