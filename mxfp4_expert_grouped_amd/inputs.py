@@ -211,8 +211,9 @@ def gen_mx_matrix(seed: int, code_stream: int, scale_stream: int, rows: int, k: 
 
     step = 1 << 15
     spans = [(lo, min(lo + step, nblk)) for lo in range(0, nblk, step)]
-    if len(spans) > 1:
-        with ThreadPoolExecutor(max_workers=min(len(spans), os.cpu_count() or 1, 16)) as ex:
+    threads = min(len(spans), os.cpu_count() or 1, 16, int(os.environ.get("MXMOE_GEN_THREADS", "16")))
+    if threads > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(lambda sp: fill(*sp), spans))
     else:
         for sp in spans:

@@ -178,38 +178,103 @@ def test_quantize_act_strided_and_ragged_rows():
 # exact-arithmetic regime: gate/up accumulators bit-exact
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d,f", [(256, 128), (1024, 512)])
-def test_gate_up_accumulators_exact(d, f):
-    """x integer-valued in [-16, 16]: every MXFP8 element is exact and every
-    partial sum is an integer multiple of 2^-7 below 2^14, so fp32 accumulation
-    is exact and the GPU's gate/up values must equal the float64 ones bit for bit
-    (any lane/K/scale layout error shows up as a mismatch)."""
-    cfg = I.LayerConfig("exact", 40, d, 8, 2, f, 1, seed=21)
-    rng = np.random.default_rng(5)
-    xi = rng.integers(-16, 17, size=(cfg.tokens, d)).astype(np.float32)
-    bits = I.f32_to_bf16_bits(xi)
+def _pack_device(codes: np.ndarray, scales: np.ndarray, rows: int, k: int, interleave: int):
+    """Canonical MXFP4 matrices [n, rows, k/2] / [n, rows, k/32] (numpy) ->
+    packed device tensors [n, ...] through moe_pack_mx4."""
+    from mxfp4_expert_grouped_amd import mxmoe as M
+    n = codes.shape[0]
+    sb = M.moe_packed_scale_bytes(rows, k)
+    cp = torch.empty((n, rows * k // 2), dtype=torch.uint8, device="cuda")
+    sp = torch.empty((n, sb), dtype=torch.uint8, device="cuda")
+    tc, ts = torch.from_numpy(np.ascontiguousarray(codes)).cuda(), torch.from_numpy(np.ascontiguousarray(scales)).cuda()
+    M.moe_pack_mx4(tc.data_ptr(), ts.data_ptr(), n, rows, k, interleave, cp.data_ptr(), sp.data_ptr(),
+                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return cp, sp
+
+
+def _weights_with_scale_range(cfg, seed: int, lo: int, hi: int):
+    """Expert weights whose E2M1 codes are uniform random bytes and whose E8M0
+    scale bytes are uniform in [lo, hi] (a spread the standard recipe never
+    produces), as device weights and as the oracle's weight source."""
+    from mxfp4_expert_grouped_amd.layer import DeviceWeights
+    rng = np.random.default_rng(seed)
+    d, f = cfg.d_model, cfg.d_ff
+
+    def mats(n, rows, k):
+        return (rng.integers(0, 256, size=(n, rows, k // 2), dtype=np.uint8),
+                rng.integers(lo, hi + 1, size=(n, rows, k // 32), dtype=np.uint8))
+
+    E, S = cfg.num_experts, cfg.num_shared
+    gu, dn = mats(E, 2 * f, d), mats(E, d, f)
+    sgu, sdn = mats(S, 2 * f, d), mats(S, d, f)
+    src = lambda kind, i: ((gu[0][i], gu[1][i], dn[0][i], dn[1][i]) if kind == "routed"
+                           else (sgu[0][i], sgu[1][i], sdn[0][i], sdn[1][i]))
+    g_ = _pack_device(*gu, 2 * f, d, 1)
+    d_ = _pack_device(*dn, d, f, 0)
+    sg = _pack_device(*sgu, 2 * f, d, 1) if S else (None, None)
+    sd = _pack_device(*sdn, d, f, 0) if S else (None, None)
+    wr = torch.from_numpy(I.gen_router_w(cfg)).cuda()
+    return DeviceWeights(g_[0], g_[1], d_[0], d_[1], sg[0], sg[1], sd[0], sd[1], wr, None), src
+
+
+def _integer_x(cfg, seed):
+    rng = np.random.default_rng(seed)
+    xi = rng.integers(-16, 17, size=(cfg.tokens, cfg.d_model)).astype(np.float32)
+    return I.f32_to_bf16_bits(xi)
+
+
+# (name, tokens, d, d_ff, experts, top_k, scale bytes or None for the standard
+# recipe).  The kernel each case reaches: 40 tokens of 8 experts -> 10 rows
+# per expert, 8-row tiles, the K-split streaming gate_up; 300 tokens -> 75 per
+# expert, 256-row tiles, the prefill GEMM (per-step activation scales at
+# d = 256, scales grouped per four K steps at d = 1024); 2048 tokens of 1024
+# experts at top-8 -> 16 rows per expert but enough items for the streaming
+# gate_up without the K split and the two-group down items.
+EXACT_CASES = [
+    ("stream_ksplit", 40, 256, 128, 8, 2, None),
+    ("stream_ksplit_k1024", 40, 1024, 512, 8, 2, None),
+    ("stream_ksplit_wide_scales", 40, 256, 128, 8, 2, (122, 132)),
+    ("prefill_step_scales", 300, 256, 128, 8, 2, (122, 132)),
+    ("prefill_grouped_scales", 300, 1024, 512, 8, 2, (124, 130)),
+    ("stream_whole_items_wide_down", 2048, 256, 512, 1024, 8, (122, 132)),
+]
+
+
+@pytest.mark.parametrize("name,T,d,f,E,k,scales", EXACT_CASES, ids=[c[0] for c in EXACT_CASES])
+def test_gate_up_accumulators_exact(name, T, d, f, E, k, scales):
+    """x integer-valued in [-16, 16]: every MXFP8 element is exact, and with
+    the weights' scale bytes in a bounded range every product is a multiple
+    of q = 0.5 * 2^(lowest scale - 127) and every partial sum stays below
+    2^24 q (asserted from the oracle's term magnitudes), so fp32 accumulation
+    in any order is exact and the GPU's gate/up values must equal the float64
+    ones bit for bit: any lane, K-step or scale-byte layout error shows.  The
+    whole layer is then compared with the full parity rules on a sample."""
+    cfg = I.LayerConfig(name, T, d, E, k, f, 1, seed=21)
+    bits = _integer_x(cfg, 5)
     x = P.IG.bf16_tensor(bits)
-    W = P.IG.device_weights(cfg)
+    if scales is None:
+        W = P.IG.device_weights(cfg)
+        ref = I.ExpertWeights(cfg)
+        lo = 127 + I.scale_exponent_base(d)
+    else:
+        W, ref = _weights_with_scale_range(cfg, 77, *scales)
+        lo = scales[0]
+    P.log(f"exact case {name}: T={T} d={d} d_ff={f} E={E} k={k} scale bytes {scales}")
     g = P.run_gpu(cfg, W, x)
-    ref = I.ExpertWeights(cfg)
-    res = P.OM.forward(bits, I.gen_router_w(cfg), None, ref, num_experts=8, top_k=2, num_shared=1, d_ff=f)
-    assert np.array_equal(g["topk_ids"], res.topk_ids)
-    R = cfg.tokens * 2
-    nmis = 0
-    for r in range(R):
-        p = int(res.row_src[r])
-        t, e = p // 2, int(res.topk_ids[p // 2, p % 2])
-        a = OX.mx_decode(res.x_codes[t:t + 1], res.x_scales[t:t + 1], "e4m3")
-        guc, gus, _, _ = ref("routed", e)
-        want = a @ OX.mx_decode(guc, gus, "e2m1").T
-        assert np.all(np.abs(want) < 2 ** 14)
-        nmis += int(np.sum(g["gu_acc"][r].astype(np.float64) != want[0]))
-    for t in range(cfg.tokens):
-        a = OX.mx_decode(res.x_codes[t:t + 1], res.x_scales[t:t + 1], "e4m3")
-        guc, gus, _, _ = ref("shared", 0)
-        want = a @ OX.mx_decode(guc, gus, "e2m1").T
-        nmis += int(np.sum(g["gu_acc"][R + t].astype(np.float64) != want[0]))
-    assert nmis == 0
+    tokens = None if T <= 64 else sorted(set(range(0, T, max(1, T // 48))) | {T - 1})
+    wr = I.gen_router_w(cfg)
+    res, differ = P.compare_layer(cfg, bits, wr, None, ref, g, tokens=tokens)
+    assert not differ
+    q = 0.5 * 2.0 ** (lo - 127)
+    acc = g["gu_acc"]
+    nmis = nrows = 0
+    for r, mid in list(res.mid_rows.items()) + [(T * k + t, m) for (s, t), m in res.mid_shared.items()]:
+        assert np.all(mid["gu_abs"] < 2.0 ** 24 * q), "case outside the exact regime"
+        nmis += int(np.sum(acc[r].astype(np.float64) != mid["gu"]))
+        nrows += 1
+    P.log(f"{name}: {nrows} rows of gate/up accumulators, {nmis} differ from the exact values")
+    assert nrows > 0 and nmis == 0
 
 
 # ---------------------------------------------------------------------------
