@@ -5,11 +5,13 @@ One step = one whole forward of the layer (router, top-k, MXFP8 quantisation,
 permutation, gate_up + SwiGLU + re-quantisation, down, combine) over one batch
 of synthetic tokens, inputs already resident in HBM.
 
-Default workload: decode with 1 token (d=7168, 896 experts, top-16, d_ff=2048,
-2 shared).  Consecutive steps use different token batches and rotate over
-several independently generated copies of the layer's weights, so no step finds
-its experts in the 256 MB last-level cache (as in a real decode step, where the
-other layers' weights pass through in between).
+Default workload: the largest one, prefill of 32768 tokens with the Zipf-skewed
+router bias (d=7168, 896 experts, top-16, d_ff=2048, 2 shared).  `--config`
+selects the others (tiny, decode1, decode256, prefill8k).  Decode steps use
+different token batches and rotate over several independently generated
+copies of the layer's weights, so no step finds its experts in the 256 MB
+last-level cache (as in a real decode step, where the other layers' weights
+pass through in between).
 
 Prints ONE JSON line.  Also reports the dominant kernel's achieved bandwidth
 (or MFMA rate) against the MI355X peak, timed with HIP events inside the timed
@@ -37,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="decode1",
+    ap.add_argument("--config", default="prefill32k_skew",
                     choices=["tiny", "decode1", "decode256", "prefill8k", "prefill32k_skew"])
     ap.add_argument("--layers", type=int, default=None,
                     help="independent weight copies rotated per step")
@@ -151,6 +153,20 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = wall_ms / steps
 
+    # ---- the same steps again, one event pair per step (torch's current stream,
+    # where every launch of the forward goes): per-step median and spread.  A
+    # separate pass, because an event between two steps idles the GPU for a few
+    # microseconds, which the timed region above must not include -------------------
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+    for s in range(steps):
+        step_ev[s][0].record()
+        run(s)
+        step_ev[s][1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) for a, b in step_ev])
+    p10, p50, p90 = (float(np.percentile(per_step, q)) for q in (10, 50, 90))
+
     # ---- the same steps again with HIP events around the gate_up launch (on the
     # stream it runs on) for the dominant kernel's average duration ------------------
     gu_ms = None
@@ -212,10 +228,15 @@ def main():
         kern_ms = gu_ms if gu_ms else ms_per_step
         gu_flops = 2.0 * R * cfg.d_model * 2 * cfg.d_ff
         achieved = gu_flops / (kern_ms / 1e3) / 1e12
+        # MXFP8 x MXFP4 operands issue at the dense FP8 rate on gfx950, so that
+        # is the contraction's own peak; the fraction of the dense MXFP4 peak
+        # (the rate FP4 x FP4 operands would reach) is reported beside it
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4),
+                    "peak_mxfp4": FP4_MFMA_PEAK_TFLOPS,
                     "frac_of_mxfp4_peak": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4),
-                    "traffic": None, "kernel": "gate_up grouped GEMM (k_gemm_pf, 256-row tiles)",
+                    "traffic": profiled_traffic(cfg.name),
+                    "kernel": "gate_up grouped GEMM (k_gemm_pf, 256-row tiles)",
                     "kernel_ms": round(kern_ms, 5), "algorithmic_flops_per_launch": gu_flops}
 
     cpu = None
@@ -245,6 +266,10 @@ def main():
         "layer_tflops": round(layer_tflops, 2),
         "algorithmic_bytes_per_step": int(mean_step_bytes),
         "gpu_event_ms_per_step": round(gpu_ms / steps, 5),
+        "step_ms_p10": round(p10, 5), "step_ms_p50": round(p50, 5), "step_ms_p90": round(p90, 5),
+        "layer_tflops_p50": round(flops / (p50 / 1e3) / 1e12, 2),
+        "layer_frac_of_fp8_rate": round(layer_tflops / FP8_MFMA_PEAK_TFLOPS, 4),
+        "layer_frac_of_mxfp4_peak": round(layer_tflops / FP4_MFMA_PEAK_TFLOPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
