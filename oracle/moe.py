@@ -340,3 +340,42 @@ def forward_dense(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, to
         _, _, o = expert_mlp(x_codes, x_scales, *weights("shared", s), d_ff=d_ff)
         y += o
     return y
+
+
+# --------------------------------------------------------------------------
+# LatentMoE tail ("Kimi K3 Tech Intro", section 4.3: after the routed and
+# shared experts come the latent up-projection, RMSNorm and an element-wise
+# add; section 4.4: the routed output goes through RMSNorm and the up
+# projection, the shared output is added to it directly)
+# --------------------------------------------------------------------------
+
+
+def rms_norm(z, gamma, eps: float) -> np.ndarray:
+    """Each row z / sqrt(mean(z^2) + eps), times the per-column gain gamma (float64)."""
+    z = np.asarray(z, dtype=np.float64)
+    ms = np.mean(z * z, axis=1, keepdims=True)
+    return z / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64)[None, :]
+
+
+def latent_tail(z, gamma, eps: float, up_codes, up_scales, s=None,
+                intermediates: Optional[dict] = None) -> np.ndarray:
+    """y = MXFP8(RMSNorm(z)) W_up^T + s for the routed experts' weighted sum z
+    [T, l] (float32 values), the gain gamma [l], the up projection W_up
+    [H, l] in MXFP4 (codes [H, l/2], scales [H, l/32]) and the shared
+    experts' output s [T, H] (None: zero).  The normalised rows enter the
+    projection as MXFP8 (32-element blocks along l), like every activation
+    of the layer.  Returns y [T, H] in float64 (the layer rounds it to bf16).
+    With a dict `intermediates`: "n" (the normalised rows, float64), "a_codes",
+    "a_scales" (their MXFP8 bytes), "y_abs" (|A| |W_up|^T, the magnitude of
+    the dot products' terms).
+    """
+    n = rms_norm(z, gamma, eps)
+    a_codes, a_scales = mx.mx_quantize(n, "e4m3")
+    a = mx.mx_decode(a_codes, a_scales, "e4m3")
+    w = mx.mx_decode(up_codes, up_scales, "e2m1")
+    y = a @ w.T
+    if s is not None:
+        y = y + np.asarray(s, dtype=np.float64)
+    if intermediates is not None:
+        intermediates.update(n=n, a_codes=a_codes, a_scales=a_scales, y_abs=np.abs(a) @ np.abs(w).T)
+    return y

@@ -241,3 +241,70 @@ def test_forward_intermediates_match_rows():
     y_r = sum(res.topk_w[t, j] * res.mid_rows[int(res.token_row[t, j])]["o"] for j in range(2))
     assert np.allclose(y_r, res.y_routed[t], rtol=1e-13, atol=0)
     assert np.allclose(res.mid_shared[(0, t)]["o"], res.y_shared[t], rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# LatentMoE tail
+# ---------------------------------------------------------------------------
+
+def test_rms_norm_matches_torch():
+    rng = np.random.default_rng(30)
+    z = rng.standard_normal((9, 256)) * rng.uniform(0.01, 50, size=(9, 1))
+    gamma = 1 + 0.1 * rng.standard_normal(256)
+    for eps in (0.0, 1e-6, 1e-2):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(z), (256,), torch.from_numpy(gamma), eps)
+        assert np.allclose(moe.rms_norm(z, gamma, eps), ref.numpy(), rtol=1e-14, atol=0)
+
+
+def test_rms_norm_properties():
+    rng = np.random.default_rng(31)
+    z = rng.standard_normal((4, 128))
+    one = np.ones(128)
+    n = moe.rms_norm(z, one, 0.0)
+    assert np.allclose(np.mean(n * n, axis=1), 1.0, rtol=1e-14)       # unit mean square
+    assert np.allclose(moe.rms_norm(37.5 * z, one, 0.0), n, rtol=1e-14)  # scale invariant
+    assert np.allclose(moe.rms_norm(n, one, 0.0), n, rtol=1e-14)        # idempotent
+    g = rng.uniform(0.5, 2, 128)
+    assert np.allclose(moe.rms_norm(z, g, 0.0), n * g, rtol=1e-14)       # gain per column
+    assert np.all(moe.rms_norm(np.zeros((1, 128)), one, 1e-6) == 0)     # zero row with eps
+
+
+def test_latent_tail_exact_on_integer_operands():
+    # rows whose RMSNorm is integer-valued (z = c * v with v in {-1, 1}, so
+    # mean(v^2) = 1 and n = v), integer weights with scale 2^0: the projection
+    # is the exact integer matmul, plus s
+    rng = np.random.default_rng(32)
+    T, l, H = 3, 64, 96
+    v = rng.choice([-1.0, 1.0], size=(T, l))
+    z = v * np.array([[0.5], [3.0], [1e3]])
+    value_code = {1: 2, 2: 4, 3: 5, 4: 6, 6: 7}
+    wi = rng.choice([1, 2, 3, 4, 6], size=(H, l)) * rng.choice([-1, 1], size=(H, l))
+    codes = np.vectorize(lambda q: value_code[abs(q)] | (8 if q < 0 else 0))(wi).astype(np.uint8)
+    up_c, up_s = mx.pack_fp4(codes), np.full((H, l // 32), 127, np.uint8)
+    s = rng.integers(-5, 6, size=(T, H)).astype(np.float64)
+    mid = {}
+    y = moe.latent_tail(z, np.ones(l), 0.0, up_c, up_s, s, intermediates=mid)
+    assert np.array_equal(mid["n"], v)
+    want = v.astype(np.int64) @ wi.T.astype(np.int64) + s.astype(np.int64)
+    assert np.array_equal(y, want.astype(np.float64))
+    assert np.array_equal(mid["y_abs"], np.abs(v) @ np.abs(wi).T.astype(np.float64))
+    assert np.array_equal(moe.latent_tail(z, np.ones(l), 0.0, up_c, up_s), want - s)
+
+
+def test_latent_tail_is_norm_quantise_project_add():
+    # the composition against torch: rms_norm, torch's float8 cast for the
+    # MXFP8 elements, matmul with the decoded weights, add
+    cfg = I.LayerConfig("tail", 5, 256, 1, 1, 128, 0, seed=33)
+    rng = np.random.default_rng(34)
+    z = (rng.standard_normal((5, 256)) * 0.3).astype(np.float32)
+    s = rng.standard_normal((5, 256)).astype(np.float32)
+    gamma = (1 + 0.05 * rng.standard_normal(256)).astype(np.float32)
+    up_c, up_s = I.gen_mx_matrix(33, I.stream_id(7, 0), I.stream_id(8, 0), 256, 256,
+                                 I.scale_exponent_base(256))
+    y = moe.latent_tail(z, gamma, 1e-6, up_c, up_s, s)
+    n = torch.nn.functional.rms_norm(torch.from_numpy(z.astype(np.float64)), (256,),
+                                     torch.from_numpy(gamma.astype(np.float64)), 1e-6)
+    a = _torch_mx8_roundtrip(n)
+    w = torch.from_numpy(mx.mx_decode(up_c, up_s, "e2m1"))
+    ref = a @ w.T + torch.from_numpy(s.astype(np.float64))
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12 * float(ref.abs().max()))
