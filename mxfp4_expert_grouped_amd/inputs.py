@@ -173,6 +173,7 @@ assert MAG_TABLE.size == 128
 DELTA_TABLE = np.array([0, 0, 0, 0, 0, 0, 1, 1], dtype=np.int64)
 
 KIND_GU_CODES, KIND_GU_SCALES, KIND_DN_CODES, KIND_DN_SCALES = 1, 2, 3, 4
+KIND_UP_CODES, KIND_UP_SCALES = 5, 6  # LatentMoE tail up projection
 SHARED_BASE = 0x10000
 
 
@@ -228,6 +229,23 @@ def gen_mx_matrix(seed: int, code_stream: int, scale_stream: int, rows: int, k: 
     return packed, scales
 
 
+def gen_mx_matrix_kblocks(seed: int, code_stream: int, scale_stream: int, rows: int, k: int,
+                          e_base: int, kblocks):
+    """The same matrix as gen_mx_matrix, only the 32-wide K blocks `kblocks`
+    of every row: (packed codes [rows, len(kblocks), 16], scales [rows,
+    len(kblocks)]), drawn from the same counters."""
+    kb = np.asarray(kblocks, dtype=np.int64)
+    nb = k // 32
+    blk = (np.arange(rows, dtype=np.int64)[:, None] * nb + kb[None, :]).reshape(-1)
+    rb = philox4x64_10((seed, code_stream), blk.astype(np.uint64)).astype("<u8").view(np.uint8).reshape(-1, 32)
+    codes = MAG_TABLE[rb & 0x7F] | ((rb >> 7) << 3)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).reshape(rows, kb.size, 16)
+    sw = philox4x64_10((seed, scale_stream), (blk // 32).astype(np.uint64)).astype("<u8").view(np.uint8)
+    sb = sw.reshape(-1, 32)[np.arange(blk.size), blk % 32]
+    scales = (127 + e_base + DELTA_TABLE[sb & 7]).astype(np.uint8).reshape(rows, kb.size)
+    return packed, scales
+
+
 def gen_expert(cfg: LayerConfig, kind: str, index: int, layer: int = 0):
     """(gu_codes [2 d_ff, d/2], gu_scales [2 d_ff, d/32],
         dn_codes [d, d_ff/2],   dn_scales [d, d_ff/32]) of one expert."""
@@ -256,6 +274,19 @@ class ExpertWeights:
             self._c[key] = w
         return w
 
+    def dn_blocks(self, kind: str, index: int, kblocks):
+        """Blocks `kblocks` (32 columns each) of every row of W_dn [d, d_ff]:
+        (packed codes [d, n, 16], scales [d, n]), without drawing the rest."""
+        key = (kind, index)
+        kb = np.asarray(kblocks, dtype=np.int64)
+        if key in self._c:
+            dnc, dns = self._c[key][2], self._c[key][3]
+            return (dnc.reshape(dnc.shape[0], -1, 16)[:, kb], dns[:, kb])
+        slot = expert_slot(kind, index)
+        return gen_mx_matrix_kblocks(self.cfg.seed, stream_id(KIND_DN_CODES, slot, self.layer),
+                                     stream_id(KIND_DN_SCALES, slot, self.layer), self.cfg.d_model,
+                                     self.cfg.d_ff, scale_exponent_base(self.cfg.d_model), kb)
+
     def stacked(self):
         """All routed and shared experts stacked (small configs only)."""
         e, s = self.cfg.num_experts, self.cfg.num_shared
@@ -272,3 +303,27 @@ def matrix_bytes(rows: int, k: int) -> int:
 def expert_bytes(cfg: LayerConfig) -> int:
     return matrix_bytes(2 * cfg.d_ff, cfg.d_model) + matrix_bytes(cfg.d_model, cfg.d_ff)
 
+
+
+# ---------------------------------------------------------------------------
+# LatentMoE tail inputs
+# ---------------------------------------------------------------------------
+
+
+def gen_up_matrix(hidden: int, latent: int, seed: int = 0, layer: int = 0):
+    """W_up [hidden, latent] in canonical MXFP4 (codes [hidden, latent/2],
+    scales [hidden, latent/32]), by the same direct MXFP4 recipe as the
+    experts (scale base from the reduction width `latent`)."""
+    return gen_mx_matrix(seed, stream_id(KIND_UP_CODES, 0, layer), stream_id(KIND_UP_SCALES, 0, layer),
+                         hidden, latent, scale_exponent_base(latent))
+
+
+def gen_tail_inputs(tokens: int, latent: int, hidden: int, seed: int = 0, layer: int = 0):
+    """(z [T, latent], s [T, hidden], gamma [latent]) float32: z ~ N(0, 0.5^2)
+    (the routed experts' weighted sum), s ~ N(0, 1) (the shared experts'
+    output), gamma ~ 1 + N(0, 0.1^2) (the RMSNorm gain)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 3, layer])))
+    z = rng.standard_normal((tokens, latent), dtype=np.float32) * np.float32(0.5)
+    s = rng.standard_normal((tokens, hidden), dtype=np.float32)
+    gamma = np.float32(1) + rng.standard_normal(latent, dtype=np.float32) * np.float32(0.1)
+    return z, s, gamma

@@ -69,3 +69,18 @@ def test_dense_inputs():
     assert abs(b[0] - 1.5 * np.log(1 / h)) < 1e-5
     assert abs(b[895] - 1.5 * np.log(896 ** -1.1 / h)) < 1e-5
     assert np.all(np.diff(b) < 0)
+
+
+def test_dn_blocks_are_the_matrix_blocks():
+    cfg = I.LayerConfig("blk", 3, 256, 4, 2, 128, 1, seed=4)
+    full = I.gen_expert(cfg, "routed", 2)
+    for cache in (False, True):
+        W = I.ExpertWeights(cfg, cache=cache)
+        if cache:
+            W("routed", 2)
+        c, s = W.dn_blocks("routed", 2, [0, 3])
+        assert np.array_equal(c, full[2].reshape(256, -1, 16)[:, [0, 3]])
+        assert np.array_equal(s, full[3][:, [0, 3]])
+    sh = I.gen_expert(cfg, "shared", 0)
+    c, s = I.ExpertWeights(cfg, cache=False).dn_blocks("shared", 0, [1])
+    assert np.array_equal(c[:, 0], sh[2].reshape(256, -1, 16)[:, 1]) and np.array_equal(s[:, 0], sh[3][:, 1])

@@ -252,3 +252,41 @@ def test_swap_that_is_not_a_near_tie_is_rejected():
     ids[t] = np.sort([ids[t][0], other])
     with pytest.raises(AssertionError, match="routing differs|near-tie"):
         P.compare_layer(CFG, x, wr, None, W, g)
+
+
+def test_multi_step_move_of_a_cancelling_accumulator_is_accepted():
+    # an up accumulator far smaller than its terms (heavy cancellation): an
+    # error well inside the accumulator bound moves its h element by two or
+    # more E4M3 steps; bytes that are the quantisation of the moved sums, with
+    # the outputs moved by their exact effect, are legitimate
+    cfg = CFG
+    x, wr, W, res, g = _oracle_as_gpu(cfg)
+    f = cfg.d_ff
+    vals = _vals()
+    best = None
+    for t in range(cfg.tokens):
+        mid = res.mid_shared[(0, t)]
+        cond = mid["gu_abs"][f:] / np.maximum(np.abs(mid["gu"][f:]), 1e-300)
+        hb = np.abs(mid["h"]).reshape(-1, 32).max(axis=1)
+        for c in np.argsort(-cond)[:8]:
+            if abs(mid["h"][c]) < hb[c // 32] / 2 and mid["h"][c] != 0:
+                if best is None or cond[c] > best[0]:
+                    best = (cond[c], t, int(c))
+    cond, t, c = best
+    mid = res.mid_shared[(0, t)]
+    r = _shared_row(cfg, t)
+    acc = g.taps["gu_acc"]
+    du = 0.5 * P.EPS_ACC * mid["gu_abs"][f + c] * np.sign(mid["gu"][f + c])
+    acc[r, f + c] = np.float32(mid["gu"][f + c] + du)
+    h_new = OM.silu(acc[r, :f].astype(np.float64)) * acc[r, f:].astype(np.float64)
+    qc, qs = OX.mx_quantize(h_new[None], "e4m3")
+    hc, hs = res.h_shared[(0, t)]
+    assert np.array_equal(qs[0], hs)
+    steps = abs(P._grid_index(vals[qc[0][c:c + 1]]) - P._grid_index(vals[hc[c:c + 1]]))[0]
+    assert steps >= 2, f"the planted move is {steps} step(s) (condition {cond:.3g})"
+    old = OX.mx_decode(hc[None], hs[None], "e4m3")[0]
+    new = OX.mx_decode(qc, qs, "e4m3")[0]
+    g.taps["h_codes"][r] = qc[0]
+    for col in np.nonzero(qc[0] != hc)[0]:
+        _shift_outputs(cfg, W, g, t, 0, int(col), new[col] - old[col])
+    P.compare_layer(cfg, x, wr, None, W, g)
