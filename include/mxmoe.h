@@ -168,6 +168,49 @@ moe_status moe_forward(const moe_plan_t *plan, const moe_weights *w, const void 
                        int64_t num_tokens, void *y_bf16, void *workspace, size_t workspace_bytes,
                        const moe_taps *taps, void *stream);
 
+/* LatentMoE tail: y = MXFP8(RMSNorm(z)) W_up^T + s.  "Kimi K3 Tech Intro",
+ * section 4.3 places a latent up-projection, an RMSNorm and an element-wise
+ * add after the routed and shared experts; section 4.4 sends the routed
+ * output through RMSNorm and the up projection and adds the shared output to
+ * it directly.  Readings taken where the pages are silent: RMSNorm(z) =
+ * z / sqrt(mean(z^2) + eps) * gamma per row; the normalised rows enter the
+ * projection as MXFP8 (E4M3, one E8M0 scale per 32 columns, the quantiser of
+ * moe_quantize_act) and W_up is MXFP4, like every other activation and weight
+ * of the layer; fp32 accumulation; y rounded to bf16.
+ *   z      fp32 [T][latent]   the routed experts' weighted sum (moe_forward's
+ *                             y_routed tap when the experts run at the latent
+ *                             width)
+ *   s      fp32 [T][hidden]   the shared experts' output, or NULL (zero)
+ *   y      bf16 [T][hidden]
+ *   W_up   MXFP4 [hidden][latent], packed by moe_pack_mx4 with interleave 0;
+ *          gamma fp32 [latent]; layout must be MOE_WEIGHTS_PACKED.
+ * latent: a multiple of 128, hidden: a multiple of 256, both <= 65536;
+ * 0 <= T <= 2^20 (T == 0 enqueues nothing); eps >= 0 and finite.
+ * z, s, y, gamma and up_codes 16-byte aligned, up_scales 4 bytes; workspace
+ * of moe_latent_tail_workspace_bytes bytes, 256-byte aligned, contents on
+ * entry irrelevant.  Errors and streams as for moe_forward. */
+typedef struct {
+  const uint8_t *up_codes, *up_scales;
+  const float *gamma;
+  uint32_t layout; /* MOE_WEIGHTS_PACKED */
+} moe_tail_weights;
+
+/* Optional device outputs (NULL = skip): the fp32 1/sqrt(mean(z^2)+eps) of
+ * each row as computed (4-byte aligned) and the MXFP8 bytes of the normalised
+ * rows (16-byte aligned). */
+typedef struct {
+  float *inv_rms;    /* [T]              */
+  uint8_t *a_codes;  /* [T][latent]      */
+  uint8_t *a_scales; /* [T][latent/32]   */
+} moe_tail_taps;
+
+moe_status moe_latent_tail_workspace_bytes(int64_t num_tokens, int32_t latent, int32_t hidden,
+                                           size_t *out_bytes);
+moe_status moe_latent_tail(int64_t num_tokens, int32_t latent, int32_t hidden, float eps,
+                           const moe_tail_weights *w, const float *z, const float *s, void *y_bf16,
+                           void *workspace, size_t workspace_bytes, const moe_tail_taps *taps,
+                           void *stream);
+
 /* Stages of moe_forward, for per-stage timing. */
 typedef enum {
   MOE_STAGE_ROUTER = 0,  /* router logits                                   */

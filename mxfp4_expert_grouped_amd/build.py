@@ -29,7 +29,8 @@ FLAGS = [
 ]
 
 LIBS = {
-    "libmxmoe.so": ["api.cpp", "kernels_route.hip", "kernels_gemm.hip", "kernels_pack.hip"],
+    "libmxmoe.so": ["api.cpp", "kernels_route.hip", "kernels_gemm.hip", "kernels_pack.hip",
+                    "kernels_tail.hip"],
     "libmxmoe_inputs.so": ["gen_inputs.hip"],
 }
 

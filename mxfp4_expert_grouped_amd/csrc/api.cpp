@@ -242,9 +242,13 @@ moe_status moe_pack_mx4(const uint8_t* codes, const uint8_t* scales, int64_t mat
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void* x_bf16,
-                       int64_t num_tokens, void* y_bf16, void* workspace, size_t workspace_bytes,
-                       const moe_taps* taps, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void* x_bf16,
+                        int64_t num_tokens, void* y_bf16, void* workspace, size_t workspace_bytes,
+                        const moe_taps* taps, void* stream) {
   if (!plan) return fail(MOE_ERR_INVALID_ARG, "plan is NULL");
   const moe_config& c = plan->cfg;
   if (num_tokens < 0 || num_tokens > c.max_tokens)
@@ -354,6 +358,130 @@ moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void*
     if (!stage(i, stages[i], a))
       return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(hipGetLastError()));
   if (prof) pl->prof_n++;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void* x_bf16,
+                       int64_t num_tokens, void* y_bf16, void* workspace, size_t workspace_bytes,
+                       const moe_taps* taps, void* stream) {
+  return forward_impl(plan, w, x_bf16, num_tokens, y_bf16, workspace, workspace_bytes, taps, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+struct TailLayout {
+  size_t codes, scales, o16, row_src, tiles, tile_count, ex_tiles, total;
+  int bm;
+};
+
+TailLayout tail_layout(int64_t T, int64_t latent, int64_t hidden, bool with_s) {
+  TailLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += (bytes + 255) / 256 * 256;
+    return at;
+  };
+  // rows per projection tile: the weight-streaming kernel for a few rows,
+  // the 256-row kernel from 24 rows on (as for an expert's rows in moe_forward)
+  L.bm = T >= 24 ? 256 : kDecodeMaxRows;
+  L.codes = take(T * latent);
+  L.scales = take(T * latent / 32);
+  L.o16 = take(with_s ? T * hidden * 2 : 0);
+  L.row_src = take(T * 4);
+  L.tiles = take(((T + L.bm - 1) / L.bm) * sizeof(Tile));
+  L.tile_count = take(4);
+  L.ex_tiles = take(8);
+  L.total = off;
+  return L;
+}
+
+moe_status check_tail_shape(int64_t T, int32_t latent, int32_t hidden) {
+  if (T < 0 || T > (int64_t(1) << 20)) return fail(MOE_ERR_INVALID_ARG, "num_tokens outside [0, 2^20]");
+  if (latent <= 0 || hidden <= 0) return fail(MOE_ERR_INVALID_ARG, "non-positive width");
+  if (latent % 128 || hidden % 256 || latent > 65536 || hidden > 65536)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "latent (%d) must be a multiple of 128 and hidden (%d) of 256, both <= 65536", latent,
+                hidden);
+  if (T * latent >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "num_tokens * latent must be below 2^31");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_latent_tail_workspace_bytes(int64_t num_tokens, int32_t latent, int32_t hidden,
+                                           size_t* out_bytes) {
+  if (!out_bytes) return fail(MOE_ERR_INVALID_ARG, "out_bytes is NULL");
+  moe_status s = check_tail_shape(num_tokens, latent, hidden);
+  if (s != MOE_OK) return s;
+  // sized for a call with s (the projection then has rows of its own)
+  *out_bytes = num_tokens == 0 ? 0 : tail_layout(num_tokens, latent, hidden, true).total;
+  return MOE_OK;
+}
+
+moe_status moe_latent_tail(int64_t num_tokens, int32_t latent, int32_t hidden, float eps,
+                           const moe_tail_weights* w, const float* z, const float* s, void* y_bf16,
+                           void* workspace, size_t workspace_bytes, const moe_tail_taps* taps,
+                           void* stream) {
+  moe_status st = check_tail_shape(num_tokens, latent, hidden);
+  if (st != MOE_OK) return st;
+  if (!(eps >= 0.0f) || eps > 3.4e38f) return fail(MOE_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (num_tokens == 0) return MOE_OK;
+  if (!w || !z || !y_bf16) return fail(MOE_ERR_INVALID_ARG, "weights, z or y is NULL");
+  if (w->layout != MOE_WEIGHTS_PACKED)
+    return fail(MOE_ERR_INVALID_ARG,
+                "tail weights.layout is 0x%x: W_up must be packed by moe_pack_mx4 and tagged "
+                "MOE_WEIGHTS_PACKED",
+                w->layout);
+  if (!w->up_codes || !w->up_scales || !w->gamma) return fail(MOE_ERR_INVALID_ARG, "tail weight pointer is NULL");
+  if (!aligned(z, 16) || (s && !aligned(s, 16)) || !aligned(y_bf16, 16) || !aligned(w->gamma, 16) ||
+      !aligned(w->up_codes, 16) || !aligned(w->up_scales, 4))
+    return fail(MOE_ERR_INVALID_ARG,
+                "misaligned buffer (z, s, y, gamma, up_codes: 16 bytes; up_scales: 4 bytes)");
+  if (taps && ((taps->inv_rms && !aligned(taps->inv_rms, 4)) ||
+               (taps->a_codes && !aligned(taps->a_codes, 16)) ||
+               (taps->a_scales && !aligned(taps->a_scales, 16))))
+    return fail(MOE_ERR_INVALID_ARG, "misaligned tap buffer");
+  const TailLayout L = tail_layout(num_tokens, latent, hidden, s != nullptr);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", L.total, workspace_bytes,
+                workspace ? "" : " (NULL)");
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  int num_cus = 0;
+  st = check_device(&num_cus);
+  if (st != MOE_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  TailArgs a{};
+  a.T = static_cast<int>(num_tokens);
+  a.latent = latent;
+  a.hidden = hidden;
+  a.bm = L.bm;
+  a.eps = eps;
+  a.z = z;
+  a.gamma = w->gamma;
+  a.s = s;
+  a.up_c = w->up_codes;
+  a.up_s = w->up_scales;
+  a.y = static_cast<uint16_t*>(y_bf16);
+  a.codes = (taps && taps->a_codes) ? taps->a_codes : reinterpret_cast<uint8_t*>(ws + L.codes);
+  a.scales = (taps && taps->a_scales) ? taps->a_scales : reinterpret_cast<uint8_t*>(ws + L.scales);
+  a.inv_rms = taps ? taps->inv_rms : nullptr;
+  a.o16 = s ? reinterpret_cast<uint16_t*>(ws + L.o16) : a.y;
+  a.row_src = reinterpret_cast<int32_t*>(ws + L.row_src);
+  a.tiles = reinterpret_cast<Tile*>(ws + L.tiles);
+  a.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
+  a.ex_tiles = reinterpret_cast<int32_t*>(ws + L.ex_tiles);
+  hipError_t e = launch_tail(a, num_cus > 0 ? num_cus : 256, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }
 

@@ -59,7 +59,27 @@ struct FwdArgs {
   int nchunks;          // 64-token chunks
 };
 
+// Everything the kernels of one LatentMoE tail call need (device pointers).
+struct TailArgs {
+  int T, latent, hidden, bm;
+  float eps;
+  const float* z;        // [T][latent] routed experts' weighted sum
+  const float* gamma;    // [latent]
+  const float* s;        // [T][hidden] shared experts' output, or null
+  const uint8_t *up_c, *up_s;  // packed MXFP4 W_up [hidden][latent]
+  uint16_t* y;           // bf16 [T][hidden]
+  uint8_t* codes;        // [T][latent] MXFP8 of the normalised rows
+  uint8_t* scales;       // [T][latent/32]
+  float* inv_rms;        // [T] tap, or null
+  uint16_t* o16;         // [T][hidden] projection (y itself when s is null)
+  int32_t* row_src;      // [T] identity
+  Tile* tiles;           // [ceil(T/bm)]
+  int32_t* tile_count;   // [1]
+  int32_t* ex_tiles;     // [2]
+};
+
 // Launchers (kernels_*.hip).  Each returns hipSuccess or the launch error.
+hipError_t launch_tail(const TailArgs& a, int num_cus, hipStream_t st);
 hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t cols, int64_t ld,
                            uint8_t* codes, uint8_t* scales, hipStream_t st);
 // Tokens up to which the per-expert GEMV router (with the x quantisation

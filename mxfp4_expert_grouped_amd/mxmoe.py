@@ -19,7 +19,8 @@ MOE_SRC_BF16, MOE_SRC_FP32 = 0, 1
 
 EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_workspace_bytes", "moe_quantize_act",
             "moe_forward", "moe_profile_begin", "moe_profile_end", "moe_packed_scale_bytes",
-            "moe_pack_mx4", "moe_status_string", "moe_last_error")
+            "moe_pack_mx4", "moe_latent_tail_workspace_bytes", "moe_latent_tail",
+            "moe_status_string", "moe_last_error")
 STAGES = ("router", "topk", "permute", "gate_up", "down", "combine")
 
 
@@ -56,6 +57,17 @@ class MoeTaps(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in TAP_FIELDS]
 
 
+class MoeTailWeights(ctypes.Structure):
+    """W_up (packed MXFP4, interleave 0) and the RMSNorm gain; ``layout``
+    must be MOE_WEIGHTS_PACKED."""
+    _fields_ = [("up_codes", c_void_p), ("up_scales", c_void_p), ("gamma", c_void_p),
+                ("layout", c_uint32)]
+
+
+class MoeTailTaps(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("inv_rms", "a_codes", "a_scales")]
+
+
 _lib = None
 
 
@@ -88,6 +100,12 @@ def load_library(path: str = LIB_PATH):
     lib.moe_pack_mx4.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int, c_void_p,
                                  c_void_p, c_void_p]
     lib.moe_pack_mx4.restype = c_int
+    lib.moe_latent_tail_workspace_bytes.argtypes = [c_int64, c_int32, c_int32, POINTER(c_size_t)]
+    lib.moe_latent_tail_workspace_bytes.restype = c_int
+    lib.moe_latent_tail.argtypes = [c_int64, c_int32, c_int32, ctypes.c_float, POINTER(MoeTailWeights),
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                    POINTER(MoeTailTaps), c_void_p]
+    lib.moe_latent_tail.restype = c_int
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_status_string.restype = c_char_p
     lib.moe_last_error.argtypes = []
@@ -157,3 +175,17 @@ def moe_pack_mx4(codes: int, scales: int, mats: int, rows: int, k: int, interlea
                  scales_p: int, stream: Optional[int] = None) -> None:
     _check(load_library().moe_pack_mx4(codes, scales, mats, rows, k, interleave, codes_p, scales_p,
                                        stream))
+
+
+def moe_latent_tail_workspace_bytes(num_tokens: int, latent: int, hidden: int) -> int:
+    out = c_size_t()
+    _check(load_library().moe_latent_tail_workspace_bytes(num_tokens, latent, hidden, ctypes.byref(out)))
+    return out.value
+
+
+def moe_latent_tail(num_tokens: int, latent: int, hidden: int, eps: float, weights: MoeTailWeights,
+                    z: int, s: Optional[int], y: int, workspace: int, workspace_bytes: int,
+                    taps: Optional[MoeTailTaps] = None, stream: Optional[int] = None) -> None:
+    _check(load_library().moe_latent_tail(num_tokens, latent, hidden, eps, ctypes.byref(weights), z, s, y,
+                                          workspace, workspace_bytes,
+                                          ctypes.byref(taps) if taps else None, stream))

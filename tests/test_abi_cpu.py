@@ -221,3 +221,31 @@ def test_pack_sizes_and_argument_errors(M):
         with pytest.raises(M.MoeError) as ei:
             M.moe_pack_mx4(*args)
         assert ei.value.status == status
+
+
+def test_latent_tail_host_checks(M):
+    fake = 1 << 20
+    W = M.MoeTailWeights(fake, fake, fake, M.MOE_WEIGHTS_PACKED)
+    assert M.moe_latent_tail_workspace_bytes(0, 7168, 7168) == 0
+    w1 = M.moe_latent_tail_workspace_bytes(1, 7168, 7168)
+    w8k = M.moe_latent_tail_workspace_bytes(8192, 7168, 7168)
+    assert 0 < w1 < w8k and w8k >= 8192 * 7168 * 2
+    # T == 0 is a no-op with null buffers
+    M.moe_latent_tail(0, 256, 256, 1e-6, W, None, None, None, None, 0)
+    ws = M.moe_latent_tail_workspace_bytes(4, 256, 256)
+    for args, status in [
+        ((4, 200, 256, 1e-6, W, fake, fake, fake, fake, ws), M.MOE_ERR_UNSUPPORTED),   # latent % 128
+        ((4, 256, 128, 1e-6, W, fake, fake, fake, fake, ws), M.MOE_ERR_UNSUPPORTED),   # hidden % 256
+        ((4, 256, 256, -1.0, W, fake, fake, fake, fake, ws), M.MOE_ERR_INVALID_ARG),   # eps < 0
+        ((4, 256, 256, float("nan"), W, fake, fake, fake, fake, ws), M.MOE_ERR_INVALID_ARG),
+        ((4, 256, 256, 1e-6, M.MoeTailWeights(fake, fake, fake, 0), fake, fake, fake, fake, ws),
+         M.MOE_ERR_INVALID_ARG),                                                       # not tagged packed
+        ((4, 256, 256, 1e-6, W, None, fake, fake, fake, ws), M.MOE_ERR_INVALID_ARG),   # z NULL
+        ((4, 256, 256, 1e-6, W, fake + 4, fake, fake, fake, ws), M.MOE_ERR_INVALID_ARG),  # z misaligned
+        ((4, 256, 256, 1e-6, W, fake, fake, fake, fake, ws - 1), M.MOE_ERR_WORKSPACE),
+        ((4, 256, 256, 1e-6, W, fake, fake, fake, fake + 16, ws), M.MOE_ERR_WORKSPACE),
+        ((-1, 256, 256, 1e-6, W, fake, fake, fake, fake, ws), M.MOE_ERR_INVALID_ARG),
+    ]:
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_latent_tail(*args)
+        assert ei.value.status == status, (args, ei.value)
