@@ -168,6 +168,24 @@ moe_status moe_forward(const moe_plan_t *plan, const moe_weights *w, const void 
                        int64_t num_tokens, void *y_bf16, void *workspace, size_t workspace_bytes,
                        const moe_taps *taps, void *stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same layer, the same arguments and the same results as moe_forward, but the
+ * workspace is a fixed scratch array of MOE_NOALLOC_SCRATCH_BYTES bytes that
+ * the library's code object holds on every GPU it runs on, from the first
+ * call on that device until the process ends.  The call allocates and frees
+ * nothing and makes no host synchronisation.  Every call on one GPU uses that
+ * GPU's one array and leaves its contents behind (no part of it has to start
+ * at zero): calls that overlap on one GPU -- on two streams, or from two
+ * threads without ordering -- race on it and must not be issued.  Token counts
+ * whose moe_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES are rejected
+ * with MOE_ERR_WORKSPACE before anything is enqueued (at d_model = 7168,
+ * 896 experts, top-16, d_ff = 2048, 2 shared: up to 256 tokens fit). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+moe_status moe_forward_noalloc(const moe_plan_t *plan, const moe_weights *w, const void *x_bf16,
+                               int64_t num_tokens, void *y_bf16, const moe_taps *taps,
+                               void *stream);
+
 /* LatentMoE tail: y = MXFP8(RMSNorm(z)) W_up^T + s.  "Kimi K3 Tech Intro",
  * section 4.3 places a latent up-projection, an RMSNorm and an element-wise
  * add after the routed and shared experts; section 4.4 sends the routed

@@ -246,9 +246,42 @@ moe_status moe_pack_mx4(const uint8_t* codes, const uint8_t* scales, int64_t mat
 
 namespace {
 
+// Scratch memory of moe_forward_noalloc: one array per GPU in the library's
+// code object, allocated when the code object is loaded on that device and
+// held until the process ends.  In host code `noalloc_scratch` names a
+// host-side stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) uint8_t noalloc_scratch[kNoAllocScratchBytes];
+
+// Device address of this device's scratch array (looked up once per device;
+// concurrent first calls look it up twice and store the same address).
+moe_status noalloc_scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return fail(MOE_ERR_DEVICE, "no usable HIP device (index %d)", dev);
+  }
+  static std::atomic<void*> ptrs[64];
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (!p) {
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                  dev, hipGetErrorString(e));
+    }
+    ptrs[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+// workspace == nullptr with noalloc: the per-device scratch array
 moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void* x_bf16,
                         int64_t num_tokens, void* y_bf16, void* workspace, size_t workspace_bytes,
-                        const moe_taps* taps, void* stream) {
+                        const moe_taps* taps, void* stream, bool noalloc) {
   if (!plan) return fail(MOE_ERR_INVALID_ARG, "plan is NULL");
   const moe_config& c = plan->cfg;
   if (num_tokens < 0 || num_tokens > c.max_tokens)
@@ -273,10 +306,18 @@ moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void
     return fail(MOE_ERR_INVALID_ARG,
                 "misaligned buffer (x, y, codes, router_w: 16 bytes; scales, bias: 4 bytes)");
   const Layout L = make_layout(c, num_tokens);
-  if (!workspace || workspace_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", L.total,
-                workspace_bytes, workspace ? "" : " (NULL)");
-  if (!aligned(workspace, 256)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (noalloc) {
+    if (L.total > kNoAllocScratchBytes)
+      return fail(MOE_ERR_WORKSPACE,
+                  "moe_forward_noalloc: %lld tokens need %zu bytes of scratch, above its fixed %zu "
+                  "bytes; use moe_forward with a workspace",
+                  static_cast<long long>(num_tokens), L.total, kNoAllocScratchBytes);
+  } else {
+    if (!workspace || workspace_bytes < L.total)
+      return fail(MOE_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s", L.total,
+                  workspace_bytes, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
   if (taps) {
     if ((taps->x_codes && !aligned(taps->x_codes, 16)) ||
         (taps->h_codes && !aligned(taps->h_codes, 16)) ||
@@ -294,6 +335,10 @@ moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void
   int num_cus = 0;
   moe_status s = check_device(&num_cus);
   if (s != MOE_OK) return s;
+  if (noalloc) {
+    s = noalloc_scratch_ptr(&workspace);
+    if (s != MOE_OK) return s;
+  }
 
   char* ws = static_cast<char*>(workspace);
   FwdArgs a{};
@@ -368,7 +413,13 @@ extern "C" {
 moe_status moe_forward(const moe_plan_t* plan, const moe_weights* w, const void* x_bf16,
                        int64_t num_tokens, void* y_bf16, void* workspace, size_t workspace_bytes,
                        const moe_taps* taps, void* stream) {
-  return forward_impl(plan, w, x_bf16, num_tokens, y_bf16, workspace, workspace_bytes, taps, stream);
+  return forward_impl(plan, w, x_bf16, num_tokens, y_bf16, workspace, workspace_bytes, taps, stream,
+                      false);
+}
+
+moe_status moe_forward_noalloc(const moe_plan_t* plan, const moe_weights* w, const void* x_bf16,
+                               int64_t num_tokens, void* y_bf16, const moe_taps* taps, void* stream) {
+  return forward_impl(plan, w, x_bf16, num_tokens, y_bf16, nullptr, 0, taps, stream, true);
 }
 
 }  // extern "C"

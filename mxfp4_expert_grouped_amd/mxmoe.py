@@ -18,7 +18,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEV
 MOE_SRC_BF16, MOE_SRC_FP32 = 0, 1
 
 EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_workspace_bytes", "moe_quantize_act",
-            "moe_forward", "moe_profile_begin", "moe_profile_end", "moe_packed_scale_bytes",
+            "moe_forward", "moe_forward_noalloc", "moe_profile_begin", "moe_profile_end", "moe_packed_scale_bytes",
             "moe_pack_mx4", "moe_latent_tail_workspace_bytes", "moe_latent_tail",
             "moe_status_string", "moe_last_error")
 STAGES = ("router", "topk", "permute", "gate_up", "down", "combine")
@@ -91,6 +91,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_forward.argtypes = [c_void_p, POINTER(MoeWeights), c_void_p, c_int64, c_void_p,
                                 c_void_p, c_size_t, POINTER(MoeTaps), c_void_p]
     lib.moe_forward.restype = c_int
+    lib.moe_forward_noalloc.argtypes = [c_void_p, POINTER(MoeWeights), c_void_p, c_int64, c_void_p,
+                                        POINTER(MoeTaps), c_void_p]
+    lib.moe_forward_noalloc.restype = c_int
     lib.moe_profile_begin.argtypes = [c_void_p, c_uint32, c_int32]
     lib.moe_profile_begin.restype = c_int
     lib.moe_profile_end.argtypes = [c_void_p, POINTER(ctypes.c_double), POINTER(c_int32)]
@@ -149,6 +152,15 @@ def moe_forward(plan: c_void_p, weights: MoeWeights, x: int, num_tokens: int, y:
     _check(load_library().moe_forward(plan, ctypes.byref(weights), x, num_tokens, y, workspace,
                                       workspace_bytes, ctypes.byref(taps) if taps else None,
                                       stream))
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(plan: c_void_p, weights: MoeWeights, x: int, num_tokens: int, y: int,
+                        taps: Optional[MoeTaps] = None, stream: Optional[int] = None) -> None:
+    _check(load_library().moe_forward_noalloc(plan, ctypes.byref(weights), x, num_tokens, y,
+                                              ctypes.byref(taps) if taps else None, stream))
 
 
 def moe_profile_begin(plan: c_void_p, stages, max_calls: int) -> None:

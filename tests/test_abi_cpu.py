@@ -223,6 +223,25 @@ def test_pack_sizes_and_argument_errors(M):
         assert ei.value.status == status
 
 
+def test_noalloc_forward_rejects_token_counts_above_its_scratch(M):
+    # checked on the host before any device call: 300 tokens of the full layer
+    # need more than the fixed scratch array; 0 tokens is a no-op
+    p = M.moe_plan(7168, 2048, 896, 16, 2, 1024)
+    fake = 1 << 20
+    W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, M.MOE_WEIGHTS_PACKED)
+    try:
+        assert M.moe_workspace_bytes(p, 256) <= M.NOALLOC_SCRATCH_BYTES < M.moe_workspace_bytes(p, 300)
+        M.moe_forward_noalloc(p, W, None, 0, None)
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_forward_noalloc(p, W, fake, 300, fake)
+        assert ei.value.status == M.MOE_ERR_WORKSPACE and "scratch" in ei.value.detail
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_forward_noalloc(p, M.MoeWeights(), fake, 8, fake)
+        assert ei.value.status == M.MOE_ERR_INVALID_ARG
+    finally:
+        M.moe_plan_destroy(p)
+
+
 def test_latent_tail_host_checks(M):
     fake = 1 << 20
     W = M.MoeTailWeights(fake, fake, fake, M.MOE_WEIGHTS_PACKED)
