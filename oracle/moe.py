@@ -186,11 +186,43 @@ def expert_mlp(a_codes, a_scales, gu_codes, gu_scales, dn_codes, dn_scales, d_ff
     return h_codes, h_scales, o
 
 
+def expert_mlp_a16(a_bf16, gu_codes, gu_scales, dn_codes, dn_scales, d_ff: int,
+                   intermediates: Optional[dict] = None):
+    """One expert with bf16 activations and MXFP4 weights (the A16W4 variant
+    of "Kimi K3 Tech Intro", sections 4.3 and 10): A = the bf16 rows as they
+    are; [g | u] = A W_gu^T; h = silu(g) * u rounded to bf16 (round to
+    nearest even), the 16-bit activation between the two projections;
+    o = h W_dn^T.  Returns (h bf16 bit patterns [n, d_ff], o [n, d] float64).
+    ``intermediates`` as for expert_mlp ("gu", "gu_abs", "h" before its
+    rounding, "o_abs")."""
+    a = bf16_to_f64(a_bf16)
+    wgu = mx.mx_decode(gu_codes, gu_scales, "e2m1")
+    gu = a @ wgu.T
+    if intermediates is not None:
+        intermediates["gu"] = gu
+        intermediates["gu_abs"] = np.abs(a) @ np.abs(wgu).T
+    del wgu
+    h = silu(gu[:, :d_ff]) * gu[:, d_ff:]
+    h_bits = f64_to_bf16(h)
+    hq = bf16_to_f64(h_bits)
+    wdn = mx.mx_decode(dn_codes, dn_scales, "e2m1")
+    o = hq @ wdn.T
+    if intermediates is not None:
+        intermediates["h"] = h
+        intermediates["o_abs"] = np.abs(hq) @ np.abs(wdn).T
+    return h_bits, o
+
+
 def _expert_job(job):
-    """expert_mlp of one expert on its rows: job = (weights, kind, index,
-    a_codes, a_scales, d_ff, intermediates) -> (h_codes, h_scales, o, mid)."""
-    weights, kind, index, a_codes, a_scales, d_ff, intermediates = job
+    """One expert on its rows: job = (weights, kind, index, a_codes, a_scales,
+    d_ff, intermediates, activations) -> (h_codes, h_scales, o, mid); with
+    bf16 activations a_codes are the rows' bf16 bits, h_codes h's bf16 bits
+    and h_scales None."""
+    weights, kind, index, a_codes, a_scales, d_ff, intermediates, activations = job
     mid = {} if intermediates else None
+    if activations == "bf16":
+        h_c, o = expert_mlp_a16(a_codes, *weights(kind, index), d_ff=d_ff, intermediates=mid)
+        return h_c, None, o, mid
     h_c, h_s, o = expert_mlp(a_codes, a_scales, *weights(kind, index), d_ff=d_ff, intermediates=mid)
     return h_c, h_s, o, mid
 
@@ -234,7 +266,7 @@ class LayerResult:
 def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: int,
             num_shared: int, d_ff: int, tokens: Optional[Sequence[int]] = None,
             topk_ids=None, intermediates: bool = False, logits=None,
-            expert_map=map) -> LayerResult:
+            expert_map=map, activations: str = "mxfp8") -> LayerResult:
     """Full layer.  Routing, permutation and the MXFP8 quantisation of x are
     computed for every token; expert outputs only for ``tokens`` (all when
     None).  Each token's output depends only on its own row, so a subset gives
@@ -252,7 +284,12 @@ def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: i
     ``expert_map(fn, jobs)`` evaluates the independent per-expert jobs (the
     builtin map: one after another here; a process pool's map runs them side
     by side); results are used in job order.
+    ``activations``: "mxfp8" (the layer: MXFP8 x and h) or "bf16" (the A16W4
+    variant: x as given, h rounded to bf16; expert_mlp_a16).  With "bf16",
+    x_codes holds the computed tokens' bf16 bits, x_scales has no columns,
+    and h_rows / h_shared hold (h bf16 bits, None).
     """
+    assert activations in ("mxfp8", "bf16")
     x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
     t_count, d = x_bf16.shape
     if logits is None:
@@ -270,7 +307,10 @@ def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: i
     toks = np.arange(t_count) if tokens is None else np.asarray(sorted(set(int(t) for t in tokens)))
     pos = {int(t): i for i, t in enumerate(toks)}
     # MXFP8 activations of the computed tokens (row i <-> token toks[i])
-    x_codes, x_scales = mx.mx_quantize(bf16_to_f64(x_bf16[toks]), "e4m3")
+    if activations == "bf16":
+        x_codes, x_scales = x_bf16[toks].copy(), np.zeros((len(toks), 0), np.uint8)
+    else:
+        x_codes, x_scales = mx.mx_quantize(bf16_to_f64(x_bf16[toks]), "e4m3")
     y_routed = np.zeros((len(toks), d))
     y_shared = np.zeros((len(toks), d))
     res_h: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
@@ -290,23 +330,23 @@ def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: i
             continue
         pairs = row_src[rows]
         xi = np.array([pos[int(t)] for t in pairs // top_k])
-        jobs.append((weights, "routed", e, x_codes[xi], x_scales[xi], d_ff, intermediates))
+        jobs.append((weights, "routed", e, x_codes[xi], x_scales[xi], d_ff, intermediates, activations))
         placement.append(("routed", e, rows, pairs // top_k, pairs % top_k))
     for s in range(num_shared):
-        jobs.append((weights, "shared", s, x_codes, x_scales, d_ff, intermediates))
+        jobs.append((weights, "shared", s, x_codes, x_scales, d_ff, intermediates, activations))
         placement.append(("shared", s, None, toks, None))
     # expert_map only decides where the jobs run (default: here, in order);
     # the results are summed below in job order either way
     for (kind, e, rows, tk, jj), (h_c, h_s, o, mid) in zip(placement, expert_map(_expert_job, jobs)):
         if kind == "routed":
             for i in range(rows.size):
-                res_h[int(rows[i])] = (h_c[i], h_s[i])
+                res_h[int(rows[i])] = (h_c[i], None if h_s is None else h_s[i])
                 y_routed[pos[int(tk[i])]] += w[tk[i], jj[i]] * o[i]
                 if intermediates:
                     res_mid[int(rows[i])] = dict({k: v[i] for k, v in mid.items()}, o=o[i])
         else:
             for i, t in enumerate(toks):
-                res_hs[(e, int(t))] = (h_c[i], h_s[i])
+                res_hs[(e, int(t))] = (h_c[i], None if h_s is None else h_s[i])
                 if intermediates:
                     res_mids[(e, int(t))] = dict({k: v[i] for k, v in mid.items()}, o=o[i])
             y_shared += o
@@ -318,7 +358,7 @@ def forward(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: i
 
 
 def forward_dense(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, top_k: int,
-                  num_shared: int, d_ff: int) -> np.ndarray:
+                  num_shared: int, d_ff: int, activations: str = "mxfp8") -> np.ndarray:
     """The same layer computed densely: every expert on every token, scaled by a
     full [T, E] weight matrix that is zero for unselected experts.  Used only to
     pin :func:`forward` (sparse gather/scatter) against a computation that has
@@ -332,13 +372,17 @@ def forward_dense(x_bf16, w_r, b, weights: WeightSource, *, num_experts: int, to
     dense_w = np.zeros((t_count, num_experts))
     np.put_along_axis(dense_w, ids.astype(np.int64), w, axis=1)
     x_codes, x_scales = mx.mx_quantize(bf16_to_f64(x_bf16), "e4m3")
+
+    def run(kind, idx):
+        if activations == "bf16":
+            return expert_mlp_a16(x_bf16, *weights(kind, idx), d_ff=d_ff)[1]
+        return expert_mlp(x_codes, x_scales, *weights(kind, idx), d_ff=d_ff)[2]
+
     y = np.zeros((t_count, d))
     for e in range(num_experts):
-        _, _, o = expert_mlp(x_codes, x_scales, *weights("routed", e), d_ff=d_ff)
-        y += dense_w[:, e:e + 1] * o
+        y += dense_w[:, e:e + 1] * run("routed", e)
     for s in range(num_shared):
-        _, _, o = expert_mlp(x_codes, x_scales, *weights("shared", s), d_ff=d_ff)
-        y += o
+        y += run("shared", s)
     return y
 
 

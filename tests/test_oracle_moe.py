@@ -308,3 +308,55 @@ def test_latent_tail_is_norm_quantise_project_add():
     w = torch.from_numpy(mx.mx_decode(up_c, up_s, "e2m1"))
     ref = a @ w.T + torch.from_numpy(s.astype(np.float64))
     assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12 * float(ref.abs().max()))
+
+
+# ---------------------------------------------------------------------------
+# A16W4 variant (bf16 activations, MXFP4 weights)
+# ---------------------------------------------------------------------------
+
+def test_a16w4_single_expert_is_textbook_swiglu_with_bf16_h():
+    cfg = I.LayerConfig("one16", 4, 128, 1, 1, 64, 0, seed=6)
+    x, wr = I.gen_x(cfg), I.gen_router_w(cfg)
+    W = I.ExpertWeights(cfg)
+    res = moe.forward(x, wr, None, W, num_experts=1, top_k=1, num_shared=0, d_ff=cfg.d_ff,
+                      activations="bf16")
+    guc, gus, dnc, dns = W("routed", 0)
+    xt = torch.from_numpy(moe.bf16_to_f64(x))
+    wgu = torch.from_numpy(mx.mx_decode(guc, gus, "e2m1"))
+    wdn = torch.from_numpy(mx.mx_decode(dnc, dns, "e2m1"))
+    h = torch.nn.functional.silu(xt @ wgu[:64].T) * (xt @ wgu[64:].T)
+    hb = h.to(torch.bfloat16)
+    y = hb.to(torch.float64) @ wdn.T
+    assert np.allclose(res.y, y.numpy(), rtol=1e-12, atol=1e-13 * float(y.abs().max()))
+    assert np.array_equal(res.h_rows[0][0], hb[0].view(torch.int16).numpy().view(np.uint16))
+    assert res.h_rows[0][1] is None and res.x_scales.shape == (4, 0)
+
+
+def test_a16w4_sparse_equals_dense():
+    cfg = I.LayerConfig("t16", 12, 128, 24, 4, 64, 2, zipf_bias=True, seed=7)
+    x, wr, b = I.gen_x(cfg), I.gen_router_w(cfg), I.gen_router_b(cfg)
+    W = I.ExpertWeights(cfg)
+    kw = dict(num_experts=24, top_k=4, num_shared=2, d_ff=64, activations="bf16")
+    dense = moe.forward_dense(x, wr, b, W, **kw)
+    sparse = moe.forward(x, wr, b, W, **kw)
+    assert np.allclose(sparse.y, dense, rtol=1e-12, atol=1e-14 * np.abs(dense).max())
+    # and it differs from the MXFP8-activation layer by more than rounding noise
+    a8 = moe.forward(x, wr, b, W, num_experts=24, top_k=4, num_shared=2, d_ff=64)
+    assert np.linalg.norm(a8.y - sparse.y) > 1e-4 * np.linalg.norm(sparse.y)
+
+
+def test_a16w4_intermediates_exact_on_integer_operands():
+    rng = np.random.default_rng(16)
+    d, f, n = 64, 32, 4
+    xi = rng.integers(-16, 17, size=(n, d)).astype(np.float32)
+    bits = I.f32_to_bf16_bits(xi)
+    value_code = {1: 2, 2: 4, 3: 5, 4: 6, 6: 7}
+    wg = rng.choice([1, 2, 3, 4, 6], size=(2 * f, d)) * rng.choice([-1, 1], size=(2 * f, d))
+    enc = np.vectorize(lambda q: value_code[abs(q)] | (8 if q < 0 else 0))
+    guc, gus = mx.pack_fp4(enc(wg).astype(np.uint8)), np.full((2 * f, d // 32), 127, np.uint8)
+    dnc = mx.pack_fp4(enc(rng.choice([1, 2], size=(d, f))).astype(np.uint8))
+    dns = np.full((d, f // 32), 127, np.uint8)
+    mid = {}
+    hb, o = moe.expert_mlp_a16(bits, guc, gus, dnc, dns, d_ff=f, intermediates=mid)
+    assert np.array_equal(mid["gu"], (xi.astype(np.int64) @ wg.T.astype(np.int64)).astype(np.float64))
+    assert np.array_equal(hb, moe.f64_to_bf16(mid["h"]))
