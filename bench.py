@@ -47,6 +47,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the forward as a HIP graph")
     ap.add_argument("--breakdown", action="store_true", help="also time every stage (untimed pass)")
+    ap.add_argument("--a16w4", action="store_true",
+                    help="the A16W4 variant (bf16 activations; decode workloads only)")
+    ap.add_argument("--tail", action="store_true",
+                    help="also time the LatentMoE tail (moe_latent_tail) on the same token count, "
+                         "latent = hidden = d_model, and report it as 'latent_tail'")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once (a plain copy "
                          "kernel of known size, to calibrate hardware byte counters)")
@@ -70,6 +75,11 @@ def main():
     torch.cuda.set_device(0)
     cfg = I.CONFIGS[args.config]
     decode = cfg.tokens <= 256
+    if args.a16w4 and not decode:
+        print(json.dumps({"error": "the A16W4 variant runs the weight-streaming kernels only "
+                                   "(decode workloads: tiny, decode1, decode256)"}))
+        sys.exit(2)
+    flags = M.MOE_FLAG_A16W4 if args.a16w4 else 0
     steps = args.steps or (200 if decode else 10)
     warmup = args.warmup if args.warmup is not None else (20 if decode else 2)
     nlayers = args.layers or (4 if decode else 1)
@@ -81,7 +91,8 @@ def main():
     layers, xs = [], []
     for li in range(nlayers):
         W = IG.device_weights(cfg, layer=li)
-        layers.append(MoeLayer(cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k, cfg.num_shared, T, W))
+        layers.append(MoeLayer(cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k, cfg.num_shared, T, W,
+                               flags=flags))
         xs.append([IG.device_x(cfg, layer=1000 * li + bi) for bi in range(nbatch)])
     ws = torch.empty(layers[0].workspace_bytes(T), dtype=torch.uint8, device="cuda")
     ys = torch.empty((T, cfg.d_model), dtype=torch.bfloat16, device="cuda")
@@ -99,8 +110,12 @@ def main():
             counts = np.diff(offs.cpu().numpy())
             touched[(li, bi)] = (int((counts > 0).sum()), counts)
     R = T * cfg.top_k + cfg.num_shared * T
-    act_in = T * (cfg.d_model + cfg.d_model // 32)            # MXFP8 x rows
-    h_bytes = R * (cfg.d_ff + cfg.d_ff // 32)                  # MXFP8 h rows
+    if args.a16w4:
+        act_in = T * cfg.d_model * 2                            # bf16 x rows
+        h_bytes = R * cfg.d_ff * 2                              # bf16 h rows
+    else:
+        act_in = T * (cfg.d_model + cfg.d_model // 32)          # MXFP8 x rows
+        h_bytes = R * (cfg.d_ff + cfg.d_ff // 32)               # MXFP8 h rows
     router_bytes = cfg.num_experts * cfg.d_model * 4
     xy_bytes = 2 * T * cfg.d_model * 2
 
@@ -254,13 +269,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8 x mxfp4, fp32 accumulate",
+        "dtype": ("bf16 x mxfp4 (A16W4), fp32 accumulate" if args.a16w4
+                  else "mxfp8 x mxfp4, fp32 accumulate"),
         "data": "synthetic (seeded; random-init MXFP4 weights)",
         "config": {"workload": f"{cfg.name}: T={T}, d_model={cfg.d_model}, experts={cfg.num_experts}, "
                                f"top_k={cfg.top_k}, d_ff={cfg.d_ff}, shared={cfg.num_shared}"
                                + (", Zipf(1.1) router bias" if cfg.zipf_bias else ""),
                    "tokens_per_step": T, "weight_copies_rotated": nlayers,
-                   "token_batches": nbatch, "hip_graph": bool(args.graph)},
+                   "token_batches": nbatch, "hip_graph": bool(args.graph),
+                   "variant": "A16W4" if args.a16w4 else "A8W4"},
         "layer_hbm_gbps": round(layer_gbs, 1),
         "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
         "layer_tflops": round(layer_tflops, 2),
@@ -276,7 +293,61 @@ def main():
     }
     if stage_avg:
         out["stage_ms"] = stage_avg
+    if args.tail:
+        out["latent_tail"] = bench_tail(cfg, steps, warmup)
     print(json.dumps(out), flush=True)
+
+
+def bench_tail(cfg, steps: int, warmup: int):
+    """The LatentMoE tail y = MXFP8(RMSNorm(z)) W_up^T + s on the workload's
+    token count at latent = hidden = d_model, inputs resident in HBM; HIP
+    events around the timed calls on torch's current stream (the stream every
+    launch of the call goes to)."""
+    import torch
+    from mxfp4_expert_grouped_amd import inputs as I
+    from mxfp4_expert_grouped_amd import mxmoe as M
+    T, l = cfg.tokens, cfg.d_model
+    H = l
+    z, s, gamma = I.gen_tail_inputs(T, l, H, seed=1)
+    up_c, up_s = I.gen_up_matrix(H, l, seed=1)
+    tc, ts = torch.from_numpy(up_c).cuda(), torch.from_numpy(up_s).cuda()
+    cp = torch.empty(H * l // 2, dtype=torch.uint8, device="cuda")
+    sp = torch.empty(M.moe_packed_scale_bytes(H, l), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    M.moe_pack_mx4(tc.data_ptr(), ts.data_ptr(), 1, H, l, 0, cp.data_ptr(), sp.data_ptr(), st)
+    zt, stt, gt = (torch.from_numpy(a).cuda() for a in (z, s, gamma))
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    nb = M.moe_latent_tail_workspace_bytes(T, l, H)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    W = M.MoeTailWeights(cp.data_ptr(), sp.data_ptr(), gt.data_ptr(), M.MOE_WEIGHTS_PACKED)
+
+    def call():
+        M.moe_latent_tail(T, l, H, 1e-6, W, zt.data_ptr(), stt.data_ptr(), y.data_ptr(), ws.data_ptr(),
+                          nb, None, st)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = T * l * 4 + T * H * 4 + T * H * 2 + H * l // 2 + H * l // 32 + l * 4
+    flops = 2.0 * T * l * H
+    t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e9), flops / (FP8_MFMA_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    achieved = nbytes / (ms / 1e3) / 1e9 if bound == "hbm" else flops / (ms / 1e3) / 1e12
+    peak = HBM_PEAK_GBS if bound == "hbm" else FP8_MFMA_PEAK_TFLOPS
+    return {"tokens": T, "latent": l, "hidden": H, "ms_per_call": round(ms, 5),
+            "tokens_per_s": round(T / (ms / 1e3), 1), "algorithmic_bytes": int(nbytes),
+            "algorithmic_flops": flops,
+            "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                         "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+                         "frac": round(achieved / peak, 4),
+                         "frac_of_bound_time": round(max(t_hbm, t_mfma) * 1e3 / ms, 4)}}
 
 
 def profiled_traffic(workload: str):

@@ -71,7 +71,20 @@ typedef enum { MOE_SRC_BF16 = 0, MOE_SRC_FP32 = 1 } moe_src_dtype;
 
 /* Layer shape.  d_model: a multiple of 256; d_ff: a multiple of 128.  1 <= num_experts <= 1024.
  * 1 <= top_k <= min(32, num_experts).  0 <= num_shared <= 8.
- * 1 <= max_tokens <= 2^20.  flags: reserved, must be 0. */
+ * 1 <= max_tokens <= 2^20.  flags: 0 (the layer with MXFP8 activations,
+ * "A8W4") or MOE_FLAG_A16W4. */
+
+/* The A16W4 variant ("Kimi K3 Tech Intro", sections 4.3 and 10 name A16W4
+ * and A8W4 fused operators on MI355X): x stays bf16 into the gate_up
+ * projection and h = silu(g)*u is rounded to bf16 (round to nearest even)
+ * into the down projection; no MXFP8 activation anywhere; weights, router,
+ * permutation and combine as in the A8W4 layer.  Implemented on the
+ * weight-streaming kernels only: moe_forward returns MOE_ERR_UNSUPPORTED
+ * when num_tokens * top_k / num_experts >= 24 (the average rows per expert
+ * at which the A8W4 layer switches to its 256-row prefill kernels).  The
+ * x_codes, x_scales, h_codes and h_scales taps must be NULL; h comes out
+ * through the h_bf16 tap. */
+#define MOE_FLAG_A16W4 1u
 typedef struct {
   int32_t d_model, d_ff, num_experts, top_k, num_shared;
   int64_t max_tokens;
@@ -98,9 +111,9 @@ typedef struct {
  * Permuted rows: R = T*top_k routed rows (expert-major, tokens ascending)
  * followed by num_shared blocks of T rows (shared expert s, token t at
  * T*top_k + s*T + t). */
-/* Alignment: x_codes, x_scales, h_codes, h_scales, y_routed and y_shared
- * 16 bytes (the kernels move them in 16-byte pieces), every other tap 4
- * bytes; a misaligned tap is rejected with MOE_ERR_INVALID_ARG. */
+/* Alignment: x_codes, x_scales, h_codes, h_scales, h_bf16, y_routed and
+ * y_shared 16 bytes (the kernels move them in 16-byte pieces), every other
+ * tap 4 bytes; a misaligned tap is rejected with MOE_ERR_INVALID_ARG. */
 typedef struct {
   float *logits;          /* [T][E]   router logits incl. bias (fp32)        */
   int32_t *topk_ids;      /* [T][top_k] selected experts, ascending          */
@@ -115,6 +128,7 @@ typedef struct {
   float *gu_acc;          /* [R][2*d_ff]   fp32 gate|up accumulators         */
   float *y_routed;        /* [T][d_model]  sum_j w o (fp32)                  */
   float *y_shared;        /* [T][d_model]  sum_s o_s (fp32)                  */
+  uint16_t *h_bf16;       /* [R][d_ff] bf16 h, permuted rows (A16W4 only)    */
 } moe_taps;
 
 /* Packed MXFP4 matrix (one-time conversion at weight-load time).  For a

@@ -120,8 +120,13 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.tiles = take(size_t(std::max(L.max_tiles, 1)) * sizeof(Tile));
   L.tile_count = take(4);
   L.ex_tiles = take((E + S + 1) * 4);
-  L.h_codes = take(R * f);
-  L.h_scales = take(R * f / 32);
+  if (c.flags & MOE_FLAG_A16W4) {
+    L.h_codes = take(R * f * 2);   // bf16 h
+    L.h_scales = take(0);
+  } else {
+    L.h_codes = take(R * f);
+    L.h_scales = take(R * f / 32);
+  }
   L.o = take(R * d * 2);
   L.total = off;
   return L;
@@ -132,7 +137,7 @@ moe_status check_config(const moe_config* c) {
   if (c->d_model <= 0 || c->d_ff <= 0 || c->num_experts <= 0 || c->top_k <= 0 ||
       c->num_shared < 0 || c->max_tokens <= 0)
     return fail(MOE_ERR_INVALID_ARG, "non-positive size in config");
-  if (c->flags != 0) return fail(MOE_ERR_INVALID_ARG, "flags must be 0");
+  if (c->flags & ~MOE_FLAG_A16W4) return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
   if (c->d_model % 256 || c->d_ff % 128)
     return fail(MOE_ERR_UNSUPPORTED, "d_model (%d) must be a multiple of 256 and d_ff (%d) of 128",
                 c->d_model, c->d_ff);
@@ -305,6 +310,16 @@ moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void
                             !aligned(w->sgu_scales, 4) || !aligned(w->sdn_scales, 4))))
     return fail(MOE_ERR_INVALID_ARG,
                 "misaligned buffer (x, y, codes, router_w: 16 bytes; scales, bias: 4 bytes)");
+  const bool a16 = (c.flags & MOE_FLAG_A16W4) != 0;
+  if (a16 && choose_bm(c, num_tokens) != kDecodeMaxRows)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "A16W4 runs the weight-streaming kernels only: %lld tokens x top-%d over %d experts is "
+                "24 or more rows per expert on average",
+                static_cast<long long>(num_tokens), c.top_k, c.num_experts);
+  if (taps && a16 && (taps->x_codes || taps->x_scales || taps->h_codes || taps->h_scales))
+    return fail(MOE_ERR_INVALID_ARG, "A16W4 has no MXFP8 activations: x/h code and scale taps must be NULL");
+  if (taps && !a16 && taps->h_bf16)
+    return fail(MOE_ERR_INVALID_ARG, "the h_bf16 tap exists only in the A16W4 variant");
   const Layout L = make_layout(c, num_tokens);
   if (noalloc) {
     if (L.total > kNoAllocScratchBytes)
@@ -329,7 +344,8 @@ moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void
         (taps->topk_ids && !aligned(taps->topk_ids, 4)) ||
         (taps->expert_offsets && !aligned(taps->expert_offsets, 4)) ||
         (taps->row_src && !aligned(taps->row_src, 4)) ||
-        (taps->token_row && !aligned(taps->token_row, 4)) || (taps->gu_acc && !aligned(taps->gu_acc, 4)))
+        (taps->token_row && !aligned(taps->token_row, 4)) || (taps->gu_acc && !aligned(taps->gu_acc, 4)) ||
+        (taps->h_bf16 && !aligned(taps->h_bf16, 16)))
       return fail(MOE_ERR_INVALID_ARG, "misaligned tap buffer");
   }
   int num_cus = 0;
@@ -373,8 +389,13 @@ moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void
   a.tiles = reinterpret_cast<Tile*>(ws + L.tiles);
   a.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
   a.ex_tiles = reinterpret_cast<int32_t*>(ws + L.ex_tiles);
-  a.h_codes = pick(tp.h_codes, L.h_codes, static_cast<uint8_t*>(nullptr));
-  a.h_scales = pick(tp.h_scales, L.h_scales, static_cast<uint8_t*>(nullptr));
+  a.a16 = a16 ? 1 : 0;
+  if (a16) {
+    a.h16 = pick(tp.h_bf16, L.h_codes, static_cast<uint16_t*>(nullptr));
+  } else {
+    a.h_codes = pick(tp.h_codes, L.h_codes, static_cast<uint8_t*>(nullptr));
+    a.h_scales = pick(tp.h_scales, L.h_scales, static_cast<uint8_t*>(nullptr));
+  }
   a.o16 = reinterpret_cast<uint16_t*>(ws + L.o);
   a.gu_acc = tp.gu_acc;
   a.y_routed = tp.y_routed;

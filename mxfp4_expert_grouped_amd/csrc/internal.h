@@ -45,6 +45,8 @@ struct FwdArgs {
   int32_t* ex_tiles;    // [E+S+1] first tile of each expert (prefix over tile counts)
   uint8_t* h_codes;     // [R][dff]
   uint8_t* h_scales;    // [R][dff/32]
+  uint16_t* h16;        // [R][dff] bf16 h (A16W4 variant), else unused
+  int a16;              // 1: A16W4 variant (bf16 x and h, no MXFP8 activations)
   uint16_t* o16;        // [R][d] bf16 down outputs: permuted-row order after the
                         // decode kernels, (token, slot) order after the prefill ones
   // optional taps (null = skip)

@@ -27,6 +27,8 @@
 namespace mxmoe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, v4f c, uint32_t sa, uint32_t sb) {
@@ -126,6 +128,7 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // ---------------------------------------------------------------------------
 constexpr int kDsS = 7;                        // ring slots per wave (5632-byte slots)
 constexpr int kDsSWide = 4;                    // ring slots per wave of wide items (9984 bytes)
+constexpr int kDsS16 = 6;                      // ring slots per wave with bf16 activations (6400 bytes)
 // LDS: four waves' rings, then per wave 8 x {ex, row_begin, row_end, group}
 constexpr int kDsLds = 4 * kDsSWide * 9984 + 4 * 8 * 16;   // 160256 bytes (the larger ring)
 __shared__ __attribute__((aligned(1024))) uint8_t ds_lds[kDsLds];
@@ -151,13 +154,21 @@ __device__ __forceinline__ int sload1(const void* p) {
   return v;
 }
 
-template <bool GU, bool KSPLIT, bool WIDE>
+// A16 (the A16W4 variant: bf16 activations): the activation rows are bf16
+// (8 rows x 256 bytes per K step, two copies, no activation scales), the
+// weights are expanded in registers from FP4 to bf16 with their block scale
+// (V_CVT_SCALEF32_PK_BF16_FP4) and multiplied on the bf16 MFMA
+// (16x16x32: four per 16-row block and K step); h leaves the gate_up
+// epilogue as bf16.  Six ring slots of 6400 bytes; no two-group items.
+template <bool GU, bool KSPLIT, bool WIDE, bool A16 = false>
 __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   // ring geometry: WIDE items (down only) cover two 64-row groups
   constexpr int GPI = WIDE ? 2 : 1;                 // packed groups per item
-  constexpr int S = WIDE ? kDsSWide : kDsS;         // ring slots per wave
+  constexpr int S = A16 ? kDsS16 : (WIDE ? kDsSWide : kDsS);  // ring slots per wave
   constexpr int NC = 4 * GPI + 2 + GPI;             // copies per element
-  constexpr int SW = 0, SA = 4096 * GPI, SAS = SA + 1024, SBS = SAS + 256, SLOT = SBS + 256 * GPI;
+  constexpr int SW = 0, SA = 4096 * GPI, SAS = SA + (A16 ? 2048 : 1024), SBS = A16 ? SAS : SAS + 256,
+                SLOT = SBS + 256 * GPI;
+  static_assert(!(A16 && WIDE), "no two-group items with bf16 activations");
   constexpr int WAVE = S * SLOT, FIFO = 4 * WAVE;
   static_assert(FIFO + 4 * 8 * 16 <= kDsLds, "ring does not fit");
   static_assert(!(WIDE && (GU || KSPLIT)), "wide items are for the down GEMM");
@@ -205,6 +216,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   const uint8_t* bs_src = nullptr;
   const uint8_t* a_src = nullptr;
   const uint8_t* as_src = nullptr;
+  const uint8_t* a16_src[2] = {nullptr, nullptr};
   const int ar = lane >> 3;                           // A row of this lane's copy
   const int achunk = (lane & 7) ^ ((ar >> 1) & 3);    // global chunk landing at chunk lane&7
   int cur_tile = -1, ex = 0, rb = 0, nr = 0;
@@ -229,29 +241,34 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     w_src = wc + int64_t(G) * GPI * ns * 4096 + 16 * lane;
     bs_src = ws + int64_t(G) * GPI * ns * 256 + 4 * lane;
     if (!new_tile) return;
-    // activation rows of the tile (rows past the end repeat the first)
-    int src_a, src_s;
-    const int r_a = ar < nr ? ar : 0, r_s = (lane & 7) < nr ? (lane & 7) : 0;
-    if (!GU) {
-      src_a = rb + r_a;
-      src_s = rb + r_s;
-    } else if (shared) {
-      src_a = rb - a.Rr - sidx * a.T + r_a;
-      src_s = rb - a.Rr - sidx * a.T + r_s;
-    } else {
-      // eight entries (the workspace pads row_token by eight past the last
-      // routed row); only rows < nr are used
-      const v8i_s rt = sload8(a.row_token + rb);
-      src_a = rt[0];
-      src_s = rt[0];
+    // activation row of tile row r (rows past the end repeat the first); a
+    // routed gate_up tile reads its eight row-token entries with one scalar
+    // load (the workspace pads row_token by eight past the last routed row;
+    // only rows < nr are used)
+    v8i_s rt = {};
+    if (GU && !shared) rt = sload8(a.row_token + rb);
+    auto act_row = [&](int r) -> int {
+      const int rr = r < nr ? r : 0;
+      if (!GU) return rb + rr;
+      if (shared) return rb - a.Rr - sidx * a.T + rr;
+      int v = rt[0];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) {
-        src_a = r_a == j ? rt[j] : src_a;
-        src_s = r_s == j ? rt[j] : src_s;
+      for (int j = 1; j < 8; ++j) v = rr == j ? rt[j] : v;
+      return v;
+    };
+    if constexpr (A16) {
+      // copy q moves rows 4q .. 4q+3 (lane -> row 4q + lane/16, 16-byte chunk
+      // lane%16 ^ row%16, landing at chunk lane%16), so both copies always go out
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rr = 4 * q + (lane >> 4);
+        a16_src[q] = reinterpret_cast<const uint8_t*>(GU ? a.x : a.h16) + int64_t(act_row(rr)) * K * 2 +
+                     16 * ((lane & 15) ^ (rr & 15));
       }
+      return;
     }
-    a_src = (GU ? a.x_codes : a.h_codes) + int64_t(src_a) * K + 16 * achunk;
-    as_src = (GU ? a.x_scales : a.h_scales) + int64_t(src_s) * (K / 32);
+    a_src = (GU ? a.x_codes : a.h_codes) + int64_t(act_row(ar)) * K + 16 * achunk;
+    as_src = (GU ? a.x_scales : a.h_scales) + int64_t(act_row(lane & 7)) * (K / 32);
   };
   auto issue = [&](int el) {
     const int il = el / nsw, si = el - il * nsw;
@@ -271,8 +288,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
       }
     // only the tile's rows (tiles are never empty, so the copy is always
     // issued and every element counts NC copies)
-    if (lane < 8 * nr) lds_copy16(a_src + 128 * st, slot + SA);
-    lds_copy4(as_src + 4 * st, slot + SAS);
+    if constexpr (A16) {
+      lds_copy16(a16_src[0] + 256 * st, slot + SA);
+      lds_copy16(a16_src[1] + 256 * st, slot + SA + 1024);
+    } else {
+      if (lane < 8 * nr) lds_copy16(a_src + 128 * st, slot + SA);
+      lds_copy4(as_src + 4 * st, slot + SAS);
+    }
 #pragma unroll
     for (int g2 = 0; g2 < GPI; ++g2) {
       if (WIDE) lds_copy4(bs_src + int64_t(g2) * ns * 256 + st * 256, slot + SBS + g2 * 256);
@@ -287,7 +309,41 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   v4f acc[4 * GPI];
 #pragma unroll
   for (int j = 0; j < 4 * GPI; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // bf16 operands: lane (row i = lane%16, group kg = lane/16) supplies, for
+  // MFMA c of a step, the 8 values k = 32 kg + 8c .. +7: its A row's 16
+  // bytes at chunk 4 kg + c, and 8 of the 32 FP4 weights it holds (block kg
+  // of its weight row), expanded with that block's scale.  Any assignment of
+  // k to (lane group, element) gives the same sum as long as A and B agree.
+  const int a16_row = r16 & 7;
+  auto compute16 = [&](int el) {
+    const uint8_t* sl = wlds + (el % S) * SLOT;
+    v8bf16 av[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      av[c] = *reinterpret_cast<const v8bf16*>(sl + SA + a16_row * 256 + 16 * ((4 * g + c) ^ a16_row));
+    const uint32_t sbw = *reinterpret_cast<const uint32_t*>(sl + SBS + 4 * lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 wv = ld16(sl + SW + j * 1024 + 16 * lane);
+      const uint32_t sb = (sbw >> (8 * j)) & 0xFFu;
+      const float scl = __uint_as_float(sb ? sb << 23 : 0x00400000u);  // 2^(sb-127)
+      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const v2bf16 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], scl, 0);
+        const v2bf16 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], scl, 1);
+        const v2bf16 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], scl, 2);
+        const v2bf16 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], scl, 3);
+        const v8bf16 bv = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], bv, acc[j], 0, 0, 0);
+      }
+    }
+  };
   auto compute = [&](int el) {
+    if constexpr (A16) {
+      compute16(el);
+      return;
+    }
     const uint8_t* sl = wlds + (el % S) * SLOT;
     const v8i av = make_a(ld16(sl + SA + a_off0), ld16(sl + SA + a_off1));
     const uint32_t sa = *reinterpret_cast<const uint32_t*>(sl + SAS + 4 * arow) >> (8 * g);
@@ -322,6 +378,14 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
         a.gu_acc[int64_t(row) * 2 * a.dff + c] = v[j];
         a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + c] = v[2 + j];
       }
+    }
+    if constexpr (A16) {
+      if (valid) {
+        uint16_t* hb = a.h16 + int64_t(row) * a.dff + 32 * G + col;
+        hb[0] = f32_to_bf16_rne(h[0]);
+        hb[16] = f32_to_bf16_rne(h[1]);
+      }
+      return;
     }
     const int e = mx8_block_exp(group_max<16>(fmaxf(fabsf(h[0]), fabsf(h[1]))));
     const float sc = exp2_int(-e);
@@ -427,6 +491,15 @@ static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
   // down keeps one-group items and the deeper ring; many: whole items per
   // wave, two groups per down item
   const bool few = max_items < 16 * 4 * int64_t(a.num_cus);
+  if (a.a16) {
+    if (!GU)
+      hipLaunchKernelGGL((k_gemm_stream<false, false, false, true>), dim3(grid), dim3(256), 0, st, a);
+    else if (few)
+      hipLaunchKernelGGL((k_gemm_stream<true, true, false, true>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_gemm_stream<true, false, false, true>), dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (!GU && !few)
     hipLaunchKernelGGL((k_gemm_stream<false, false, true>), dim3(grid), dim3(256), 0, st, a);
   else if (!GU)

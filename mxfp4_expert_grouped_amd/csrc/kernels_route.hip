@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(256) k_router_small(FwdArgs a) {
   // operand is loaded with the first router weights and used after the dot
   // products (loaded before the loop it would be waited for at the loop head).
   const int qb = 32 * e + (tid >> 3), qj = tid & 7;
-  const bool qok = qb < T * nb;
+  const bool qok = qb < T * nb && !a.a16;  // bf16 activations (A16W4): nothing to quantise
   const int qt = qok ? qb / nb : 0, qc = qok ? qb - qt * nb : 0;
   uint2 qraw = make_uint2(0u, 0u);
 
@@ -526,6 +526,7 @@ __global__ void __launch_bounds__(256) k_topk_quant(FwdArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
   topk_token(a, t, lane, cand[threadIdx.x >> 6]);
+  if (a.a16) return;  // bf16 activations (A16W4): x is used as it is
   const int nb = a.d / 32;
   const uint16_t* xr = a.x + int64_t(t) * a.d;
   for (int b = lane; b < nb; b += 64) {

@@ -38,10 +38,10 @@ class MoeLayer:
     """One MoE layer on the current CUDA/HIP device."""
 
     def __init__(self, d_model: int, d_ff: int, num_experts: int, top_k: int, num_shared: int,
-                 max_tokens: int, weights: DeviceWeights):
+                 max_tokens: int, weights: DeviceWeights, flags: int = 0):
         self.shape = dict(d_model=d_model, d_ff=d_ff, num_experts=num_experts, top_k=top_k,
-                          num_shared=num_shared, max_tokens=max_tokens)
-        self.plan = M.moe_plan(d_model, d_ff, num_experts, top_k, num_shared, max_tokens)
+                          num_shared=num_shared, max_tokens=max_tokens, flags=flags)
+        self.plan = M.moe_plan(d_model, d_ff, num_experts, top_k, num_shared, max_tokens, flags)
         self.weights = weights
         self._wabi = weights.abi()
         self._ws: Optional[torch.Tensor] = None

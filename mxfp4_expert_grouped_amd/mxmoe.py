@@ -50,7 +50,9 @@ class MoeWeights(ctypes.Structure):
 
 
 TAP_FIELDS = ("logits", "topk_ids", "topk_w", "expert_offsets", "row_src", "token_row",
-              "x_codes", "x_scales", "h_codes", "h_scales", "gu_acc", "y_routed", "y_shared")
+              "x_codes", "x_scales", "h_codes", "h_scales", "gu_acc", "y_routed", "y_shared",
+              "h_bf16")
+MOE_FLAG_A16W4 = 1
 
 
 class MoeTaps(ctypes.Structure):

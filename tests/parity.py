@@ -109,13 +109,15 @@ class Run:
         idx = np.asarray(idx, dtype=np.int64)
         t = self.taps[name]
         if isinstance(t, np.ndarray):
-            return t[idx]
-        if name in self._host:
-            return self._host[name][idx]
-        return t.index_select(0, torch.from_numpy(idx).to(t.device)).cpu().numpy()
+            out = t[idx]
+        elif name in self._host:
+            out = self._host[name][idx]
+        else:
+            out = t.index_select(0, torch.from_numpy(idx).to(t.device)).cpu().numpy()
+        return out.view(np.uint16) if name == "h_bf16" else out
 
 
-def alloc_taps(cfg: I.LayerConfig, T: int, device="cuda", skip=()) -> Dict[str, torch.Tensor]:
+def alloc_taps(cfg: I.LayerConfig, T: int, device="cuda", skip=(), a16: bool = False) -> Dict[str, torch.Tensor]:
     E, k, S, d, f = cfg.num_experts, cfg.top_k, cfg.num_shared, cfg.d_model, cfg.d_ff
     R = T * k + S * T
     z = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)
@@ -123,19 +125,23 @@ def alloc_taps(cfg: I.LayerConfig, T: int, device="cuda", skip=()) -> Dict[str, 
         logits=z((T, E), torch.float32), topk_ids=z((T, k), torch.int32),
         topk_w=z((T, k), torch.float32), expert_offsets=z((E + 1,), torch.int32),
         row_src=z((T * k,), torch.int32), token_row=z((T, k), torch.int32),
-        x_codes=z((T, d), torch.uint8), x_scales=z((T, d // 32), torch.uint8),
-        h_codes=z((R, f), torch.uint8), h_scales=z((R, f // 32), torch.uint8),
         gu_acc=z((R, 2 * f), torch.float32), y_routed=z((T, d), torch.float32),
         y_shared=z((T, d), torch.float32))
+    if a16:
+        taps["h_bf16"] = z((R, f), torch.int16)
+    else:
+        taps.update(x_codes=z((T, d), torch.uint8), x_scales=z((T, d // 32), torch.uint8),
+                    h_codes=z((R, f), torch.uint8), h_scales=z((R, f // 32), torch.uint8))
     return {n: t for n, t in taps.items() if n not in skip}
 
 
 def run_gpu(cfg: I.LayerConfig, W: DeviceWeights, x: torch.Tensor, taps: bool = True,
-            workspace_fill: Optional[int] = None, skip=()) -> Run:
+            workspace_fill: Optional[int] = None, skip=(), a16: bool = False) -> Run:
+    from mxfp4_expert_grouped_amd import mxmoe as M
     T = x.shape[0]
     layer = MoeLayer(cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k, cfg.num_shared,
-                     max(T, 1), W)
-    tp = alloc_taps(cfg, T, skip=skip) if taps and T > 0 else None
+                     max(T, 1), W, flags=M.MOE_FLAG_A16W4 if a16 else 0)
+    tp = alloc_taps(cfg, T, skip=skip, a16=a16) if taps and T > 0 else None
     ws = torch.empty(max(layer.workspace_bytes(T), 256), dtype=torch.uint8, device=x.device)
     if workspace_fill is not None:
         ws.fill_(workspace_fill)
@@ -152,6 +158,56 @@ def device_inputs(cfg: I.LayerConfig, W: Optional[DeviceWeights] = None, bias=No
     if bias is not None:
         W.router_b = torch.from_numpy(np.asarray(bias, np.float32)).cuda()
     return IG.device_x(cfg), W
+
+
+# ---------------------------------------------------------------------------
+# inputs outside the standard recipe
+# ---------------------------------------------------------------------------
+
+def pack_device(codes: np.ndarray, scales: np.ndarray, rows: int, k: int, interleave: int):
+    """Canonical MXFP4 matrices [n, rows, k/2] / [n, rows, k/32] (numpy) ->
+    packed device tensors [n, ...] through moe_pack_mx4."""
+    from mxfp4_expert_grouped_amd import mxmoe as M
+    n = codes.shape[0]
+    sb = M.moe_packed_scale_bytes(rows, k)
+    cp = torch.empty((n, rows * k // 2), dtype=torch.uint8, device="cuda")
+    sp = torch.empty((n, sb), dtype=torch.uint8, device="cuda")
+    tc, ts = torch.from_numpy(np.ascontiguousarray(codes)).cuda(), torch.from_numpy(np.ascontiguousarray(scales)).cuda()
+    M.moe_pack_mx4(tc.data_ptr(), ts.data_ptr(), n, rows, k, interleave, cp.data_ptr(), sp.data_ptr(),
+                   torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return cp, sp
+
+
+def weights_with_scale_range(cfg, seed: int, lo: int, hi: int):
+    """Expert weights whose E2M1 codes are uniform random bytes and whose E8M0
+    scale bytes are uniform in [lo, hi] (a spread the standard recipe never
+    produces), as device weights and as the oracle's weight source."""
+    from mxfp4_expert_grouped_amd.layer import DeviceWeights
+    rng = np.random.default_rng(seed)
+    d, f = cfg.d_model, cfg.d_ff
+
+    def mats(n, rows, k):
+        return (rng.integers(0, 256, size=(n, rows, k // 2), dtype=np.uint8),
+                rng.integers(lo, hi + 1, size=(n, rows, k // 32), dtype=np.uint8))
+
+    E, S = cfg.num_experts, cfg.num_shared
+    gu, dn = mats(E, 2 * f, d), mats(E, d, f)
+    sgu, sdn = mats(S, 2 * f, d), mats(S, d, f)
+    src = lambda kind, i: ((gu[0][i], gu[1][i], dn[0][i], dn[1][i]) if kind == "routed"
+                           else (sgu[0][i], sgu[1][i], sdn[0][i], sdn[1][i]))
+    g_ = pack_device(*gu, 2 * f, d, 1)
+    d_ = pack_device(*dn, d, f, 0)
+    sg = pack_device(*sgu, 2 * f, d, 1) if S else (None, None)
+    sd = pack_device(*sdn, d, f, 0) if S else (None, None)
+    wr = torch.from_numpy(I.gen_router_w(cfg)).cuda()
+    return DeviceWeights(g_[0], g_[1], d_[0], d_[1], sg[0], sg[1], sd[0], sd[1], wr, None), src
+
+
+def integer_x(cfg, seed):
+    rng = np.random.default_rng(seed)
+    xi = rng.integers(-16, 17, size=(cfg.tokens, cfg.d_model)).astype(np.float32)
+    return I.f32_to_bf16_bits(xi)
 
 
 # ---------------------------------------------------------------------------
@@ -211,12 +267,13 @@ def oracle_workers() -> int:
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def oracle_forward(cfg, x_bits, wr, b, weights, tokens, ids, logits, workers: int = 1):
+def oracle_forward(cfg, x_bits, wr, b, weights, tokens, ids, logits, workers: int = 1,
+                   activations: str = "mxfp8"):
     """The oracle layer for the given routing.  With workers > 1 its
     per-expert jobs run in that many CPU processes; `weights` must then be
     picklable (an ExpertWeights without cache)."""
     kw = dict(num_experts=cfg.num_experts, top_k=cfg.top_k, num_shared=cfg.num_shared,
-              d_ff=cfg.d_ff, topk_ids=ids, intermediates=True, logits=logits)
+              d_ff=cfg.d_ff, topk_ids=ids, intermediates=True, logits=logits, activations=activations)
     if workers > 1:
         kw["expert_map"] = _process_map(workers)
     return OM.forward(x_bits, wr, b, weights, tokens=tokens, **kw)
@@ -394,9 +451,54 @@ def check_outputs(name: str, got: np.ndarray, ref: np.ndarray, allow: Optional[n
     return rel, mx
 
 
+def compare_h_row_bf16(gb, gacc, ob, mid, d_ff: int, stats: dict) -> np.ndarray:
+    """One permuted row of the A16W4 variant, whose h is bf16: gb / ob the
+    GPU's and the oracle's h bits.  The GPU bits must be the bf16 rounding of
+    silu(g)*u rebuilt from the GPU's own accumulators (the neighbouring bf16
+    value only within H_SLACK of the rounding midpoint), those accumulators
+    within EPS_ACC of the oracle's term magnitudes.  Returns dh (decoded GPU h
+    minus decoded oracle h)."""
+    stats["bytes"] = stats.get("bytes", 0) + gb.size
+    vg, vo = OM.bf16_to_f64(gb), OM.bf16_to_f64(ob)
+    if gacc is not None:
+        gacc = gacc.astype(np.float64)
+        err = np.abs(gacc - mid["gu"])
+        ratio = float(np.max(err / np.maximum(mid["gu_abs"], 1e-300)))
+        stats["acc_ratio"] = max(stats.get("acc_ratio", 0.0), ratio)
+        assert np.all(err <= EPS_ACC * mid["gu_abs"]), \
+            f"gate/up accumulators off by {ratio:.3e} of their term magnitudes"
+        # the rounding decision in the kernel's precision: silu(g) * u from the
+        # GPU's fp32 sums evaluated in fp32 as the kernel does (an fp32
+        # exp(-g) overflows for g < -88.7, giving -0 where float64 still has a
+        # value near 1e-38; last-ulp differences of exp stay within H_SLACK)
+        g32, u32 = gacc[:d_ff].astype(np.float32), gacc[d_ff:].astype(np.float32)
+        with np.errstate(over="ignore"):
+            h_g = ((g32 / (np.float32(1) + np.exp(-g32))) * u32).astype(np.float64)
+        want = OM.f64_to_bf16(h_g)
+        bad = np.nonzero(gb != want)[0]
+        if bad.size:
+            vw = OM.bf16_to_f64(want[bad])
+            m = (vg[bad] + vw) / 2
+            # neighbours: no bf16 value strictly between them (their bit
+            # patterns differ by one in the same sign, or both are zeros)
+            adj = (np.abs(gb[bad].astype(np.int64) - want[bad].astype(np.int64)) == 1) | (vg[bad] == vw)
+            assert np.all(adj), f"h bits {bad[~adj][:4]} are not the bf16 rounding of the GPU's sums"
+            assert np.all(np.abs(h_g[bad] - m) <= H_SLACK * np.abs(h_g[bad])), \
+                f"h bits {bad[:4]}: value not at a bf16 rounding midpoint"
+    else:
+        d = np.abs(gb.astype(np.int64) - ob.astype(np.int64))
+        assert np.all((d <= 1) | (vg == vo)), "h bits differ by more than one bf16 step"
+    stats["code_flips"] = stats.get("code_flips", 0) + int(np.sum(gb != ob))
+    return vg - vo
+
+
 def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g: Run,
-                  tokens: Optional[Sequence[int]] = None, workers: int = 1):
-    """Full comparison of a GPU run `g` (taps) against the oracle."""
+                  tokens: Optional[Sequence[int]] = None, workers: int = 1,
+                  activations: str = "mxfp8"):
+    """Full comparison of a GPU run `g` (taps) against the oracle.
+    activations="bf16": the A16W4 variant (bf16 x and h; h through the
+    h_bf16 tap)."""
+    a16 = activations == "bf16"
     T = x_bits.shape[0]
     k, S, f = cfg.top_k, cfg.num_shared, cfg.d_ff
     t0 = time.time()
@@ -409,7 +511,7 @@ def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g: Run
     differ = check_routing(cfg, logits, own_ids, gap, ids_g)
     # the oracle layer for the GPU's (accepted) routing
     t0 = time.time()
-    res = oracle_forward(cfg, x_bits, wr, b, weights, tokens, ids_g, logits, workers)
+    res = oracle_forward(cfg, x_bits, wr, b, weights, tokens, ids_g, logits, workers, activations)
     log(f"oracle forward with the GPU routing ({len(res.tokens)} tokens, "
         f"{sum(1 for t in res.tokens if int(t) in differ)} of them near-ties) {time.time() - t0:.1f}s")
     assert len(res.tokens) >= 1
@@ -430,14 +532,28 @@ def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g: Run
     assert np.all(werr <= bound)
     # MXFP8 bytes of x: bit-exact
     toks = res.tokens
-    assert np.array_equal(g.rows("x_codes", toks), res.x_codes)
-    assert np.array_equal(g.rows("x_scales", toks), res.x_scales)
+    if a16:
+        assert "x_codes" not in g and "h_codes" not in g
+    else:
+        assert np.array_equal(g.rows("x_codes", toks), res.x_codes)
+        assert np.array_equal(g.rows("x_scales", toks), res.x_scales)
     # h rows of the computed tokens, in one gather per tap
     nt, d = len(toks), res.y.shape[1]
     rows_r = np.array([int(res.token_row[t, j]) for t in toks for j in range(k)], np.int64)
     rows_s = np.array([T * k + s * T + int(t) for t in toks for s in range(S)], np.int64)
     rows = np.concatenate([rows_r, rows_s]).astype(np.int64)
-    hc, hs = g.rows("h_codes", rows), g.rows("h_scales", rows)
+    if a16:
+        hc, hs = g.rows("h_bf16", rows), None
+    else:
+        hc, hs = g.rows("h_codes", rows), g.rows("h_scales", rows)
+
+    def h_row(q, oc, os_, mid):
+        if a16:
+            dh = compare_h_row_bf16(hc[q], None if acc is None else acc[q], oc, mid, f, stats)
+            return dh, OM.bf16_to_f64(oc)
+        dh = compare_h_row(hc[q], hs[q], None if acc is None else acc[q], oc, os_, mid, f, stats)
+        return dh, OX.mx_decode(oc[None], os_[None], "e4m3")[0]
+
     acc = g.rows("gu_acc", rows) if "gu_acc" in g else None
     stats: dict = {}
     allow_r, allow_s = np.zeros((nt, d)), np.zeros((nt, d))
@@ -451,8 +567,8 @@ def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g: Run
             r = int(rows_r[q])
             oc, os_ = res.h_rows[r]
             mid = res.mid_rows[r]
-            dh = compare_h_row(hc[q], hs[q], None if acc is None else acc[q], oc, os_, mid, f, stats)
-            hdiff.append((dh, OX.mx_decode(oc[None], os_[None], "e4m3")[0]))
+            dh, hov = h_row(q, oc, os_, mid)
+            hdiff.append((dh, hov))
             e = int(ids_g[t, j])
             w = max(float(wref[t, j]), float(wg[t, j]))
             eff = _flip_effect(dh, weights, "routed", e)
@@ -465,7 +581,7 @@ def compare_layer(cfg: I.LayerConfig, x_bits: np.ndarray, wr, b, weights, g: Run
             q = len(rows_r) + i * S + s
             oc, os_ = res.h_shared[(s, t)]
             mid = res.mid_shared[(s, t)]
-            dh = compare_h_row(hc[q], hs[q], None if acc is None else acc[q], oc, os_, mid, f, stats)
+            dh, _ = h_row(q, oc, os_, mid)
             eff = _flip_effect(dh, weights, "shared", s)
             allow_s[i] += eff
             o = mid["o"]

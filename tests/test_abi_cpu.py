@@ -65,7 +65,9 @@ def test_status_strings(M):
     (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=-1, max_tokens=8), 1),
     (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=9, max_tokens=8), 2),
     (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=0), 1),
-    (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8, flags=1), 1),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8, flags=1), 0),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8, flags=2), 1),
+    (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8, flags=3), 1),
 ])
 def test_plan_validation(M, kw, status):
     if status == 0:
@@ -268,3 +270,29 @@ def test_latent_tail_host_checks(M):
         with pytest.raises(M.MoeError) as ei:
             M.moe_latent_tail(*args)
         assert ei.value.status == status, (args, ei.value)
+
+
+def test_a16w4_host_checks(M):
+    # bf16 activations: the streaming kernels only (below 24 rows per expert
+    # on average), no MXFP8 taps, h through its own bf16 tap
+    fake = 1 << 20
+    W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, M.MOE_WEIGHTS_PACKED)
+    p = M.moe_plan(256, 128, 16, 2, 1, 1024, M.MOE_FLAG_A16W4)
+    p8 = M.moe_plan(256, 128, 16, 2, 1, 1024)
+    try:
+        ws = M.moe_workspace_bytes(p, 1024)
+        with pytest.raises(M.MoeError) as ei:  # 192 tokens x 2 / 16 = 24 rows per expert
+            M.moe_forward(p, W, fake, 192, fake, fake, ws)
+        assert ei.value.status == M.MOE_ERR_UNSUPPORTED and "A16W4" in ei.value.detail
+        for name in ("x_codes", "x_scales", "h_codes", "h_scales"):
+            with pytest.raises(M.MoeError) as ei:
+                M.moe_forward(p, W, fake, 8, fake, fake, ws, M.MoeTaps(**{name: fake}))
+            assert ei.value.status == M.MOE_ERR_INVALID_ARG
+        with pytest.raises(M.MoeError) as ei:
+            M.moe_forward(p8, W, fake, 8, fake, fake, M.moe_workspace_bytes(p8, 8), M.MoeTaps(h_bf16=fake))
+        assert ei.value.status == M.MOE_ERR_INVALID_ARG
+        # h in bf16 takes twice the bytes of MXFP8 codes, no scales
+        assert M.moe_workspace_bytes(p, 8) > M.moe_workspace_bytes(p8, 8)
+    finally:
+        M.moe_plan_destroy(p)
+        M.moe_plan_destroy(p8)

@@ -178,52 +178,6 @@ def test_quantize_act_strided_and_ragged_rows():
 # exact-arithmetic regime: gate/up accumulators bit-exact
 # ---------------------------------------------------------------------------
 
-def _pack_device(codes: np.ndarray, scales: np.ndarray, rows: int, k: int, interleave: int):
-    """Canonical MXFP4 matrices [n, rows, k/2] / [n, rows, k/32] (numpy) ->
-    packed device tensors [n, ...] through moe_pack_mx4."""
-    from mxfp4_expert_grouped_amd import mxmoe as M
-    n = codes.shape[0]
-    sb = M.moe_packed_scale_bytes(rows, k)
-    cp = torch.empty((n, rows * k // 2), dtype=torch.uint8, device="cuda")
-    sp = torch.empty((n, sb), dtype=torch.uint8, device="cuda")
-    tc, ts = torch.from_numpy(np.ascontiguousarray(codes)).cuda(), torch.from_numpy(np.ascontiguousarray(scales)).cuda()
-    M.moe_pack_mx4(tc.data_ptr(), ts.data_ptr(), n, rows, k, interleave, cp.data_ptr(), sp.data_ptr(),
-                   torch.cuda.current_stream().cuda_stream)
-    torch.cuda.synchronize()
-    return cp, sp
-
-
-def _weights_with_scale_range(cfg, seed: int, lo: int, hi: int):
-    """Expert weights whose E2M1 codes are uniform random bytes and whose E8M0
-    scale bytes are uniform in [lo, hi] (a spread the standard recipe never
-    produces), as device weights and as the oracle's weight source."""
-    from mxfp4_expert_grouped_amd.layer import DeviceWeights
-    rng = np.random.default_rng(seed)
-    d, f = cfg.d_model, cfg.d_ff
-
-    def mats(n, rows, k):
-        return (rng.integers(0, 256, size=(n, rows, k // 2), dtype=np.uint8),
-                rng.integers(lo, hi + 1, size=(n, rows, k // 32), dtype=np.uint8))
-
-    E, S = cfg.num_experts, cfg.num_shared
-    gu, dn = mats(E, 2 * f, d), mats(E, d, f)
-    sgu, sdn = mats(S, 2 * f, d), mats(S, d, f)
-    src = lambda kind, i: ((gu[0][i], gu[1][i], dn[0][i], dn[1][i]) if kind == "routed"
-                           else (sgu[0][i], sgu[1][i], sdn[0][i], sdn[1][i]))
-    g_ = _pack_device(*gu, 2 * f, d, 1)
-    d_ = _pack_device(*dn, d, f, 0)
-    sg = _pack_device(*sgu, 2 * f, d, 1) if S else (None, None)
-    sd = _pack_device(*sdn, d, f, 0) if S else (None, None)
-    wr = torch.from_numpy(I.gen_router_w(cfg)).cuda()
-    return DeviceWeights(g_[0], g_[1], d_[0], d_[1], sg[0], sg[1], sd[0], sd[1], wr, None), src
-
-
-def _integer_x(cfg, seed):
-    rng = np.random.default_rng(seed)
-    xi = rng.integers(-16, 17, size=(cfg.tokens, cfg.d_model)).astype(np.float32)
-    return I.f32_to_bf16_bits(xi)
-
-
 # (name, tokens, d, d_ff, experts, top_k, scale bytes or None for the standard
 # recipe).  The kernel each case reaches: 40 tokens of 8 experts -> 10 rows
 # per expert, 8-row tiles, the K-split streaming gate_up; 300 tokens -> 75 per
@@ -251,14 +205,14 @@ def test_gate_up_accumulators_exact(name, T, d, f, E, k, scales):
     ones bit for bit: any lane, K-step or scale-byte layout error shows.  The
     whole layer is then compared with the full parity rules on a sample."""
     cfg = I.LayerConfig(name, T, d, E, k, f, 1, seed=21)
-    bits = _integer_x(cfg, 5)
+    bits = P.integer_x(cfg, 5)
     x = P.IG.bf16_tensor(bits)
     if scales is None:
         W = P.IG.device_weights(cfg)
         ref = I.ExpertWeights(cfg)
         lo = 127 + I.scale_exponent_base(d)
     else:
-        W, ref = _weights_with_scale_range(cfg, 77, *scales)
+        W, ref = P.weights_with_scale_range(cfg, 77, *scales)
         lo = scales[0]
     P.log(f"exact case {name}: T={T} d={d} d_ff={f} E={E} k={k} scale bytes {scales}")
     g = P.run_gpu(cfg, W, x)

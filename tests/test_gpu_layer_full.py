@@ -80,21 +80,23 @@ def pick_tokens(cfg, offsets: np.ndarray, row_src: np.ndarray, n: int):
     return sorted(set(picks))
 
 
-@pytest.mark.parametrize("name,nsample", [
-    ("decode1", 1),
-    ("decode256", 12),
-    ("prefill8k", 32),
-    ("prefill32k_skew", 32),
-])
-def test_full_layer(big, name, nsample):
+@pytest.mark.parametrize("name,nsample,a16", [
+    ("decode1", 1, False),
+    ("decode256", 12, False),
+    ("prefill8k", 32, False),
+    ("prefill32k_skew", 32, False),
+    ("decode1", 1, True),
+    ("decode256", 12, True),
+], ids=["decode1", "decode256", "prefill8k", "prefill32k_skew", "decode1_a16w4", "decode256_a16w4"])
+def test_full_layer(big, name, nsample, a16):
     P, W, ref = big
     cfg = I.CONFIGS[name]
     b = I.gen_router_b(cfg)
     W.router_b = torch.from_numpy(b).cuda() if b is not None else None
     x_bits = I.gen_x(cfg)
     x = P.IG.bf16_tensor(x_bits)
-    P.log(f"{name}: GPU forward T={cfg.tokens} (all taps)")
-    g = P.run_gpu(cfg, W, x)
+    P.log(f"{name}: GPU forward T={cfg.tokens} (all taps{', A16W4' if a16 else ''})")
+    g = P.run_gpu(cfg, W, x, a16=a16)
     # every token: routing weights sum to one, outputs finite
     assert np.all(np.abs(g["topk_w"].sum(1) - 1) < 1e-5)
     y = P.bf16_bits_to_f64(g["y"])
@@ -103,8 +105,11 @@ def test_full_layer(big, name, nsample):
     P.log(f"{name}: sampled tokens {sample}")
     assert len(sample) >= nsample
     res, differ = P.compare_layer(cfg, x_bits, I.gen_router_w(cfg), b, ref, g, tokens=sample,
-                                  workers=P.oracle_workers())
+                                  workers=P.oracle_workers(), activations="bf16" if a16 else "mxfp8")
     assert len(res.tokens) == len(sample)
+    if a16:
+        W.router_b = None
+        return
     # the x bytes of every 1/512th token, not only the sampled ones
     from oracle import moe as OM, mx as OX
     step = max(1, cfg.tokens // 512)
