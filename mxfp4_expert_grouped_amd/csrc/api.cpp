@@ -448,7 +448,7 @@ moe_status moe_forward_noalloc(const moe_plan_t* plan, const moe_weights* w, con
 namespace {
 
 struct TailLayout {
-  size_t codes, scales, o16, row_src, tiles, tile_count, ex_tiles, total;
+  size_t codes, scales, o16, row_src, tiles, tile_count, ex_tiles, part, total;
   int bm;
 };
 
@@ -470,6 +470,7 @@ TailLayout tail_layout(int64_t T, int64_t latent, int64_t hidden, bool with_s) {
   L.tiles = take(((T + L.bm - 1) / L.bm) * sizeof(Tile));
   L.tile_count = take(4);
   L.ex_tiles = take(8);
+  L.part = take(T <= kTailGemvMaxT ? size_t(tail_gemv_slices(static_cast<int>(latent))) * T * hidden * 4 : 0);
   L.total = off;
   return L;
 }
@@ -552,6 +553,7 @@ moe_status moe_latent_tail(int64_t num_tokens, int32_t latent, int32_t hidden, f
   a.tiles = reinterpret_cast<Tile*>(ws + L.tiles);
   a.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
   a.ex_tiles = reinterpret_cast<int32_t*>(ws + L.ex_tiles);
+  a.part = reinterpret_cast<float*>(ws + L.part);
   hipError_t e = launch_tail(a, num_cus > 0 ? num_cus : 256, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
   return MOE_OK;

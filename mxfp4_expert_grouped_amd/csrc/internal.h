@@ -78,7 +78,17 @@ struct TailArgs {
   Tile* tiles;           // [ceil(T/bm)]
   int32_t* tile_count;   // [1]
   int32_t* ex_tiles;     // [2]
+  float* part;           // [slices][T][hidden] split-K partials (T <= kTailGemvMaxT)
 };
+
+// The tail's projection for at most kTailGemvMaxT rows runs split along K:
+// each wave takes at most kTailGemvSteps of the 128-wide K steps.
+constexpr int kTailGemvMaxT = 16;
+constexpr int kTailGemvSteps = 4;
+inline int tail_gemv_slices(int latent) {
+  const int ns = latent / 128;
+  return (ns + 4 * kTailGemvSteps - 1) / (4 * kTailGemvSteps);
+}
 
 // Launchers (kernels_*.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_tail(const TailArgs& a, int num_cus, hipStream_t st);
@@ -104,7 +114,15 @@ inline int router_splits(int64_t T, int64_t E, int64_t d) {
   return ks < 1 ? 1 : static_cast<int>(ks);
 }
 
+// The few-token forward splits its gate_up in two launches (top-k +
+// permutation + shared experts, then the routed experts) when routing runs in
+// one workgroup and every tile is a weight-streaming one, with the K split.
+inline bool stream_split_phases(const FwdArgs& a) {
+  return router_small(a.T, a.d, a.E) && a.bm <= kDecodeMaxRows && a.S > 0;
+}
+
 hipError_t launch_router(const FwdArgs& a, hipStream_t st);
+hipError_t launch_topk_shared_gate_up(const FwdArgs& a, hipStream_t st);
 hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st);
 hipError_t launch_permute(const FwdArgs& a, hipStream_t st);
 hipError_t launch_gemm_gate_up(const FwdArgs& a, hipStream_t st);

@@ -23,6 +23,7 @@
 
 #include "internal.h"
 #include "mx_device.h"
+#include "topk_device.h"
 
 namespace mxmoe {
 
@@ -160,8 +161,24 @@ __device__ __forceinline__ int sload1(const void* p) {
 // (V_CVT_SCALEF32_PK_BF16_FP4) and multiplied on the bf16 MFMA
 // (16x16x32: four per 16-row block and K step); h leaves the gate_up
 // epilogue as bf16.  Six ring slots of 6400 bytes; no two-group items.
-template <bool GU, bool KSPLIT, bool WIDE, bool A16 = false>
+// PH (phase) splits a few-token gate_up in two launches: PH = 1 is the top-k
+// and permutation (workgroup 0, topk_permute_block256) together with the
+// shared experts' items (every other workgroup: their tiles need no
+// routing, only x, which the router launch has quantised), so the GPU
+// streams the shared experts' weights while one workgroup routes; PH = 2 is
+// then the routed experts' items alone.  PH = 0: every item of the tile list.
+template <bool GU, bool KSPLIT, bool WIDE, bool A16 = false, int PH = 0>
 __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
+  static_assert(PH == 0 || (GU && !WIDE), "the phases split the gate_up GEMM");
+  if constexpr (PH == 1) {
+    if (blockIdx.x == 0) {
+      topk_permute_block256(a, ds_lds);
+      return;
+    }
+  }
+  // workgroups that walk items (all of them, or all but the routing one)
+  const int wg_id = PH == 1 ? static_cast<int>(blockIdx.x) - 1 : static_cast<int>(blockIdx.x);
+  const int wg_n = PH == 1 ? static_cast<int>(gridDim.x) - 1 : static_cast<int>(gridDim.x);
   // ring geometry: WIDE items (down only) cover two 64-row groups
   constexpr int GPI = WIDE ? 2 : 1;                 // packed groups per item
   constexpr int S = A16 ? kDsS16 : (WIDE ? kDsSWide : kDsS);  // ring slots per wave
@@ -182,7 +199,11 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   auto wsteps = [&](int w) { return KSPLIT ? (ns - w + 3) / 4 : ns; };
   const int nsw = wsteps(wu);
   const int ngrp = (GU ? a.dff / 32 : a.d / 64) / GPI;   // items per tile
-  const int nitems = sload1(a.tile_count) * ngrp;
+  // shared experts' tiles (T rows each, in tiles of a.bm), last in the list
+  const int nts_sh = (a.T + a.bm - 1) / a.bm;
+  const int nitems = PH == 1 ? a.S * nts_sh * ngrp
+                   : PH == 2 ? (sload1(a.tile_count) - a.S * nts_sh) * ngrp
+                             : sload1(a.tile_count) * ngrp;
   // item walkers: workgroups (split) or single waves, round-robin.  With
   // many items per walker (16+) the items are first cut into 8 contiguous
   // ranges, one per XCD (workgroups go to the XCDs round-robin), and an
@@ -190,11 +211,11 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   // then share its activation rows in one L2 while every XCD streams
   // neighbouring weight groups.  With few items plain round-robin keeps the
   // whole grid on one contiguous stretch of weights, which measured faster.
-  const int walkers = KSPLIT ? gridDim.x : gridDim.x * 4;
-  const bool by_xcd = nitems >= 16 * walkers;
-  const int xcd = by_xcd ? blockIdx.x & 7 : 0;
-  const int xw = by_xcd ? blockIdx.x >> 3 : blockIdx.x;
-  const int nxw = by_xcd ? gridDim.x >> 3 : gridDim.x;
+  const int walkers = KSPLIT ? wg_n : wg_n * 4;
+  const bool by_xcd = PH == 0 && nitems >= 16 * walkers;
+  const int xcd = by_xcd ? wg_id & 7 : 0;
+  const int xw = by_xcd ? wg_id >> 3 : wg_id;
+  const int nxw = by_xcd ? wg_n >> 3 : wg_n;
   const int bid = KSPLIT ? xw : xw * 4 + wu;
   const int nwg = KSPLIT ? nxw : nxw * 4;
   const int per_xcd = by_xcd ? (nitems + 7) / 8 : nitems;
@@ -226,10 +247,18 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     const bool new_tile = tidx != cur_tile;
     if (new_tile) {
       cur_tile = tidx;
-      const v4i_s tl = sload4(a.tiles + tidx);        // ex, row_begin, row_end
-      ex = tl.x;
-      rb = tl.y;
-      nr = tl.z - tl.y;
+      if constexpr (PH == 1) {
+        // shared tile tidx: expert tidx / nts_sh, its rows in tiles of a.bm
+        const int sx = tidx / nts_sh, i = tidx - sx * nts_sh;
+        ex = a.E + sx;
+        rb = a.Rr + sx * a.T + i * a.bm;
+        nr = min(a.bm, a.T - i * a.bm);
+      } else {
+        const v4i_s tl = sload4(a.tiles + tidx);      // ex, row_begin, row_end
+        ex = tl.x;
+        rb = tl.y;
+        nr = tl.z - tl.y;
+      }
     }
     if (lane < 4) fifo[(il & 7) * 4 + lane] = lane == 0 ? ex : lane == 1 ? rb : lane == 2 ? rb + nr : G;
     const bool shared = ex >= a.E;
@@ -289,8 +318,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     // only the tile's rows (tiles are never empty, so the copy is always
     // issued and every element counts NC copies)
     if constexpr (A16) {
-      lds_copy16(a16_src[0] + 256 * st, slot + SA);
-      lds_copy16(a16_src[1] + 256 * st, slot + SA + 1024);
+      // only the tile's rows (lane 0's row 0 or 4 always goes, so both
+      // copies are issued and every element counts NC copies)
+      if ((lane >> 4) < nr || lane == 0) lds_copy16(a16_src[0] + 256 * st, slot + SA);
+      if (4 + (lane >> 4) < nr || lane == 0) lds_copy16(a16_src[1] + 256 * st, slot + SA + 1024);
     } else {
       if (lane < 8 * nr) lds_copy16(a_src + 128 * st, slot + SA);
       lds_copy4(as_src + 4 * st, slot + SAS);
@@ -322,22 +353,27 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     for (int c = 0; c < 4; ++c)
       av[c] = *reinterpret_cast<const v8bf16*>(sl + SA + a16_row * 256 + 16 * ((4 * g + c) ^ a16_row));
     const uint32_t sbw = *reinterpret_cast<const uint32_t*>(sl + SBS + 4 * lane);
+    uint32_t wd[4][4];
+    float scl[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint4 wv = ld16(sl + SW + j * 1024 + 16 * lane);
+      wd[j][0] = wv.x; wd[j][1] = wv.y; wd[j][2] = wv.z; wd[j][3] = wv.w;
       const uint32_t sb = (sbw >> (8 * j)) & 0xFFu;
-      const float scl = __uint_as_float(sb ? sb << 23 : 0x00400000u);  // 2^(sb-127)
-      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+      scl[j] = __uint_as_float(sb ? sb << 23 : 0x00400000u);  // 2^(sb-127)
+    }
+    // K chunk outer, block inner: consecutive MFMAs use different accumulators
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const v2bf16 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], scl, 0);
-        const v2bf16 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], scl, 1);
-        const v2bf16 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], scl, 2);
-        const v2bf16 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[c], scl, 3);
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v2bf16 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 0);
+        const v2bf16 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 1);
+        const v2bf16 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 2);
+        const v2bf16 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 3);
         const v8bf16 bv = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], bv, acc[j], 0, 0, 0);
       }
-    }
   };
   auto compute = [&](int el) {
     if constexpr (A16) {
@@ -491,13 +527,27 @@ static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
   // down keeps one-group items and the deeper ring; many: whole items per
   // wave, two groups per down item
   const bool few = max_items < 16 * 4 * int64_t(a.num_cus);
+  // few-token routing in one workgroup: the shared experts' items already ran
+  // in the routing launch (stream_topk_shared), only the routed ones here
+  const bool routed_only = GU && stream_split_phases(a);
   if (a.a16) {
     if (!GU)
       hipLaunchKernelGGL((k_gemm_stream<false, false, false, true>), dim3(grid), dim3(256), 0, st, a);
+    else if (routed_only && few)
+      hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 2>), dim3(grid), dim3(256), 0, st, a);
+    else if (routed_only)
+      hipLaunchKernelGGL((k_gemm_stream<true, false, false, true, 2>), dim3(grid), dim3(256), 0, st, a);
     else if (few)
       hipLaunchKernelGGL((k_gemm_stream<true, true, false, true>), dim3(grid), dim3(256), 0, st, a);
     else
       hipLaunchKernelGGL((k_gemm_stream<true, false, false, true>), dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  if (routed_only) {
+    if (few)
+      hipLaunchKernelGGL((k_gemm_stream<true, true, false, false, 2>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_gemm_stream<true, false, false, false, 2>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   if (!GU && !few)
@@ -1000,6 +1050,17 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+
+// The routing launch of a few tokens: top-k and permutation in workgroup 0,
+// the shared experts' gate_up items in the others (PH = 1).
+hipError_t launch_topk_shared_gate_up(const FwdArgs& a, hipStream_t st) {
+  const unsigned grid = 8u * static_cast<unsigned>(a.num_cus >= 16 ? a.num_cus / 8 : 1);
+  if (a.a16)
+    hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 1>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm_stream<true, true, false, false, 1>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_gate_up(const FwdArgs& a, hipStream_t st) {
   if (a.bm <= kDecodeMaxRows) return launch_stream<true>(a, st);

@@ -12,6 +12,7 @@
 
 #include "internal.h"
 #include "mx_device.h"
+#include "topk_device.h"
 
 namespace mxmoe {
 
@@ -399,126 +400,6 @@ hipError_t launch_router(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Top-k + sigmoid renormalisation + MXFP8 quantisation of x: one wave per token
-// ---------------------------------------------------------------------------
-
-constexpr int kMaxSlots = 16;
-
-// k-th largest of one key per lane (keys of 0 never count): the threshold is
-// built bit by bit from the top, counting candidates with a ballot.
-__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t key, int k) {
-  uint32_t th = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = th | (1u << bit);
-    th = __popcll(__ballot(key >= cand)) >= k ? cand : th;
-  }
-  return th;
-}
-
-__device__ __forceinline__ float order_key_to_float(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
-}
-
-// Top-k of token t by one wave: ids ascending, w = sigmoid / sum sigmoid.
-// Keys are order-preserving 32-bit images of the logits; slot i of lane l
-// holds expert l + 64 i (slots past E hold key 0, which never counts).
-// 1. The k-th largest of the 64 per-lane maxima is a lower bound L of the
-//    k-th largest key (at least k lanes hold a key >= L).
-// 2. Keys >= L are compacted in (slot, lane) = ascending expert order into
-//    `cand` (LDS, 64 entries per wave); if more than 64 qualify, the full
-//    16-slot search runs instead.
-// 3. With one candidate per lane, the k-th largest key th is found by a
-//    one-slot radix select; keys > th are taken and keys == th fill the
-//    remaining places in ascending expert order (ties -> lower index).
-// With s_ids non-null the chosen ids are also stored there (LDS, [t*k + j]).
-__device__ void topk_token(const FwdArgs& a, int t, int lane, uint2* cand, int* s_ids = nullptr) {
-  // t is the same in every lane: saying so keeps the buffer resource in
-  // scalar registers, so the 16 loads below go out together (a lane-varying
-  // resource would get one waterfall loop with a full wait per load)
-  t = __builtin_amdgcn_readfirstlane(t);
-  const __amdgpu_buffer_rsrc_t rl =
-      __builtin_amdgcn_make_buffer_rsrc(a.logits + int64_t(t) * a.E, static_cast<short>(0), a.E * 4, 0x00020000);
-  // every load is issued before any is used (offsets past the row read 0
-  // through the resource's bound); slots past E get key 0
-  uint32_t key[kMaxSlots];
-#pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) key[i] = __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * (lane + 64 * i), 0, 0);
-#pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i)
-    key[i] = float_order_key(__builtin_bit_cast(float, key[i])) & (lane + 64 * i < a.E ? ~0u : 0u);
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint32_t lmax = 0;
-#pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) lmax = max(lmax, key[i]);
-  const uint32_t lo = wave_kth_largest(lmax, a.k);
-  int ncand = 0;
-#pragma unroll
-  for (int i = 0; i < kMaxSlots; ++i) ncand += __popcll(__ballot(key[i] >= lo));
-
-  uint32_t ck;   // this lane's candidate key (0: none)
-  int cidx;      // its expert index
-  if (ncand <= 64) {
-    int base = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxSlots; ++i) {
-      const bool c = key[i] >= lo;
-      const uint64_t m = __ballot(c);
-      if (c) cand[base + __popcll(m & lt_mask)] = make_uint2(key[i], uint32_t(lane + 64 * i));
-      base += __popcll(m);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint2 cv = lane < ncand ? cand[lane] : make_uint2(0u, 0u);
-    ck = cv.x;
-    cidx = static_cast<int>(cv.y);
-  } else {
-    // many equal or clustered keys: radix select over all slots, then keep the
-    // selected keys as candidates (at most k <= 32 of them)
-    uint32_t th = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = th | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < kMaxSlots; ++i) cnt += __popcll(__ballot(key[i] >= c));
-      th = cnt >= a.k ? c : th;
-    }
-    int need = a.k;
-#pragma unroll
-    for (int i = 0; i < kMaxSlots; ++i) need -= __popcll(__ballot(key[i] > th));
-    int base = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxSlots; ++i) {
-      const uint64_t eq = __ballot(key[i] == th);
-      const bool take = key[i] > th || (key[i] == th && __popcll(eq & lt_mask) < need);
-      need -= min(need, __popcll(eq));
-      const uint64_t m = __ballot(take);
-      if (take) cand[base + __popcll(m & lt_mask)] = make_uint2(key[i], uint32_t(lane + 64 * i));
-      base += __popcll(m);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const uint2 cv = lane < a.k ? cand[lane] : make_uint2(0u, 0u);
-    ck = cv.x;
-    cidx = static_cast<int>(cv.y);
-  }
-  const uint32_t th = wave_kth_largest(ck, a.k);
-  const int need = a.k - __popcll(__ballot(ck > th));
-  const uint64_t eq = __ballot(ck == th && ck != 0u);
-  const bool take = ck > th || (ck == th && ck != 0u && __popcll(eq & lt_mask) < need);
-  const uint64_t m = __ballot(take);
-  const float sig = 1.0f / (1.0f + expf(-order_key_to_float(ck)));
-  const float inv = 1.0f / group_sum<64>(take ? sig : 0.f);
-  if (take) {
-    const int pos = __popcll(m & lt_mask);  // candidates are in ascending expert order
-    a.topk_ids[int64_t(t) * a.k + pos] = cidx;
-    a.topk_w[int64_t(t) * a.k + pos] = sig * inv;
-    if (s_ids) s_ids[t * a.k + pos] = cidx;
-  }
-}
-
 // Many tokens: one wave per token, top-k then the token's MXFP8 row.
 __global__ void __launch_bounds__(256) k_topk_quant(FwdArgs a) {
   __shared__ uint2 cand[4][64];
@@ -807,6 +688,7 @@ __global__ void __launch_bounds__(256) k_perm_scatter(FwdArgs a) {
 }
 
 hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st) {
+  if (stream_split_phases(a)) return launch_topk_shared_gate_up(a, st);
   if (router_small(a.T, a.d, a.E))
     hipLaunchKernelGGL(k_topk_permute_small, dim3(1), dim3(1024), 0, st, a);
   else

@@ -23,19 +23,46 @@ namespace mxmoe {
 // scaling, as for every other activation of the layer.  Workgroup t also
 // writes row_src[t] = t (the projection's rows are in token order) and
 // workgroup 0 the projection's tile list.
+// The row's values a thread holds in registers between the two passes (rows
+// of up to 8192 columns; wider rows load again in pass 2, from L2).
+constexpr int kTailRegF4 = 8;
+
 __global__ void __launch_bounds__(256) k_tail_norm_quant(TailArgs a) {
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l = a.latent;
   const float4* z4 = reinterpret_cast<const float4*>(a.z + int64_t(t) * l);
   const int n4 = l / 4;
+  const bool in_regs = n4 <= 256 * kTailRegF4;
+  // pass 1: every load of the row issued before the first use; float4 i of
+  // sweep p is element block (p*256 + tid), the one pass 2 quantises
+  const float4* g4 = reinterpret_cast<const float4*>(a.gamma);
+  float4 zr[kTailRegF4], gr[kTailRegF4];
   float ss = 0.f;
-  for (int i = tid; i < n4; i += 256) {
-    const float4 v = z4[i];
-    ss = fmaf(v.x, v.x, ss);
-    ss = fmaf(v.y, v.y, ss);
-    ss = fmaf(v.z, v.z, ss);
-    ss = fmaf(v.w, v.w, ss);
+  if (in_regs) {
+#pragma unroll
+    for (int p = 0; p < kTailRegF4; ++p) {
+      const int i = p * 256 + tid;
+      zr[p] = z4[i < n4 ? i : 0];
+      gr[p] = g4[i < n4 ? i : 0];
+    }
+#pragma unroll
+    for (int p = 0; p < kTailRegF4; ++p) {
+      if (p * 256 + tid < n4) {
+        ss = fmaf(zr[p].x, zr[p].x, ss);
+        ss = fmaf(zr[p].y, zr[p].y, ss);
+        ss = fmaf(zr[p].z, zr[p].z, ss);
+        ss = fmaf(zr[p].w, zr[p].w, ss);
+      }
+    }
+  } else {
+    for (int i = tid; i < n4; i += 256) {
+      const float4 v = z4[i];
+      ss = fmaf(v.x, v.x, ss);
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+    }
   }
   ss = group_sum<64>(ss);
   if (lane == 0) red[wv] = ss;
@@ -46,14 +73,12 @@ __global__ void __launch_bounds__(256) k_tail_norm_quant(TailArgs a) {
     if (a.inv_rms) a.inv_rms[t] = inv;
     a.row_src[t] = t;
   }
-  // pass 2: 8 threads per block, 32 blocks per sweep of the workgroup
-  const float4* g4 = reinterpret_cast<const float4*>(a.gamma);
+  // pass 2: 8 threads per block, 32 blocks per sweep of the workgroup (thread
+  // tid of sweep p holds float4 p*256 + tid: block 32p + tid/8, part tid%8)
   const int nb = l / 32;
-  for (int b0 = 0; b0 < nb; b0 += 32) {
+  auto quant = [&](int b0, const float4& v, const float4& g) {
     const int b = b0 + (tid >> 3), j = tid & 7;
     const bool ok = b < nb;                         // the same for the 8 threads of a block
-    const int i4 = ok ? b * 8 + j : 0;
-    const float4 v = z4[i4], g = g4[i4];
     float q[4] = {v.x * inv * g.x, v.y * inv * g.y, v.z * inv * g.z, v.w * inv * g.w};
     const float amax = group_max<8>(fmaxf(fmaxf(fabsf(q[0]), fabsf(q[1])), fmaxf(fabsf(q[2]), fabsf(q[3]))));
     const int e = mx8_block_exp(amax);
@@ -62,6 +87,17 @@ __global__ void __launch_bounds__(256) k_tail_norm_quant(TailArgs a) {
     if (ok) {
       *reinterpret_cast<uint32_t*>(a.codes + int64_t(t) * l + 32 * b + 4 * j) = w;
       if (j == 0) a.scales[int64_t(t) * nb + b] = static_cast<uint8_t>(e + 127);
+    }
+  };
+  if (in_regs) {
+    // compile-time sweep index: the registers stay registers
+#pragma unroll
+    for (int p = 0; p < kTailRegF4; ++p)
+      if (32 * p < nb) quant(32 * p, zr[p], gr[p]);  // the same in every thread
+  } else {
+    for (int b0 = 0; b0 < nb; b0 += 32) {
+      const int i4 = min(b0 * 8 + tid, n4 - 1);
+      quant(b0, z4[i4], g4[i4]);
     }
   }
   if (t == 0) {
@@ -102,10 +138,123 @@ __global__ void __launch_bounds__(256) k_tail_add(const uint16_t* __restrict__ o
   }
 }
 
+// Few rows (T <= kTailGemvMaxT): the projection split along K.  Workgroup
+// (G, ks) computes the 64 outputs of packed weight group G over K steps
+// [ks*spk, min((ks+1)*spk, ns)); its wave w takes steps w, w+4, ... of that
+// range -- at most kTailGemvSteps -- and issues every load of them (weights
+// non-temporal: read once) before its first MFMA, straight into registers:
+// a few hundred workgroups each with all of their bytes in flight at once.
+// The 16 MFMA rows are the rows of z (rows past T repeat the last one and
+// are not written).  The four waves' sums meet in LDS and are added in wave
+// order; the fp32 partial of slice ks goes to part[ks][T][hidden], and
+// k_tail_reduce adds the slices in order (plus s) and rounds to bf16.
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u_nt_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f_t tail_mfma(const v8i_t& av, const v8i_t& bv, v4f_t c, uint32_t sa, uint32_t sb) {
+  // A: FP8 E4M3 (format 0), B: FP4 E2M1 (format 4); scales in byte 0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 4, 0, static_cast<int>(sa), 0,
+                                                          static_cast<int>(sb));
+}
+
+__global__ void __launch_bounds__(256) k_tail_gemv(TailArgs a, float* __restrict__ part, int ks_n) {
+  __shared__ v4f_t red[4][4][64];
+  const int G = blockIdx.x, ks = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int g = lane >> 4, r16 = lane & 15;
+  const int K = a.latent, ns = K / 128;
+  const int spk = (ns + ks_n - 1) / ks_n;
+  const int s0 = ks * spk, s1 = min(ns, s0 + spk);
+  const uint8_t* wc = a.up_c + int64_t(G) * ns * 4096 + 16 * lane;
+  const uint8_t* wsc = a.up_s + int64_t(G) * ns * 256 + 4 * lane;
+  const int row = min(r16, a.T - 1);
+  const uint8_t* ac = a.codes + int64_t(row) * K;
+  const uint8_t* asc = a.scales + int64_t(row) * (K / 32);
+  uint4 wv[kTailGemvSteps][4], a0[kTailGemvSteps], a1[kTailGemvSteps];
+  uint32_t sbw[kTailGemvSteps], sa[kTailGemvSteps];
+#pragma unroll
+  for (int i = 0; i < kTailGemvSteps; ++i) {
+    const int st = s0 + w + 4 * i;
+    const int sst = st < s1 ? st : min(s0, ns - 1);  // past the range: a valid step, its values unused
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4u_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt_t*>(wc + int64_t(sst) * 4096 + j * 1024));
+      wv[i][j] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+    sbw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wsc + int64_t(sst) * 256));
+    a0[i] = *reinterpret_cast<const uint4*>(ac + sst * 128 + 16 * g);
+    a1[i] = *reinterpret_cast<const uint4*>(ac + sst * 128 + 64 + 16 * g);
+    sa[i] = *reinterpret_cast<const uint32_t*>(asc + 4 * sst);
+  }
+  v4f_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = v4f_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kTailGemvSteps; ++i) {
+    if (s0 + w + 4 * i < s1) {  // the same in every lane
+      v8i_t av;
+      av[0] = a0[i].x; av[1] = a0[i].y; av[2] = a0[i].z; av[3] = a0[i].w;
+      av[4] = a1[i].x; av[5] = a1[i].y; av[6] = a1[i].z; av[7] = a1[i].w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v8i_t bv;
+        bv[0] = wv[i][j].x; bv[1] = wv[i][j].y; bv[2] = wv[i][j].z; bv[3] = wv[i][j].w;
+        bv[4] = 0; bv[5] = 0; bv[6] = 0; bv[7] = 0;
+        acc[j] = tail_mfma(av, bv, acc[j], sa[i] >> (8 * g), sbw[i] >> (8 * j));
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[w][j][lane] = acc[j];
+  __syncthreads();
+  // thread (j, l): block j's lane l -- rows 4(l/16) .. +3, column 16j + l%16
+  const int j = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const v4f_t s = ((red[0][j][l] + red[1][j][l]) + red[2][j][l]) + red[3][j][l];
+  const int col = 64 * G + 16 * j + (l & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * (l >> 4) + i;
+    if (r < a.T) part[(int64_t(ks) * a.T + r) * a.hidden + col] = s[i];
+  }
+}
+
+// y = bf16(sum of the K slices in order (+ s)); 4 columns per thread
+__global__ void __launch_bounds__(256) k_tail_reduce(const float* __restrict__ part, int ks_n,
+                                                     const float* __restrict__ s, uint16_t* __restrict__ y,
+                                                     int64_t n4) {
+  for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < n4; i += int64_t(gridDim.x) * 256) {
+    float4 v = reinterpret_cast<const float4*>(part)[i];
+    for (int k = 1; k < ks_n; ++k) {
+      const float4 p = reinterpret_cast<const float4*>(part)[k * n4 + i];
+      v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+    }
+    if (s) {
+      const float4 q = reinterpret_cast<const float4*>(s)[i];
+      v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+    }
+    const uint32_t lo = uint32_t(f32_to_bf16_rne(v.x)) | (uint32_t(f32_to_bf16_rne(v.y)) << 16);
+    const uint32_t hi = uint32_t(f32_to_bf16_rne(v.z)) | (uint32_t(f32_to_bf16_rne(v.w)) << 16);
+    reinterpret_cast<uint2*>(y)[i] = make_uint2(lo, hi);
+  }
+}
+
 hipError_t launch_tail(const TailArgs& a, int num_cus, hipStream_t st) {
   hipLaunchKernelGGL(k_tail_norm_quant, dim3(a.T), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.T <= kTailGemvMaxT) {
+    const int ks_n = tail_gemv_slices(a.latent);
+    hipLaunchKernelGGL(k_tail_gemv, dim3(a.hidden / 64, ks_n), dim3(256), 0, st, a, a.part, ks_n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n4 = int64_t(a.T) * a.hidden / 4;
+    const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, int64_t(num_cus) * 4);
+    hipLaunchKernelGGL(k_tail_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a.part, ks_n,
+                       a.s, a.y, n4);
+    return hipGetLastError();
+  }
   // the projection: the down-GEMM kernels with one expert, K = latent,
   // N = hidden, rows in token order
   FwdArgs f{};
