@@ -115,6 +115,24 @@ def routing_weights(logits, ids) -> np.ndarray:
     return s / s.sum(axis=1, keepdims=True)
 
 
+def router_bias_update(b, counts, num_tokens: int, top_k: int, rate: float) -> np.ndarray:
+    """One balancing step of the router bias from the loads of a batch.
+
+    "Kimi K3 Tech Intro" (section 1 table, section 4.3) names "quantile
+    balancing" for the router without defining it; the router bias is the
+    layer's only balancing hook.  The step taken here: an expert loaded above
+    the mean load T*k/E has its bias lowered by `rate`, one below it raised
+    by `rate`, one exactly at it kept (b_e + rate * sign(mean - c_e)).  The
+    bias is an fp32 tensor, so the update is one fp32 addition per expert:
+    computed here in float32 exactly as defined, rate rounded to fp32 first.
+    """
+    b = np.asarray(b, dtype=np.float32)
+    c = np.asarray(counts, dtype=np.float64)
+    mean = num_tokens * top_k / b.size
+    step = np.sign(mean - c).astype(np.float32) * np.float32(rate)
+    return (b + step).astype(np.float32)
+
+
 # --------------------------------------------------------------------------
 # Permutation
 # --------------------------------------------------------------------------

@@ -360,3 +360,36 @@ def test_a16w4_intermediates_exact_on_integer_operands():
     hb, o = moe.expert_mlp_a16(bits, guc, gus, dnc, dns, d_ff=f, intermediates=mid)
     assert np.array_equal(mid["gu"], (xi.astype(np.int64) @ wg.T.astype(np.int64)).astype(np.float64))
     assert np.array_equal(hb, moe.f64_to_bf16(mid["h"]))
+
+
+# ---------------------------------------------------------------------------
+# router bias balancing step
+# ---------------------------------------------------------------------------
+
+def test_router_bias_update_by_hand():
+    # 4 experts, 6 tokens, top-2: mean load 3
+    b = np.array([0.5, -1.0, 0.0, 2.0], np.float32)
+    counts = np.array([5, 3, 1, 3])
+    out = moe.router_bias_update(b, counts, 6, 2, 0.25)
+    assert out.dtype == np.float32
+    assert out.tolist() == [0.25, -1.0, 0.25, 2.0]
+    # the addition is the fp32 one: 1 + 2^-30 stays 1
+    out = moe.router_bias_update(np.ones(2, np.float32), [0, 4], 2, 1, 2.0 ** -30)
+    assert out.tolist() == [1.0, 1.0]
+
+
+def test_router_bias_updates_even_out_a_skewed_load():
+    # repeated steps on the Zipf-skewed router of a small layer: the most
+    # loaded expert's share falls and the spread of the loads shrinks
+    cfg = I.LayerConfig("bal", 512, 128, 32, 4, 64, 0, zipf_bias=True, seed=17)
+    x, wr, b = I.gen_x(cfg), I.gen_router_w(cfg), I.gen_router_b(cfg)
+    def loads(bias):
+        ids, _ = moe.topk_select(moe.router_logits(x, wr, bias), cfg.top_k)
+        return np.bincount(ids.reshape(-1), minlength=cfg.num_experts)
+    c0 = loads(b)
+    for _ in range(40):
+        b = moe.router_bias_update(b, loads(b), cfg.tokens, cfg.top_k, 0.2)
+    c1 = loads(b)
+    mean = cfg.tokens * cfg.top_k / cfg.num_experts
+    assert c1.max() < 0.5 * c0.max() and np.std(c1) < 0.5 * np.std(c0)
+    assert abs(c1.max() - mean) < abs(c0.max() - mean)
