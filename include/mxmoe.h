@@ -243,6 +243,22 @@ moe_status moe_latent_tail(int64_t num_tokens, int32_t latent, int32_t hidden, f
                            void *workspace, size_t workspace_bytes, const moe_tail_taps *taps,
                            void *stream);
 
+/* One balancing step of the router bias from the expert loads of a forward:
+ * b_e <- b_e + rate * sign(num_tokens*top_k/num_experts - c_e), with c_e =
+ * expert_offsets[e+1] - expert_offsets[e] (moe_forward's expert_offsets tap
+ * of that forward, num_tokens its token count): experts above the mean load
+ * are made less likely, those below more likely.  "Kimi K3 Tech Intro"
+ * (section 1 table, section 4.3) names "quantile balancing" for the router
+ * without defining it; the router bias is the layer's only balancing hook,
+ * and this step is the reading taken.  The sign is decided in integers, the
+ * addition is one fp32 addition per expert.
+ *   expert_offsets  int32 [E+1] device, 4-byte aligned
+ *   router_b        fp32 [E] device, updated in place, 4-byte aligned
+ *   rate            finite, >= 0
+ * num_tokens == 0 enqueues nothing.  Errors and streams as for moe_forward. */
+moe_status moe_router_bias_update(const moe_plan_t *plan, const int32_t *expert_offsets,
+                                  int64_t num_tokens, float rate, float *router_b, void *stream);
+
 /* Stages of moe_forward, for per-stage timing. */
 typedef enum {
   MOE_STAGE_ROUTER = 0,  /* router logits                                   */

@@ -559,6 +559,26 @@ moe_status moe_latent_tail(int64_t num_tokens, int32_t latent, int32_t hidden, f
   return MOE_OK;
 }
 
+moe_status moe_router_bias_update(const moe_plan_t* plan, const int32_t* expert_offsets,
+                                  int64_t num_tokens, float rate, float* router_b, void* stream) {
+  if (!plan) return fail(MOE_ERR_INVALID_ARG, "plan is NULL");
+  const moe_config& c = plan->cfg;
+  if (num_tokens < 0 || num_tokens > c.max_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "num_tokens %lld outside [0, %lld]",
+                static_cast<long long>(num_tokens), static_cast<long long>(c.max_tokens));
+  if (!(rate >= 0.0f) || rate > 3.4e38f) return fail(MOE_ERR_INVALID_ARG, "rate must be finite and >= 0");
+  if (num_tokens == 0) return MOE_OK;
+  if (!expert_offsets || !router_b) return fail(MOE_ERR_INVALID_ARG, "expert_offsets or router_b is NULL");
+  if (!aligned(expert_offsets, 4) || !aligned(router_b, 4))
+    return fail(MOE_ERR_INVALID_ARG, "expert_offsets and router_b need 4-byte alignment");
+  moe_status s = check_device();
+  if (s != MOE_OK) return s;
+  hipError_t e = launch_router_bias_update(expert_offsets, c.num_experts, num_tokens * c.top_k, rate,
+                                           router_b, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
 moe_status moe_profile_begin(moe_plan_t* plan, uint32_t stage_mask, int32_t max_calls) {
   if (!plan) return fail(MOE_ERR_INVALID_ARG, "plan is NULL");
   if (max_calls < 1 || max_calls > 65536) return fail(MOE_ERR_INVALID_ARG, "max_calls outside [1, 65536]");

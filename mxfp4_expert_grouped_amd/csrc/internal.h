@@ -121,6 +121,8 @@ inline bool stream_split_phases(const FwdArgs& a) {
   return router_small(a.T, a.d, a.E) && a.bm <= kDecodeMaxRows && a.S > 0;
 }
 
+hipError_t launch_router_bias_update(const int32_t* offsets, int E, int64_t tk, float rate, float* b,
+                                     hipStream_t st);
 hipError_t launch_router(const FwdArgs& a, hipStream_t st);
 hipError_t launch_topk_shared_gate_up(const FwdArgs& a, hipStream_t st);
 hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st);

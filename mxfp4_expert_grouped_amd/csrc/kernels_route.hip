@@ -687,6 +687,28 @@ __global__ void __launch_bounds__(256) k_perm_scatter(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Router bias balancing step: b_e += rate * sign(T*k/E - c_e), the loads c_e
+// from a forward's expert offsets.  "Kimi K3 Tech Intro" names quantile
+// balancing for the router without defining it; this is the reading taken.
+// The sign is decided in integers (T*k - c_e*E), the addition in fp32.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_router_bias_update(const int32_t* __restrict__ offsets, int E,
+                                                            int64_t tk, float rate, float* __restrict__ b) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const int64_t c = offsets[e + 1] - offsets[e];
+  const int64_t d = tk - c * E;
+  const float step = d > 0 ? rate : (d < 0 ? -rate : 0.0f);
+  b[e] = b[e] + step;
+}
+
+hipError_t launch_router_bias_update(const int32_t* offsets, int E, int64_t tk, float rate, float* b,
+                                     hipStream_t st) {
+  hipLaunchKernelGGL(k_router_bias_update, dim3((E + 255) / 256), dim3(256), 0, st, offsets, E, tk, rate, b);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_quant(const FwdArgs& a, hipStream_t st) {
   if (stream_split_phases(a)) return launch_topk_shared_gate_up(a, st);
   if (router_small(a.T, a.d, a.E))

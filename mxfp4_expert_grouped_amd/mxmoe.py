@@ -20,6 +20,7 @@ MOE_SRC_BF16, MOE_SRC_FP32 = 0, 1
 EXPORTED = ("moe_plan", "moe_plan_destroy", "moe_workspace_bytes", "moe_quantize_act",
             "moe_forward", "moe_forward_noalloc", "moe_profile_begin", "moe_profile_end", "moe_packed_scale_bytes",
             "moe_pack_mx4", "moe_latent_tail_workspace_bytes", "moe_latent_tail",
+            "moe_router_bias_update",
             "moe_status_string", "moe_last_error")
 STAGES = ("router", "topk", "permute", "gate_up", "down", "combine")
 
@@ -111,6 +112,8 @@ def load_library(path: str = LIB_PATH):
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                     POINTER(MoeTailTaps), c_void_p]
     lib.moe_latent_tail.restype = c_int
+    lib.moe_router_bias_update.argtypes = [c_void_p, c_void_p, c_int64, ctypes.c_float, c_void_p, c_void_p]
+    lib.moe_router_bias_update.restype = c_int
     lib.moe_status_string.argtypes = [c_int]
     lib.moe_status_string.restype = c_char_p
     lib.moe_last_error.argtypes = []
@@ -203,3 +206,8 @@ def moe_latent_tail(num_tokens: int, latent: int, hidden: int, eps: float, weigh
     _check(load_library().moe_latent_tail(num_tokens, latent, hidden, eps, ctypes.byref(weights), z, s, y,
                                           workspace, workspace_bytes,
                                           ctypes.byref(taps) if taps else None, stream))
+
+
+def moe_router_bias_update(plan: c_void_p, expert_offsets: int, num_tokens: int, rate: float,
+                           router_b: int, stream: Optional[int] = None) -> None:
+    _check(load_library().moe_router_bias_update(plan, expert_offsets, num_tokens, rate, router_b, stream))

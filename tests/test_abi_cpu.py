@@ -296,3 +296,21 @@ def test_a16w4_host_checks(M):
     finally:
         M.moe_plan_destroy(p)
         M.moe_plan_destroy(p8)
+
+
+def test_router_bias_update_host_checks(M):
+    p = M.moe_plan(256, 128, 16, 2, 1, 8)
+    fake = 1 << 20
+    try:
+        M.moe_router_bias_update(p, None, 0, 0.1, None)  # no tokens: nothing to do
+        for args, status in [((p, fake, 9, 0.1, fake), M.MOE_ERR_INVALID_ARG),
+                             ((p, fake, 4, -0.1, fake), M.MOE_ERR_INVALID_ARG),
+                             ((p, fake, 4, float("inf"), fake), M.MOE_ERR_INVALID_ARG),
+                             ((p, None, 4, 0.1, fake), M.MOE_ERR_INVALID_ARG),
+                             ((p, fake, 4, 0.1, fake + 2), M.MOE_ERR_INVALID_ARG),
+                             ((None, fake, 4, 0.1, fake), M.MOE_ERR_INVALID_ARG)]:
+            with pytest.raises(M.MoeError) as ei:
+                M.moe_router_bias_update(*args)
+            assert ei.value.status == status
+    finally:
+        M.moe_plan_destroy(p)
