@@ -630,7 +630,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr int kPfSlot = 52224;                 // A 32 KB | B 16 KB | A scales 2 KB | B scales 1 KB
 constexpr int kPfA = 0, kPfB = 32768, kPfAS = 49152, kPfBS = 51200;
-constexpr int kPfLds = 3 * kPfSlot;            // 156672 bytes
+constexpr int kPfRowTab = 3 * kPfSlot;         // the ring: 156672 bytes; then 256 row entries
+constexpr int kPfLds = kPfRowTab + 1024;
 __shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 
 
@@ -695,26 +696,45 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   // output rows (down)
   const int c0 = GU ? nblk * 128 : nblk * 256;
   const int64_t grp0 = 4 * int64_t(nblk);
-  // activation row r of the tile; padding rows read the tile's first row
+  const uint32_t lds0 = lds_addr(pf_lds);
+  // A routed tile's row indirections come to LDS ahead of everything else,
+  // one direct copy per wave (tile rows 64 wu .. 64 wu + 63, rows past the
+  // tile's end reading its first row): the row-to-token entries of gate_up,
+  // which the activation copies' addresses need (so the weight copies of the
+  // first steps can go out while they travel), and the row-to-pair entries
+  // of down, which only its epilogue's stores need.
+  const int* const row_tab = reinterpret_cast<const int*>(pf_lds + kPfRowTab);
+  const bool routed = tile.row_begin < a.Rr;   // (a tile never mixes routed and shared rows)
+  if (routed) {
+    const int r = 64 * wu + lane;
+    const int row = tile.row_begin + (tile.row_begin + r < tile.row_end ? r : 0);
+    lds_copy4((GU ? a.row_token : a.row_src) + row, lds0 + kPfRowTab + wu * 256);
+  }
+  // activation row of tile row r; padding rows read the tile's first row
+  // (gate_up: only once the row table has landed)
   auto src_row = [&](int r) -> int64_t {
+    if (GU && routed) return row_tab[r];
     int row = tile.row_begin + r;
     if (row >= tile.row_end) row = tile.row_begin;
-    return GU ? (row < a.Rr ? a.row_token[row] : row - a.Rr - sidx * a.T) : row;
+    return GU ? row - a.Rr - sidx * a.T : row;
   };
 
   // ---- copy sources of this wave.  A copy q covers rows 64wu + 8q .. +7:
   // lane l reads chunk (l%8) ^ swz(row) of row 64wu + 8q + l/8 and lands at
-  // LDS row*128 + 16(l%8).
+  // LDS row*128 + 16(l%8).  (Set once the rows are known: every row this
+  // wave looks up is one it copied into the row table itself.)
   const uint8_t* a_src[8];
+  const uint8_t* as_src = nullptr;
+  auto set_act_sources = [&]() {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int rl = 64 * wu + 8 * q + (lane >> 3);
-    a_src[q] = (GU ? a.x_codes : a.h_codes) + src_row(rl) * K + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
-  }
-  const uint8_t* as_src = (GU ? a.x_scales : a.h_scales) + src_row(64 * wu + lane) * (K / 32);
+    for (int q = 0; q < 8; ++q) {
+      const int rl = 64 * wu + 8 * q + (lane >> 3);
+      a_src[q] = (GU ? a.x_codes : a.h_codes) + src_row(rl) * K + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
+    }
+    as_src = (GU ? a.x_scales : a.h_scales) + src_row(64 * wu + lane) * (K / 32);
+  };
   const uint8_t* b_src = wc + (grp0 + wu) * nsteps * 4096 + 16 * lane;
   const uint8_t* bs_src = ws + (grp0 + wu) * nsteps * 256 + 4 * lane;
-  const uint32_t lds0 = lds_addr(pf_lds);
 
   // Copies of step st into slot st % 3 (and of the activation scales of
   // group st / 4 when st starts a group).  Their number per step is fixed --
@@ -894,12 +914,31 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 
     // prologue: steps 0 and 1, and the activation copies of step 2 (its
     // weight copies come in step 0)
-    static_for<0, 8>([&](auto qc) { copy_a(0, qc); });
-    static_for<0, 6>([&](auto mc) { copy_w(0, mc, IntC<1>{}, wnt_c); });
-    static_for<0, 8>([&](auto qc) { copy_a(1, qc); });
-    static_for<0, 6>([&](auto mc) { copy_w(1, mc, IntC<0>{}, wnt_c); });
-    static_for<0, 8>([&](auto qc) { copy_a(2, qc); });
-    PF_WAIT_VM(ncop(1) + 8);                   // step 0 has landed
+    if constexpr (GU) {
+      // the weights and weight scales of steps 0 and 1 while the row table
+      // travels; then, with the rows known, the activation scales of steps 0
+      // and 1 and the activations of steps 0-2
+      static_for<0, 5>([&](auto mc) { copy_w(0, mc, IntC<1>{}, wnt_c); });
+      static_for<0, 5>([&](auto mc) { copy_w(1, mc, IntC<0>{}, wnt_c); });
+      PF_WAIT_VM(10);                          // the row table (the oldest copy) has landed
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      set_act_sources();
+      copy_w(0, IntC<5>{}, IntC<1>{}, wnt_c);
+      copy_w(1, IntC<5>{}, IntC<0>{}, wnt_c);
+      static_for<0, 8>([&](auto qc) { copy_a(0, qc); });
+      static_for<0, 8>([&](auto qc) { copy_a(1, qc); });
+      static_for<0, 8>([&](auto qc) { copy_a(2, qc); });
+      PF_WAIT_VM(16);                          // step 0 (and 1 but its last activations) has landed
+    } else {
+      set_act_sources();
+      static_for<0, 8>([&](auto qc) { copy_a(0, qc); });
+      static_for<0, 6>([&](auto mc) { copy_w(0, mc, IntC<1>{}, wnt_c); });
+      static_for<0, 8>([&](auto qc) { copy_a(1, qc); });
+      static_for<0, 6>([&](auto mc) { copy_w(1, mc, IntC<0>{}, wnt_c); });
+      static_for<0, 8>([&](auto qc) { copy_a(2, qc); });
+      PF_WAIT_VM(ncop(1) + 8);                 // step 0 has landed
+    }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -953,7 +992,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int rl = 32 * i + 8 * (r / 4) + 4 * g32 + (r % 4);
           const float gt = acc[i][pp][r], up = acc[i][pp + 2][r];
-          hs[rl * 68 + 32 * pp + l32] = gt / (1.0f + __expf(-gt)) * up;
+          hs[rl * 68 + 32 * pp + l32] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
           if (a.gu_acc) {
             const int row = tile.row_begin + wrow0 + rl;
             if (row < tile.row_end) {
@@ -999,14 +1038,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   } else {
     // o rows are stored in (token, slot) order: routed row r goes to its pair
     // index row_src[r] (token-major, so the combine reads a token's rows
-    // back to back), shared rows keep their place.  Destinations of this
-    // wave's 128 rows into an LDS table after the four staging areas.
-    int* dst_tab = reinterpret_cast<int*>(pf_lds + 4 * (128 * 136 * 2)) + wu * 128;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int row = tile.row_begin + wrow0 + 64 * hh + lane;
-      dst_tab[64 * hh + lane] = row < tile.row_end && row < a.Rr ? a.row_src[row] : row;
-    }
+    // back to back), shared rows keep their place.  The routed rows'
+    // destinations are in the row table, copied ahead of the operands and
+    // landed before the barrier above.
     // bf16 outputs [128 rows][128 columns] (row stride 136 halves), then
     // 16-byte row chunks: 16 per row, 2048 per wave, 32 per lane
     uint16_t* os = reinterpret_cast<uint16_t*>(pf_lds) + wu * (128 * 136);
@@ -1028,7 +1062,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
       const int row = tile.row_begin + wrow0 + rl;
       if (rl < 32 * nact && row < tile.row_end) {
         const uint4 t = *reinterpret_cast<const uint4*>(os + rl * 136 + cc);
-        *reinterpret_cast<uint4*>(a.o16 + int64_t(dst_tab[rl]) * a.d + c0 + 128 * wn + cc) = t;
+        const int dst = routed ? row_tab[wrow0 + rl] : row;
+        *reinterpret_cast<uint4*>(a.o16 + int64_t(dst) * a.d + c0 + 128 * wn + cc) = t;
       }
     }
   }
