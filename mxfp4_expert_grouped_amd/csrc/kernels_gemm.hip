@@ -665,6 +665,13 @@ __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int*
   return true;
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// lane l reads lane l^1's x
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+
 // LDS address of the A-scale group area written by wave w (0..3)
 __device__ __forceinline__ int pf_asg_off(int w) { return (w >> 1) * kPfSlot + kPfAS + (w & 1) * 1024; }
 
@@ -1041,18 +1048,30 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
     // back to back), shared rows keep their place.  The routed rows'
     // destinations are in the row table, copied ahead of the operands and
     // landed before the barrier above.
-    // bf16 outputs [128 rows][128 columns] (row stride 136 halves), then
-    // 16-byte row chunks: 16 per row, 2048 per wave, 32 per lane
-    uint16_t* os = reinterpret_cast<uint16_t*>(pf_lds) + wu * (128 * 136);
+    // bf16 outputs [128 rows][128 columns] staged in LDS, then 16-byte row
+    // chunks to HBM: 16 per row, 2048 per wave, 32 per lane.  Staging: the
+    // registers r, r+1 of a lane hold rows R, R+1 of one column; one exchange
+    // with the neighbouring lane gives the even lane row R and the odd lane
+    // row R+1, each for two adjacent columns, written as one packed dword.
+    // Rows are 256 bytes apart, with their four 32-column chunks permuted by
+    // bits 0 and 2 of the row, so that the four rows one write instruction
+    // touches fall on distinct banks (and a row read touches every bank once).
+    uint16_t* os = reinterpret_cast<uint16_t*>(pf_lds) + wu * (128 * 128);
+    auto chunk_of = [](int rl, int c32) { return c32 ^ ((rl & 1) | (((rl >> 2) & 1) << 1)); };
+    const bool odd = (lane & 1) != 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (i >= nact) break;
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = 32 * i + 8 * (r / 4) + 4 * g32 + (r % 4);
-          os[rl * 136 + 32 * pp + l32] = f32_to_bf16_rne(acc[i][pp][r]);
+        for (int r = 0; r < 16; r += 2) {
+          const float v0 = acc[i][pp][r], v1 = acc[i][pp][r + 1];
+          const float rv = dpp_xor1(odd ? v0 : v1);
+          const v2bf16 pk = __builtin_convertvector((v2f){odd ? rv : v0, odd ? v1 : rv}, v2bf16);
+          const int rl = 32 * i + 8 * (r / 4) + 4 * g32 + (r % 4) + (odd ? 1 : 0);
+          *reinterpret_cast<uint32_t*>(os + rl * 128 + chunk_of(rl, pp) * 32 + (l32 & ~1)) =
+              __builtin_bit_cast(uint32_t, pk);
         }
     }
 #pragma unroll 4
@@ -1061,7 +1080,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
       const int rl = ch >> 4, cc = 8 * (ch & 15);
       const int row = tile.row_begin + wrow0 + rl;
       if (rl < 32 * nact && row < tile.row_end) {
-        const uint4 t = *reinterpret_cast<const uint4*>(os + rl * 136 + cc);
+        const uint4 t = *reinterpret_cast<const uint4*>(os + rl * 128 + chunk_of(rl, cc >> 5) * 32 + (cc & 31));
         const int dst = routed ? row_tab[wrow0 + rl] : row;
         *reinterpret_cast<uint4*>(a.o16 + int64_t(dst) * a.d + c0 + 128 * wn + cc) = t;
       }
