@@ -1000,15 +1000,28 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
           const int rl = 32 * i + 8 * (r / 4) + 4 * g32 + (r % 4);
           const float gt = acc[i][pp][r], up = acc[i][pp + 2][r];
           hs[rl * 68 + 32 * pp + l32] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
-          if (a.gu_acc) {
+        }
+    }
+    // (the optional accumulator tap in a loop of its own: a branch inside the
+    // loop above would cut it into one basic block per value and serialise
+    // the exponential / reciprocal chains)
+    if (a.gu_acc) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nact) break;
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rl = 32 * i + 8 * (r / 4) + 4 * g32 + (r % 4);
             const int row = tile.row_begin + wrow0 + rl;
             if (row < tile.row_end) {
               const int col = c0 + 64 * wn + 32 * pp + l32;
-              a.gu_acc[int64_t(row) * 2 * a.dff + col] = gt;
-              a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + col] = up;
+              a.gu_acc[int64_t(row) * 2 * a.dff + col] = acc[i][pp][r];
+              a.gu_acc[int64_t(row) * 2 * a.dff + a.dff + col] = acc[i][pp + 2][r];
             }
           }
-        }
+      }
     }
     // lane l quantises rows l and l + 64: two MXFP8 blocks of 32 h values each
 #pragma unroll
