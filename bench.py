@@ -123,7 +123,15 @@ def main():
         n = touched[key][0] + cfg.num_shared
         return n * (gu_bytes + dn_bytes) + router_bytes + xy_bytes
 
+    # For a few tokens the library runs the shared experts' gate_up inside the
+    # routing launch (next to the top-k), so the gate_up launch then streams
+    # the routed experts alone (the library's rule: T <= 32 with the one-pass
+    # router, 8-row tiles, shared experts present).
+    phase_split = decode and T <= 32 and T * (cfg.d_model // 32) <= 32 * cfg.num_experts and cfg.num_shared > 0
+
     def gate_up_bytes(key):
+        if phase_split:
+            return touched[key][0] * gu_bytes + act_in + h_bytes * cfg.top_k // (cfg.top_k + cfg.num_shared)
         n = touched[key][0] + cfg.num_shared
         return n * gu_bytes + act_in + h_bytes
 
@@ -236,7 +244,9 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": profiled_traffic(cfg.name),
-                    "kernel": "gate_up grouped GEMM (k_gemm_stream, 8-row tiles)",
+                    "kernel": ("gate_up grouped GEMM, routed experts (k_gemm_stream, 8-row tiles; the shared "
+                               "experts' gate_up runs in the routing launch)" if phase_split
+                               else "gate_up grouped GEMM (k_gemm_stream, 8-row tiles)"),
                     "kernel_ms": round(kern_ms, 5),
                     "algorithmic_bytes_per_launch": int(mean_gu_bytes)}
     else:
@@ -256,7 +266,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg)
+        cpu = cpu_baseline(cfg, a16w4=args.a16w4)
 
     out = {
         "metric": METRIC,
@@ -365,14 +375,14 @@ def profiled_traffic(workload: str):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in ("kernels_gemm.hip", "mx_device.h", "internal.h"):
+    for f in ("kernels_gemm.hip", "mx_device.h", "internal.h", "topk_device.h"):
         h.update(open(os.path.join(root, "mxfp4_expert_grouped_amd", "csrc", f), "rb").read())
     if fields.get("source_sha256") != h.hexdigest():
         return None
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(cfg):
+def cpu_baseline(cfg, a16w4: bool = False):
     """The oracle, untuned, on the host cores for a bounded sample of the
     workload: the whole step at the tiny and decode1 workloads, else the first
     tokens of the batch (rows are independent).  The decode of the touched
@@ -399,7 +409,7 @@ def cpu_baseline(cfg):
     for _ in range(runs):  # best of `runs`; input generation stays outside the timing
         t0 = time.perf_counter()
         OM.forward(x, wr, b, W, num_experts=cfg.num_experts, top_k=cfg.top_k,
-                   num_shared=cfg.num_shared, d_ff=cfg.d_ff)
+                   num_shared=cfg.num_shared, d_ff=cfg.d_ff, activations="bf16" if a16w4 else "mxfp8")
         total = min(total, time.perf_counter() - t0)
         t0 = time.perf_counter()
         for gc, gs, dc, ds in mats:
@@ -409,8 +419,9 @@ def cpu_baseline(cfg):
     return {"value": round(ntok / total, 4), "unit": "tokens/s",
             "cores": int(max(blas_threads, 1)), "kind": "oracle",
             "sample": f"{ntok} token(s) of the {cfg.name} workload (layer copy 0, batch 0): "
-                      f"routing, MXFP8 quantisation, {len(touched)} routed + {cfg.num_shared} shared "
-                      f"experts in float64; {total:.2f} s" + (f" (best of {runs})" if runs > 1 else ""),
+                      + ("routing, bf16 activations (A16W4), " if a16w4 else "routing, MXFP8 quantisation, ")
+                      + f"{len(touched)} routed + {cfg.num_shared} shared experts in float64; {total:.2f} s"
+                      + (f" (best of {runs})" if runs > 1 else ""),
             "seconds": round(total, 4), "weight_decode_s": round(decode, 4),
             "compute_s": round(max(total - decode, 0.0), 4),
             "host_cpus": len(os.sched_getaffinity(0))}
