@@ -470,7 +470,11 @@ TailLayout tail_layout(int64_t T, int64_t latent, int64_t hidden, bool with_s) {
   L.tiles = take(((T + L.bm - 1) / L.bm) * sizeof(Tile));
   L.tile_count = take(4);
   L.ex_tiles = take(8);
-  L.part = take(T <= kTailGemvMaxT ? size_t(tail_gemv_slices(static_cast<int>(latent))) * T * hidden * 4 : 0);
+  // fp32 partials: of the K slices of the few-row projection, or of the
+  // K slices of few 256-row tiles
+  const int64_t ks = T <= kTailGemvMaxT ? tail_gemv_slices(static_cast<int>(latent))
+                   : L.bm > kDecodeMaxRows ? tail_ksplit(T, latent, hidden) : 1;
+  L.part = take(ks > 1 ? size_t(ks) * T * hidden * 4 : 0);
   L.total = off;
   return L;
 }

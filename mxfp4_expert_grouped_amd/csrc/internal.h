@@ -59,6 +59,11 @@ struct FwdArgs {
   int num_cus;          // compute units of the device (persistent decode grid)
   int max_tiles;
   int nchunks;          // 64-token chunks
+  // the prefill down GEMM's K split (LatentMoE tail only): > 1 cuts K into
+  // ksplit equal slices (multiples of 512) and writes fp32 partials
+  // kpart[slice][R][d] in row order instead of bf16 o rows
+  int ksplit;
+  float* kpart;
 };
 
 // Everything the kernels of one LatentMoE tail call need (device pointers).
@@ -91,6 +96,24 @@ inline int tail_gemv_slices(int latent) {
 }
 
 // Launchers (kernels_*.hip).  Each returns hipSuccess or the launch error.
+// K slices of the LatentMoE tail's projection on 256-row tiles, when its
+// tiles x 256-column blocks alone would give fewer workgroups than the 256
+// CUs of the chip: the smallest divisor of latent/512 (at most 8) that
+// reaches 256 workgroups, else the largest.  Each slice adds one fp32
+// partial of the output, summed in order (with s) by the tail's reduction.
+inline int tail_ksplit(int64_t T, int64_t latent, int64_t hidden) {
+  if (T < 24 || latent % 512 != 0) return 1;
+  const int64_t base = ((T + 255) / 256) * (hidden / 256);
+  const int64_t g = latent / 512;
+  int best = 1;
+  for (int d = 1; d <= 8 && d <= g; ++d) {
+    if (g % d != 0) continue;
+    best = d;
+    if (base * d >= 256) break;
+  }
+  return best;
+}
+
 hipError_t launch_tail(const TailArgs& a, int num_cus, hipStream_t st);
 hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t cols, int64_t ld,
                            uint8_t* codes, uint8_t* scales, hipStream_t st);

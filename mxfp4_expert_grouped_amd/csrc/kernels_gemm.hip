@@ -653,6 +653,15 @@ constexpr int kPfGroupTiles = 4;
 __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int* tile_out, int* blk_out) {
   const int ntiles = *a.tile_count;
   const int ngroups = (ntiles + kPfGroupTiles - 1) / kPfGroupTiles;
+  if (ngroups < 8) {
+    // fewer groups than XCDs: items one by one, tile fastest, so that every
+    // XCD gets a share (the grid holds at least 32 items per group)
+    const int i = blockIdx.x;
+    if (i >= ntiles * nblocks) return false;
+    *tile_out = i % ntiles;
+    *blk_out = i / ntiles;
+    return true;
+  }
   const int xcd = blockIdx.x & 7, i = blockIdx.x >> 3;
   const int gitems = kPfGroupTiles * nblocks;                  // items of a full group
   const int j = i / gitems, rem = i - j * gitems;
@@ -667,9 +676,23 @@ __device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int*
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-// lane l reads lane l^1's x
+// lane l reads lane l^1's (l^2's) x
 __device__ __forceinline__ float dpp_xor1(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+// In every quad of lanes (4m .. 4m+3), with lane q holding v[j] = M[q][j]:
+// afterwards lane q holds v[j] = M[j][q].  Two exchanges, between lanes q and
+// q^2 then q and q^1, each of the two entries that sit in the other half.
+__device__ __forceinline__ void quad_transpose4(float (&v)[4], int q) {
+  const bool h2 = (q & 2) != 0, h1 = (q & 1) != 0;
+  float r0 = dpp_xor2(h2 ? v[0] : v[2]), r1 = dpp_xor2(h2 ? v[1] : v[3]);
+  if (h2) { v[0] = r0; v[1] = r1; } else { v[2] = r0; v[3] = r1; }
+  r0 = dpp_xor1(h1 ? v[0] : v[1]);
+  r1 = dpp_xor1(h1 ? v[2] : v[3]);
+  if (h1) { v[0] = r0; v[2] = r1; } else { v[1] = r0; v[3] = r1; }
 }
 
 // LDS address of the A-scale group area written by wave w (0..3)
@@ -678,7 +701,11 @@ __device__ __forceinline__ int pf_asg_off(int w) { return (w >> 1) * kPfSlot + k
 template <bool GU, bool AG>
 __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   int tile_idx, nblk;
-  if (!pf_work_item(a, GU ? a.dff / 128 : a.d / 256, &tile_idx, &nblk)) return;
+  // down with a K split: the slices of a column block are further blocks
+  const int kspl = GU || a.ksplit <= 1 ? 1 : a.ksplit;
+  if (!pf_work_item(a, GU ? a.dff / 128 : (a.d / 256) * kspl, &tile_idx, &nblk)) return;
+  const int kslice = nblk % kspl;
+  nblk /= kspl;
   const Tile tile = a.tiles[tile_idx];
   // the tile's expert has no other tile: its weights are read once
   const bool w_once = a.ex_tiles[tile.ex + 1] - a.ex_tiles[tile.ex] == 1;
@@ -687,7 +714,11 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy of the wave index
   const int wm = wu & 1, wn = wu >> 1;
   const int K = GU ? a.d : a.dff;
-  const int nsteps = K / 128;
+  const int nsteps_all = K / 128;
+  // K steps of this item (the whole K, or one slice of it: a multiple of 4
+  // steps, so the grouped activation scales stay aligned)
+  const int nsteps = nsteps_all / kspl;
+  const int k0 = kslice * nsteps;
 
   const bool shared = tile.ex >= a.E;
   const int sidx = tile.ex - a.E;
@@ -736,12 +767,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int rl = 64 * wu + 8 * q + (lane >> 3);
-      a_src[q] = (GU ? a.x_codes : a.h_codes) + src_row(rl) * K + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
+      a_src[q] = (GU ? a.x_codes : a.h_codes) + src_row(rl) * K + 128 * k0 + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
     }
-    as_src = (GU ? a.x_scales : a.h_scales) + src_row(64 * wu + lane) * (K / 32);
+    as_src = (GU ? a.x_scales : a.h_scales) + src_row(64 * wu + lane) * (K / 32) + (AG ? 16 * (k0 / 4) : 4 * k0);
   };
-  const uint8_t* b_src = wc + (grp0 + wu) * nsteps * 4096 + 16 * lane;
-  const uint8_t* bs_src = ws + (grp0 + wu) * nsteps * 256 + 4 * lane;
+  const uint8_t* b_src = wc + (grp0 + wu) * nsteps_all * 4096 + int64_t(k0) * 4096 + 16 * lane;
+  const uint8_t* bs_src = ws + (grp0 + wu) * nsteps_all * 256 + int64_t(k0) * 256 + 4 * lane;
 
   // Copies of step st into slot st % 3 (and of the activation scales of
   // group st / 4 when st starts a group).  Their number per step is fixed --
@@ -1056,6 +1087,29 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
       }
     }
   } else {
+    if (kspl > 1) {
+      // K slice: fp32 partials of this slice, rows in tile order, 16 bytes
+      // per lane after a 4x4 transpose inside each lane quad (lane q of a
+      // quad then holds one row and the quad's four columns)
+      float* const pbase = a.kpart + int64_t(kslice) * a.R * a.d + c0 + 128 * wn + (l32 & ~3);
+      const int q4 = lane & 3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nact) break;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int row = tile.row_begin + wrow0 + 32 * i + 8 * rb + 4 * g32 + q4;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            float v[4] = {acc[i][pp][4 * rb], acc[i][pp][4 * rb + 1], acc[i][pp][4 * rb + 2], acc[i][pp][4 * rb + 3]};
+            quad_transpose4(v, q4);
+            if (row < tile.row_end)
+              *reinterpret_cast<float4*>(pbase + int64_t(row) * a.d + 32 * pp) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+      return;
+    }
     // o rows are stored in (token, slot) order: routed row r goes to its pair
     // index row_src[r] (token-major, so the combine reads a token's rows
     // back to back), shared rows keep their place.  The routed rows'
@@ -1103,7 +1157,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 
 template <bool GU>
 static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
-  const int64_t N = GU ? a.dff / 128 : a.d / 256;
+  const int64_t N = GU ? a.dff / 128 : int64_t(a.d / 256) * (a.ksplit > 1 ? a.ksplit : 1);
   // room for the most groups one XCD can get (the tile count is known on the
   // device only; max_tiles bounds it)
   const int64_t max_groups = (int64_t(a.max_tiles) + kPfGroupTiles - 1) / kPfGroupTiles;

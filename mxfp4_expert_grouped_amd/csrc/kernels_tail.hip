@@ -277,6 +277,19 @@ hipError_t launch_tail(const TailArgs& a, int num_cus, hipStream_t st) {
   f.bm = a.bm;
   f.num_cus = num_cus;
   f.max_tiles = (a.T + a.bm - 1) / a.bm;
+  // few 256-row tiles: K slices into fp32 partials, summed in order with s
+  const int ks = a.bm > kDecodeMaxRows ? tail_ksplit(a.T, a.latent, a.hidden) : 1;
+  if (ks > 1) {
+    f.ksplit = ks;
+    f.kpart = a.part;
+    e = launch_gemm_down(f, st);
+    if (e != hipSuccess) return e;
+    const int64_t n4 = int64_t(a.T) * a.hidden / 4;
+    const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, int64_t(num_cus) * 4);
+    hipLaunchKernelGGL(k_tail_reduce, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a.part, ks,
+                       a.s, a.y, n4);
+    return hipGetLastError();
+  }
   e = launch_gemm_down(f, st);
   if (e != hipSuccess || !a.s) return e;
   const int64_t n8 = int64_t(a.T) * a.hidden / 8;
