@@ -69,7 +69,7 @@ typedef enum {
 
 typedef enum { MOE_SRC_BF16 = 0, MOE_SRC_FP32 = 1 } moe_src_dtype;
 
-/* Layer shape.  d_model: a multiple of 256; d_ff: a multiple of 128.  1 <= num_experts <= 1024.
+/* Layer shape.  d_model and d_ff: multiples of 128.  1 <= num_experts <= 1024.
  * 1 <= top_k <= min(32, num_experts).  0 <= num_shared <= 8.
  * 1 <= max_tokens <= 2^20.  flags: 0 (the layer with MXFP8 activations,
  * "A8W4") or MOE_FLAG_A16W4. */
@@ -216,7 +216,7 @@ moe_status moe_forward_noalloc(const moe_plan_t *plan, const moe_weights *w, con
  *   y      bf16 [T][hidden]
  *   W_up   MXFP4 [hidden][latent], packed by moe_pack_mx4 with interleave 0;
  *          gamma fp32 [latent]; layout must be MOE_WEIGHTS_PACKED.
- * latent: a multiple of 128, hidden: a multiple of 256, both <= 65536;
+ * latent and hidden: multiples of 128, both <= 65536;
  * 0 <= T <= 2^20 (T == 0 enqueues nothing); eps >= 0 and finite.
  * z, s, y, gamma and up_codes 16-byte aligned, up_scales 4 bytes; workspace
  * of moe_latent_tail_workspace_bytes bytes, 256-byte aligned, contents on

@@ -138,8 +138,8 @@ moe_status check_config(const moe_config* c) {
       c->num_shared < 0 || c->max_tokens <= 0)
     return fail(MOE_ERR_INVALID_ARG, "non-positive size in config");
   if (c->flags & ~MOE_FLAG_A16W4) return fail(MOE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
-  if (c->d_model % 256 || c->d_ff % 128)
-    return fail(MOE_ERR_UNSUPPORTED, "d_model (%d) must be a multiple of 256 and d_ff (%d) of 128",
+  if (c->d_model % 128 || c->d_ff % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model (%d) and d_ff (%d) must be multiples of 128",
                 c->d_model, c->d_ff);
   if (c->d_model > 65536 || c->d_ff > 65536)
     return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be <= 65536");
@@ -482,9 +482,9 @@ TailLayout tail_layout(int64_t T, int64_t latent, int64_t hidden, bool with_s) {
 moe_status check_tail_shape(int64_t T, int32_t latent, int32_t hidden) {
   if (T < 0 || T > (int64_t(1) << 20)) return fail(MOE_ERR_INVALID_ARG, "num_tokens outside [0, 2^20]");
   if (latent <= 0 || hidden <= 0) return fail(MOE_ERR_INVALID_ARG, "non-positive width");
-  if (latent % 128 || hidden % 256 || latent > 65536 || hidden > 65536)
+  if (latent % 128 || hidden % 128 || latent > 65536 || hidden > 65536)
     return fail(MOE_ERR_UNSUPPORTED,
-                "latent (%d) must be a multiple of 128 and hidden (%d) of 256, both <= 65536", latent,
+                "latent (%d) and hidden (%d) must be multiples of 128, both <= 65536", latent,
                 hidden);
   if (T * latent >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "num_tokens * latent must be below 2^31");

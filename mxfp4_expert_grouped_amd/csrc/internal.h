@@ -103,7 +103,7 @@ inline int tail_gemv_slices(int latent) {
 // partial of the output, summed in order (with s) by the tail's reduction.
 inline int tail_ksplit(int64_t T, int64_t latent, int64_t hidden) {
   if (T < 24 || latent % 512 != 0) return 1;
-  const int64_t base = ((T + 255) / 256) * (hidden / 256);
+  const int64_t base = ((T + 255) / 256) * ((hidden + 255) / 256);
   const int64_t g = latent / 512;
   int best = 1;
   for (int d = 1; d <= 8 && d <= g; ++d) {

@@ -703,7 +703,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   int tile_idx, nblk;
   // down with a K split: the slices of a column block are further blocks
   const int kspl = GU || a.ksplit <= 1 ? 1 : a.ksplit;
-  if (!pf_work_item(a, GU ? a.dff / 128 : (a.d / 256) * kspl, &tile_idx, &nblk)) return;
+  if (!pf_work_item(a, GU ? a.dff / 128 : ((a.d + 255) / 256) * kspl, &tile_idx, &nblk)) return;
   const int kslice = nblk % kspl;
   nblk /= kspl;
   const Tile tile = a.tiles[tile_idx];
@@ -771,8 +771,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
     }
     as_src = (GU ? a.x_scales : a.h_scales) + src_row(64 * wu + lane) * (K / 32) + (AG ? 16 * (k0 / 4) : 4 * k0);
   };
-  const uint8_t* b_src = wc + (grp0 + wu) * nsteps_all * 4096 + int64_t(k0) * 4096 + 16 * lane;
-  const uint8_t* bs_src = ws + (grp0 + wu) * nsteps_all * 256 + int64_t(k0) * 256 + 4 * lane;
+  // down with d an odd multiple of 128: the last column block has two
+  // groups; the waves of the missing half copy group grp0 instead (the
+  // same number of copies, data never stored) and store nothing
+  const int64_t gw = GU || grp0 + wu < a.d / 64 ? grp0 + wu : grp0;
+  const bool cols_live = GU || c0 + 128 * wn < a.d;
+  const uint8_t* b_src = wc + gw * nsteps_all * 4096 + int64_t(k0) * 4096 + 16 * lane;
+  const uint8_t* bs_src = ws + gw * nsteps_all * 256 + int64_t(k0) * 256 + 4 * lane;
 
   // Copies of step st into slot st % 3 (and of the activation scales of
   // group st / 4 when st starts a group).  Their number per step is fixed --
@@ -1017,7 +1022,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   // and column l32 of weight fragment p.
   PF_WAIT_VM(0);
   __syncthreads();
-  if (nact == 0) return;
+  if (nact == 0 || !cols_live) return;
   if (GU) {
     // h = silu(gate) * up as fp32 [128 rows][64 h columns] (row stride 68)
     float* hs = reinterpret_cast<float*>(pf_lds) + wu * (128 * 68);
@@ -1157,7 +1162,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 
 template <bool GU>
 static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
-  const int64_t N = GU ? a.dff / 128 : int64_t(a.d / 256) * (a.ksplit > 1 ? a.ksplit : 1);
+  const int64_t N = GU ? a.dff / 128 : int64_t((a.d + 255) / 256) * (a.ksplit > 1 ? a.ksplit : 1);
   // room for the most groups one XCD can get (the tile count is known on the
   // device only; max_tiles bounds it)
   const int64_t max_groups = (int64_t(a.max_tiles) + kPfGroupTiles - 1) / kPfGroupTiles;

@@ -56,7 +56,8 @@ def test_status_strings(M):
     (dict(d_model=7168, d_ff=2048, num_experts=896, top_k=16, num_shared=2, max_tokens=32768), 0),
     (dict(d_model=256, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 0),
     (dict(d_model=200, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 2),
-    (dict(d_model=384, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 2),
+    (dict(d_model=384, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 0),
+    (dict(d_model=320, d_ff=128, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 2),
     (dict(d_model=256, d_ff=96, num_experts=16, top_k=2, num_shared=1, max_tokens=8), 2),
     (dict(d_model=256, d_ff=128, num_experts=1025, top_k=2, num_shared=1, max_tokens=8), 2),
     (dict(d_model=256, d_ff=128, num_experts=16, top_k=17, num_shared=1, max_tokens=8), 2),
@@ -256,7 +257,7 @@ def test_latent_tail_host_checks(M):
     ws = M.moe_latent_tail_workspace_bytes(4, 256, 256)
     for args, status in [
         ((4, 200, 256, 1e-6, W, fake, fake, fake, fake, ws), M.MOE_ERR_UNSUPPORTED),   # latent % 128
-        ((4, 256, 128, 1e-6, W, fake, fake, fake, fake, ws), M.MOE_ERR_UNSUPPORTED),   # hidden % 256
+        ((4, 256, 192, 1e-6, W, fake, fake, fake, fake, ws), M.MOE_ERR_UNSUPPORTED),   # hidden % 128
         ((4, 256, 256, -1.0, W, fake, fake, fake, fake, ws), M.MOE_ERR_INVALID_ARG),   # eps < 0
         ((4, 256, 256, float("nan"), W, fake, fake, fake, fake, ws), M.MOE_ERR_INVALID_ARG),
         ((4, 256, 256, 1e-6, M.MoeTailWeights(fake, fake, fake, 0), fake, fake, fake, fake, ws),

@@ -197,6 +197,10 @@ EXACT_CASES = [
     ("prefill_rows64_step_scales", 128, 256, 128, 8, 2, (122, 132)),
     ("prefill_rows64_grouped_scales", 128, 1024, 512, 8, 2, (124, 130)),
     ("prefill_rows256_grouped_scales", 1200, 1024, 512, 8, 2, (124, 130)),
+    # d_model an odd multiple of 128: half of the last output block
+    ("stream_d384", 40, 384, 128, 8, 2, (122, 132)),
+    ("prefill_d384", 300, 384, 128, 8, 2, (122, 132)),
+    ("prefill_d640_grouped", 300, 640, 512, 8, 2, (124, 130)),
 ]
 
 
