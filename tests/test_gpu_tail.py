@@ -64,6 +64,7 @@ def run_tail(z, s, gamma, eps, up_c, up_s, hidden):
     (1, 256, 256, True), (5, 256, 512, True), (13, 384, 256, False),
     (40, 1024, 256, True), (300, 384, 512, True), (300, 512, 768, False),
     (100, 2048, 512, False),  # four K slices, no shared output
+    (300, 2048, 256, True),   # four K slices over a full and a partial tile
     (60, 512, 384, True), (3, 256, 384, True),  # hidden an odd multiple of 128
     (1, 7168, 7168, True), (256, 7168, 7168, True), (8192, 7168, 7168, True),
 ])
