@@ -32,15 +32,18 @@
  *     W_dn  [d_model][d_ff]
  *   each as codes u8 [rows][K/2] (E2M1 pairs, element 2i in the low nibble of
  *   byte i) and scales u8 [rows][K/32] (E8M0), K the reduction width.
- *   moe_forward takes them only in the packed tile order made by
- *   moe_pack_mx4 (below): gu_codes/gu_scales hold E packed W_gu matrices back
- *   to back, dn_codes/dn_scales E packed W_dn matrices, sgu_* / sdn_* the
- *   shared ones.  The caller says so by setting moe_weights.layout to
- *   MOE_WEIGHTS_PACKED; a weight set without that tag (for example a
- *   zero-initialised struct pointing at canonical matrices) is rejected with
- *   MOE_ERR_INVALID_ARG before anything is enqueued.  Packing is a one-time
- *   load-time conversion: the canonical order would cost the decode kernels
- *   strided 2-byte scale loads and the prefill kernels a re-layout per tile.
+ *   moe_forward takes them in that canonical form or in the packed tile
+ *   order made by moe_pack_mx4 (below), and the caller says which in
+ *   moe_weights.layout: MOE_WEIGHTS_CANONICAL or MOE_WEIGHTS_PACKED.  Either
+ *   way gu_codes/gu_scales hold the E W_gu matrices back to back (same sizes
+ *   in both forms), dn_codes/dn_scales the E W_dn matrices, sgu_* / sdn_*
+ *   the shared ones, and the results are bit-identical.  The packed order is
+ *   the fast one: a weight step of a 64-row group is one contiguous 4 KB and
+ *   its scales one dword per lane, where the canonical form makes every
+ *   copy a gather of 64-byte row pieces and 4-byte scale words.  Packing is
+ *   a one-time load-time conversion.  A weight set with any other tag (for
+ *   example a zero-initialised struct) is rejected with MOE_ERR_INVALID_ARG
+ *   before anything is enqueued.
  *
  * Errors: every argument is checked on the host before anything is enqueued;
  * on an error nothing is written and the call returns a non-zero status
@@ -96,7 +99,7 @@ typedef struct {
 typedef struct moe_plan_s moe_plan_t;
 
 /* Layout tags of moe_weights.layout. */
-#define MOE_WEIGHTS_CANONICAL 0u          /* not accepted by moe_forward */
+#define MOE_WEIGHTS_CANONICAL 0x4E4E4143u /* every expert matrix as codes [N][K/2], scales [N][K/32] */
 #define MOE_WEIGHTS_PACKED 0x3450584Du    /* every expert matrix made by moe_pack_mx4 */
 
 typedef struct {
@@ -104,7 +107,7 @@ typedef struct {
   const uint8_t *sgu_codes, *sgu_scales, *sdn_codes, *sdn_scales; /* NULL if num_shared==0 */
   const float *router_w;
   const float *router_b; /* may be NULL */
-  uint32_t layout;       /* MOE_WEIGHTS_PACKED (required) */
+  uint32_t layout;       /* MOE_WEIGHTS_PACKED or MOE_WEIGHTS_CANONICAL */
 } moe_weights;
 
 /* Optional device outputs for inspection; each NULL pointer is skipped.
@@ -214,8 +217,10 @@ moe_status moe_forward_noalloc(const moe_plan_t *plan, const moe_weights *w, con
  *                             width)
  *   s      fp32 [T][hidden]   the shared experts' output, or NULL (zero)
  *   y      bf16 [T][hidden]
- *   W_up   MXFP4 [hidden][latent], packed by moe_pack_mx4 with interleave 0;
- *          gamma fp32 [latent]; layout must be MOE_WEIGHTS_PACKED.
+ *   W_up   MXFP4 [hidden][latent], packed by moe_pack_mx4 with interleave 0
+ *          (layout MOE_WEIGHTS_PACKED); gamma fp32 [latent]; or
+ *          MOE_WEIGHTS_CANONICAL for W_up as codes [hidden][latent/2] and
+ *          scales [hidden][latent/32].
  * latent and hidden: multiples of 128, both <= 65536;
  * 0 <= T <= 2^20 (T == 0 enqueues nothing); eps >= 0 and finite.
  * z, s, y, gamma and up_codes 16-byte aligned, up_scales 4 bytes; workspace
@@ -224,7 +229,7 @@ moe_status moe_forward_noalloc(const moe_plan_t *plan, const moe_weights *w, con
 typedef struct {
   const uint8_t *up_codes, *up_scales;
   const float *gamma;
-  uint32_t layout; /* MOE_WEIGHTS_PACKED */
+  uint32_t layout; /* MOE_WEIGHTS_PACKED or MOE_WEIGHTS_CANONICAL */
 } moe_tail_weights;
 
 /* Optional device outputs (NULL = skip): the fp32 1/sqrt(mean(z^2)+eps) of

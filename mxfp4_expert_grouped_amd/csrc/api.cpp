@@ -294,11 +294,11 @@ moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void
                 static_cast<long long>(num_tokens), static_cast<long long>(c.max_tokens));
   if (num_tokens == 0) return MOE_OK;
   if (!w || !x_bf16 || !y_bf16) return fail(MOE_ERR_INVALID_ARG, "weights, x or y is NULL");
-  if (w->layout != MOE_WEIGHTS_PACKED)
+  if (w->layout != MOE_WEIGHTS_PACKED && w->layout != MOE_WEIGHTS_CANONICAL)
     return fail(MOE_ERR_INVALID_ARG,
-                "weights.layout is 0x%x: moe_forward reads only expert matrices packed by "
-                "moe_pack_mx4, tagged MOE_WEIGHTS_PACKED (0x%x)",
-                w->layout, MOE_WEIGHTS_PACKED);
+                "weights.layout is 0x%x: expected MOE_WEIGHTS_PACKED (0x%x, matrices made by "
+                "moe_pack_mx4) or MOE_WEIGHTS_CANONICAL (0x%x)",
+                w->layout, MOE_WEIGHTS_PACKED, MOE_WEIGHTS_CANONICAL);
   if (!w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales || !w->router_w)
     return fail(MOE_ERR_INVALID_ARG, "routed-expert or router weight pointer is NULL");
   if (c.num_shared > 0 && (!w->sgu_codes || !w->sgu_scales || !w->sdn_codes || !w->sdn_scales))
@@ -390,6 +390,7 @@ moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void
   a.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
   a.ex_tiles = reinterpret_cast<int32_t*>(ws + L.ex_tiles);
   a.a16 = a16 ? 1 : 0;
+  a.wcanon = w->layout == MOE_WEIGHTS_CANONICAL ? 1 : 0;
   if (a16) {
     a.h16 = pick(tp.h_bf16, L.h_codes, static_cast<uint16_t*>(nullptr));
   } else {
@@ -514,10 +515,9 @@ moe_status moe_latent_tail(int64_t num_tokens, int32_t latent, int32_t hidden, f
   if (!(eps >= 0.0f) || eps > 3.4e38f) return fail(MOE_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (num_tokens == 0) return MOE_OK;
   if (!w || !z || !y_bf16) return fail(MOE_ERR_INVALID_ARG, "weights, z or y is NULL");
-  if (w->layout != MOE_WEIGHTS_PACKED)
+  if (w->layout != MOE_WEIGHTS_PACKED && w->layout != MOE_WEIGHTS_CANONICAL)
     return fail(MOE_ERR_INVALID_ARG,
-                "tail weights.layout is 0x%x: W_up must be packed by moe_pack_mx4 and tagged "
-                "MOE_WEIGHTS_PACKED",
+                "tail weights.layout is 0x%x: expected MOE_WEIGHTS_PACKED or MOE_WEIGHTS_CANONICAL",
                 w->layout);
   if (!w->up_codes || !w->up_scales || !w->gamma) return fail(MOE_ERR_INVALID_ARG, "tail weight pointer is NULL");
   if (!aligned(z, 16) || (s && !aligned(s, 16)) || !aligned(y_bf16, 16) || !aligned(w->gamma, 16) ||
@@ -547,6 +547,7 @@ moe_status moe_latent_tail(int64_t num_tokens, int32_t latent, int32_t hidden, f
   a.gamma = w->gamma;
   a.s = s;
   a.up_c = w->up_codes;
+  a.wcanon = w->layout == MOE_WEIGHTS_CANONICAL ? 1 : 0;
   a.up_s = w->up_scales;
   a.y = static_cast<uint16_t*>(y_bf16);
   a.codes = (taps && taps->a_codes) ? taps->a_codes : reinterpret_cast<uint8_t*>(ws + L.codes);

@@ -64,6 +64,9 @@ struct FwdArgs {
   // kpart[slice][R][d] in row order instead of bf16 o rows
   int ksplit;
   float* kpart;
+  // 1: expert weights in the canonical layout ([N][K/2] codes, [N][K/32]
+  // scales) instead of the packed one
+  int wcanon;
 };
 
 // Everything the kernels of one LatentMoE tail call need (device pointers).
@@ -73,7 +76,8 @@ struct TailArgs {
   const float* z;        // [T][latent] routed experts' weighted sum
   const float* gamma;    // [latent]
   const float* s;        // [T][hidden] shared experts' output, or null
-  const uint8_t *up_c, *up_s;  // packed MXFP4 W_up [hidden][latent]
+  const uint8_t *up_c, *up_s;  // MXFP4 W_up [hidden][latent], packed or canonical
+  int wcanon;                  // 1: canonical layout
   uint16_t* y;           // bf16 [T][hidden]
   uint8_t* codes;        // [T][latent] MXFP8 of the normalised rows
   uint8_t* scales;       // [T][latent/32]

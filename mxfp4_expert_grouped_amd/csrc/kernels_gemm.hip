@@ -167,7 +167,16 @@ __device__ __forceinline__ int sload1(const void* p) {
 // routing, only x, which the router launch has quantised), so the GPU
 // streams the shared experts' weights while one workgroup routes; PH = 2 is
 // then the routed experts' items alone.  PH = 0: every item of the tile list.
-template <bool GU, bool KSPLIT, bool WIDE, bool A16 = false, int PH = 0>
+// Canonical (unpacked) weights [N][K/2] codes, [N][K/32] scales: the row
+// offset of 16-row block jb of a packed group from the group's first row --
+// gate_up groups pair the gate rows 32G .. 32G+31 with the up rows of the
+// same h columns (d_ff further), down groups are 64 consecutive rows.
+template <bool GU>
+__device__ __forceinline__ int canon_row_off(int jb, int dff) {
+  return GU ? (jb >> 1) * dff + 16 * (jb & 1) : 16 * jb;
+}
+
+template <bool GU, bool KSPLIT, bool WIDE, bool A16 = false, int PH = 0, bool CANON = false>
 __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   static_assert(PH == 0 || (GU && !WIDE), "the phases split the gate_up GEMM");
   if constexpr (PH == 1) {
@@ -267,8 +276,18 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
                            : (shared ? a.sdn_c + sidx * wc_stride : a.dn_c + ex * wc_stride);
     const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + ex * ws_stride)
                            : (shared ? a.sdn_s + sidx * ws_stride : a.dn_s + ex * ws_stride);
-    w_src = wc + int64_t(G) * GPI * ns * 4096 + 16 * lane;
-    bs_src = ws + int64_t(G) * GPI * ns * 256 + 4 * lane;
+    if constexpr (CANON) {
+      // canonical weights: lane 16g + r of a block's copy reads the 16 bytes
+      // of its row that the packed order would hold (row r of the block, K
+      // bytes 64 st + 16g ..), and lane 16jb + r of the scale copy the
+      // dword of blocks 4st .. 4st+3 of row r of block jb
+      const int64_t row0 = GU ? 32 * int64_t(G) : 64 * int64_t(G) * GPI;
+      w_src = wc + (row0 + r16) * (K / 2) + 16 * g;
+      bs_src = ws + (row0 + canon_row_off<GU>(lane >> 4, a.dff) + r16) * (K / 32);
+    } else {
+      w_src = wc + int64_t(G) * GPI * ns * 4096 + 16 * lane;
+      bs_src = ws + int64_t(G) * GPI * ns * 256 + 4 * lane;
+    }
     if (!new_tile) return;
     // activation row of tile row r (rows past the end repeat the first); a
     // routed gate_up tile reads its eight row-token entries with one scalar
@@ -311,7 +330,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     for (int g2 = 0; g2 < GPI; ++g2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint8_t* src = w_src + int64_t(g2) * ns * 4096 + st * 4096 + j * 1024;
+        const uint8_t* src = CANON ? w_src + (int64_t(g2) * 64 + canon_row_off<GU>(j, a.dff)) * (K / 2) + st * 64
+                                   : w_src + int64_t(g2) * ns * 4096 + st * 4096 + j * 1024;
         if (WIDE) lds_copy16(src, slot + SW + g2 * 4096 + j * 1024);
         else lds_copy16_nt(src, slot + SW + g2 * 4096 + j * 1024);
       }
@@ -328,8 +348,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     }
 #pragma unroll
     for (int g2 = 0; g2 < GPI; ++g2) {
-      if (WIDE) lds_copy4(bs_src + int64_t(g2) * ns * 256 + st * 256, slot + SBS + g2 * 256);
-      else lds_copy4_nt(bs_src + int64_t(g2) * ns * 256 + st * 256, slot + SBS + g2 * 256);
+      const uint8_t* src = CANON ? bs_src + int64_t(g2) * 64 * (K / 32) + st * 4 : bs_src + int64_t(g2) * ns * 256 + st * 256;
+      if (WIDE) lds_copy4(src, slot + SBS + g2 * 256);
+      else lds_copy4_nt(src, slot + SBS + g2 * 256);
     }
   };
 
@@ -359,7 +380,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     for (int j = 0; j < 4; ++j) {
       const uint4 wv = ld16(sl + SW + j * 1024 + 16 * lane);
       wd[j][0] = wv.x; wd[j][1] = wv.y; wd[j][2] = wv.z; wd[j][3] = wv.w;
-      const uint32_t sb = (sbw >> (8 * j)) & 0xFFu;
+      // scale of block j of this lane's row, K block 4st + g: byte j of the
+      // packed dword, or byte g of the row's dword (canonical)
+      const uint32_t sb = CANON ? (*reinterpret_cast<const uint32_t*>(sl + SBS + 4 * (16 * j + r16)) >> (8 * g)) & 0xFFu
+                                : (sbw >> (8 * j)) & 0xFFu;
       scl[j] = __uint_as_float(sb ? sb << 23 : 0x00400000u);  // 2^(sb-127)
     }
     // K chunk outer, block inner: consecutive MFMAs use different accumulators
@@ -389,7 +413,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const v8i bv = make_b(ld16(sl + SW + g2 * 4096 + j * 1024 + 16 * lane));
-        acc[4 * g2 + j] = mfma_mx(av, bv, acc[4 * g2 + j], sa, sbw >> (8 * j));
+        const uint32_t sb = CANON ? *reinterpret_cast<const uint32_t*>(sl + SBS + g2 * 256 + 4 * (16 * j + r16)) >> (8 * g)
+                                  : sbw >> (8 * j);
+        acc[4 * g2 + j] = mfma_mx(av, bv, acc[4 * g2 + j], sa, sb);
       }
     }
   };
@@ -517,8 +543,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   }
 }
 
-template <bool GU>
-static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
+template <bool GU, bool C>
+static hipError_t launch_stream_w(const FwdArgs& a, hipStream_t st) {
   // the item count is known on the device only; max_tiles bounds it
   const int64_t max_items = int64_t(a.max_tiles) * (GU ? a.dff / 32 : a.d / 64);
   // persistent: one workgroup per CU, a multiple of 8 (one share per XCD)
@@ -532,33 +558,38 @@ static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
   const bool routed_only = GU && stream_split_phases(a);
   if (a.a16) {
     if (!GU)
-      hipLaunchKernelGGL((k_gemm_stream<false, false, false, true>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_stream<false, false, false, true, 0, C>), dim3(grid), dim3(256), 0, st, a);
     else if (routed_only && few)
-      hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 2>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 2, C>), dim3(grid), dim3(256), 0, st, a);
     else if (routed_only)
-      hipLaunchKernelGGL((k_gemm_stream<true, false, false, true, 2>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_stream<true, false, false, true, 2, C>), dim3(grid), dim3(256), 0, st, a);
     else if (few)
-      hipLaunchKernelGGL((k_gemm_stream<true, true, false, true>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 0, C>), dim3(grid), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((k_gemm_stream<true, false, false, true>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_stream<true, false, false, true, 0, C>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   if (routed_only) {
     if (few)
-      hipLaunchKernelGGL((k_gemm_stream<true, true, false, false, 2>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_stream<true, true, false, false, 2, C>), dim3(grid), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((k_gemm_stream<true, false, false, false, 2>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_stream<true, false, false, false, 2, C>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   if (!GU && !few)
-    hipLaunchKernelGGL((k_gemm_stream<false, false, true>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_stream<false, false, true, false, 0, C>), dim3(grid), dim3(256), 0, st, a);
   else if (!GU)
-    hipLaunchKernelGGL((k_gemm_stream<false, false, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_stream<false, false, false, false, 0, C>), dim3(grid), dim3(256), 0, st, a);
   else if (few)
-    hipLaunchKernelGGL((k_gemm_stream<true, true, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_stream<true, true, false, false, 0, C>), dim3(grid), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_stream<true, false, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_stream<true, false, false, false, 0, C>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <bool GU>
+static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
+  return a.wcanon ? launch_stream_w<GU, true>(a, st) : launch_stream_w<GU, false>(a, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -698,7 +729,7 @@ __device__ __forceinline__ void quad_transpose4(float (&v)[4], int q) {
 // LDS address of the A-scale group area written by wave w (0..3)
 __device__ __forceinline__ int pf_asg_off(int w) { return (w >> 1) * kPfSlot + kPfAS + (w & 1) * 1024; }
 
-template <bool GU, bool AG>
+template <bool GU, bool AG, bool CANON>
 __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   int tile_idx, nblk;
   // down with a K split: the slices of a column block are further blocks
@@ -776,8 +807,17 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
   // same number of copies, data never stored) and store nothing
   const int64_t gw = GU || grp0 + wu < a.d / 64 ? grp0 + wu : grp0;
   const bool cols_live = GU || c0 + 128 * wn < a.d;
-  const uint8_t* b_src = wc + gw * nsteps_all * 4096 + int64_t(k0) * 4096 + 16 * lane;
-  const uint8_t* bs_src = ws + gw * nsteps_all * 256 + int64_t(k0) * 256 + 4 * lane;
+  // canonical weights: the same LDS image as the packed order for the codes
+  // (lane 16g + r of block m's copy reads row r of the block, K bytes
+  // 64 st + 16g ..), and per row a dword of four block scales (lane 16jb + r
+  // of the scale copy: row r of block jb, blocks 4st .. 4st+3)
+  const int64_t crow0 = GU ? 32 * gw : 64 * gw;
+  const uint8_t* b_src = CANON ? wc + (crow0 + (lane & 15)) * (K / 2) + 16 * (lane >> 4) + int64_t(k0) * 64
+                               : wc + gw * nsteps_all * 4096 + int64_t(k0) * 4096 + 16 * lane;
+  const uint8_t* bs_src = CANON ? ws + (crow0 + canon_row_off<GU>(lane >> 4, a.dff) + (lane & 15)) * (K / 32) + int64_t(k0) * 4
+                                : ws + gw * nsteps_all * 256 + int64_t(k0) * 256 + 4 * lane;
+  // per-step strides of the two
+  constexpr int kBStep = CANON ? 64 : 4096, kBSStep = CANON ? 4 : 256;
 
   // Copies of step st into slot st % 3 (and of the activation scales of
   // group st / 4 when st starts a group).  Their number per step is fixed --
@@ -802,10 +842,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
     constexpr bool GS = decltype(gsc)::value != 0;
     const int ss = st < nsteps ? st : 0;
     const uint32_t slot = lds0 + (st % 3) * kPfSlot;
-    if constexpr (m < 4 && WNT) lds_copy16_nt(b_src + ss * 4096 + m * 1024, slot + kPfB + (4 * wu + m) * 1024);
-    if constexpr (m < 4 && !WNT) lds_copy16(b_src + ss * 4096 + m * 1024, slot + kPfB + (4 * wu + m) * 1024);
-    if constexpr (m == 4 && WNT) lds_copy4_nt(bs_src + ss * 256, slot + kPfBS + wu * 256);
-    if constexpr (m == 4 && !WNT) lds_copy4(bs_src + ss * 256, slot + kPfBS + wu * 256);
+    constexpr int64_t kBlk = 1024;   // packed: block m of the group's step is 1 KB further
+    const uint8_t* bsrc = CANON ? b_src + ss * kBStep + int64_t(canon_row_off<GU>(m < 4 ? m : 0, a.dff)) * (K / 2)
+                                : b_src + ss * kBStep + m * kBlk;
+    if constexpr (m < 4 && WNT) lds_copy16_nt(bsrc, slot + kPfB + (4 * wu + m) * 1024);
+    if constexpr (m < 4 && !WNT) lds_copy16(bsrc, slot + kPfB + (4 * wu + m) * 1024);
+    if constexpr (m == 4 && WNT) lds_copy4_nt(bs_src + ss * kBSStep, slot + kPfBS + wu * 256);
+    if constexpr (m == 4 && !WNT) lds_copy4(bs_src + ss * kBSStep, slot + kPfBS + wu * 256);
     if constexpr (m == 5 && !AG) lds_copy4(as_src + 4 * ss, slot + kPfAS + wu * 256);
     if constexpr (m == 5 && AG && GS) lds_copy16(as_src + 16 * (ss >> 2), lds0 + pf_asg_off(wu));
   };
@@ -865,11 +908,22 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
       constexpr int I = decltype(ic)::value;
       if (NACT == 0) return;
       const uint8_t* sb = pf_lds + (st % 3) * kPfSlot;
+      if constexpr (CANON) {
+        // fragment P = 2a + b in bs_raw[a][b]: the dword of its row l32
+        // (block SB(P) + l32/16 of group 2wn + GI(P)); both K halves in it
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
+        for (int P = 0; P < 4; ++P) {
+          const int gi = GU ? (P & 1) : (P >> 1), sbk = GU ? (P >= 2 ? 2 : 0) : ((P & 1) ? 2 : 0);
+          bs_raw[P >> 1][P & 1] =
+              *reinterpret_cast<const uint32_t*>(sb + kPfBS + (2 * wn + gi) * 256 + 4 * (16 * sbk + l32));
+        }
+      } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          bs_raw[gi][h] = *reinterpret_cast<const uint32_t*>(sb + kPfBS + gi * 256 + 128 * h + bs_lane);
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            bs_raw[gi][h] = *reinterpret_cast<const uint32_t*>(sb + kPfBS + gi * 256 + 128 * h + bs_lane);
+      }
       if (AG) {
         if (I == 0) {
 #pragma unroll
@@ -888,7 +942,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) bsd[B][gi][h] = bs_raw[gi][h] >> (8 * (l32 >> 4));
+        for (int h = 0; h < 2; ++h) bsd[B][gi][h] = bs_raw[gi][h] >> (CANON ? 8 * g32 : 8 * (l32 >> 4));
 #pragma unroll
       for (int i = 0; i < NACT; ++i) {
         const uint32_t v = AG ? (I == 0 ? asg[i].x : I == 1 ? asg[i].y : I == 2 ? asg[i].z : asg[i].w) : as_raw[i];
@@ -902,8 +956,14 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
       constexpr int I_ = Kk >> 2, P = Kk & 3;
       constexpr int GI = GU ? (P & 1) : (P >> 1);
       constexpr int SB = GU ? (P >= 2 ? 2 : 0) : ((P & 1) ? 2 : 0);
-      if (I_ < NACT)
-        acc[I_][P] = mfma32_mx<2 * H, SB>(av[H][I_], bv[H][P], acc[I_][P], asr[B][I_], bsd[B][GI][H]);
+      // canonical: byte 2H + g32 of the row's dword (shifted by 8 g32 already)
+      if constexpr (CANON) {
+        if (I_ < NACT)
+          acc[I_][P] = mfma32_mx<2 * H, 2 * H>(av[H][I_], bv[H][P], acc[I_][P], asr[B][I_], bsd[B][P >> 1][P & 1]);
+      } else {
+        if (I_ < NACT)
+          acc[I_][P] = mfma32_mx<2 * H, SB>(av[H][I_], bv[H][P], acc[I_][P], asr[B][I_], bsd[B][GI][H]);
+      }
     };
 
     // step st: the memory work of the step sits between its MFMAs in a fixed
@@ -1169,10 +1229,14 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
   const int64_t per_xcd = (max_groups + 7) / 8 * kPfGroupTiles * N;
   const int K = GU ? a.d : a.dff;
   const dim3 grid(static_cast<unsigned>(8 * per_xcd));
-  if (K % 512 == 0)
-    hipLaunchKernelGGL((k_gemm_pf<GU, true>), grid, dim3(256), 0, st, a);
+  if (K % 512 == 0 && a.wcanon)
+    hipLaunchKernelGGL((k_gemm_pf<GU, true, true>), grid, dim3(256), 0, st, a);
+  else if (K % 512 == 0)
+    hipLaunchKernelGGL((k_gemm_pf<GU, true, false>), grid, dim3(256), 0, st, a);
+  else if (a.wcanon)
+    hipLaunchKernelGGL((k_gemm_pf<GU, false, true>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm_pf<GU, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_pf<GU, false, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1181,8 +1245,12 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
 // the shared experts' gate_up items in the others (PH = 1).
 hipError_t launch_topk_shared_gate_up(const FwdArgs& a, hipStream_t st) {
   const unsigned grid = 8u * static_cast<unsigned>(a.num_cus >= 16 ? a.num_cus / 8 : 1);
-  if (a.a16)
+  if (a.a16 && a.wcanon)
+    hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 1, true>), dim3(grid), dim3(256), 0, st, a);
+  else if (a.a16)
     hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 1>), dim3(grid), dim3(256), 0, st, a);
+  else if (a.wcanon)
+    hipLaunchKernelGGL((k_gemm_stream<true, true, false, false, 1, true>), dim3(grid), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((k_gemm_stream<true, true, false, false, 1>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();

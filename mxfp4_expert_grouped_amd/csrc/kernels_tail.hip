@@ -158,6 +158,7 @@ __device__ __forceinline__ v4f_t tail_mfma(const v8i_t& av, const v8i_t& bv, v4f
                                                           static_cast<int>(sb));
 }
 
+template <bool CANON>
 __global__ void __launch_bounds__(256) k_tail_gemv(TailArgs a, float* __restrict__ part, int ks_n) {
   __shared__ v4f_t red[4][4][64];
   const int G = blockIdx.x, ks = blockIdx.y;
@@ -167,23 +168,35 @@ __global__ void __launch_bounds__(256) k_tail_gemv(TailArgs a, float* __restrict
   const int K = a.latent, ns = K / 128;
   const int spk = (ns + ks_n - 1) / ks_n;
   const int s0 = ks * spk, s1 = min(ns, s0 + spk);
-  const uint8_t* wc = a.up_c + int64_t(G) * ns * 4096 + 16 * lane;
-  const uint8_t* wsc = a.up_s + int64_t(G) * ns * 256 + 4 * lane;
+  // packed: the group's step is 4 KB in lane order, its scales a dword per
+  // lane; canonical: lane (g, r) of block j reads row 64G + 16j + r at K
+  // bytes 64 st + 16g, and byte g of the dword of that row's blocks
+  // 4st .. 4st+3
+  const uint8_t* wc = CANON ? a.up_c + (int64_t(G) * 64 + r16) * (K / 2) + 16 * g
+                            : a.up_c + int64_t(G) * ns * 4096 + 16 * lane;
+  const uint8_t* wsc = CANON ? a.up_s + (int64_t(G) * 64 + r16) * (K / 32) : a.up_s + int64_t(G) * ns * 256 + 4 * lane;
   const int row = min(r16, a.T - 1);
   const uint8_t* ac = a.codes + int64_t(row) * K;
   const uint8_t* asc = a.scales + int64_t(row) * (K / 32);
   uint4 wv[kTailGemvSteps][4], a0[kTailGemvSteps], a1[kTailGemvSteps];
-  uint32_t sbw[kTailGemvSteps], sa[kTailGemvSteps];
+  uint32_t sbw[kTailGemvSteps][CANON ? 4 : 1], sa[kTailGemvSteps];
 #pragma unroll
   for (int i = 0; i < kTailGemvSteps; ++i) {
     const int st = s0 + w + 4 * i;
     const int sst = st < s1 ? st : min(s0, ns - 1);  // past the range: a valid step, its values unused
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const v4u_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt_t*>(wc + int64_t(sst) * 4096 + j * 1024));
+      const uint8_t* src = CANON ? wc + int64_t(16 * j) * (K / 2) + int64_t(sst) * 64 : wc + int64_t(sst) * 4096 + j * 1024;
+      const v4u_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_nt_t*>(src));
       wv[i][j] = make_uint4(v.x, v.y, v.z, v.w);
     }
-    sbw[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wsc + int64_t(sst) * 256));
+    if constexpr (CANON) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sbw[i][j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wsc + int64_t(16 * j) * (K / 32) + int64_t(sst) * 4));
+    } else {
+      sbw[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wsc + int64_t(sst) * 256));
+    }
     a0[i] = *reinterpret_cast<const uint4*>(ac + sst * 128 + 16 * g);
     a1[i] = *reinterpret_cast<const uint4*>(ac + sst * 128 + 64 + 16 * g);
     sa[i] = *reinterpret_cast<const uint32_t*>(asc + 4 * sst);
@@ -202,7 +215,7 @@ __global__ void __launch_bounds__(256) k_tail_gemv(TailArgs a, float* __restrict
         v8i_t bv;
         bv[0] = wv[i][j].x; bv[1] = wv[i][j].y; bv[2] = wv[i][j].z; bv[3] = wv[i][j].w;
         bv[4] = 0; bv[5] = 0; bv[6] = 0; bv[7] = 0;
-        acc[j] = tail_mfma(av, bv, acc[j], sa[i] >> (8 * g), sbw[i] >> (8 * j));
+        acc[j] = tail_mfma(av, bv, acc[j], sa[i] >> (8 * g), CANON ? sbw[i][CANON ? j : 0] >> (8 * g) : sbw[i][0] >> (8 * j));
       }
     }
   }
@@ -246,7 +259,10 @@ hipError_t launch_tail(const TailArgs& a, int num_cus, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (a.T <= kTailGemvMaxT) {
     const int ks_n = tail_gemv_slices(a.latent);
-    hipLaunchKernelGGL(k_tail_gemv, dim3(a.hidden / 64, ks_n), dim3(256), 0, st, a, a.part, ks_n);
+    if (a.wcanon)
+      hipLaunchKernelGGL(k_tail_gemv<true>, dim3(a.hidden / 64, ks_n), dim3(256), 0, st, a, a.part, ks_n);
+    else
+      hipLaunchKernelGGL(k_tail_gemv<false>, dim3(a.hidden / 64, ks_n), dim3(256), 0, st, a, a.part, ks_n);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n4 = int64_t(a.T) * a.hidden / 4;
@@ -275,6 +291,7 @@ hipError_t launch_tail(const TailArgs& a, int num_cus, hipStream_t st) {
   f.tile_count = a.tile_count;
   f.ex_tiles = a.ex_tiles;
   f.bm = a.bm;
+  f.wcanon = a.wcanon;
   f.num_cus = num_cus;
   f.max_tiles = (a.T + a.bm - 1) / a.bm;
   // few 256-row tiles: K slices into fp32 partials, summed in order with s

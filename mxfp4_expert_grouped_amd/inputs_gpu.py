@@ -115,6 +115,19 @@ def device_weights(cfg: I.LayerConfig, layer: int = 0, device="cuda") -> DeviceW
     return DeviceWeights(guc, gus, dnc, dns, sguc, sgus, sdnc, sdns, wr, br)
 
 
+def device_weights_canonical(cfg: I.LayerConfig, layer: int = 0, device="cuda") -> DeviceWeights:
+    """The same weights as device_weights, expert matrices in canonical form."""
+    guc, gus, dnc, dns = gen_experts_device(cfg, "routed", cfg.num_experts, layer, device)
+    if cfg.num_shared:
+        sguc, sgus, sdnc, sdns = gen_experts_device(cfg, "shared", cfg.num_shared, layer, device)
+    else:
+        sguc = sgus = sdnc = sdns = None
+    wr = torch.from_numpy(I.gen_router_w(cfg, layer)).to(device)
+    b = I.gen_router_b(cfg)
+    br = torch.from_numpy(b).to(device) if b is not None else None
+    return DeviceWeights(guc, gus, dnc, dns, sguc, sgus, sdnc, sdns, wr, br, M.MOE_WEIGHTS_CANONICAL)
+
+
 def device_x(cfg: I.LayerConfig, tokens: Optional[int] = None, layer: int = 0,
              device="cuda") -> torch.Tensor:
     return bf16_tensor(I.gen_x(cfg, tokens, layer), device)

@@ -13,8 +13,9 @@ from . import mxmoe as M
 
 @dataclass
 class DeviceWeights:
-    """MXFP4 expert weights (packed tile order, one flat row per expert) and
-    router parameters resident on one GPU."""
+    """MXFP4 expert weights (packed tile order, one flat row per expert, or
+    canonical [E, N, K/2] codes and [E, N, K/32] scales, as ``layout`` says)
+    and router parameters resident on one GPU."""
     gu_codes: torch.Tensor    # uint8 [E, d_ff*d]
     gu_scales: torch.Tensor   # uint8 [E, moe_packed_scale_bytes(2 d_ff, d)]
     dn_codes: torch.Tensor    # uint8 [E, d*d_ff/2]
@@ -25,13 +26,14 @@ class DeviceWeights:
     sdn_scales: Optional[torch.Tensor]
     router_w: torch.Tensor    # float32 [E, d]
     router_b: Optional[torch.Tensor]
+    layout: int = M.MOE_WEIGHTS_PACKED
 
     def abi(self) -> M.MoeWeights:
         p = lambda t: (t.data_ptr() if t is not None else None)
         return M.MoeWeights(p(self.gu_codes), p(self.gu_scales), p(self.dn_codes),
                             p(self.dn_scales), p(self.sgu_codes), p(self.sgu_scales),
                             p(self.sdn_codes), p(self.sdn_scales), p(self.router_w),
-                            p(self.router_b), M.MOE_WEIGHTS_PACKED)
+                            p(self.router_b), self.layout)
 
 
 class MoeLayer:

@@ -38,13 +38,14 @@ class MoeConfig(ctypes.Structure):
                 ("flags", c_uint32)]
 
 
-MOE_WEIGHTS_CANONICAL = 0
+MOE_WEIGHTS_CANONICAL = 0x4E4E4143
 MOE_WEIGHTS_PACKED = 0x3450584D
 
 
 class MoeWeights(ctypes.Structure):
-    """Device pointers of the layer's weights.  ``layout`` must be
-    MOE_WEIGHTS_PACKED (expert matrices made by moe_pack_mx4)."""
+    """Device pointers of the layer's weights.  ``layout``:
+    MOE_WEIGHTS_PACKED (expert matrices made by moe_pack_mx4) or
+    MOE_WEIGHTS_CANONICAL (codes [N][K/2], scales [N][K/32])."""
     _fields_ = [(n, c_void_p) for n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales",
                                          "sgu_codes", "sgu_scales", "sdn_codes", "sdn_scales",
                                          "router_w", "router_b")] + [("layout", c_uint32)]
@@ -61,8 +62,8 @@ class MoeTaps(ctypes.Structure):
 
 
 class MoeTailWeights(ctypes.Structure):
-    """W_up (packed MXFP4, interleave 0) and the RMSNorm gain; ``layout``
-    must be MOE_WEIGHTS_PACKED."""
+    """W_up (MXFP4, packed with interleave 0 or canonical, as ``layout``
+    says) and the RMSNorm gain."""
     _fields_ = [("up_codes", c_void_p), ("up_scales", c_void_p), ("gamma", c_void_p),
                 ("layout", c_uint32)]
 

@@ -132,21 +132,21 @@ def test_forward_argument_errors_before_any_device_call(M):
         M.moe_plan_destroy(p)
 
 
-def test_forward_rejects_weights_not_tagged_packed(M):
-    # moe_forward reads only packed expert matrices: a weight set without the
-    # MOE_WEIGHTS_PACKED tag (canonical matrices, or a zero-initialised
-    # struct) fails before anything is enqueued, whatever else is valid
+def test_forward_rejects_untagged_weights(M):
+    # moe_forward reads packed or canonical expert matrices as the layout tag
+    # says: any other tag (a zero-initialised struct among them) fails
+    # before anything is enqueued, whatever else is valid
     p = M.moe_plan(256, 128, 16, 2, 1, 8)
     fake = 1 << 20
     ws = M.moe_workspace_bytes(p, 8)
     try:
-        for tag in (M.MOE_WEIGHTS_CANONICAL, M.MOE_WEIGHTS_PACKED + 1, 1):
+        for tag in (0, M.MOE_WEIGHTS_PACKED + 1, M.MOE_WEIGHTS_CANONICAL + 1, 1):
             W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, tag)
             with pytest.raises(M.MoeError) as ei:
                 M.moe_forward(p, W, fake, 8, fake, fake, ws)
             assert ei.value.status == M.MOE_ERR_INVALID_ARG
             assert "MOE_WEIGHTS_PACKED" in ei.value.detail
-        # the default of the binding's struct is the canonical (rejected) tag
+        # the default of the binding's struct (zero) is no tag
         W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None)
         with pytest.raises(M.MoeError) as ei:
             M.moe_forward(p, W, fake, 8, fake, fake, ws)

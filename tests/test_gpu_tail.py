@@ -38,10 +38,13 @@ def _pack(codes, scales, rows, k):
     return cp, sp
 
 
-def run_tail(z, s, gamma, eps, up_c, up_s, hidden):
+def run_tail(z, s, gamma, eps, up_c, up_s, hidden, canonical=False):
     from mxfp4_expert_grouped_amd import mxmoe as M
     T, l = z.shape
-    cp, sp = _pack(up_c, up_s, hidden, l)
+    if canonical:
+        cp, sp = torch.from_numpy(up_c).cuda(), torch.from_numpy(up_s).cuda()
+    else:
+        cp, sp = _pack(up_c, up_s, hidden, l)
     g = torch.from_numpy(gamma).cuda()
     zt = torch.from_numpy(np.ascontiguousarray(z)).cuda()
     st = torch.from_numpy(np.ascontiguousarray(s)).cuda() if s is not None else None
@@ -52,7 +55,8 @@ def run_tail(z, s, gamma, eps, up_c, up_s, hidden):
     nb = M.moe_latent_tail_workspace_bytes(T, l, hidden)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
     ws.fill_(0xA5)
-    W = M.MoeTailWeights(cp.data_ptr(), sp.data_ptr(), g.data_ptr(), M.MOE_WEIGHTS_PACKED)
+    W = M.MoeTailWeights(cp.data_ptr(), sp.data_ptr(), g.data_ptr(),
+                         M.MOE_WEIGHTS_CANONICAL if canonical else M.MOE_WEIGHTS_PACKED)
     taps = M.MoeTailTaps(inv.data_ptr(), codes.data_ptr(), scales.data_ptr())
     M.moe_latent_tail(T, l, hidden, eps, W, zt.data_ptr(), st.data_ptr() if st is not None else None,
                       y.data_ptr(), ws.data_ptr(), nb, taps, torch.cuda.current_stream().cuda_stream)
