@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the forward as a HIP graph")
     ap.add_argument("--breakdown", action="store_true", help="also time every stage (untimed pass)")
+    ap.add_argument("--canonical", action="store_true",
+                    help="expert weights in the canonical layout instead of the packed one")
     ap.add_argument("--a16w4", action="store_true",
                     help="the A16W4 variant (bf16 activations; decode workloads only)")
     ap.add_argument("--tail", action="store_true",
@@ -90,7 +92,7 @@ def main():
     t0 = time.time()
     layers, xs = [], []
     for li in range(nlayers):
-        W = IG.device_weights(cfg, layer=li)
+        W = (IG.device_weights_canonical if args.canonical else IG.device_weights)(cfg, layer=li)
         layers.append(MoeLayer(cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k, cfg.num_shared, T, W,
                                flags=flags))
         xs.append([IG.device_x(cfg, layer=1000 * li + bi) for bi in range(nbatch)])
@@ -287,7 +289,8 @@ def main():
                                + (", Zipf(1.1) router bias" if cfg.zipf_bias else ""),
                    "tokens_per_step": T, "weight_copies_rotated": nlayers,
                    "token_batches": nbatch, "hip_graph": bool(args.graph),
-                   "variant": "A16W4" if args.a16w4 else "A8W4"},
+                   "variant": "A16W4" if args.a16w4 else "A8W4",
+                   "weights": "canonical" if args.canonical else "packed"},
         "layer_hbm_gbps": round(layer_gbs, 1),
         "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
         "layer_tflops": round(layer_tflops, 2),
