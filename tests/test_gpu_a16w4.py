@@ -32,6 +32,9 @@ EXACT = [
     ("ksplit_k1024", 40, 1024, 512, 8, 2, None),
     ("ksplit_wide_scales", 40, 256, 128, 8, 2, (122, 132)),
     ("whole_items", 2048, 256, 512, 1024, 8, (122, 132)),
+    # at most four tokens: four-row activation slots, seven-slot ring
+    ("four_row_slots", 3, 256, 128, 8, 2, None),
+    ("four_row_slots_wide_scales", 4, 256, 128, 8, 3, (122, 132)),
 ]
 
 
@@ -95,7 +98,7 @@ def test_a16w4_tiny():
     _case(I.CONFIGS["tiny"])
 
 
-@pytest.mark.parametrize("T", [1, 3, 13, 64, 100])
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 13, 64, 100])
 def test_a16w4_ragged(T):
     _case(I.LayerConfig("a16_ragged", T, 256, 16, 2, 128, 1, seed=100 + T))
 

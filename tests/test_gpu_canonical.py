@@ -40,6 +40,7 @@ CASES = [
     ("prefill_grouped_scales", 300, 1024, 512, 8, 2, 2, False),
     ("prefill_d384", 300, 384, 128, 8, 2, 1, False),
     ("a16w4_few_tokens", 8, 256, 128, 16, 2, 1, True),
+    ("a16w4_four_tokens", 4, 256, 128, 16, 2, 1, True),
     ("a16w4_stream", 200, 512, 256, 64, 4, 1, True),
 ]
 
