@@ -130,6 +130,7 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 constexpr int kDsS = 7;                        // ring slots per wave (5632-byte slots)
 constexpr int kDsSWide = 4;                    // ring slots per wave of wide items (9984 bytes)
 constexpr int kDsS16 = 6;                      // ring slots per wave with bf16 activations (6400 bytes)
+constexpr int kDsS16Wide = 3;                  // ... of wide items with bf16 activations (10752 bytes)
 // LDS: four waves' rings, then per wave 8 x {ex, row_begin, row_end, group}
 constexpr int kDsLds = 4 * kDsSWide * 9984 + 4 * 8 * 16;   // 160256 bytes (the larger ring)
 __shared__ __attribute__((aligned(1024))) uint8_t ds_lds[kDsLds];
@@ -160,7 +161,8 @@ __device__ __forceinline__ int sload1(const void* p) {
 // weights are expanded in registers from FP4 to bf16 with their block scale
 // (V_CVT_SCALEF32_PK_BF16_FP4) and multiplied on the bf16 MFMA
 // (16x16x32: four per 16-row block and K step); h leaves the gate_up
-// epilogue as bf16.  Six ring slots of 6400 bytes; no two-group items.
+// epilogue as bf16.  Six ring slots of 6400 bytes (three of 10752 bytes for
+// two-group down items).
 // PH (phase) splits a few-token gate_up in two launches: PH = 1 is the top-k
 // and permutation (workgroup 0, topk_permute_block256) together with the
 // shared experts' items (every other workgroup: their tiles need no
@@ -190,11 +192,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
   const int wg_n = PH == 1 ? static_cast<int>(gridDim.x) - 1 : static_cast<int>(gridDim.x);
   // ring geometry: WIDE items (down only) cover two 64-row groups
   constexpr int GPI = WIDE ? 2 : 1;                 // packed groups per item
-  constexpr int S = A16 ? kDsS16 : (WIDE ? kDsSWide : kDsS);  // ring slots per wave
+  constexpr int S = A16 ? (WIDE ? kDsS16Wide : kDsS16) : (WIDE ? kDsSWide : kDsS);  // ring slots per wave
   constexpr int NC = 4 * GPI + 2 + GPI;             // copies per element
   constexpr int SW = 0, SA = 4096 * GPI, SAS = SA + (A16 ? 2048 : 1024), SBS = A16 ? SAS : SAS + 256,
                 SLOT = SBS + 256 * GPI;
-  static_assert(!(A16 && WIDE), "no two-group items with bf16 activations");
   constexpr int WAVE = S * SLOT, FIFO = 4 * WAVE;
   static_assert(FIFO + 4 * 8 * 16 <= kDsLds, "ring does not fit");
   static_assert(!(WIDE && (GU || KSPLIT)), "wide items are for the down GEMM");
@@ -373,31 +374,35 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       av[c] = *reinterpret_cast<const v8bf16*>(sl + SA + a16_row * 256 + 16 * ((4 * g + c) ^ a16_row));
-    const uint32_t sbw = *reinterpret_cast<const uint32_t*>(sl + SBS + 4 * lane);
-    uint32_t wd[4][4];
-    float scl[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 wv = ld16(sl + SW + j * 1024 + 16 * lane);
-      wd[j][0] = wv.x; wd[j][1] = wv.y; wd[j][2] = wv.z; wd[j][3] = wv.w;
-      // scale of block j of this lane's row, K block 4st + g: byte j of the
-      // packed dword, or byte g of the row's dword (canonical)
-      const uint32_t sb = CANON ? (*reinterpret_cast<const uint32_t*>(sl + SBS + 4 * (16 * j + r16)) >> (8 * g)) & 0xFFu
-                                : (sbw >> (8 * j)) & 0xFFu;
-      scl[j] = __uint_as_float(sb ? sb << 23 : 0x00400000u);  // 2^(sb-127)
-    }
-    // K chunk outer, block inner: consecutive MFMAs use different accumulators
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int g2 = 0; g2 < GPI; ++g2) {
+      const uint32_t sbw = *reinterpret_cast<const uint32_t*>(sl + SBS + g2 * 256 + 4 * lane);
+      uint32_t wd[4][4];
+      float scl[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const v2bf16 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 0);
-        const v2bf16 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 1);
-        const v2bf16 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 2);
-        const v2bf16 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 3);
-        const v8bf16 bv = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], bv, acc[j], 0, 0, 0);
+        const uint4 wv = ld16(sl + SW + g2 * 4096 + j * 1024 + 16 * lane);
+        wd[j][0] = wv.x; wd[j][1] = wv.y; wd[j][2] = wv.z; wd[j][3] = wv.w;
+        // scale of block j of this lane's row, K block 4st + g: byte j of the
+        // packed dword, or byte g of the row's dword (canonical)
+        const uint32_t sb =
+            CANON ? (*reinterpret_cast<const uint32_t*>(sl + SBS + g2 * 256 + 4 * (16 * j + r16)) >> (8 * g)) & 0xFFu
+                  : (sbw >> (8 * j)) & 0xFFu;
+        scl[j] = __uint_as_float(sb ? sb << 23 : 0x00400000u);  // 2^(sb-127)
       }
+      // K chunk outer, block inner: consecutive MFMAs use different accumulators
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const v2bf16 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 0);
+          const v2bf16 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 1);
+          const v2bf16 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 2);
+          const v2bf16 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[j][c], scl[j], 3);
+          const v8bf16 bv = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          acc[4 * g2 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], bv, acc[4 * g2 + j], 0, 0, 0);
+        }
+    }
   };
   auto compute = [&](int el) {
     if constexpr (A16) {
@@ -557,7 +562,9 @@ static hipError_t launch_stream_w(const FwdArgs& a, hipStream_t st) {
   // in the routing launch (stream_topk_shared), only the routed ones here
   const bool routed_only = GU && stream_split_phases(a);
   if (a.a16) {
-    if (!GU)
+    if (!GU && !few)
+      hipLaunchKernelGGL((k_gemm_stream<false, false, true, true, 0, C>), dim3(grid), dim3(256), 0, st, a);
+    else if (!GU)
       hipLaunchKernelGGL((k_gemm_stream<false, false, false, true, 0, C>), dim3(grid), dim3(256), 0, st, a);
     else if (routed_only && few)
       hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 2, C>), dim3(grid), dim3(256), 0, st, a);

@@ -32,6 +32,8 @@ EXACT = [
     ("ksplit_k1024", 40, 1024, 512, 8, 2, None),
     ("ksplit_wide_scales", 40, 256, 128, 8, 2, (122, 132)),
     ("whole_items", 2048, 256, 512, 1024, 8, (122, 132)),
+    # d_model 512: enough down items for the two-group (wide) ones
+    ("whole_items_wide_down", 2048, 512, 512, 1024, 8, (122, 132)),
     # at most four tokens: four-row activation slots, seven-slot ring
     ("four_row_slots", 3, 256, 128, 8, 2, None),
     ("four_row_slots_wide_scales", 4, 256, 128, 8, 3, (122, 132)),
