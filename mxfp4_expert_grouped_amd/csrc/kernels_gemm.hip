@@ -121,7 +121,8 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 // MFMA's rows 8-15 repeat rows 0-7 and are discarded.  With many items (16+
 // per wave) a down item covers two groups (128 output columns): one A copy
 // then feeds eight MFMAs and the per-item work halves, through a shallower
-// ring of larger slots.
+// ring of larger slots.  With bf16 activations (twice the activation bytes
+// per K step) a gate_up item covers two groups (64 h columns) as well.
 // Slot (5632 bytes; 9984 for two-group items): weights 4 KB per group (the
 // group's step, as packed) | A 8 rows x 128 B (16-byte chunks XOR-swizzled by
 // (row/2)%4; only the tile's rows are copied) | A scales (dword per row, lanes
@@ -180,7 +181,7 @@ __device__ __forceinline__ int canon_row_off(int jb, int dff) {
 
 template <bool GU, bool KSPLIT, bool WIDE, bool A16 = false, int PH = 0, bool CANON = false>
 __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
-  static_assert(PH == 0 || (GU && !WIDE), "the phases split the gate_up GEMM");
+  static_assert(PH == 0 || GU, "the phases split the gate_up GEMM");
   if constexpr (PH == 1) {
     if (blockIdx.x == 0) {
       topk_permute_block256(a, ds_lds);
@@ -198,7 +199,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
                 SLOT = SBS + 256 * GPI;
   constexpr int WAVE = S * SLOT, FIFO = 4 * WAVE;
   static_assert(FIFO + 4 * 8 * 16 <= kDsLds, "ring does not fit");
-  static_assert(!(WIDE && (GU || KSPLIT)), "wide items are for the down GEMM");
+  static_assert(!(WIDE && KSPLIT), "wide items take whole K");
   static_assert(GU || !KSPLIT, "the K split is for the gate_up GEMM");
   const int lane = threadIdx.x & 63;
   const int wu = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -282,7 +283,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
       // of its row that the packed order would hold (row r of the block, K
       // bytes 64 st + 16g ..), and lane 16jb + r of the scale copy the
       // dword of blocks 4st .. 4st+3 of row r of block jb
-      const int64_t row0 = GU ? 32 * int64_t(G) : 64 * int64_t(G) * GPI;
+      const int64_t row0 = (GU ? 32 : 64) * int64_t(G) * GPI;
       w_src = wc + (row0 + r16) * (K / 2) + 16 * g;
       bs_src = ws + (row0 + canon_row_off<GU>(lane >> 4, a.dff) + r16) * (K / 32);
     } else {
@@ -331,9 +332,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     for (int g2 = 0; g2 < GPI; ++g2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint8_t* src = CANON ? w_src + (int64_t(g2) * 64 + canon_row_off<GU>(j, a.dff)) * (K / 2) + st * 64
+        const uint8_t* src = CANON ? w_src + (int64_t(g2) * (GU ? 32 : 64) + canon_row_off<GU>(j, a.dff)) * (K / 2) + st * 64
                                    : w_src + int64_t(g2) * ns * 4096 + st * 4096 + j * 1024;
-        if (WIDE) lds_copy16(src, slot + SW + g2 * 4096 + j * 1024);
+        if (WIDE && !GU) lds_copy16(src, slot + SW + g2 * 4096 + j * 1024);
         else lds_copy16_nt(src, slot + SW + g2 * 4096 + j * 1024);
       }
     // only the tile's rows (tiles are never empty, so the copy is always
@@ -349,8 +350,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
     }
 #pragma unroll
     for (int g2 = 0; g2 < GPI; ++g2) {
-      const uint8_t* src = CANON ? bs_src + int64_t(g2) * 64 * (K / 32) + st * 4 : bs_src + int64_t(g2) * ns * 256 + st * 256;
-      if (WIDE) lds_copy4(src, slot + SBS + g2 * 256);
+      const uint8_t* src = CANON ? bs_src + int64_t(g2) * (GU ? 32 : 64) * (K / 32) + st * 4
+                                 : bs_src + int64_t(g2) * ns * 256 + st * 256;
+      if (WIDE && !GU) lds_copy4(src, slot + SBS + g2 * 256);
       else lds_copy4_nt(src, slot + SBS + g2 * 256);
     }
   };
@@ -470,12 +472,15 @@ __global__ void __launch_bounds__(256, 1) k_gemm_stream(FwdArgs a) {
       const int* md = fifo_ep + (il & 7) * 4;
       const int t_rb = md[1], t_re = md[2], G = md[3];
       if (GU) {
+        // group g2 of the item: h columns 32 (GPI G + g2) ..
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = t_rb + 4 * g + i;
-          float v[4] = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-          gu_epilogue(v, row, row < t_re, G, r16);
-        }
+        for (int g2 = 0; g2 < GPI; ++g2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = t_rb + 4 * g + i;
+            float v[4] = {acc[4 * g2][i], acc[4 * g2 + 1][i], acc[4 * g2 + 2][i], acc[4 * g2 + 3][i]};
+            gu_epilogue(v, row, row < t_re, GPI * G + g2, r16);
+          }
       } else {
         // o rows [8][64*GPI] as bf16 (RNE), staged in the slot of the item's
         // last element (no copy lands there before the next element is
@@ -556,7 +561,8 @@ static hipError_t launch_stream_w(const FwdArgs& a, hipStream_t st) {
   const unsigned grid = 8u * static_cast<unsigned>(a.num_cus >= 16 ? a.num_cus / 8 : 1);
   // few items per wave (< 16): gate_up splits K across a workgroup's waves,
   // down keeps one-group items and the deeper ring; many: whole items per
-  // wave, two groups per down item
+  // wave, two groups per down item and, with bf16 activations, per gate_up
+  // item
   const bool few = max_items < 16 * 4 * int64_t(a.num_cus);
   // few-token routing in one workgroup: the shared experts' items already ran
   // in the routing launch (stream_topk_shared), only the routed ones here
@@ -569,11 +575,11 @@ static hipError_t launch_stream_w(const FwdArgs& a, hipStream_t st) {
     else if (routed_only && few)
       hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 2, C>), dim3(grid), dim3(256), 0, st, a);
     else if (routed_only)
-      hipLaunchKernelGGL((k_gemm_stream<true, false, false, true, 2, C>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_stream<true, false, true, true, 2, C>), dim3(grid), dim3(256), 0, st, a);
     else if (few)
       hipLaunchKernelGGL((k_gemm_stream<true, true, false, true, 0, C>), dim3(grid), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((k_gemm_stream<true, false, false, true, 0, C>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((k_gemm_stream<true, false, true, true, 0, C>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   if (routed_only) {
