@@ -163,7 +163,7 @@ __device__ __forceinline__ int sload1(const void* p) {
 // (V_CVT_SCALEF32_PK_BF16_FP4) and multiplied on the bf16 MFMA
 // (16x16x32: four per 16-row block and K step); h leaves the gate_up
 // epilogue as bf16.  Six ring slots of 6400 bytes (three of 10752 bytes for
-// two-group down items).
+// two-group items).
 // PH (phase) splits a few-token gate_up in two launches: PH = 1 is the top-k
 // and permutation (workgroup 0, topk_permute_block256) together with the
 // shared experts' items (every other workgroup: their tiles need no
