@@ -40,19 +40,6 @@ __device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, v4f c, uint32
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Raw buffer access (offsets in bytes): an offset past num_records reads as
-// zero without touching memory, which gives padding rows for free.
-constexpr uint32_t kBufOOB = 0x80000000u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-__device__ __forceinline__ uint4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
-}
-__device__ __forceinline__ uint32_t buf4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
-}
 __device__ __forceinline__ v8i make_a(uint4 lo, uint4 hi) {
   v8i r;
   r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;

@@ -57,10 +57,7 @@ __device__ __forceinline__ uint32_t e4m3_cvt4(float a, float b, float c, float d
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, lo, true));
 }
 
-// bf16 <-> fp32
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
+// fp32 -> bf16, round to nearest even (finite values)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -78,14 +75,6 @@ template <int W>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
-  }
   return v;
 }
 
