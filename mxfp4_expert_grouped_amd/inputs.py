@@ -35,7 +35,7 @@ from __future__ import annotations
 
 import os
 from concurrent.futures import ThreadPoolExecutor
-from dataclasses import dataclass, replace
+from dataclasses import dataclass
 from typing import Optional, Tuple
 
 import numpy as np
@@ -56,9 +56,6 @@ class LayerConfig:
     num_shared: int
     zipf_bias: bool = False
     seed: int = 0
-
-    def with_tokens(self, t: int) -> "LayerConfig":
-        return replace(self, tokens=t)
 
 
 CONFIGS = {
@@ -298,10 +295,6 @@ class ExpertWeights:
 
 def matrix_bytes(rows: int, k: int) -> int:
     return rows * k // 2 + rows * k // 32
-
-
-def expert_bytes(cfg: LayerConfig) -> int:
-    return matrix_bytes(2 * cfg.d_ff, cfg.d_model) + matrix_bytes(cfg.d_model, cfg.d_ff)
 
 
 

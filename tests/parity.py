@@ -151,15 +151,6 @@ def run_gpu(cfg: I.LayerConfig, W: DeviceWeights, x: torch.Tensor, taps: bool = 
     return Run(tp or {}, y)
 
 
-def device_inputs(cfg: I.LayerConfig, W: Optional[DeviceWeights] = None, bias=None):
-    """x and device weights for a config (weights generated on the GPU)."""
-    if W is None:
-        W = IG.device_weights(cfg)
-    if bias is not None:
-        W.router_b = torch.from_numpy(np.asarray(bias, np.float32)).cuda()
-    return IG.device_x(cfg), W
-
-
 # ---------------------------------------------------------------------------
 # inputs outside the standard recipe
 # ---------------------------------------------------------------------------
