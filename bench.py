@@ -234,6 +234,8 @@ def main():
         stage_avg = {k: round(v / max(calls, 1), 5) for k, v in acc.items()}
 
     # ---- derived figures ------------------------------------------------------------------
+    # counter traffic is kept per kernel variant: activation type and weight layout
+    traffic_key = cfg.name + ("_a16w4" if args.a16w4 else "") + ("_canonical" if args.canonical else "")
     mean_step_bytes = float(np.mean([step_bytes(k) for k in sched]))
     mean_gu_bytes = float(np.mean([gate_up_bytes(k) for k in sched]))
     flops = 2.0 * R * 3 * cfg.d_model * cfg.d_ff
@@ -245,7 +247,7 @@ def main():
         achieved = mean_gu_bytes / (kern_ms / 1e3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": profiled_traffic(cfg.name),
+                    "traffic": profiled_traffic(traffic_key),
                     "kernel": ("gate_up grouped GEMM, routed experts (k_gemm_stream, 8-row tiles; the shared "
                                "experts' gate_up runs in the routing launch)" if phase_split
                                else "gate_up grouped GEMM (k_gemm_stream, 8-row tiles)"),
@@ -262,7 +264,7 @@ def main():
                     "unit": "TFLOP/s", "frac": round(achieved / FP8_MFMA_PEAK_TFLOPS, 4),
                     "peak_mxfp4": FP4_MFMA_PEAK_TFLOPS,
                     "frac_of_mxfp4_peak": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4),
-                    "traffic": profiled_traffic(cfg.name),
+                    "traffic": profiled_traffic(traffic_key),
                     "kernel": "gate_up grouped GEMM (k_gemm_pf, 256-row tiles)",
                     "kernel_ms": round(kern_ms, 5), "algorithmic_flops_per_launch": gu_flops}
 
@@ -365,8 +367,9 @@ def bench_tail(cfg, steps: int, warmup: int):
 
 def profiled_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed hardware-
-    counter summary, if one exists for this workload and the kernel sources are
-    unchanged since it was taken (else None)."""
+    counter summary, if one exists for this workload and kernel variant (e.g.
+    "decode256_a16w4") and the kernel sources are unchanged since it was taken
+    (else None)."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", f"gate_up_{workload}_hbm_traffic.txt")
