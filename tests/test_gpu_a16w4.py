@@ -34,6 +34,9 @@ EXACT = [
     ("whole_items", 2048, 256, 512, 1024, 8, (122, 132)),
     # d_model 512: enough down items for the two-group (wide) ones
     ("whole_items_wide_down", 2048, 512, 512, 1024, 8, (122, 132)),
+    # 32 tokens: routing launch with the shared items, then two-group routed
+    # gate_up items
+    ("phases_wide_items", 32, 512, 2048, 256, 16, None),
     # at most four tokens: four-row activation slots, seven-slot ring
     ("four_row_slots", 3, 256, 128, 8, 2, None),
     ("four_row_slots_wide_scales", 4, 256, 128, 8, 3, (122, 132)),

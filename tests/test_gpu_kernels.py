@@ -193,6 +193,9 @@ EXACT_CASES = [
     ("prefill_grouped_scales", 300, 1024, 512, 8, 2, (124, 130)),
     # d_model 512: 26,624 down items, enough for the two-group (wide) items
     ("stream_whole_items_wide_down", 2048, 512, 512, 1024, 8, (122, 132)),
+    # 32 tokens: the routing launch runs the shared experts' items and the
+    # routed gate_up launch has enough items (20,736) for whole items per wave
+    ("stream_phases_whole_items", 32, 512, 2048, 256, 16, None),
     # prefill tiles of at most 64 rows (six-slot ring), of 161-256 rows
     # (three slots) next to a short remainder tile, per-step and grouped scales
     ("prefill_rows64_step_scales", 128, 256, 128, 8, 2, (122, 132)),
