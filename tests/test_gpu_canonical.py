@@ -36,6 +36,7 @@ CASES = [
     ("few_tokens_phases", 8, 256, 128, 16, 2, 1, False),
     ("stream_ksplit", 40, 256, 128, 8, 2, 1, False),
     ("stream_whole_items_wide_down", 2048, 512, 512, 1024, 8, 1, False),
+    ("phases_whole_items", 32, 512, 2048, 256, 16, 1, False),
     ("prefill_step_scales", 300, 256, 128, 8, 2, 1, False),
     ("prefill_grouped_scales", 300, 1024, 512, 8, 2, 2, False),
     ("prefill_d384", 300, 384, 128, 8, 2, 1, False),
@@ -43,6 +44,7 @@ CASES = [
     ("a16w4_four_tokens", 4, 256, 128, 16, 2, 1, True),
     ("a16w4_stream", 200, 512, 256, 64, 4, 1, True),
     ("a16w4_whole_items_wide_down", 2048, 512, 512, 1024, 8, 1, True),
+    ("a16w4_phases_wide_items", 32, 512, 2048, 256, 16, 1, True),
 ]
 
 
