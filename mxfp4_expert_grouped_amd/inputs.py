@@ -20,15 +20,18 @@ x      : N(0, 1) drawn in float32 (numpy PCG64, seed sequence [seed, 1]),
 W_r    : N(0, 0.02) float32 (seed sequence [seed, 2]).
 bias   : zero, or for the skewed workload b_e = fp32(1.5 * ln p_e) with
          p_e = (e+1)^-1.1 / sum_r r^-1.1 (expert 0 hottest).
-experts: MXFP4 bytes drawn directly by a counter-based generator (Philox4x64-10,
-         Salmon et al., SC'11), so that any expert can be regenerated alone and
-         the GPU can generate the 21 GB layer itself bit-identically.  Each E2M1
-         element takes one random byte: bit 7 is the sign, bits 0-6 pick the
-         magnitude code from 128 equiprobable slots (10, 20, 19, 16, 20, 18, 16,
-         9 slots for codes 0..7 -- the code frequencies of N(0, 1/sqrt(d))
-         blocks quantised to MXFP4).  Each block scale is 127 + e with
-         e = floor(log2(1/sqrt(d))) - 1 + delta, delta = 1 with probability 1/4
-         (one random byte per block, its low 3 bits >= 6), else 0.
+experts: N(0, 1/sqrt(d)) quantised to MXFP4, from a counter-based generator
+         (Philox4x64-10, Salmon et al., SC'11) so that any expert can be
+         regenerated alone and the GPU can generate the 21 GB layer itself
+         bit-identically.  Block b (32 consecutive elements of a row) takes the
+         64 bytes of counters 2b and 2b+1: 32 little-endian 16-bit uniforms u,
+         each mapped through the inverse normal CDF at (u + 1/2) / 65536 (a
+         float32 table of 65536 entries) and multiplied in float32 by
+         sigma = float32(1/sqrt(d)).  The block is then quantised as the OCP MX
+         format defines: E8M0 scale 2^e with e = floor(log2(amax)) - 2 (E2M1's
+         largest exponent), elements x / 2^e rounded to the nearest E2M1 value
+         (ties to the even code, saturating at 6).  The LatentMoE tail's W_up
+         takes sigma from its own reduction width.
 """
 
 from __future__ import annotations
@@ -159,27 +162,29 @@ def philox_bytes(key: Tuple[int, int], first: int, count: int, c1: int = 0) -> n
 
 
 # ---------------------------------------------------------------------------
-# Direct MXFP4 weight generation
+# MXFP4 weights: N(0, sigma) samples quantised block by block
 # ---------------------------------------------------------------------------
 
-# slots (out of 128) per E2M1 magnitude code 0..7
-MAG_SLOTS = (10, 20, 19, 16, 20, 18, 16, 9)
-MAG_TABLE = np.repeat(np.arange(8, dtype=np.uint8), MAG_SLOTS)
-assert MAG_TABLE.size == 128
-# block-scale exponent offset from the low 3 bits of a random byte
-DELTA_TABLE = np.array([0, 0, 0, 0, 0, 0, 1, 1], dtype=np.int64)
-
-KIND_GU_CODES, KIND_GU_SCALES, KIND_DN_CODES, KIND_DN_SCALES = 1, 2, 3, 4
-KIND_UP_CODES, KIND_UP_SCALES = 5, 6  # LatentMoE tail up projection
+KIND_GU_CODES, KIND_DN_CODES = 1, 3
+KIND_UP_CODES = 5  # LatentMoE tail up projection
 SHARED_BASE = 0x10000
 
+_NORMAL_TABLE = None
 
-def scale_exponent_base(d_model: int) -> int:
-    """floor(log2(1/sqrt(d))) - 1, in integers: -(smallest n with 4**n >= d) - 1."""
-    n = 0
-    while 4 ** n < d_model:
-        n += 1
-    return -n - 1
+
+def normal_table() -> np.ndarray:
+    """float32 [65536]: the standard normal quantile at (u + 1/2) / 65536."""
+    global _NORMAL_TABLE
+    if _NORMAL_TABLE is None:
+        from scipy.special import ndtri
+        _NORMAL_TABLE = ndtri((np.arange(65536, dtype=np.float64) + 0.5) / 65536.0).astype(np.float32)
+    return _NORMAL_TABLE
+
+
+def weight_sigma(width: int) -> np.float32:
+    """float32(1 / sqrt(width)): the standard deviation of the weights of a
+    matrix whose rows are `width` long."""
+    return np.float32(1.0 / np.sqrt(float(width)))
 
 
 def stream_id(kind: int, expert_slot: int, layer: int = 0) -> int:
@@ -190,24 +195,66 @@ def expert_slot(kind: str, index: int) -> int:
     return index if kind == "routed" else SHARED_BASE + index
 
 
-def gen_mx_matrix(seed: int, code_stream: int, scale_stream: int, rows: int, k: int,
-                  e_base: int, row0: int = 0, nrows: Optional[int] = None):
-    """Rows [row0, row0+nrows) of one MXFP4 matrix [rows, k]:
-    (packed codes [n, k/2] uint8, scales [n, k/32] uint8)."""
+# E2M1 rounding boundaries of |x| / 2^e, each with the side a tie goes to:
+# values at a boundary round to the code with the even mantissa (0, 1.0, 2.0,
+# 4.0), so a code is reached above 0.25, 1.25, 2.5 and 5 but from 0.75, 1.75
+# and 3.5 on
+_E2M1_ABOVE = np.array([0.25, 1.25, 2.5, 5.0], dtype=np.float32)
+_E2M1_FROM = np.array([0.75, 1.75, 3.5], dtype=np.float32)
+
+
+def quantize_blocks_mx4(x: np.ndarray):
+    """OCP MX quantisation of float32 blocks [n, 32] to (packed E2M1 codes
+    [n, 16] uint8, element 2i in the low nibble of byte i; E8M0 scale bytes
+    [n] uint8)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=1)
+    ebits = ((amax.view(np.uint32) >> 23) & 0xFF).astype(np.int64)   # biased exponent of amax
+    zero = amax == 0
+    # floor(log2 amax) - 2, kept where 2^-e is a normal float32 (blocks of
+    # normal, finite values well inside the float32 range stay unclamped)
+    e = np.where(zero, -127, np.clip(ebits - 127 - 2, -126, 125))
+    # 2^-e as float32 (exact); all-zero blocks use 1
+    inv = np.where(zero, np.uint32(127 << 23), ((127 - e) << 23).astype(np.uint32)).astype(np.uint32).view(np.float32)
+    a = np.abs(x) * inv[:, None]
+    mag = np.zeros(x.shape, dtype=np.uint8)
+    for t in _E2M1_ABOVE:
+        mag += (a > t).astype(np.uint8)
+    for t in _E2M1_FROM:
+        mag += (a >= t).astype(np.uint8)
+    codes = mag | ((x < 0).astype(np.uint8) << 3)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    scales = (e + 127).astype(np.uint8)
+    return packed, scales
+
+
+def normal_blocks(seed: int, stream: int, blocks: np.ndarray, sigma: np.float32) -> np.ndarray:
+    """float32 [n, 32]: the N(0, sigma) samples of blocks `blocks` (counters
+    2b and 2b+1 of each block b)."""
+    blocks = np.asarray(blocks, dtype=np.uint64)
+    ctr = np.stack([2 * blocks, 2 * blocks + np.uint64(1)], axis=1).reshape(-1)
+    words = philox4x64_10((seed, stream), ctr).astype("<u8")                # [2n, 4]
+    u = words.view(np.uint16).reshape(blocks.size, 32)                      # 64 bytes -> 32 uniforms
+    return normal_table()[u] * np.float32(sigma)
+
+
+def gen_mx_matrix(seed: int, stream: int, rows: int, k: int, sigma: np.float32,
+                  row0: int = 0, nrows: Optional[int] = None):
+    """Rows [row0, row0+nrows) of one MXFP4 matrix [rows, k] drawn from
+    N(0, sigma): (packed codes [n, k/2] uint8, scales [n, k/32] uint8)."""
     n = rows - row0 if nrows is None else nrows
     nb = k // 32
     b0 = row0 * nb
     nblk = n * nb
-    # element codes: one Philox call per block of 32 elements (chunked over
-    # threads; numpy releases the GIL inside its array operations)
     packed = np.empty((nblk, 16), dtype=np.uint8)
+    scales = np.empty(nblk, dtype=np.uint8)
 
+    # chunked over threads (numpy releases the GIL inside its array operations)
     def fill(lo: int, hi: int) -> None:
-        rb = philox_bytes((seed, code_stream), b0 + lo, hi - lo)  # [hi-lo, 32]
-        codes = MAG_TABLE[rb & 0x7F] | ((rb >> 7) << 3)
-        packed[lo:hi] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+        x = normal_blocks(seed, stream, np.arange(b0 + lo, b0 + hi, dtype=np.uint64), sigma)
+        packed[lo:hi], scales[lo:hi] = quantize_blocks_mx4(x)
 
-    step = 1 << 15
+    step = 1 << 14
     spans = [(lo, min(lo + step, nblk)) for lo in range(0, nblk, step)]
     threads = min(len(spans), os.cpu_count() or 1, 16, int(os.environ.get("MXMOE_GEN_THREADS", "16")))
     if threads > 1:
@@ -216,42 +263,27 @@ def gen_mx_matrix(seed: int, code_stream: int, scale_stream: int, rows: int, k: 
     else:
         for sp in spans:
             fill(*sp)
-    packed = packed.reshape(n, k // 2)
-    # scales: one Philox call per 32 blocks
-    c_first = b0 // 32
-    c_last = (b0 + nblk - 1) // 32
-    sb = philox_bytes((seed, scale_stream), c_first, c_last - c_first + 1).reshape(-1)
-    sb = sb[b0 - c_first * 32: b0 - c_first * 32 + nblk]
-    scales = (127 + e_base + DELTA_TABLE[sb & 7]).astype(np.uint8).reshape(n, nb)
-    return packed, scales
+    return packed.reshape(n, k // 2), scales.reshape(n, nb)
 
 
-def gen_mx_matrix_kblocks(seed: int, code_stream: int, scale_stream: int, rows: int, k: int,
-                          e_base: int, kblocks):
+def gen_mx_matrix_kblocks(seed: int, stream: int, rows: int, k: int, sigma: np.float32, kblocks):
     """The same matrix as gen_mx_matrix, only the 32-wide K blocks `kblocks`
     of every row: (packed codes [rows, len(kblocks), 16], scales [rows,
     len(kblocks)]), drawn from the same counters."""
     kb = np.asarray(kblocks, dtype=np.int64)
     nb = k // 32
     blk = (np.arange(rows, dtype=np.int64)[:, None] * nb + kb[None, :]).reshape(-1)
-    rb = philox4x64_10((seed, code_stream), blk.astype(np.uint64)).astype("<u8").view(np.uint8).reshape(-1, 32)
-    codes = MAG_TABLE[rb & 0x7F] | ((rb >> 7) << 3)
-    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).reshape(rows, kb.size, 16)
-    sw = philox4x64_10((seed, scale_stream), (blk // 32).astype(np.uint64)).astype("<u8").view(np.uint8)
-    sb = sw.reshape(-1, 32)[np.arange(blk.size), blk % 32]
-    scales = (127 + e_base + DELTA_TABLE[sb & 7]).astype(np.uint8).reshape(rows, kb.size)
-    return packed, scales
+    packed, scales = quantize_blocks_mx4(normal_blocks(seed, stream, blk.astype(np.uint64), sigma))
+    return packed.reshape(rows, kb.size, 16), scales.reshape(rows, kb.size)
 
 
 def gen_expert(cfg: LayerConfig, kind: str, index: int, layer: int = 0):
     """(gu_codes [2 d_ff, d/2], gu_scales [2 d_ff, d/32],
         dn_codes [d, d_ff/2],   dn_scales [d, d_ff/32]) of one expert."""
     slot = expert_slot(kind, index)
-    eb = scale_exponent_base(cfg.d_model)
-    guc, gus = gen_mx_matrix(cfg.seed, stream_id(KIND_GU_CODES, slot, layer),
-                             stream_id(KIND_GU_SCALES, slot, layer), 2 * cfg.d_ff, cfg.d_model, eb)
-    dnc, dns = gen_mx_matrix(cfg.seed, stream_id(KIND_DN_CODES, slot, layer),
-                             stream_id(KIND_DN_SCALES, slot, layer), cfg.d_model, cfg.d_ff, eb)
+    sg = weight_sigma(cfg.d_model)
+    guc, gus = gen_mx_matrix(cfg.seed, stream_id(KIND_GU_CODES, slot, layer), 2 * cfg.d_ff, cfg.d_model, sg)
+    dnc, dns = gen_mx_matrix(cfg.seed, stream_id(KIND_DN_CODES, slot, layer), cfg.d_model, cfg.d_ff, sg)
     return guc, gus, dnc, dns
 
 
@@ -271,6 +303,12 @@ class ExpertWeights:
             self._c[key] = w
         return w
 
+    def min_scale_byte(self) -> Optional[int]:
+        """The smallest E8M0 scale byte among the experts drawn so far (None if none)."""
+        if not self._c:
+            return None
+        return int(min(min(int(w[1].min()), int(w[3].min())) for w in self._c.values()))
+
     def dn_blocks(self, kind: str, index: int, kblocks):
         """Blocks `kblocks` (32 columns each) of every row of W_dn [d, d_ff]:
         (packed codes [d, n, 16], scales [d, n]), without drawing the rest."""
@@ -281,8 +319,7 @@ class ExpertWeights:
             return (dnc.reshape(dnc.shape[0], -1, 16)[:, kb], dns[:, kb])
         slot = expert_slot(kind, index)
         return gen_mx_matrix_kblocks(self.cfg.seed, stream_id(KIND_DN_CODES, slot, self.layer),
-                                     stream_id(KIND_DN_SCALES, slot, self.layer), self.cfg.d_model,
-                                     self.cfg.d_ff, scale_exponent_base(self.cfg.d_model), kb)
+                                     self.cfg.d_model, self.cfg.d_ff, weight_sigma(self.cfg.d_model), kb)
 
     def stacked(self):
         """All routed and shared experts stacked (small configs only)."""
@@ -305,10 +342,9 @@ def matrix_bytes(rows: int, k: int) -> int:
 
 def gen_up_matrix(hidden: int, latent: int, seed: int = 0, layer: int = 0):
     """W_up [hidden, latent] in canonical MXFP4 (codes [hidden, latent/2],
-    scales [hidden, latent/32]), by the same direct MXFP4 recipe as the
-    experts (scale base from the reduction width `latent`)."""
-    return gen_mx_matrix(seed, stream_id(KIND_UP_CODES, 0, layer), stream_id(KIND_UP_SCALES, 0, layer),
-                         hidden, latent, scale_exponent_base(latent))
+    scales [hidden, latent/32]): N(0, 1/sqrt(latent)) quantised to MXFP4 by
+    the experts' recipe."""
+    return gen_mx_matrix(seed, stream_id(KIND_UP_CODES, 0, layer), hidden, latent, weight_sigma(latent))
 
 
 def gen_tail_inputs(tokens: int, latent: int, hidden: int, seed: int = 0, layer: int = 0):

@@ -2,16 +2,17 @@
 
 Dense inputs (x, W_r, bias) come from :mod:`.inputs` on the host and are
 copied over.  The MXFP4 expert weights (21 GB for the full layer) are drawn on
-the device by ``libmxmoe_inputs.so``, the GPU twin of the Philox recipe in
-:mod:`.inputs`, which produces the same canonical bytes as the numpy
-generator; the layer library then packs them into its tile order.
+the device by ``libmxmoe_inputs.so``, the GPU twin of the recipe in
+:mod:`.inputs` (Philox uniforms, the same float32 normal-quantile table,
+MXFP4 quantisation of each block), which produces the same canonical bytes as
+the numpy generator; the layer library then packs them into its tile order.
 """
 
 from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import c_int, c_int64, c_uint64, c_void_p
+from ctypes import c_float, c_int, c_int64, c_uint64, c_void_p
 from typing import Optional, Tuple
 
 import numpy as np
@@ -33,16 +34,30 @@ def _genlib():
             raise ImportError(f"{GEN_LIB_PATH} is not built")
         lib = ctypes.CDLL(GEN_LIB_PATH)
         lib.mxmoe_gen_mx_matrix.argtypes = [c_void_p, c_void_p, c_int64, c_int64, c_uint64,
-                                            c_uint64, c_uint64, c_int, c_void_p]
+                                            c_uint64, c_void_p, c_float, c_void_p]
         lib.mxmoe_gen_mx_matrix.restype = c_int
         _gen = lib
     return _gen
 
 
+_tables = {}
+
+
+def _normal_table_device(device) -> torch.Tensor:
+    """The generator's float32 normal-quantile table on `device` (one copy per device)."""
+    dev = torch.device(device)
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    if dev not in _tables:
+        _tables[dev] = torch.from_numpy(I.normal_table()).to(dev)
+    return _tables[dev]
+
+
 def gen_mx_matrix_device(codes: torch.Tensor, scales: torch.Tensor, rows: int, k: int, seed: int,
-                         code_stream: int, scale_stream: int, e_base: int) -> None:
-    rc = _genlib().mxmoe_gen_mx_matrix(codes.data_ptr(), scales.data_ptr(), rows, k, seed,
-                                       code_stream, scale_stream, e_base,
+                         stream: int, sigma: float) -> None:
+    table = _normal_table_device(codes.device)
+    rc = _genlib().mxmoe_gen_mx_matrix(codes.data_ptr(), scales.data_ptr(), rows, k, seed, stream,
+                                       table.data_ptr(), float(sigma),
                                        torch.cuda.current_stream().cuda_stream)
     if rc != 0:
         raise RuntimeError(f"mxmoe_gen_mx_matrix failed ({rc})")
@@ -56,15 +71,11 @@ def gen_experts_device(cfg: I.LayerConfig, kind: str, count: int, layer: int = 0
     gus = torch.empty((count, 2 * f, d // 32), dtype=torch.uint8, device=device)
     dnc = torch.empty((count, d, f // 2), dtype=torch.uint8, device=device)
     dns = torch.empty((count, d, f // 32), dtype=torch.uint8, device=device)
-    eb = I.scale_exponent_base(d)
+    sg = I.weight_sigma(d)
     for i in range(count):
         slot = I.expert_slot(kind, i)
-        gen_mx_matrix_device(guc[i], gus[i], 2 * f, d, cfg.seed,
-                             I.stream_id(I.KIND_GU_CODES, slot, layer),
-                             I.stream_id(I.KIND_GU_SCALES, slot, layer), eb)
-        gen_mx_matrix_device(dnc[i], dns[i], d, f, cfg.seed,
-                             I.stream_id(I.KIND_DN_CODES, slot, layer),
-                             I.stream_id(I.KIND_DN_SCALES, slot, layer), eb)
+        gen_mx_matrix_device(guc[i], gus[i], 2 * f, d, cfg.seed, I.stream_id(I.KIND_GU_CODES, slot, layer), sg)
+        gen_mx_matrix_device(dnc[i], dns[i], d, f, cfg.seed, I.stream_id(I.KIND_DN_CODES, slot, layer), sg)
     return guc, gus, dnc, dns
 
 
@@ -87,14 +98,12 @@ def packed_experts_device(cfg: I.LayerConfig, kind: str, count: int, layer: int 
     tgs = torch.empty((2 * f, d // 32), dtype=torch.uint8, device=device)
     tdc = torch.empty((d, f // 2), dtype=torch.uint8, device=device)
     tds = torch.empty((d, f // 32), dtype=torch.uint8, device=device)
-    eb = I.scale_exponent_base(d)
+    sg = I.weight_sigma(d)
     st = torch.cuda.current_stream().cuda_stream
     for i in range(count):
         slot = I.expert_slot(kind, i)
-        gen_mx_matrix_device(tgc, tgs, 2 * f, d, cfg.seed, I.stream_id(I.KIND_GU_CODES, slot, layer),
-                             I.stream_id(I.KIND_GU_SCALES, slot, layer), eb)
-        gen_mx_matrix_device(tdc, tds, d, f, cfg.seed, I.stream_id(I.KIND_DN_CODES, slot, layer),
-                             I.stream_id(I.KIND_DN_SCALES, slot, layer), eb)
+        gen_mx_matrix_device(tgc, tgs, 2 * f, d, cfg.seed, I.stream_id(I.KIND_GU_CODES, slot, layer), sg)
+        gen_mx_matrix_device(tdc, tds, d, f, cfg.seed, I.stream_id(I.KIND_DN_CODES, slot, layer), sg)
         M.moe_pack_mx4(tgc.data_ptr(), tgs.data_ptr(), 1, 2 * f, d, 1, out[0][i].data_ptr(),
                        out[1][i].data_ptr(), st)
         M.moe_pack_mx4(tdc.data_ptr(), tds.data_ptr(), 1, d, f, 0, out[2][i].data_ptr(),

@@ -55,10 +55,8 @@ def test_a16w4_gate_up_accumulators_exact(name, T, d, f, E, k, scales):
     if scales is None:
         W = P.IG.device_weights(cfg)
         ref = I.ExpertWeights(cfg)
-        lo = 127 + I.scale_exponent_base(d)
     else:
         W, ref = P.weights_with_scale_range(cfg, 78, *scales)
-        lo = scales[0]
     P.log(f"A16W4 exact case {name}: T={T} d={d} d_ff={f} E={E} k={k} scale bytes {scales}")
     g = P.run_gpu(cfg, W, x, a16=True)
     tokens = None if T <= 64 else sorted(set(range(0, T, max(1, T // 48))) | {T - 1})
@@ -76,6 +74,8 @@ def test_a16w4_gate_up_accumulators_exact(name, T, d, f, E, k, scales):
         res, differ = P.compare_layer(cfg, bits, I.gen_router_w(cfg), None, ref, g, tokens=tokens,
                                       activations="bf16")
         assert not differ
+    # the lowest scale byte of the experts the compared rows use
+    lo = scales[0] if scales is not None else ref.min_scale_byte()
     q = 0.5 * 2.0 ** (lo - 127)
     acc = g["gu_acc"]
     nmis = nrows = 0

@@ -94,13 +94,13 @@ def test_pack_mx4_layout(rows, k, interleave):
 def test_gpu_generator_matches_numpy_full_shape_sample():
     cfg = I.CONFIGS["decode1"]
     guc, gus, dnc, dns = P.IG.gen_experts_device(cfg, "routed", 1)
-    eb = I.scale_exponent_base(cfg.d_model)
-    c, s = I.gen_mx_matrix(cfg.seed, I.stream_id(I.KIND_GU_CODES, 0), I.stream_id(I.KIND_GU_SCALES, 0),
-                           2 * cfg.d_ff, cfg.d_model, eb, row0=1000, nrows=64)
+    sg = I.weight_sigma(cfg.d_model)
+    c, s = I.gen_mx_matrix(cfg.seed, I.stream_id(I.KIND_GU_CODES, 0), 2 * cfg.d_ff, cfg.d_model, sg,
+                           row0=1000, nrows=64)
     assert np.array_equal(guc[0, 1000:1064].cpu().numpy(), c)
     assert np.array_equal(gus[0, 1000:1064].cpu().numpy(), s)
-    c, s = I.gen_mx_matrix(cfg.seed, I.stream_id(I.KIND_DN_CODES, 0), I.stream_id(I.KIND_DN_SCALES, 0),
-                           cfg.d_model, cfg.d_ff, eb, row0=7100, nrows=68)
+    c, s = I.gen_mx_matrix(cfg.seed, I.stream_id(I.KIND_DN_CODES, 0), cfg.d_model, cfg.d_ff, sg,
+                           row0=7100, nrows=68)
     assert np.array_equal(dnc[0, 7100:].cpu().numpy(), c)
     assert np.array_equal(dns[0, 7100:].cpu().numpy(), s)
 
@@ -223,16 +223,16 @@ def test_gate_up_accumulators_exact(name, T, d, f, E, k, scales):
     if scales is None:
         W = P.IG.device_weights(cfg)
         ref = I.ExpertWeights(cfg)
-        lo = 127 + I.scale_exponent_base(d)
     else:
         W, ref = P.weights_with_scale_range(cfg, 77, *scales)
-        lo = scales[0]
     P.log(f"exact case {name}: T={T} d={d} d_ff={f} E={E} k={k} scale bytes {scales}")
     g = P.run_gpu(cfg, W, x)
     tokens = None if T <= 64 else sorted(set(range(0, T, max(1, T // 48))) | {T - 1})
     wr = I.gen_router_w(cfg)
     res, differ = P.compare_layer(cfg, bits, wr, None, ref, g, tokens=tokens)
     assert not differ
+    # the lowest scale byte of the experts the compared rows use
+    lo = scales[0] if scales is not None else ref.min_scale_byte()
     q = 0.5 * 2.0 ** (lo - 127)
     acc = g["gu_acc"]
     nmis = nrows = 0

@@ -299,8 +299,7 @@ def test_latent_tail_is_norm_quantise_project_add():
     z = (rng.standard_normal((5, 256)) * 0.3).astype(np.float32)
     s = rng.standard_normal((5, 256)).astype(np.float32)
     gamma = (1 + 0.05 * rng.standard_normal(256)).astype(np.float32)
-    up_c, up_s = I.gen_mx_matrix(33, I.stream_id(7, 0), I.stream_id(8, 0), 256, 256,
-                                 I.scale_exponent_base(256))
+    up_c, up_s = I.gen_mx_matrix(33, I.stream_id(7, 0), 256, 256, I.weight_sigma(256))
     y = moe.latent_tail(z, gamma, 1e-6, up_c, up_s, s)
     n = torch.nn.functional.rms_norm(torch.from_numpy(z.astype(np.float64)), (256,),
                                      torch.from_numpy(gamma.astype(np.float64)), 1e-6)

@@ -182,13 +182,22 @@ def test_accumulator_outside_the_bound_is_rejected():
 
 def test_same_output_error_without_a_flipped_byte_is_rejected():
     x, wr, W, res, g = _oracle_as_gpu(CFG)
-    col, hc, hs = _largest_shared_element(res)
-    c = int(hc[col])
-    dh = (_vals()[c - 1] - _vals()[c]) * OX.decode_e8m0(hs[col // 32])
-    wcol = _shift_outputs(CFG, W, g, 0, 0, col, dh)
     rms = np.sqrt(np.mean(res.y_shared ** 2))
-    assert np.max(np.abs(dh * wcol)) / rms > P.MAX_ERR_RMS, "must exceed the plain elementwise bar"
-    with pytest.raises(AssertionError, match="max error"):
+    # the token whose largest shared-expert h element, moved one E4M3 step,
+    # moves an output the most
+    best = None
+    for t in range(CFG.tokens):
+        col, hc, hs = _largest_shared_element(res, t)
+        c = int(hc[col])
+        dh = (_vals()[c - 1] - _vals()[c]) * OX.decode_e8m0(hs[col // 32])
+        wcol = P._dn_columns(W("shared", 0)[2], W("shared", 0)[3], np.array([col]))[:, 0]
+        m = float(np.max(np.abs(dh * wcol)))
+        if best is None or m > best[0]:
+            best = (m, t, col, dh)
+    m, t, col, dh = best
+    _shift_outputs(CFG, W, g, t, 0, col, dh)
+    assert m / rms > P.MAX_ERR_RMS, "must exceed the plain elementwise bar"
+    with pytest.raises(AssertionError, match="max error|relative L2 error"):
         P.compare_layer(CFG, x, wr, None, W, g)
 
 
