@@ -81,12 +81,10 @@ typedef enum { MOE_SRC_BF16 = 0, MOE_SRC_FP32 = 1 } moe_src_dtype;
  * and A8W4 fused operators on MI355X): x stays bf16 into the gate_up
  * projection and h = silu(g)*u is rounded to bf16 (round to nearest even)
  * into the down projection; no MXFP8 activation anywhere; weights, router,
- * permutation and combine as in the A8W4 layer.  Implemented on the
- * weight-streaming kernels only: moe_forward returns MOE_ERR_UNSUPPORTED
- * when num_tokens * top_k / num_experts >= 24 (the average rows per expert
- * at which the A8W4 layer switches to its 256-row prefill kernels).  The
- * x_codes, x_scales, h_codes and h_scales taps must be NULL; h comes out
- * through the h_bf16 tap. */
+ * permutation and combine as in the A8W4 layer, at every token count: the
+ * weight-streaming kernels below 24 rows per expert on average, 256-row
+ * tiles on the bf16 MFMA from there on.  The x_codes, x_scales, h_codes and
+ * h_scales taps must be NULL; h comes out through the h_bf16 tap. */
 #define MOE_FLAG_A16W4 1u
 typedef struct {
   int32_t d_model, d_ff, num_experts, top_k, num_shared;

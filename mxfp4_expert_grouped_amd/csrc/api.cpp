@@ -311,11 +311,6 @@ moe_status forward_impl(const moe_plan_t* plan, const moe_weights* w, const void
     return fail(MOE_ERR_INVALID_ARG,
                 "misaligned buffer (x, y, codes, router_w: 16 bytes; scales, bias: 4 bytes)");
   const bool a16 = (c.flags & MOE_FLAG_A16W4) != 0;
-  if (a16 && choose_bm(c, num_tokens) != kDecodeMaxRows)
-    return fail(MOE_ERR_UNSUPPORTED,
-                "A16W4 runs the weight-streaming kernels only: %lld tokens x top-%d over %d experts is "
-                "24 or more rows per expert on average",
-                static_cast<long long>(num_tokens), c.top_k, c.num_experts);
   if (taps && a16 && (taps->x_codes || taps->x_scales || taps->h_codes || taps->h_scales))
     return fail(MOE_ERR_INVALID_ARG, "A16W4 has no MXFP8 activations: x/h code and scale taps must be NULL");
   if (taps && !a16 && taps->h_bf16)

@@ -1241,6 +1241,246 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
 }
 
 
+// ---------------------------------------------------------------------------
+// Prefill variant with bf16 activations (A16W4): the tiles of k_gemm_pf (256
+// rows x 256 weight rows per workgroup, four waves of 128 x 128, the same
+// work order), on the bf16 MFMA 32x32x16 with every FP4 weight fragment
+// expanded to bf16 with its block scale in registers
+// (V_CVT_SCALEF32_PK_BF16_FP4).  K steps of 64: a bf16 activation row is then
+// 128 bytes per step, so the A slot is the MXFP8 kernel's (row-major, 16-byte
+// chunks XOR-swizzled by (row/2)%8).  A slot of the three-slot ring holds
+//   * A 32 KB;
+//   * B 8 KB: per packed 64-row group 2 KB, per 16-row block the 512 bytes of
+//     its packed 1 KB step that hold this K half (lanes 16g'+r, g' = 0, 1:
+//     row r, K group g' of the half);
+//   * B scales 1 KB: per group 256 bytes -- packed: the 32 scale dwords of
+//     this half (lane 16g'+r, byte = block); canonical: a dword per row
+//     (lane 16 block + r) holding the scales of the row's four K groups of
+//     the 128-wide step, of which this half uses bytes 2h, 2h+1.
+// Wave w copies 64 activation rows (eight 8-row copies; rows past the
+// tile's end read its first row), packed group w's weights (two copies) and
+// their scales (one): eleven copies per step.  Per step each wave waits for
+// its own copies of the step, then a barrier (every wave's copies have
+// landed, every wave is done with the slot of the step before), then the
+// copies of step st+2 go to that slot, then the LDS reads, the expansion
+// and the MFMAs.  MFMA slice q of a step takes, in lane (row or column l%32,
+// half kh = l/32), the 8 values 32 kh + 8q .. +7 of the step: four
+// consecutive bytes of the lane's 16-byte weight fragment, and the matching
+// 16 bytes of its activation row.  The row blocks of a tile are split
+// between the two row-half waves as in k_gemm_pf.  Epilogues write h (bf16,
+// SwiGLU) or o (bf16) straight from the accumulators.
+// ---------------------------------------------------------------------------
+constexpr int kP16Slot = 32768 + 8192 + 1024;  // A | B | B scales
+constexpr int kP16A = 0, kP16B = 32768, kP16BS = 40960;
+constexpr int kP16Lds = 3 * kP16Slot;           // 125952 bytes
+__shared__ __attribute__((aligned(1024))) uint8_t p16_lds[kP16Lds];
+
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+
+template <bool GU, bool CANON>
+__global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
+  int tile_idx, nblk;
+  if (!pf_work_item(a, GU ? a.dff / 128 : (a.d + 255) / 256, &tile_idx, &nblk)) return;
+  const Tile tile = a.tiles[tile_idx];
+  const int lane = threadIdx.x & 63;
+  const int wu = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int wm = wu & 1, wn = wu >> 1;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int K = GU ? a.d : a.dff;
+  const int nst = K / 64;                          // K steps of 64
+  const int ns128 = K / 128;                       // packed steps of 128
+  const bool shared = tile.ex >= a.E;
+  const int sidx = tile.ex - a.E;
+  const int64_t wrows = GU ? 2 * a.dff : a.d;
+  const int64_t wc_stride = wrows * (K / 2), ws_stride = packed_scale_bytes(wrows, K);
+  const uint8_t* wc = GU ? (shared ? a.sgu_c + sidx * wc_stride : a.gu_c + tile.ex * wc_stride)
+                         : (shared ? a.sdn_c + sidx * wc_stride : a.dn_c + tile.ex * wc_stride);
+  const uint8_t* ws = GU ? (shared ? a.sgu_s + sidx * ws_stride : a.gu_s + tile.ex * ws_stride)
+                         : (shared ? a.sdn_s + sidx * ws_stride : a.dn_s + tile.ex * ws_stride);
+  // the tile's four packed groups 4 nblk .. 4 nblk + 3 (gate_up: the gate
+  // and up rows of h columns c0 .. c0+127; down: output columns c0 ..
+  // c0+255); wave w copies group w.  Down with d an odd multiple of 128:
+  // the waves of the missing half of the last block copy group grp0 again
+  // and store nothing
+  const int grp0 = 4 * nblk;
+  const int c0 = GU ? 128 * nblk : 256 * nblk;
+  const int64_t gw = GU || grp0 + wu < a.d / 64 ? grp0 + wu : grp0;
+  const bool cols_live = GU || c0 + 128 * wn < a.d;
+  const bool routed = tile.row_begin < a.Rr;
+  const int nrows = tile.row_end - tile.row_begin;
+
+  // activation source rows of this wave's copies (rows past the end read the
+  // tile's first row): gate_up x rows (routed: through row -> token), down h
+  // rows (contiguous)
+  const uint16_t* act = GU ? a.x : a.h16;
+  const uint8_t* a_src[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int rl = 64 * wu + 8 * q + (lane >> 3);
+    const int row = tile.row_begin + (rl < nrows ? rl : 0);
+    int64_t srow = row;
+    if (GU) srow = routed ? a.row_token[row] : row - a.Rr - int64_t(sidx) * a.T;
+    a_src[q] = reinterpret_cast<const uint8_t*>(act) + srow * (2 * int64_t(K)) + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
+  }
+  // weight copies: copy c (0, 1) moves blocks 2c (lanes 0-31) and 2c+1
+  // (lanes 32-63) of group gw, 16 bytes a lane
+  const uint8_t* b_src[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int jb = 2 * c + (lane >> 5), l = lane & 31;
+    if (CANON) {
+      const int64_t crow = (GU ? 32 * gw : 64 * gw) + canon_row_off<GU>(jb, a.dff) + (l & 15);
+      b_src[c] = wc + crow * (K / 2) + 16 * (l >> 4);
+    } else {
+      b_src[c] = wc + gw * ns128 * 4096 + jb * 1024 + 16 * l;
+    }
+  }
+  // their scales: packed, lanes 0-31 take the half's 32 dwords; canonical,
+  // every lane the dword of row (lane/16 block, lane%16)
+  const uint8_t* bs_src =
+      CANON ? ws + ((GU ? 32 * gw : 64 * gw) + canon_row_off<GU>(lane >> 4, a.dff) + (lane & 15)) * (K / 32)
+            : ws + gw * ns128 * 256 + 4 * (lane & 31);
+  const uint32_t lds0 = lds_addr(p16_lds);
+  auto issue = [&](int st) {
+    const uint32_t slot = lds0 + (st % 3) * kP16Slot;
+    const int h = st & 1, s128 = st >> 1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) lds_copy16(a_src[q] + 128 * int64_t(st), slot + kP16A + (64 * wu + 8 * q) * 128);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint8_t* src = CANON ? b_src[c] + 32 * int64_t(st) : b_src[c] + int64_t(s128) * 4096 + 512 * h;
+      lds_copy16(src, slot + kP16B + wu * 2048 + c * 1024);
+    }
+    if (CANON) {
+      lds_copy4(bs_src + 4 * s128, slot + kP16BS + wu * 256);
+    } else {
+      if (lane < 32) lds_copy4(bs_src + int64_t(s128) * 256 + 128 * h, slot + kP16BS + wu * 256);
+    }
+  };
+  constexpr int NCOP = 11;
+
+  // operand offsets: weight fragment p of this wave (32 rows): 16-row chunk
+  // j0(p) of the tile's sixteen (gate_up: gate rows of h columns 32p .. of
+  // groups 2wn, 2wn+1 for p < 2, their up rows for p >= 2; down: 32 output
+  // columns each)
+  auto j0 = [&](int p) -> int { return GU ? (p < 2 ? 8 * wn + 4 * p : 8 * wn + 4 * (p - 2) + 2) : 8 * wn + 2 * p; };
+  int b_off[4], bs_off[4], bs_sh[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int jc = j0(p) + (l32 >> 4), grp = jc >> 2, jb = jc & 3, r = l32 & 15;
+    b_off[p] = kP16B + grp * 2048 + jb * 512 + 16 * (16 * kh + r);
+    bs_off[p] = kP16BS + grp * 256 + 4 * (CANON ? 16 * jb + r : 16 * kh + r);
+    bs_sh[p] = CANON ? 8 * kh : 8 * jb;              // + 16 h for canonical
+  }
+  const int nb = (nrows + 31) >> 5;
+  const int rb0 = wm ? (nb + 1) >> 1 : 0;
+  const int nact = wm ? nb >> 1 : (nb + 1) >> 1;
+  const int wrow0 = 32 * rb0;
+
+  v16f_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) acc[i][p] = v16f_t{};
+
+  auto main_loop = [&](auto nact_c) {
+    constexpr int NACT = decltype(nact_c)::value;
+    issue(0);
+    if (nst > 1) issue(1);
+    for (int st = 0; st < nst; ++st) {
+      if (st + 1 < nst) PF_WAIT_VM(NCOP); else PF_WAIT_VM(0);
+      __syncthreads();
+      if (st + 2 < nst) issue(st + 2);
+      if constexpr (NACT > 0) {
+        const uint8_t* sl = p16_lds + (st % 3) * kP16Slot;
+        const int h = st & 1;
+        uint4 bw[4];
+        float bscl[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          bw[p] = *reinterpret_cast<const uint4*>(sl + b_off[p]);
+          const uint32_t sb = (*reinterpret_cast<const uint32_t*>(sl + bs_off[p]) >> (bs_sh[p] + (CANON ? 16 * h : 0))) & 0xFFu;
+          bscl[p] = __uint_as_float(sb ? sb << 23 : 0x00400000u);   // 2^(sb-127)
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v8bf16 av[NACT];
+#pragma unroll
+          for (int i = 0; i < NACT; ++i) {
+            const int row = wrow0 + 32 * i + l32;
+            av[i] = *reinterpret_cast<const v8bf16*>(sl + kP16A + row * 128 + 16 * ((4 * kh + q) ^ ((row >> 1) & 7)));
+          }
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t w = q == 0 ? bw[p].x : q == 1 ? bw[p].y : q == 2 ? bw[p].z : bw[p].w;
+            const v2bf16 e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bscl[p], 0);
+            const v2bf16 e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bscl[p], 1);
+            const v2bf16 e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bscl[p], 2);
+            const v2bf16 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bscl[p], 3);
+            const v8bf16 bv = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+#pragma unroll
+            for (int i = 0; i < NACT; ++i)
+              acc[i][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv, acc[i][p], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+  switch (nact) {
+    case 4: main_loop(IntC<4>{}); break;
+    case 3: main_loop(IntC<3>{}); break;
+    case 2: main_loop(IntC<2>{}); break;
+    case 1: main_loop(IntC<1>{}); break;
+    default: main_loop(IntC<0>{}); break;
+  }
+  // every copy has landed (the workgroup's LDS is free once the last waves exit)
+  PF_WAIT_VM(0);
+  if (nact == 0 || !cols_live) return;
+
+  // epilogue from the accumulators: register r of acc[i][p] is tile row
+  // wrow0 + 32i + 8(r/4) + 4 kh + r%4, column l32 of fragment p
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= nact) break;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rl = wrow0 + 32 * i + 8 * (r / 4) + 4 * kh + (r % 4);
+      if (rl >= nrows) continue;
+      const int64_t row = tile.row_begin + rl;
+      if (GU) {
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int col = c0 + 64 * wn + 32 * pp + l32;
+          const float g = acc[i][pp][r], u = acc[i][pp + 2][r];
+          a.h16[row * a.dff + col] = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
+          if (a.gu_acc) {
+            a.gu_acc[row * 2 * a.dff + col] = g;
+            a.gu_acc[row * 2 * a.dff + a.dff + col] = u;
+          }
+        }
+      } else {
+        const int64_t dst = routed ? a.row_src[row] : row;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          a.o16[dst * a.d + c0 + 128 * wn + 32 * p + l32] = f32_to_bf16_rne(acc[i][p][r]);
+      }
+    }
+  }
+}
+
+template <bool GU>
+static hipError_t launch_pf16(const FwdArgs& a, hipStream_t st) {
+  const int64_t N = GU ? a.dff / 128 : (a.d + 255) / 256;
+  const int64_t max_groups = (int64_t(a.max_tiles) + kPfGroupTiles - 1) / kPfGroupTiles;
+  const int64_t per_xcd = (max_groups + 7) / 8 * kPfGroupTiles * N;
+  const dim3 grid(static_cast<unsigned>(8 * per_xcd));
+  if (a.wcanon)
+    hipLaunchKernelGGL((k_gemm_pf16<GU, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm_pf16<GU, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // The routing launch of a few tokens: top-k and permutation in workgroup 0,
 // the shared experts' gate_up items in the others (PH = 1).
 hipError_t launch_topk_shared_gate_up(const FwdArgs& a, hipStream_t st) {
@@ -1258,11 +1498,13 @@ hipError_t launch_topk_shared_gate_up(const FwdArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm_gate_up(const FwdArgs& a, hipStream_t st) {
   if (a.bm <= kDecodeMaxRows) return launch_stream<true>(a, st);
+  if (a.a16) return launch_pf16<true>(a, st);
   return launch_pf<true>(a, st);
 }
 
 hipError_t launch_gemm_down(const FwdArgs& a, hipStream_t st) {
   if (a.bm <= kDecodeMaxRows) return launch_stream<false>(a, st);
+  if (a.a16) return launch_pf16<false>(a, st);
   return launch_pf<false>(a, st);
 }
 

@@ -274,21 +274,21 @@ def test_latent_tail_host_checks(M):
 
 
 def test_a16w4_host_checks(M):
-    # bf16 activations: the streaming kernels only (below 24 rows per expert
-    # on average), no MXFP8 taps, h through its own bf16 tap
+    # bf16 activations: no MXFP8 taps, at decode and prefill sizes; h through
+    # its own bf16 tap
     fake = 1 << 20
     W = M.MoeWeights(fake, fake, fake, fake, fake, fake, fake, fake, fake, None, M.MOE_WEIGHTS_PACKED)
     p = M.moe_plan(256, 128, 16, 2, 1, 1024, M.MOE_FLAG_A16W4)
     p8 = M.moe_plan(256, 128, 16, 2, 1, 1024)
     try:
         ws = M.moe_workspace_bytes(p, 1024)
-        with pytest.raises(M.MoeError) as ei:  # 192 tokens x 2 / 16 = 24 rows per expert
-            M.moe_forward(p, W, fake, 192, fake, fake, ws)
-        assert ei.value.status == M.MOE_ERR_UNSUPPORTED and "A16W4" in ei.value.detail
-        for name in ("x_codes", "x_scales", "h_codes", "h_scales"):
-            with pytest.raises(M.MoeError) as ei:
-                M.moe_forward(p, W, fake, 8, fake, fake, ws, M.MoeTaps(**{name: fake}))
-            assert ei.value.status == M.MOE_ERR_INVALID_ARG
+        # 8 tokens: the streaming kernels; 192 x 2 / 16 = 24 rows per expert:
+        # the 256-row tiles
+        for T in (8, 192):
+            for name in ("x_codes", "x_scales", "h_codes", "h_scales"):
+                with pytest.raises(M.MoeError) as ei:
+                    M.moe_forward(p, W, fake, T, fake, fake, ws, M.MoeTaps(**{name: fake}))
+                assert ei.value.status == M.MOE_ERR_INVALID_ARG and "A16W4" in ei.value.detail
         with pytest.raises(M.MoeError) as ei:
             M.moe_forward(p8, W, fake, 8, fake, fake, M.moe_workspace_bytes(p8, 8), M.MoeTaps(h_bf16=fake))
         assert ei.value.status == M.MOE_ERR_INVALID_ARG

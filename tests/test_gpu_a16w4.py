@@ -3,7 +3,9 @@ the C ABI against the oracle's A16W4 layer: the gate/up accumulators bit for
 bit in the exact-arithmetic regime (the bf16 MFMA on weights expanded from
 FP4 in registers), the whole layer with the parity rules on the streaming
 kernels' shapes (K split and whole items, ragged token counts, top-20, five
-shared experts, the Zipf bias), and the full-size decode workloads."""
+shared experts, the Zipf bias) and on the 256-row prefill tiles (ragged
+last tiles, several tiles per expert, a d_model that ends on half a column
+block); the full-size workloads are in the full-layer tests."""
 
 import numpy as np
 import pytest
@@ -40,6 +42,13 @@ EXACT = [
     # at most four tokens: four-row activation slots, seven-slot ring
     ("four_row_slots", 3, 256, 128, 8, 2, None),
     ("four_row_slots_wide_scales", 4, 256, 128, 8, 3, (122, 132)),
+    # from 24 rows per expert on average: 256-row tiles on the bf16 MFMA
+    ("prefill_tiles", 300, 256, 128, 8, 2, None),
+    ("prefill_tiles_wide_scales", 300, 256, 256, 8, 2, (122, 132)),
+    ("prefill_k1024", 200, 1024, 512, 4, 2, None),
+    # 600 rows per shared expert (tiles of 256, 256, 88); d_model 384: the
+    # last down column block is half a block
+    ("prefill_d384_shared_tiles", 600, 384, 256, 8, 2, None),
 ]
 
 
@@ -116,6 +125,21 @@ def test_a16w4_top_20_and_five_shared():
 def test_a16w4_zipf_bias():
     _case(I.LayerConfig("a16_skew", 300, 512, 64, 4, 256, 2, zipf_bias=True, seed=122),
           tokens=list(range(0, 300, 7)) + [299])
+
+
+@pytest.mark.parametrize("cfg", [
+    I.LayerConfig("a16_prefill", 700, 512, 16, 2, 256, 1, seed=130),
+    I.LayerConfig("a16_prefill_d384", 400, 384, 8, 2, 256, 2, seed=131),
+    I.LayerConfig("a16_prefill_k1024", 260, 1024, 8, 3, 512, 1, seed=132),
+], ids=["d512", "d384_two_shared", "d1024"])
+def test_a16w4_prefill(cfg):
+    _case(cfg)
+
+
+def test_a16w4_prefill_zipf_bias():
+    # 128 rows per expert on average, skewed: one to many tiles per expert
+    _case(I.LayerConfig("a16_skew_prefill", 2048, 512, 64, 4, 256, 2, zipf_bias=True, seed=133),
+          tokens=list(range(0, 2048, 23)) + [2047])
 
 
 def test_a16w4_differs_from_a8w4_and_is_deterministic():

@@ -45,6 +45,8 @@ CASES = [
     ("a16w4_stream", 200, 512, 256, 64, 4, 1, True),
     ("a16w4_whole_items_wide_down", 2048, 512, 512, 1024, 8, 1, True),
     ("a16w4_phases_wide_items", 32, 512, 2048, 256, 16, 1, True),
+    ("a16w4_prefill", 300, 1024, 512, 8, 2, 2, True),
+    ("a16w4_prefill_d384", 300, 384, 128, 8, 2, 1, True),
 ]
 
 

@@ -87,7 +87,9 @@ def pick_tokens(cfg, offsets: np.ndarray, row_src: np.ndarray, n: int):
     ("prefill32k_skew", 32, False),
     ("decode1", 1, True),
     ("decode256", 12, True),
-], ids=["decode1", "decode256", "prefill8k", "prefill32k_skew", "decode1_a16w4", "decode256_a16w4"])
+    ("prefill8k", 32, True),
+], ids=["decode1", "decode256", "prefill8k", "prefill32k_skew", "decode1_a16w4", "decode256_a16w4",
+        "prefill8k_a16w4"])
 def test_full_layer(big, name, nsample, a16):
     P, W, ref = big
     cfg = I.CONFIGS[name]
