@@ -1266,9 +1266,10 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
 // and the MFMAs.  MFMA slice q of a step takes, in lane (row or column l%32,
 // half kh = l/32), the 8 values 32 kh + 8q .. +7 of the step: four
 // consecutive bytes of the lane's 16-byte weight fragment, and the matching
-// 16 bytes of its activation row.  The row blocks of a tile are split
-// between the two row-half waves as in k_gemm_pf.  Epilogues write h (bf16,
-// SwiGLU) or o (bf16) straight from the accumulators.
+// 16 bytes of its activation row.  The 32-row blocks of a tile are split
+// between the two row-half waves as in k_gemm_pf (an odd block shared by
+// column halves).  Epilogues write h (bf16, SwiGLU) or o (bf16) straight
+// from the accumulators.
 // ---------------------------------------------------------------------------
 constexpr int kP16Slot = 32768 + 8192 + 1024;  // A | B | B scales
 constexpr int kP16A = 0, kP16B = 32768, kP16BS = 40960;
@@ -1372,10 +1373,16 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
     bs_off[p] = kP16BS + grp * 256 + 4 * (CANON ? 16 * jb + r : 16 * kh + r);
     bs_sh[p] = CANON ? 8 * kh : 8 * jb;              // + 16 h for canonical
   }
+  // row blocks: nb / 2 whole ones per wave (the first half of the tile's
+  // blocks for wm = 0, the last for wm = 1) and, for odd nb, the middle
+  // block hb shared by both, each taking half of its weight fragments
+  // (gate_up: the gate and up fragments of h columns 32 wm .. of the wave's
+  // 64; down: output columns 64 wm .. of its 128).  Accumulator set i < nfull
+  // is block rb0 + i, set nfull the shared block.
   const int nb = (nrows + 31) >> 5;
+  const int nfull = nb >> 1, hb = nb >> 1;
   const int rb0 = wm ? (nb + 1) >> 1 : 0;
-  const int nact = wm ? nb >> 1 : (nb + 1) >> 1;
-  const int wrow0 = 32 * rb0;
+  auto half_frag = [&](int p) -> bool { return GU ? (p & 1) == wm : (p >> 1) == wm; };
 
   v16f_t acc[4][4];
 #pragma unroll
@@ -1383,15 +1390,17 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[i][p] = v16f_t{};
 
-  auto main_loop = [&](auto nact_c) {
+  auto main_loop = [&](auto nact_c, auto half_c) {
     constexpr int NACT = decltype(nact_c)::value;
+    constexpr bool HALF = decltype(half_c)::value != 0;
+    constexpr int NSET = NACT + (HALF ? 1 : 0);   // accumulator sets in use
     issue(0);
     if (nst > 1) issue(1);
     for (int st = 0; st < nst; ++st) {
       if (st + 1 < nst) PF_WAIT_VM(NCOP); else PF_WAIT_VM(0);
       __syncthreads();
       if (st + 2 < nst) issue(st + 2);
-      if constexpr (NACT > 0) {
+      if constexpr (NSET > 0) {
         const uint8_t* sl = p16_lds + (st % 3) * kP16Slot;
         const int h = st & 1;
         uint4 bw[4];
@@ -1404,10 +1413,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          v8bf16 av[NACT];
+          v8bf16 av[NSET];
 #pragma unroll
-          for (int i = 0; i < NACT; ++i) {
-            const int row = wrow0 + 32 * i + l32;
+          for (int i = 0; i < NSET; ++i) {
+            const int row = 32 * (i < NACT ? rb0 + i : hb) + l32;
             av[i] = *reinterpret_cast<const v8bf16*>(sl + kP16A + row * 128 + 16 * ((4 * kh + q) ^ ((row >> 1) & 7)));
           }
 #pragma unroll
@@ -1421,35 +1430,45 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
 #pragma unroll
             for (int i = 0; i < NACT; ++i)
               acc[i][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv, acc[i][p], 0, 0, 0);
+            if (HALF && half_frag(p))
+              acc[NSET - 1][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[NSET - 1], bv, acc[NSET - 1][p], 0, 0, 0);
           }
         }
       }
     }
   };
-  switch (nact) {
-    case 4: main_loop(IntC<4>{}); break;
-    case 3: main_loop(IntC<3>{}); break;
-    case 2: main_loop(IntC<2>{}); break;
-    case 1: main_loop(IntC<1>{}); break;
-    default: main_loop(IntC<0>{}); break;
+  switch (nb) {
+    case 8: main_loop(IntC<4>{}, IntC<0>{}); break;
+    case 7: main_loop(IntC<3>{}, IntC<1>{}); break;
+    case 6: main_loop(IntC<3>{}, IntC<0>{}); break;
+    case 5: main_loop(IntC<2>{}, IntC<1>{}); break;
+    case 4: main_loop(IntC<2>{}, IntC<0>{}); break;
+    case 3: main_loop(IntC<1>{}, IntC<1>{}); break;
+    case 2: main_loop(IntC<1>{}, IntC<0>{}); break;
+    case 1: main_loop(IntC<0>{}, IntC<1>{}); break;
+    default: main_loop(IntC<0>{}, IntC<0>{}); break;
   }
   // every copy has landed (the workgroup's LDS is free once the last waves exit)
   PF_WAIT_VM(0);
-  if (nact == 0 || !cols_live) return;
+  const int nset = nfull + (nb & 1);
+  if (nset == 0 || !cols_live) return;
 
   // epilogue from the accumulators: register r of acc[i][p] is tile row
-  // wrow0 + 32i + 8(r/4) + 4 kh + r%4, column l32 of fragment p
+  // 32 rb(i) + 8(r/4) + 4 kh + r%4, column l32 of fragment p
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (i >= nact) break;
+    if (i >= nset) break;
+    const bool shared_blk = i == nfull;
+    const int rbase = 32 * (shared_blk ? hb : rb0 + i);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rl = wrow0 + 32 * i + 8 * (r / 4) + 4 * kh + (r % 4);
+      const int rl = rbase + 8 * (r / 4) + 4 * kh + (r % 4);
       if (rl >= nrows) continue;
       const int64_t row = tile.row_begin + rl;
       if (GU) {
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
+          if (shared_blk && !half_frag(pp)) continue;
           const int col = c0 + 64 * wn + 32 * pp + l32;
           const float g = acc[i][pp][r], u = acc[i][pp + 2][r];
           a.h16[row * a.dff + col] = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
@@ -1462,7 +1481,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
         const int64_t dst = routed ? a.row_src[row] : row;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-          a.o16[dst * a.d + c0 + 128 * wn + 32 * p + l32] = f32_to_bf16_rne(acc[i][p][r]);
+          if (!shared_blk || half_frag(p))
+            a.o16[dst * a.d + c0 + 128 * wn + 32 * p + l32] = f32_to_bf16_rne(acc[i][p][r]);
       }
     }
   }
