@@ -1342,17 +1342,21 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
       CANON ? ws + ((GU ? 32 * gw : 64 * gw) + canon_row_off<GU>(lane >> 4, a.dff) + (lane & 15)) * (K / 32)
             : ws + gw * ns128 * 256 + 4 * (lane & 31);
   const uint32_t lds0 = lds_addr(p16_lds);
-  auto issue = [&](int st) {
+  // copy c (0-10) of step st: activations (c < 8), weights (8, 9), weight
+  // scales (10).  Steps past K re-read the last step into a slot that is not
+  // read again, so that every step issues the same eleven copies and every
+  // wait on them is a constant.
+  auto issue_one = [&](int st, auto cc) {
+    constexpr int c = decltype(cc)::value;
+    const int ss = st < nst ? st : nst - 1;
     const uint32_t slot = lds0 + (st % 3) * kP16Slot;
-    const int h = st & 1, s128 = st >> 1;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) lds_copy16(a_src[q] + 128 * int64_t(st), slot + kP16A + (64 * wu + 8 * q) * 128);
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint8_t* src = CANON ? b_src[c] + 32 * int64_t(st) : b_src[c] + int64_t(s128) * 4096 + 512 * h;
-      lds_copy16(src, slot + kP16B + wu * 2048 + c * 1024);
-    }
-    if (CANON) {
+    const int h = ss & 1, s128 = ss >> 1;
+    if constexpr (c < 8) {
+      lds_copy16(a_src[c] + 128 * int64_t(ss), slot + kP16A + (64 * wu + 8 * c) * 128);
+    } else if constexpr (c < 10) {
+      const uint8_t* src = CANON ? b_src[c - 8] + 32 * int64_t(ss) : b_src[c - 8] + int64_t(s128) * 4096 + 512 * h;
+      lds_copy16(src, slot + kP16B + wu * 2048 + (c - 8) * 1024);
+    } else if constexpr (CANON) {
       lds_copy4(bs_src + 4 * s128, slot + kP16BS + wu * 256);
     } else {
       if (lane < 32) lds_copy4(bs_src + int64_t(s128) * 256 + 128 * h, slot + kP16BS + wu * 256);
@@ -1360,19 +1364,6 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
   };
   constexpr int NCOP = 11;
 
-  // operand offsets: weight fragment p of this wave (32 rows): 16-row chunk
-  // j0(p) of the tile's sixteen (gate_up: gate rows of h columns 32p .. of
-  // groups 2wn, 2wn+1 for p < 2, their up rows for p >= 2; down: 32 output
-  // columns each)
-  auto j0 = [&](int p) -> int { return GU ? (p < 2 ? 8 * wn + 4 * p : 8 * wn + 4 * (p - 2) + 2) : 8 * wn + 2 * p; };
-  int b_off[4], bs_off[4], bs_sh[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int jc = j0(p) + (l32 >> 4), grp = jc >> 2, jb = jc & 3, r = l32 & 15;
-    b_off[p] = kP16B + grp * 2048 + jb * 512 + 16 * (16 * kh + r);
-    bs_off[p] = kP16BS + grp * 256 + 4 * (CANON ? 16 * jb + r : 16 * kh + r);
-    bs_sh[p] = CANON ? 8 * kh : 8 * jb;              // + 16 h for canonical
-  }
   // row blocks: nb / 2 whole ones per wave (the first half of the tile's
   // blocks for wm = 0, the last for wm = 1) and, for odd nb, the middle
   // block hb shared by both, each taking half of its weight fragments
@@ -1382,7 +1373,22 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
   const int nb = (nrows + 31) >> 5;
   const int nfull = nb >> 1, hb = nb >> 1;
   const int rb0 = wm ? (nb + 1) >> 1 : 0;
-  auto half_frag = [&](int p) -> bool { return GU ? (p & 1) == wm : (p >> 1) == wm; };
+  // accumulator p holds weight fragment pc(p): numbered per wave so that the
+  // shared block's half is p = 0, 2 (gate_up) or p = 0, 1 (down) in both
+  // row-half waves
+  auto pc = [&](int p) -> int { return GU ? (((p & 1) ^ wm) | (p & 2)) : p ^ (2 * wm); };
+  // operand offsets: weight fragment f (32 rows): 16-row chunk j0(f) of the
+  // tile's sixteen (gate_up: gate rows of h columns 32f .. of groups 2wn,
+  // 2wn+1 for f < 2, their up rows for f >= 2; down: 32 output columns each)
+  auto j0 = [&](int f) -> int { return GU ? (f < 2 ? 8 * wn + 4 * f : 8 * wn + 4 * (f - 2) + 2) : 8 * wn + 2 * f; };
+  int b_off[4], bs_off[4], bs_sh[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int jc = j0(pc(p)) + (l32 >> 4), grp = jc >> 2, jb = jc & 3, r = l32 & 15;
+    b_off[p] = kP16B + grp * 2048 + jb * 512 + 16 * (16 * kh + r);
+    bs_off[p] = kP16BS + grp * 256 + 4 * (CANON ? 16 * jb + r : 16 * kh + r);
+    bs_sh[p] = CANON ? 8 * kh : 8 * jb;              // + 16 h for canonical
+  }
 
   v16f_t acc[4][4];
 #pragma unroll
@@ -1390,17 +1396,23 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) acc[i][p] = v16f_t{};
 
+  // A step: after the barrier, the weight fragments and their scales, and the
+  // activation fragments of slice 0; then per slice q the activation reads of
+  // slice q+1 go out first, and each fragment's expansion, MFMAs and one of
+  // the eleven copies of step st+2 follow in a fixed order (one scheduling
+  // region per fragment), so the copies spread over the step's MFMAs.
   auto main_loop = [&](auto nact_c, auto half_c) {
     constexpr int NACT = decltype(nact_c)::value;
     constexpr bool HALF = decltype(half_c)::value != 0;
     constexpr int NSET = NACT + (HALF ? 1 : 0);   // accumulator sets in use
-    issue(0);
-    if (nst > 1) issue(1);
+    static_for<0, NCOP>([&](auto cc) { issue_one(0, cc); });
+    static_for<0, NCOP>([&](auto cc) { issue_one(1, cc); });
     for (int st = 0; st < nst; ++st) {
-      if (st + 1 < nst) PF_WAIT_VM(NCOP); else PF_WAIT_VM(0);
+      PF_WAIT_VM(NCOP);                       // this wave's copies of step st have landed
       __syncthreads();
-      if (st + 2 < nst) issue(st + 2);
-      if constexpr (NSET > 0) {
+      if constexpr (NSET == 0) {
+        static_for<0, NCOP>([&](auto cc) { issue_one(st + 2, cc); });
+      } else {
         const uint8_t* sl = p16_lds + (st % 3) * kP16Slot;
         const int h = st & 1;
         uint4 bw[4];
@@ -1411,16 +1423,23 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
           const uint32_t sb = (*reinterpret_cast<const uint32_t*>(sl + bs_off[p]) >> (bs_sh[p] + (CANON ? 16 * h : 0))) & 0xFFu;
           bscl[p] = __uint_as_float(sb ? sb << 23 : 0x00400000u);   // 2^(sb-127)
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v8bf16 av[NSET];
+        v8bf16 av[2][NSET];
+        auto read_a = [&](auto qc) {
+          constexpr int q = decltype(qc)::value;
 #pragma unroll
           for (int i = 0; i < NSET; ++i) {
             const int row = 32 * (i < NACT ? rb0 + i : hb) + l32;
-            av[i] = *reinterpret_cast<const v8bf16*>(sl + kP16A + row * 128 + 16 * ((4 * kh + q) ^ ((row >> 1) & 7)));
+            av[q & 1][i] = *reinterpret_cast<const v8bf16*>(sl + kP16A + row * 128 + 16 * ((4 * kh + q) ^ ((row >> 1) & 7)));
           }
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
+        };
+        read_a(IntC<0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, 4>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          if constexpr (q < 3) read_a(IntC<q + 1>{});
+          __builtin_amdgcn_sched_barrier(0);
+          static_for<0, 4>([&](auto pcc) {
+            constexpr int p = decltype(pcc)::value;
             const uint32_t w = q == 0 ? bw[p].x : q == 1 ? bw[p].y : q == 2 ? bw[p].z : bw[p].w;
             const v2bf16 e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bscl[p], 0);
             const v2bf16 e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, bscl[p], 1);
@@ -1429,11 +1448,14 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
             const v8bf16 bv = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
 #pragma unroll
             for (int i = 0; i < NACT; ++i)
-              acc[i][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv, acc[i][p], 0, 0, 0);
-            if (HALF && half_frag(p))
-              acc[NSET - 1][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[NSET - 1], bv, acc[NSET - 1][p], 0, 0, 0);
-          }
-        }
+              acc[i][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[q & 1][i], bv, acc[i][p], 0, 0, 0);
+            if constexpr (HALF && (GU ? (p & 1) == 0 : p < 2))
+              acc[NACT][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[q & 1][NACT], bv, acc[NACT][p], 0, 0, 0);
+            constexpr int c = 4 * q + p - 2;       // copies in regions 2 .. 12
+            if constexpr (c >= 0 && c < NCOP) issue_one(st + 2, IntC<c>{});
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        });
       }
     }
   };
@@ -1468,8 +1490,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
       if (GU) {
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-          if (shared_blk && !half_frag(pp)) continue;
-          const int col = c0 + 64 * wn + 32 * pp + l32;
+          if (shared_blk && pp != 0) continue;
+          const int col = c0 + 64 * wn + 32 * pc(pp) + l32;
           const float g = acc[i][pp][r], u = acc[i][pp + 2][r];
           a.h16[row * a.dff + col] = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
           if (a.gu_acc) {
@@ -1481,8 +1503,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
         const int64_t dst = routed ? a.row_src[row] : row;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-          if (!shared_blk || half_frag(p))
-            a.o16[dst * a.d + c0 + 128 * wn + 32 * p + l32] = f32_to_bf16_rne(acc[i][p][r]);
+          if (!shared_blk || p < 2)
+            a.o16[dst * a.d + c0 + 128 * wn + 32 * pc(p) + l32] = f32_to_bf16_rne(acc[i][p][r]);
       }
     }
   }
