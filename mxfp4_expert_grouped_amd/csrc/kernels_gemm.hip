@@ -667,8 +667,8 @@ __shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 
 
 // Work order of the prefill GEMMs.  Items (tile, column block) run in groups
-// of kPfGroupTiles consecutive tiles (tiles are expert-major), column block
-// next and tile fastest, so the workgroups an XCD runs at once cover a few
+// of G consecutive tiles (tiles are expert-major; G is chosen by the launch),
+// column block next and tile fastest, so the workgroups an XCD runs at once cover a few
 // tiles x several column blocks: every activation window and every weight
 // window they read in the same K step is shared by several of them and comes
 // from that XCD's L2.  Whole groups are dealt to the XCDs round-robin in list
@@ -681,8 +681,7 @@ __shared__ __attribute__((aligned(1024))) uint8_t pf_lds[kPfLds];
 // ends).  The mapping needs only the tile count.  Returns false for a
 // workgroup with no item.
 constexpr int kPfGroupTiles = 4;
-template <int G = kPfGroupTiles>
-__device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int* tile_out, int* blk_out) {
+__device__ __forceinline__ bool pf_work_item(const FwdArgs& a, int nblocks, int G, int* tile_out, int* blk_out) {
   const int ntiles = *a.tile_count;
   const int ngroups = (ntiles + G - 1) / G;
   if (ngroups < 8) {
@@ -731,11 +730,11 @@ __device__ __forceinline__ void quad_transpose4(float (&v)[4], int q) {
 __device__ __forceinline__ int pf_asg_off(int w) { return (w >> 1) * kPfSlot + kPfAS + (w & 1) * 1024; }
 
 template <bool GU, bool AG, bool CANON>
-__global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
+__global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a, int group) {
   int tile_idx, nblk;
   // down with a K split: the slices of a column block are further blocks
   const int kspl = GU || a.ksplit <= 1 ? 1 : a.ksplit;
-  if (!pf_work_item(a, GU ? a.dff / 128 : ((a.d + 255) / 256) * kspl, &tile_idx, &nblk)) return;
+  if (!pf_work_item(a, GU ? a.dff / 128 : ((a.d + 255) / 256) * kspl, group, &tile_idx, &nblk)) return;
   const int kslice = nblk % kspl;
   nblk /= kspl;
   const Tile tile = a.tiles[tile_idx];
@@ -1224,20 +1223,26 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a) {
 template <bool GU>
 static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
   const int64_t N = GU ? a.dff / 128 : int64_t((a.d + 255) / 256) * (a.ksplit > 1 ? a.ksplit : 1);
+  // tile groups of four when experts have several tiles (they then share
+  // each weight window in L2); of one when experts have 256 rows or fewer
+  // on average, so most have one tile and only the activation windows are
+  // shared (prefill8k 7.70-7.72 -> 7.63-7.64 ms; at prefill32k_skew groups of
+  // one re-read the hot experts' weights: 44 against 36 GB per gate_up)
+  const int group = a.Rr < int64_t(256) * a.E ? 1 : kPfGroupTiles;
   // room for the most groups one XCD can get (the tile count is known on the
   // device only; max_tiles bounds it)
-  const int64_t max_groups = (int64_t(a.max_tiles) + kPfGroupTiles - 1) / kPfGroupTiles;
-  const int64_t per_xcd = (max_groups + 7) / 8 * kPfGroupTiles * N;
+  const int64_t max_groups = (int64_t(a.max_tiles) + group - 1) / group;
+  const int64_t per_xcd = (max_groups + 7) / 8 * group * N;
   const int K = GU ? a.d : a.dff;
   const dim3 grid(static_cast<unsigned>(8 * per_xcd));
   if (K % 512 == 0 && a.wcanon)
-    hipLaunchKernelGGL((k_gemm_pf<GU, true, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_pf<GU, true, true>), grid, dim3(256), 0, st, a, group);
   else if (K % 512 == 0)
-    hipLaunchKernelGGL((k_gemm_pf<GU, true, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_pf<GU, true, false>), grid, dim3(256), 0, st, a, group);
   else if (a.wcanon)
-    hipLaunchKernelGGL((k_gemm_pf<GU, false, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_pf<GU, false, true>), grid, dim3(256), 0, st, a, group);
   else
-    hipLaunchKernelGGL((k_gemm_pf<GU, false, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_gemm_pf<GU, false, false>), grid, dim3(256), 0, st, a, group);
   return hipGetLastError();
 }
 
@@ -1291,7 +1296,7 @@ typedef float v16f_t __attribute__((ext_vector_type(16)));
 template <bool GU, bool CANON>
 __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
   int tile_idx, nblk;
-  if (!pf_work_item<kP16GroupTiles>(a, GU ? a.dff / 128 : (a.d + 255) / 256, &tile_idx, &nblk)) return;
+  if (!pf_work_item(a, GU ? a.dff / 128 : (a.d + 255) / 256, kP16GroupTiles, &tile_idx, &nblk)) return;
   const Tile tile = a.tiles[tile_idx];
   const int lane = threadIdx.x & 63;
   const int wu = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
