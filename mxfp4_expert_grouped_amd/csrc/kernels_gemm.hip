@@ -1280,7 +1280,9 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 constexpr int kP16Slot = 32768 + 8192 + 1024;  // A | B | B scales
 constexpr int kP16A = 0, kP16B = 32768, kP16BS = 40960;
-constexpr int kP16Lds = 3 * kP16Slot;           // 125952 bytes
+// the ring (125952 bytes), reused by the epilogue's staging (four waves x 128
+// rows x 128 bf16 columns)
+constexpr int kP16Lds = 3 * kP16Slot > 4 * 128 * 128 * 2 ? 3 * kP16Slot : 4 * 128 * 128 * 2;
 // Work order: groups of one tile (all column blocks of a tile, then the
 // next), so an XCD's workgroups at any time cover two tiles of gate_up (one
 // of down) and share their bf16 activation windows through its L2.  A bf16
@@ -1485,41 +1487,99 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
     case 1: main_loop(IntC<0>{}, IntC<1>{}); break;
     default: main_loop(IntC<0>{}, IntC<0>{}); break;
   }
-  // every copy has landed (the workgroup's LDS is free once the last waves exit)
+  // every copy has landed and every wave is past its last operand read: the
+  // ring becomes the epilogue's staging area, a private region per wave
   PF_WAIT_VM(0);
+  __syncthreads();
   const int nset = nfull + (nb & 1);
   if (nset == 0 || !cols_live) return;
 
-  // epilogue from the accumulators: register r of acc[i][p] is tile row
-  // 32 rb(i) + 8(r/4) + 4 kh + r%4, column l32 of fragment p
+  // Epilogue: register r of acc[i][p] is tile row 32 rb(i) + 8(r/4) + 4 kh +
+  // r%4, column l32 of fragment pc(p); it becomes staged row 32i + .. of the
+  // wave.  The bf16 outputs (h after SwiGLU: 64 columns; o: 128 columns) are
+  // staged in LDS, then leave as 16-byte row chunks.  Staging: registers r,
+  // r+1 of a lane hold rows R, R+1 of one column; one exchange with the
+  // neighbouring lane gives the even lane row R and the odd lane row R+1, each
+  // for two adjacent columns, written as one packed dword.  A staged row's
+  // 32-column chunks are permuted by bits 0 and 2 of the row (gate_up: bit 2)
+  // so that the four rows one write instruction touches fall on distinct
+  // banks.
+  constexpr int SC = GU ? 64 : 128;                        // staged columns
+  uint16_t* os = reinterpret_cast<uint16_t*>(p16_lds) + wu * (128 * SC);
+  auto chunk_of = [](int rl, int c32) {
+    return GU ? c32 ^ ((rl >> 2) & 1) : c32 ^ ((rl & 1) | (((rl >> 2) & 1) << 1));
+  };
+  const bool odd = (lane & 1) != 0;
+  auto stage_pair = [&](int i, int r, int f, float v0, float v1) {
+    const float rv = dpp_xor1(odd ? v0 : v1);
+    const v2bf16 pk = __builtin_convertvector((v2f){odd ? rv : v0, odd ? v1 : rv}, v2bf16);
+    const int rl = 32 * i + 8 * (r / 4) + 4 * kh + (r % 4) + (odd ? 1 : 0);
+    *reinterpret_cast<uint32_t*>(os + rl * SC + chunk_of(rl, f) * 32 + (l32 & ~1)) = __builtin_bit_cast(uint32_t, pk);
+  };
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i >= nset) break;
     const bool shared_blk = i == nfull;
-    const int rbase = 32 * (shared_blk ? hb : rb0 + i);
+    if (GU) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rl = rbase + 8 * (r / 4) + 4 * kh + (r % 4);
-      if (rl >= nrows) continue;
-      const int64_t row = tile.row_begin + rl;
-      if (GU) {
+      for (int pp = 0; pp < 2; ++pp) {
+        if (shared_blk && pp != 0) continue;
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          if (shared_blk && pp != 0) continue;
-          const int col = c0 + 64 * wn + 32 * pc(pp) + l32;
-          const float g = acc[i][pp][r], u = acc[i][pp + 2][r];
-          a.h16[row * a.dff + col] = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
-          if (a.gu_acc) {
-            a.gu_acc[row * 2 * a.dff + col] = g;
-            a.gu_acc[row * 2 * a.dff + a.dff + col] = u;
+        for (int r = 0; r < 16; r += 2) {
+          const float g0 = acc[i][pp][r], u0 = acc[i][pp + 2][r];
+          const float g1 = acc[i][pp][r + 1], u1 = acc[i][pp + 2][r + 1];
+          stage_pair(i, r, pc(pp), g0 / (1.0f + __expf(-g0)) * u0, g1 / (1.0f + __expf(-g1)) * u1);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if (shared_blk && p >= 2) continue;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) stage_pair(i, r, pc(p), acc[i][p][r], acc[i][p][r + 1]);
+      }
+    }
+  }
+  // (the optional accumulator tap straight from the registers)
+  if (GU && a.gu_acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nset) break;
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        if (i == nfull && pp != 0) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = 32 * (i < nfull ? rb0 + i : hb) + 8 * (r / 4) + 4 * kh + (r % 4);
+          if (rl < nrows) {
+            const int64_t row = tile.row_begin + rl;
+            const int col = c0 + 64 * wn + 32 * pc(pp) + l32;
+            a.gu_acc[row * 2 * a.dff + col] = acc[i][pp][r];
+            a.gu_acc[row * 2 * a.dff + a.dff + col] = acc[i][pp + 2][r];
           }
         }
+      }
+    }
+  }
+  // stores: a wave's staged rows in 16-byte chunks, SC / 8 chunks per row;
+  // the shared block's rows hold columns 32 wm .. (gate_up) or 64 wm ..
+  // (down) of the wave's only
+  constexpr int CPR = SC / 8;                              // chunks per row
+#pragma unroll 4
+  for (int q = 0; q < 128 * CPR / 64; ++q) {
+    const int ch = q * 64 + lane;
+    const int rl = ch / CPR, cc = 8 * (ch % CPR);
+    const int ib = rl >> 5;
+    const int trow = 32 * (ib < nfull ? rb0 + ib : hb) + (rl & 31);   // tile row
+    const bool col_ok = ib != nfull || (GU ? (cc >> 5) == wm : (cc >> 6) == wm);
+    if (ib < nset && trow < nrows && col_ok) {
+      const uint4 t = *reinterpret_cast<const uint4*>(os + rl * SC + chunk_of(rl, cc >> 5) * 32 + (cc & 31));
+      const int64_t row = tile.row_begin + trow;
+      if (GU) {
+        *reinterpret_cast<uint4*>(a.h16 + row * a.dff + c0 + 64 * wn + cc) = t;
       } else {
         const int64_t dst = routed ? a.row_src[row] : row;
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          if (!shared_blk || p < 2)
-            a.o16[dst * a.d + c0 + 128 * wn + 32 * pc(p) + l32] = f32_to_bf16_rne(acc[i][p][r]);
+        *reinterpret_cast<uint4*>(a.o16 + dst * a.d + c0 + 128 * wn + cc) = t;
       }
     }
   }
