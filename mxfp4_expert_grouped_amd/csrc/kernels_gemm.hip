@@ -1268,15 +1268,15 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
 // tile's end read its first row), packed group w's weights (two copies) and
 // their scales (one): eleven copies per step.  Per step each wave waits for
 // its own copies of the step, then a barrier (every wave's copies have
-// landed, every wave is done with the slot of the step before), then the
-// copies of step st+2 go to that slot, then the LDS reads, the expansion
-// and the MFMAs.  MFMA slice q of a step takes, in lane (row or column l%32,
-// half kh = l/32), the 8 values 32 kh + 8q .. +7 of the step: four
-// consecutive bytes of the lane's 16-byte weight fragment, and the matching
-// 16 bytes of its activation row.  The 32-row blocks of a tile are split
-// between the two row-half waves as in k_gemm_pf (an odd block shared by
-// column halves).  Epilogues write h (bf16, SwiGLU) or o (bf16) straight
-// from the accumulators.
+// landed, every wave is done with the slot of the step before); the LDS
+// reads, the expansion and the MFMAs follow, with the copies of step st+2
+// (into that slot) spread between them.  MFMA slice q of a step takes, in
+// lane (row or column l%32, half kh = l/32), the 8 values 32 kh + 8q .. +7
+// of the step: four consecutive bytes of the lane's 16-byte weight
+// fragment, and the matching 16 bytes of its activation row.  The 32-row
+// blocks of a tile are split evenly between the two row-half waves (an odd
+// block shared by column halves).  The epilogues stage bf16 h (SwiGLU) or
+// o in LDS and store 16-byte row chunks.
 // ---------------------------------------------------------------------------
 constexpr int kP16Slot = 32768 + 8192 + 1024;  // A | B | B scales
 constexpr int kP16A = 0, kP16B = 32768, kP16BS = 40960;
