@@ -339,17 +339,21 @@ def test_deterministic_and_workspace_independent():
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
-@pytest.mark.parametrize("T", [1, 40])
-def test_graph_replay_matches_eager(T):
+@pytest.mark.parametrize("T,a16", [(1, False), (40, False), (300, False), (3, True), (300, True)],
+                         ids=["T1", "T40", "T300_prefill", "T3_a16w4", "T300_prefill_a16w4"])
+def test_graph_replay_matches_eager(T, a16):
     # a captured forward (T = 1: few-token router with the fused x
     # quantisation and the one-workgroup top-k/permutation; T = 40: MFMA
-    # router, top-k launch, permutation launch) replays several times, with
-    # eager forwards of other inputs in between, and every replay equals the
-    # eager result bit for bit
+    # router, top-k launch, permutation launch; T = 300: 37.5 rows per expert,
+    # the 256-row prefill kernels; the A16W4 variant at a few tokens and at
+    # prefill size) replays several times, with eager forwards of other
+    # inputs in between, and every replay equals the eager result bit for bit
+    from mxfp4_expert_grouped_amd import mxmoe as M
     from mxfp4_expert_grouped_amd.layer import MoeLayer
-    cfg = I.LayerConfig("graph", T, 256, 16, 2, 128, 2, seed=20 + T)
+    cfg = I.LayerConfig("graph", T, 256, 16, 2, 128, 2, seed=20 + T + (7 if a16 else 0))
     W = P.IG.device_weights(cfg)
-    layer = MoeLayer(cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k, cfg.num_shared, T, W)
+    layer = MoeLayer(cfg.d_model, cfg.d_ff, cfg.num_experts, cfg.top_k, cfg.num_shared, T, W,
+                     flags=M.MOE_FLAG_A16W4 if a16 else 0)
     xs = [P.IG.device_x(cfg, layer=i) for i in range(2)]
     ws = torch.empty(layer.workspace_bytes(T), dtype=torch.uint8, device="cuda")
     refs = [layer.forward(x, workspace=ws).clone() for x in xs]
