@@ -1264,9 +1264,10 @@ static hipError_t launch_pf(const FwdArgs& a, hipStream_t st) {
 //     this half (lane 16g'+r, byte = block); canonical: a dword per row
 //     (lane 16 block + r) holding the scales of the row's four K groups of
 //     the 128-wide step, of which this half uses bytes 2h, 2h+1.
-// Wave w copies 64 activation rows (eight 8-row copies; rows past the
-// tile's end read its first row), packed group w's weights (two copies) and
-// their scales (one): eleven copies per step.  Per step each wave waits for
+// Wave w copies the 8-row activation groups w, w+4, .. of the tile's nb
+// 32-row blocks (nb copies; rows past the tile's end read its first row),
+// packed group w's weights (two copies) and their scales (one): nb + 3
+// copies per step.  Per step each wave waits for
 // its own copies of the step, then a barrier (every wave's copies have
 // landed, every wave is done with the slot of the step before); the LDS
 // reads, the expansion and the MFMAs follow, with the copies of step st+2
@@ -1327,14 +1328,16 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
   const bool routed = tile.row_begin < a.Rr;
   const int nrows = tile.row_end - tile.row_begin;
 
-  // activation source rows of this wave's copies (rows past the end read the
-  // tile's first row): gate_up x rows (routed: through row -> token), down h
-  // rows (contiguous)
+  // activation source rows of this wave's copies: copy j moves the 8-row
+  // group wu + 4j (rows past the tile's end read its first row), and a tile of
+  // nb 32-row blocks takes copies j < nb, so the four waves copy exactly its
+  // 4 nb groups; gate_up x rows (routed: through row -> token), down h rows
+  // (contiguous)
   const uint16_t* act = GU ? a.x : a.h16;
   const uint8_t* a_src[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const int rl = 64 * wu + 8 * q + (lane >> 3);
+    const int rl = 8 * wu + 32 * q + (lane >> 3);
     const int row = tile.row_begin + (rl < nrows ? rl : 0);
     int64_t srow = row;
     if (GU) srow = routed ? a.row_token[row] : row - a.Rr - int64_t(sidx) * a.T;
@@ -1359,27 +1362,26 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
       CANON ? ws + ((GU ? 32 * gw : 64 * gw) + canon_row_off<GU>(lane >> 4, a.dff) + (lane & 15)) * (K / 32)
             : ws + gw * ns128 * 256 + 4 * (lane & 31);
   const uint32_t lds0 = lds_addr(p16_lds);
-  // copy c (0-10) of step st: activations (c < 8), weights (8, 9), weight
-  // scales (10).  Steps past K re-read the last step into a slot that is not
-  // read again, so that every step issues the same eleven copies and every
-  // wait on them is a constant.
-  auto issue_one = [&](int st, auto cc) {
-    constexpr int c = decltype(cc)::value;
+  // copy c of step st for a tile of NB row blocks: activations (c < NB),
+  // weights (NB, NB+1), weight scales (NB+2).  Steps past K re-read the last
+  // step into a slot that is not read again, so that every step issues the
+  // same NB + 3 copies and every wait on them is a constant.
+  auto issue_one = [&](int st, auto cc, auto nbc) {
+    constexpr int c = decltype(cc)::value, NB = decltype(nbc)::value;
     const int ss = st < nst ? st : nst - 1;
     const uint32_t slot = lds0 + (st % 3) * kP16Slot;
     const int h = ss & 1, s128 = ss >> 1;
-    if constexpr (c < 8) {
-      lds_copy16(a_src[c] + 128 * int64_t(ss), slot + kP16A + (64 * wu + 8 * c) * 128);
-    } else if constexpr (c < 10) {
-      const uint8_t* src = CANON ? b_src[c - 8] + 32 * int64_t(ss) : b_src[c - 8] + int64_t(s128) * 4096 + 512 * h;
-      lds_copy16(src, slot + kP16B + wu * 2048 + (c - 8) * 1024);
+    if constexpr (c < NB) {
+      lds_copy16(a_src[c] + 128 * int64_t(ss), slot + kP16A + (8 * wu + 32 * c) * 128);
+    } else if constexpr (c < NB + 2) {
+      const uint8_t* src = CANON ? b_src[c - NB] + 32 * int64_t(ss) : b_src[c - NB] + int64_t(s128) * 4096 + 512 * h;
+      lds_copy16(src, slot + kP16B + wu * 2048 + (c - NB) * 1024);
     } else if constexpr (CANON) {
       lds_copy4(bs_src + 4 * s128, slot + kP16BS + wu * 256);
     } else {
       if (lane < 32) lds_copy4(bs_src + int64_t(s128) * 256 + 128 * h, slot + kP16BS + wu * 256);
     }
   };
-  constexpr int NCOP = 11;
 
   // row blocks: nb / 2 whole ones per wave (the first half of the tile's
   // blocks for wm = 0, the last for wm = 1) and, for odd nb, the middle
@@ -1422,13 +1424,15 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
     constexpr int NACT = decltype(nact_c)::value;
     constexpr bool HALF = decltype(half_c)::value != 0;
     constexpr int NSET = NACT + (HALF ? 1 : 0);   // accumulator sets in use
-    static_for<0, NCOP>([&](auto cc) { issue_one(0, cc); });
-    static_for<0, NCOP>([&](auto cc) { issue_one(1, cc); });
+    constexpr int NB = 2 * NACT + (HALF ? 1 : 0);  // the tile's row blocks
+    constexpr int NCOP = NB + 3;                   // copies per wave and step
+    static_for<0, NCOP>([&](auto cc) { issue_one(0, cc, IntC<NB>{}); });
+    static_for<0, NCOP>([&](auto cc) { issue_one(1, cc, IntC<NB>{}); });
     for (int st = 0; st < nst; ++st) {
       PF_WAIT_VM(NCOP);                       // this wave's copies of step st have landed
       __syncthreads();
       if constexpr (NSET == 0) {
-        static_for<0, NCOP>([&](auto cc) { issue_one(st + 2, cc); });
+        static_for<0, NCOP>([&](auto cc) { issue_one(st + 2, cc, IntC<NB>{}); });
       } else {
         const uint8_t* sl = p16_lds + (st % 3) * kP16Slot;
         const int h = st & 1;
@@ -1468,8 +1472,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf16(FwdArgs a) {
               acc[i][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[q & 1][i], bv, acc[i][p], 0, 0, 0);
             if constexpr (HALF && (GU ? (p & 1) == 0 : p < 2))
               acc[NACT][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[q & 1][NACT], bv, acc[NACT][p], 0, 0, 0);
-            constexpr int c = 4 * q + p - 2;       // copies in regions 2 .. 12
-            if constexpr (c >= 0 && c < NCOP) issue_one(st + 2, IntC<c>{});
+            constexpr int c = 4 * q + p - 2;       // copies in regions 2 .. NCOP + 1
+            if constexpr (c >= 0 && c < NCOP) issue_one(st + 2, IntC<c>{}, IntC<NB>{});
             __builtin_amdgcn_sched_barrier(0);
           });
         });
