@@ -283,6 +283,15 @@ def test_prefill_tiles_over_many_groups():
     _layer_case(cfg, tokens=list(range(0, 2048, 37)) + [2047])
 
 
+def test_router_many_token_and_expert_tiles():
+    # the MFMA router without a K split over 157 token tiles (the last
+    # ragged) x 8 expert tiles of 1024 experts: logits of every token within
+    # 1e-4 of the oracle, routing bit-exact up to near-ties, the layer on a
+    # token sample
+    cfg = I.LayerConfig("router_tiles", 20000, 256, 1024, 8, 128, 1, seed=71)
+    _layer_case(cfg, tokens=list(range(0, 20000, 499)) + [255, 256, 19999])
+
+
 @pytest.mark.parametrize("T", [5, 300])
 def test_more_than_two_shared_experts(T):
     # the combine reads up to eight shared rows per token once S > 2; both
