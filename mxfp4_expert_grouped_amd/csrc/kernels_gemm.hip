@@ -788,16 +788,26 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a, int group) {
     return GU ? row - a.Rr - sidx * a.T : row;
   };
 
-  // ---- copy sources of this wave.  A copy q covers rows 64wu + 8q .. +7:
-  // lane l reads chunk (l%8) ^ swz(row) of row 64wu + 8q + l/8 and lands at
-  // LDS row*128 + 16(l%8).  (Set once the rows are known: every row this
-  // wave looks up is one it copied into the row table itself.)
+  // the tile's 32-row blocks split evenly between the two row halves (a
+  // step lasts as long as its busiest wave): wave half wm takes blocks
+  // rb0 .. rb0 + nact - 1
+  const int nb = (tile.row_end - tile.row_begin + 31) >> 5;
+  const int rb0 = wm ? (nb + 1) >> 1 : 0;
+  const int nact = wm ? nb >> 1 : (nb + 1) >> 1;                        // active row blocks
+  // ---- copy sources of this wave.  The two waves of a row half copy the
+  // activation rows of its nact blocks between them: copy q of wave (wm, wn)
+  // covers the 8-row group ag(q) = 4 rb0 + 2q + wn (q < 2 nact); lane l
+  // reads chunk (l%8) ^ swz(row) of row 8 ag(q) + l/8 and lands at LDS
+  // row*128 + 16(l%8).  (Set once the rows are known: for gate_up after a
+  // barrier that follows every wave's wait for its own row-table copy, as a
+  // wave looks up rows that another wave copied.)
+  auto ag = [&](int q) -> int { return 4 * rb0 + 2 * q + wn; };
   const uint8_t* a_src[8];
   const uint8_t* as_src = nullptr;
   auto set_act_sources = [&]() {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int rl = 64 * wu + 8 * q + (lane >> 3);
+      const int rl = 8 * ag(q) + (lane >> 3);
       a_src[q] = (GU ? a.x_codes : a.h_codes) + src_row(rl) * K + 128 * k0 + 16 * ((lane & 7) ^ ((rl >> 1) & 7));
     }
     as_src = (GU ? a.x_scales : a.h_scales) + src_row(64 * wu + lane) * (K / 32) + (AG ? 16 * (k0 / 4) : 4 * k0);
@@ -824,13 +834,14 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a, int group) {
   // an 8-row copy past the tile's end reads the tile's first row, and a step
   // past K re-reads step 0 into a slot that is not read again -- so that every
   // wait on them is a constant and a step has no branches.  They come in two
-  // parts: the 8 activation copies (copy_a) and the weights, weight scales
-  // and activation scales (copy_w, items 0-5).
-  constexpr auto ncop = [](int st) -> int { return 13 + (AG ? ((st & 3) == 0 ? 1 : 0) : 1); };
+  // parts: the 2 nact activation copies (copy_a) and the weights, weight
+  // scales and activation scales (copy_w, items 0-5).  ncop(NA, st): the
+  // copies of step st for NA activation copies.
+  constexpr auto ncop = [](int na, int st) -> int { return na + 5 + (AG ? ((st & 3) == 0 ? 1 : 0) : 1); };
   auto copy_a = [&](int st, auto qc) {
     constexpr int q = decltype(qc)::value;
     const int ss = st < nsteps ? st : 0;
-    lds_copy16(a_src[q] + 128 * ss, lds0 + (st % 3) * kPfSlot + kPfA + (64 * wu + 8 * q) * 128);
+    lds_copy16(a_src[q] + 128 * ss, lds0 + (st % 3) * kPfSlot + kPfA + (8 * ag(q)) * 128);
   };
   // item m of step st; GS: st starts a group of four steps
   // WNT: the weights are read by this tile only (its expert has one tile),
@@ -867,12 +878,6 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a, int group) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) a_lane[h][c] = l32 * 128 + 16 * ((4 * h + 2 * c + g32) ^ ((l32 >> 1) & 7));
   const int bs_lane = 4 * (16 * g32 + (lane & 15)) + (2 * wn) * 256;  // + 256*group + 128h
-  // the tile's 32-row blocks split evenly between the two row halves (a
-  // step lasts as long as its busiest wave): wave half wm takes blocks
-  // rb0 .. rb0 + nact - 1
-  const int nb = (tile.row_end - tile.row_begin + 31) >> 5;
-  const int rb0 = wm ? (nb + 1) >> 1 : 0;
-  const int nact = wm ? nb >> 1 : (nb + 1) >> 1;                        // active row blocks
   const int wrow0 = 32 * rb0;                                            // first tile row of this wave
 
   v16f acc[4][4];
@@ -883,6 +888,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a, int group) {
 
   auto main_loop = [&](auto nact_c, auto wnt_c) {
     constexpr int NACT = decltype(nact_c)::value;
+    constexpr int NA = 2 * NACT;                 // this wave's activation copies per step
     uint4 asg[4];               // grouped activation scales of this lane's rows
     uint32_t asr[2][4];         // A scale dwords (shifted by 8*g32) of the current / next step
     uint32_t bsd[2][2][2];      // B scale dwords [buffer][group 2wn+gi][half] (shifted by 8*(l32/16))
@@ -990,7 +996,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a, int group) {
       // (after the last step the reads below fetch a stale slot whose values
       // go unused: one code path keeps the accumulators in place)
       __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave is done reading slot st
-      PF_WAIT_VM(ncop(I + 2));                 // its copies of step st+1 have landed
+      PF_WAIT_VM(ncop(NA, I + 2));             // its copies of step st+1 have landed
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -1008,7 +1014,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a, int group) {
         if constexpr (k == 3) { read_b(s1, IntC<0>{}, IntC<2>{}); read_b(s1, IntC<0>{}, IntC<3>{}); }
         if constexpr (k == 4) read_a(s1, IntC<0>{}, IntC<2>{});
         if constexpr (k == 5) read_a(s1, IntC<0>{}, IntC<3>{});
-        if constexpr (k >= 6 && k <= 13) copy_a(st + 3, IntC<k - 6>{});
+        if constexpr (k >= 6 && k - 6 < NA) copy_a(st + 3, IntC<k - 6>{});
         if constexpr (k == 8) shift_scales(IntC<(I + 1) & 3>{}, IntC<B ^ 1>{});
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -1023,24 +1029,27 @@ __global__ void __launch_bounds__(256, 1) k_gemm_pf(FwdArgs a, int group) {
       // and 1 and the activations of steps 0-2
       static_for<0, 5>([&](auto mc) { copy_w(0, mc, IntC<1>{}, wnt_c); });
       static_for<0, 5>([&](auto mc) { copy_w(1, mc, IntC<0>{}, wnt_c); });
-      PF_WAIT_VM(10);                          // the row table (the oldest copy) has landed
+      PF_WAIT_VM(10);                          // this wave's row-table copy (the oldest) has landed
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();            // and every wave's: a wave looks up rows others copied
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
       set_act_sources();
       copy_w(0, IntC<5>{}, IntC<1>{}, wnt_c);
       copy_w(1, IntC<5>{}, IntC<0>{}, wnt_c);
-      static_for<0, 8>([&](auto qc) { copy_a(0, qc); });
-      static_for<0, 8>([&](auto qc) { copy_a(1, qc); });
-      static_for<0, 8>([&](auto qc) { copy_a(2, qc); });
-      PF_WAIT_VM(16);                          // step 0 (and 1 but its last activations) has landed
+      static_for<0, NA>([&](auto qc) { copy_a(0, qc); });
+      static_for<0, NA>([&](auto qc) { copy_a(1, qc); });
+      static_for<0, NA>([&](auto qc) { copy_a(2, qc); });
+      PF_WAIT_VM(2 * NA);                      // step 0 (and 1 but its last activations) has landed
     } else {
       set_act_sources();
-      static_for<0, 8>([&](auto qc) { copy_a(0, qc); });
+      static_for<0, NA>([&](auto qc) { copy_a(0, qc); });
       static_for<0, 6>([&](auto mc) { copy_w(0, mc, IntC<1>{}, wnt_c); });
-      static_for<0, 8>([&](auto qc) { copy_a(1, qc); });
+      static_for<0, NA>([&](auto qc) { copy_a(1, qc); });
       static_for<0, 6>([&](auto mc) { copy_w(1, mc, IntC<0>{}, wnt_c); });
-      static_for<0, 8>([&](auto qc) { copy_a(2, qc); });
-      PF_WAIT_VM(ncop(1) + 8);                 // step 0 has landed
+      static_for<0, NA>([&](auto qc) { copy_a(2, qc); });
+      PF_WAIT_VM(ncop(NA, 1) + NA);            // step 0 has landed
     }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
