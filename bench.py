@@ -411,12 +411,22 @@ def cpu_baseline(cfg, a16w4: bool = False):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    # about 10 s of oracle work where the workload allows: six tokens touch
-    # about 80 experts of the 896-expert layer (two took 3.5 s)
-    ntok = cfg.tokens if cfg.tokens <= 8 else (1 if cfg.tokens <= 16 else 6)
-    x = I.gen_x(cfg, layer=0)[:ntok]
     wr, b = I.gen_router_w(cfg, 0), I.gen_router_b(cfg)
     W = I.ExpertWeights(cfg)
+    if cfg.tokens <= 16:
+        ntok = cfg.tokens if cfg.tokens <= 8 else 1
+    else:
+        # about 10 s of oracle work: the first tokens until they touch 80
+        # experts (at most 32; about 0.12 s of float64 work per expert)
+        x32 = I.gen_x(cfg, layer=0)[:32]
+        ids32 = OM.topk_select(OM.router_logits(x32, wr, b), cfg.top_k)[0]
+        ntok, seen = len(ids32), set()
+        for t in range(len(ids32)):
+            seen.update(ids32[t].tolist())
+            if len(seen) >= 80:
+                ntok = t + 1
+                break
+    x = I.gen_x(cfg, layer=0)[:ntok]
     ids = OM.topk_select(OM.router_logits(x, wr, b), cfg.top_k)[0]
     touched = sorted(set(ids.reshape(-1).tolist()))
     mats = [W("routed", e) for e in touched] + [W("shared", s) for s in range(cfg.num_shared)]
