@@ -614,9 +614,10 @@ static hipError_t launch_stream(const FwdArgs& a, hipStream_t st) {
 //     rows' 16 bytes in registers for the group;
 //   * B scales, 1 KB: the step's packed scale dwords of the four groups (one
 //     byte per 16-row block).
-// Wave w copies rows 64w .. 64w+63 (eight 8-row copies; one wholly past the
-// tile's end is skipped), the packed group w of the weights and its scales,
-// and its rows' activation scales.
+// The two waves of a row half (w%2 == wm) copy the activation rows of that
+// half's 32-row blocks between them (8-row copies, alternating; two per
+// block), wave w the packed group w of the weights and its scales, and the
+// activation scales of rows 64w .. 64w+63.
 //
 // Step st (K = 128) runs in two K halves of 64 with two register sets:
 //   LDS reads of half 1 into set 1;   MFMAs of half 0 from set 0;
