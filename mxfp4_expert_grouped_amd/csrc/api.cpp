@@ -456,9 +456,8 @@ TailLayout tail_layout(int64_t T, int64_t latent, int64_t hidden, bool with_s) {
     off += (bytes + 255) / 256 * 256;
     return at;
   };
-  // rows per projection tile: the weight-streaming kernel for a few rows,
-  // the 256-row kernel from 24 rows on (as for an expert's rows in moe_forward)
-  L.bm = T >= 24 ? 256 : kDecodeMaxRows;
+  // rows per projection tile (tail_tile_rows)
+  L.bm = tail_tile_rows(T);
   L.codes = take(T * latent);
   L.scales = take(T * latent / 32);
   L.o16 = take(with_s ? T * hidden * 2 : 0);
@@ -469,7 +468,7 @@ TailLayout tail_layout(int64_t T, int64_t latent, int64_t hidden, bool with_s) {
   // fp32 partials: of the K slices of the few-row projection, or of the
   // K slices of few 256-row tiles
   const int64_t ks = T <= kTailGemvMaxT ? tail_gemv_slices(static_cast<int>(latent))
-                   : L.bm > kDecodeMaxRows ? tail_ksplit(T, latent, hidden) : 1;
+                   : L.bm > kDecodeMaxRows ? tail_ksplit(T, latent, hidden, L.bm) : 1;
   L.part = take(ks > 1 ? size_t(ks) * T * hidden * 4 : 0);
   L.total = off;
   return L;

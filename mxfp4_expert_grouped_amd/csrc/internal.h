@@ -99,34 +99,40 @@ inline int tail_gemv_slices(int latent) {
   return (ns + 4 * kTailGemvSteps - 1) / (4 * kTailGemvSteps);
 }
 
-// Launchers (kernels_*.hip).  Each returns hipSuccess or the launch error.
-// K slices of the LatentMoE tail's projection on 256-row tiles, when its
-// tiles x 256-column blocks alone would give fewer workgroups than the 256
-// CUs of the chip: the smallest divisor of latent/512 (at most 8) that
-// reaches 256 workgroups, else the largest.  Each slice adds one fp32
-// partial of the output, summed in order (with s) by the tail's reduction.
-inline int tail_ksplit(int64_t T, int64_t latent, int64_t hidden) {
+// Rows per tile of the decode (weight-streaming) kernels; larger tiles go to
+// the prefill kernels.
+constexpr int kDecodeMaxRows = 8;
+
+// Rows per tile of the LatentMoE tail's projection: the weight-streaming
+// kernel for a few rows; from 24 rows on the prefill kernel, on 64-row tiles
+// up to 512 rows (more tiles per column block, so fewer K slices and fp32
+// partials are needed to fill the chip) and 256-row tiles above.
+inline int tail_tile_rows(int64_t T) { return T < 24 ? kDecodeMaxRows : T <= 512 ? 64 : 256; }
+// K slices of the tail's projection on those tiles, when its tiles x
+// 256-column blocks alone would give fewer workgroups than three quarters of
+// the 256 CUs: the smallest divisor of latent/512 (at most 8) that reaches
+// 192 workgroups, else the largest.  Each slice adds one fp32 partial of the
+// output, summed in order (with s) by the tail's reduction.
+inline int tail_ksplit(int64_t T, int64_t latent, int64_t hidden, int64_t bm) {
   if (T < 24 || latent % 512 != 0) return 1;
-  const int64_t base = ((T + 255) / 256) * ((hidden + 255) / 256);
+  const int64_t base = ((T + bm - 1) / bm) * ((hidden + 255) / 256);
   const int64_t g = latent / 512;
   int best = 1;
   for (int d = 1; d <= 8 && d <= g; ++d) {
     if (g % d != 0) continue;
     best = d;
-    if (base * d >= 256) break;
+    if (base * d >= 192) break;
   }
   return best;
 }
 
+// Launchers (kernels_*.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_tail(const TailArgs& a, int num_cus, hipStream_t st);
 hipError_t launch_quantize(const void* src, int src_fp32, int64_t rows, int64_t cols, int64_t ld,
                            uint8_t* codes, uint8_t* scales, hipStream_t st);
+
 // Tokens up to which the per-expert GEMV router (with the x quantisation
 // fused) runs; above it, the bf16 MFMA router.
-// Rows per tile of the decode (weight-streaming) kernels; larger tiles go to
-// the prefill kernels.
-constexpr int kDecodeMaxRows = 8;
-
 constexpr int kRouterSmallMaxT = 32;
 inline bool router_small(int64_t T, int64_t d, int64_t E) { return T <= kRouterSmallMaxT && T * (d / 32) <= 32 * E; }
 

@@ -294,8 +294,8 @@ hipError_t launch_tail(const TailArgs& a, int num_cus, hipStream_t st) {
   f.wcanon = a.wcanon;
   f.num_cus = num_cus;
   f.max_tiles = (a.T + a.bm - 1) / a.bm;
-  // few 256-row tiles: K slices into fp32 partials, summed in order with s
-  const int ks = a.bm > kDecodeMaxRows ? tail_ksplit(a.T, a.latent, a.hidden) : 1;
+  // few tiles: K slices into fp32 partials, summed in order with s
+  const int ks = a.bm > kDecodeMaxRows ? tail_ksplit(a.T, a.latent, a.hidden, a.bm) : 1;
   if (ks > 1) {
     f.ksplit = ks;
     f.kpart = a.part;
